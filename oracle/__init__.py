@@ -1,0 +1,14 @@
+"""fp64 CPU oracle for the attention forward pass.
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, by the smoke check of the
+repository's graft entry point and by the benchmark's CPU-baseline leg, never
+by the product path.  It shares no code with the HIP package.
+"""
+from .attention import (  # noqa: F401
+    attention,
+    visible_mask,
+    block_summary,
+    merge_summaries,
+    finalize_summary,
+    streamed_attention,
+)

@@ -1,0 +1,490 @@
+"""Pins for the fp64 oracle: checks against what the pages and mathematics fix.
+
+Nothing here compares the oracle with itself.  The pins are: the glossary
+page's two worked examples with every printed intermediate (tests/golden),
+closed forms (uniform scores, causal running means, single visible key,
+dominant key), invariants (convex hull, shift and permutation invariance),
+scipy's softmax on the unmasked case, pure-Python brute force with exact
+summation and no max shift on tiny inputs, and equality of the plain
+definition with the streamed (m, l, a) recurrence.  The last block plants
+plausible mistakes (dropped scale, transposed operand, flipped causal
+direction, unmasked padding, unrescaled merge) and checks that a pin fails.
+"""
+import itertools
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import scipy.special
+
+import oracle
+
+GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "worked_examples.json")))
+
+
+def frac(x):
+    return x[0] / x[1]
+
+
+def logs(spec):
+    return [math.log(t) for t in spec["log_of"]]
+
+
+def as_bhnd(x):
+    """1-D sequence of scalars -> [1, 1, n, 1] fp64."""
+    return np.asarray(x, dtype=np.float64).reshape(1, 1, -1, 1)
+
+
+def scalar_row(scores, values, causal=False):
+    """One query whose scores are exactly `scores`: q = [1], k_j = s_j, scale 1."""
+    q = np.ones((1, 1, 1, 1))
+    k = as_bhnd(scores)
+    v = as_bhnd(values)
+    # a single query row against n keys: pad the query side to n rows and
+    # look at the last row (sees every key, also under the causal mask)
+    n = k.shape[2]
+    qq = np.ones((1, 1, n, 1))
+    o, lse = oracle.attention(qq, k, v, 1.0, causal=causal)
+    return o[0, 0, -1, 0], lse[0, 0, -1]
+
+
+# ---------------------------------------------------------------------------
+# Worked examples printed by the glossary page
+# ---------------------------------------------------------------------------
+
+def test_two_ways_direct_softmax():
+    ex = GOLD["example_two_ways"]
+    o, lse = scalar_row(logs(ex["scores"]), ex["values"])
+    assert o == pytest.approx(frac(ex["output"]), abs=1e-13)
+    assert lse == pytest.approx(math.log(ex["lse"]["log_of"]), abs=1e-13)
+    # weights (1, 2, 3) / 6
+    s = np.array(logs(ex["scores"]))
+    w = np.exp(s - s.max()) / np.exp(s - s.max()).sum()
+    assert np.allclose(w, [frac(x) for x in ex["softmax_weights"]], atol=1e-15)
+
+
+def test_two_ways_block_summaries_and_merge():
+    ex = GOLD["example_two_ways"]
+    s = logs(ex["scores"])
+    vals = ex["values"]
+    c = ex["split_after"]
+    A = oracle.block_summary(s[:c], vals[:c])
+    B = oracle.block_summary(s[c:], vals[c:])
+    assert A[0] == pytest.approx(math.log(ex["block_a"]["m"]["log_of"]), abs=1e-15)
+    assert A[1] == pytest.approx(frac(ex["block_a"]["l"]), abs=1e-15)
+    assert A[2][0] == pytest.approx(frac(ex["block_a"]["u"]), abs=1e-15)
+    assert B[0] == pytest.approx(math.log(ex["block_b"]["m"]["log_of"]), abs=1e-15)
+    assert B[1] == pytest.approx(frac(ex["block_b"]["l"]), abs=1e-15)
+    assert B[2][0] == pytest.approx(frac(ex["block_b"]["u"]), abs=1e-15)
+    # raising A's reference maximum to ln 3 multiplies its sums by 2/3
+    assert math.exp(A[0] - B[0]) == pytest.approx(frac(ex["rescale_a_to_common_max"]), abs=1e-15)
+    M = oracle.merge_summaries(A, B)
+    assert M[0] == pytest.approx(math.log(ex["merged"]["m"]["log_of"]), abs=1e-15)
+    assert M[1] == pytest.approx(frac(ex["merged"]["l"]), abs=1e-14)
+    assert M[2][0] == pytest.approx(frac(ex["merged"]["u"]), abs=1e-14)
+    o, lse = oracle.finalize_summary(M)
+    assert o[0] == pytest.approx(frac(ex["merged"]["o"]), abs=1e-14)
+    assert lse == pytest.approx(math.log(6.0), abs=1e-14)
+    # merge order does not matter
+    M2 = oracle.merge_summaries(B, A)
+    assert oracle.finalize_summary(M2)[0][0] == pytest.approx(17 / 6, abs=1e-14)
+    # adding the sums without the rescale gives the page's wrong 2.6
+    wrong = (A[2][0] + B[2][0]) / (A[1] + B[1])
+    assert wrong == pytest.approx(frac(ex["unrescaled_merge_wrong"]), abs=1e-14)
+    assert abs(wrong - 17 / 6) > 0.2
+
+
+def test_practice_example():
+    ex = GOLD["example_practice"]
+    s = logs(ex["scores"])
+    vals = ex["values"]
+    o, lse = scalar_row(s, vals)
+    assert o == pytest.approx(frac(ex["output"]), abs=1e-13)
+    assert lse == pytest.approx(math.log(ex["lse"]["log_of"]), abs=1e-13)
+    c = ex["split_after"]
+    A = oracle.block_summary(s[:c], vals[:c])
+    B = oracle.block_summary(s[c:], vals[c:])
+    oa, _ = oracle.finalize_summary(A)
+    ob, _ = oracle.finalize_summary(B)
+    assert oa[0] == pytest.approx(frac(ex["block_outputs"][0]), abs=1e-14)
+    assert ob[0] == pytest.approx(frac(ex["block_outputs"][1]), abs=1e-14)
+    # masses relative to the unshifted exponentials: l * exp(m)
+    assert A[1] * math.exp(A[0]) == pytest.approx(frac(ex["block_masses_unshifted"][0]), abs=1e-13)
+    assert B[1] * math.exp(B[0]) == pytest.approx(frac(ex["block_masses_unshifted"][1]), abs=1e-13)
+    M = oracle.merge_summaries(A, B)
+    assert M[0] == pytest.approx(math.log(3), abs=1e-15)
+    assert M[1] == pytest.approx(frac(ex["merged_at_common_max"]["l"]), abs=1e-14)
+    assert M[2][0] == pytest.approx(frac(ex["merged_at_common_max"]["u"]), abs=1e-13)
+    assert oracle.finalize_summary(M)[0][0] == pytest.approx(20 / 3, abs=1e-13)
+    avg = (oa[0] + ob[0]) / 2
+    assert avg == pytest.approx(frac(ex["simple_average_wrong"]), abs=1e-14)
+    assert abs(avg - 20 / 3) > 0.5
+
+
+def test_worked_examples_through_streamed_recurrence():
+    """The streamed recurrence, split after the second score, passes through
+    exactly the printed intermediate state and ends at 17/6."""
+    ex = GOLD["example_two_ways"]
+    s = logs(ex["scores"])
+    n = len(s)
+    q = np.ones((1, 1, n, 1))
+    trace = []
+    o, lse = oracle.streamed_attention(q, as_bhnd(s), as_bhnd(ex["values"]), 1.0,
+                                       block_q=n, block_k=ex["split_after"], trace=trace)
+    assert o[0, 0, -1, 0] == pytest.approx(17 / 6, abs=1e-14)
+    # after block A (last query row sees both of its keys)
+    _, _, m, ell, a = trace[0]
+    assert m[-1] == pytest.approx(math.log(2), abs=1e-15)
+    assert ell[-1] == pytest.approx(1.5, abs=1e-15)
+    assert a[-1, 0] == pytest.approx(2.5, abs=1e-15)
+    _, _, m, ell, a = trace[1]
+    assert m[-1] == pytest.approx(math.log(3), abs=1e-15)
+    assert ell[-1] == pytest.approx(2.0, abs=1e-14)
+    assert a[-1, 0] == pytest.approx(17 / 3, abs=1e-14)
+    ex2 = GOLD["example_practice"]
+    o2, _ = oracle.streamed_attention(q, as_bhnd(logs(ex2["scores"])), as_bhnd(ex2["values"]), 1.0,
+                                      block_q=n, block_k=2)
+    assert o2[0, 0, -1, 0] == pytest.approx(20 / 3, abs=1e-13)
+
+
+def test_score_tile_size_arithmetic():
+    g = GOLD["score_tile_size"]
+    assert g["block_q"] * g["block_k"] == g["entries"]
+    g = GOLD["materialised_score_matrix"]
+    pairs = g["B"] * g["H"] * g["N"] ** 2
+    assert abs(pairs - g["approx_pairs"]) / g["approx_pairs"] < 0.05
+    assert pairs * g["bytes_per_element"] / 2 ** 30 == pytest.approx(g["approx_gib"])
+
+
+# ---------------------------------------------------------------------------
+# Closed forms
+# ---------------------------------------------------------------------------
+
+def rand(shape, seed, scale=1.0):
+    return np.random.default_rng(seed).standard_normal(shape) * scale
+
+
+def test_uniform_scores_give_mean_of_values():
+    B, H, N, d = 2, 3, 17, 5
+    q = np.zeros((B, H, N, d))
+    k = rand((B, H, N, d), 1)
+    v = rand((B, H, N, d), 2)
+    o, lse = oracle.attention(q, k, v, 0.3)
+    assert np.allclose(o, v.mean(axis=2, keepdims=True), atol=1e-14)
+    assert np.allclose(lse, math.log(N), atol=1e-14)
+
+
+def test_uniform_scores_causal_running_mean():
+    B, H, N, d = 1, 2, 23, 4
+    q = np.zeros((B, H, N, d))
+    k = rand((B, H, N, d), 3)
+    v = rand((B, H, N, d), 4)
+    o, lse = oracle.attention(q, k, v, 0.125, causal=True)
+    run = np.cumsum(v, axis=2) / np.arange(1, N + 1)[None, None, :, None]
+    assert np.allclose(o, run, atol=1e-13)
+    assert np.allclose(lse, np.log(np.arange(1, N + 1))[None, None], atol=1e-13)
+
+
+def test_uniform_scores_key_length():
+    B, H, N, d = 4, 2, 19, 3
+    q = np.zeros((B, H, N, d))
+    k = rand((B, H, N, d), 5)
+    v = rand((B, H, N, d), 6)
+    key_len = np.array([0, 1, 7, 40], dtype=np.int32)  # 40 clamps to N
+    for causal in (False, True):
+        o, lse = oracle.attention(q, k, v, 0.5, causal=causal, key_len=key_len)
+        for b, L in enumerate(key_len):
+            L = min(int(L), N)
+            for i in range(N):
+                if i >= L:
+                    assert np.all(o[b, :, i] == 0.0)
+                    assert np.all(lse[b, :, i] == -np.inf)
+                    continue
+                hi = i + 1 if causal else L
+                assert np.allclose(o[b, :, i], v[b, :, :hi].mean(axis=1), atol=1e-13)
+                assert np.allclose(lse[b, :, i], math.log(hi), atol=1e-13)
+
+
+def test_single_visible_key():
+    B, H, N, d = 1, 2, 9, 6
+    q, k, v = rand((B, H, N, d), 7), rand((B, H, N, d), 8), rand((B, H, N, d), 9)
+    scale = 0.37
+    o, lse = oracle.attention(q, k, v, scale, causal=True)
+    # causal row 0 sees only key 0
+    assert np.allclose(o[:, :, 0], v[:, :, 0], atol=1e-15)
+    assert np.allclose(lse[:, :, 0], scale * np.einsum("bhd,bhd->bh", q[:, :, 0], k[:, :, 0]), atol=1e-14)
+    # key length 1: row 0 sees key 0, every other row is padding
+    o, lse = oracle.attention(q, k, v, scale, key_len=np.array([1]))
+    assert np.allclose(o[:, :, 0], v[:, :, 0], atol=1e-15)
+    assert np.all(o[:, :, 1:] == 0) and np.all(lse[:, :, 1:] == -np.inf)
+    # N = 1
+    o, lse = oracle.attention(q[:, :, :1], k[:, :, :1], v[:, :, :1], scale)
+    assert np.allclose(o[:, :, 0], v[:, :, 0], atol=1e-15)
+
+
+def test_dominant_key_selects_its_value():
+    """One score 60 above all others: O is that key's value to fp64 precision."""
+    B, H, N, d = 1, 2, 31, 4
+    rng = np.random.default_rng(10)
+    e = np.zeros(d)
+    e[1] = 1.0
+    q = np.broadcast_to(e, (B, H, N, d)).copy()
+    k = rng.standard_normal((B, H, N, d)) * 0.01
+    v = rng.standard_normal((B, H, N, d))
+    j = 29
+    k[:, :, j] = 60.0 * e
+    o, lse = oracle.attention(q, k, v, 1.0)
+    assert np.allclose(o, v[:, :, j:j + 1], atol=1e-15, rtol=0)
+    # exp(-59.9) corrections are far below fp64 resolution of 60
+    assert np.allclose(lse, 60.0, atol=1e-14, rtol=0)
+
+
+def test_large_scores_no_overflow():
+    """Scores of order 1e4 would overflow exp without the max shift."""
+    B, H, N, d = 1, 1, 16, 8
+    q = rand((B, H, N, d), 11, 100.0)
+    k = rand((B, H, N, d), 12, 100.0)
+    v = rand((B, H, N, d), 13)
+    o, lse = oracle.attention(q, k, v, 1.0)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+    s = q[0, 0] @ k[0, 0].T
+    assert np.allclose(lse[0, 0], s.max(axis=1) + np.log(np.exp(s - s.max(axis=1, keepdims=True)).sum(1)),
+                       rtol=1e-15, atol=1e-9)
+
+
+# ---------------------------------------------------------------------------
+# Invariants
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_convex_hull(causal):
+    B, H, N, d = 2, 2, 40, 8
+    q, k, v = rand((B, H, N, d), 14, 2.0), rand((B, H, N, d), 15), rand((B, H, N, d), 16)
+    key_len = np.array([40, 13])
+    o, _ = oracle.attention(q, k, v, 0.5, causal=causal, key_len=key_len)
+    for b in range(B):
+        L = int(key_len[b])
+        for i in range(L):
+            hi = i + 1 if causal else L
+            lo_v = v[b, :, :hi].min(axis=1)
+            hi_v = v[b, :, :hi].max(axis=1)
+            assert np.all(o[b, :, i] >= lo_v - 1e-13) and np.all(o[b, :, i] <= hi_v + 1e-13)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_shift_invariance(causal):
+    """K' = K + 1 w^T adds scale * (q_i . w) to every score of row i:
+    O is unchanged and LSE moves by that amount."""
+    B, H, N, d = 1, 2, 33, 8
+    q, k, v = rand((B, H, N, d), 17), rand((B, H, N, d), 18), rand((B, H, N, d), 19)
+    w = rand((d,), 20)
+    scale = 0.4
+    o1, l1 = oracle.attention(q, k, v, scale, causal=causal)
+    o2, l2 = oracle.attention(q, k + w, v, scale, causal=causal)
+    assert np.allclose(o1, o2, atol=1e-12)
+    assert np.allclose(l2 - l1, scale * (q @ w), atol=1e-12)
+
+
+def test_key_value_permutation_invariance():
+    B, H, N, d = 1, 2, 29, 6
+    q, k, v = rand((B, H, N, d), 21), rand((B, H, N, d), 22), rand((B, H, N, d), 23)
+    perm = np.random.default_rng(24).permutation(N)
+    o1, l1 = oracle.attention(q, k, v, 0.3)
+    o2, l2 = oracle.attention(q, k[:, :, perm], v[:, :, perm], 0.3)
+    assert np.allclose(o1, o2, atol=1e-13) and np.allclose(l1, l2, atol=1e-13)
+
+
+def test_rows_argument_matches_full():
+    B, H, N, d = 2, 3, 50, 4
+    q, k, v = rand((B, H, N, d), 25), rand((B, H, N, d), 26), rand((B, H, N, d), 27)
+    key_len = np.array([50, 21])
+    o, lse = oracle.attention(q, k, v, 0.2, causal=True, key_len=key_len)
+    rows = np.stack([np.sort(np.random.default_rng(28 + h).choice(N, 7, replace=False)) for h in range(H)])
+    o2, l2 = oracle.attention(q, k, v, 0.2, causal=True, key_len=key_len, rows=rows)
+    for h in range(H):
+        assert np.array_equal(o2[:, h], o[:, h, rows[h]])
+        assert np.array_equal(l2[:, h], lse[:, h, rows[h]])
+
+
+# ---------------------------------------------------------------------------
+# Library routine and brute force
+# ---------------------------------------------------------------------------
+
+def test_matches_scipy_softmax_unmasked():
+    B, H, N, d = 2, 2, 37, 16
+    q, k, v = rand((B, H, N, d), 29), rand((B, H, N, d), 30), rand((B, H, N, d), 31)
+    scale = 1 / 4
+    o, lse = oracle.attention(q, k, v, scale)
+    s = scale * q @ np.swapaxes(k, -1, -2)
+    ref = scipy.special.softmax(s, axis=-1) @ v
+    assert np.allclose(o, ref, atol=1e-14)
+    assert np.allclose(lse, scipy.special.logsumexp(s, axis=-1), atol=1e-13)
+
+
+def brute(q, k, v, scale, causal, L):
+    """Direct definition with exact summation and no max shift, pure Python.
+
+    q, k, v: nested lists [N][d]; returns (o [N][d], lse [N]).
+    """
+    N = len(q)
+    d = len(q[0])
+    dv = len(v[0])
+    O, LSE = [], []
+    for i in range(N):
+        keys = [j for j in range(N) if j < L and i < L and (not causal or j <= i)]
+        if not keys:
+            O.append([0.0] * dv)
+            LSE.append(-math.inf)
+            continue
+        e = {j: math.exp(scale * math.fsum(q[i][c] * k[j][c] for c in range(d))) for j in keys}
+        den = math.fsum(e.values())
+        O.append([math.fsum(e[j] * v[j][c] for j in keys) / den for c in range(dv)])
+        LSE.append(math.log(den))
+    return O, LSE
+
+
+@pytest.mark.parametrize("N,d", [(1, 1), (2, 3), (5, 2), (8, 4), (7, 3)])
+def test_brute_force_all_masks(N, d):
+    rng = np.random.default_rng(100 + N * 10 + d)
+    q = rng.standard_normal((1, 1, N, d))
+    k = rng.standard_normal((1, 1, N, d))
+    v = rng.standard_normal((1, 1, N, d + 1))  # value width differs from d
+    scale = 0.7
+    for causal, L in itertools.product((False, True), range(0, N + 2)):
+        o, lse = oracle.attention(q, k, v, scale, causal=causal, key_len=np.array([L]))
+        O, LSE = brute(q[0, 0].tolist(), k[0, 0].tolist(), v[0, 0].tolist(), scale, causal, min(L, N))
+        assert np.allclose(o[0, 0], np.array(O), atol=1e-13, rtol=0)
+        for a, b in zip(lse[0, 0], LSE):
+            if b == -math.inf:
+                assert a == -math.inf
+            else:
+                assert abs(a - b) < 1e-13
+
+
+def test_brute_force_exact_rationals():
+    """With scores ln(n) the weights are rational: check O exactly in Fractions."""
+    # q = 1 (d = 1), k_j = ln(w_j): weights proportional to w_j
+    wts = [1, 4, 2, 7, 3]
+    vals = [3, -1, 5, 2, 8]
+    N = len(wts)
+    q = np.ones((1, 1, N, 1))
+    k = as_bhnd([math.log(w) for w in wts])
+    v = as_bhnd(vals)
+    for causal in (False, True):
+        o, lse = oracle.attention(q, k, v, 1.0, causal=causal)
+        for i in range(N):
+            hi = i + 1 if causal else N
+            exact = Fraction(sum(w * x for w, x in zip(wts[:hi], vals[:hi])), sum(wts[:hi]))
+            assert o[0, 0, i, 0] == pytest.approx(float(exact), abs=1e-14)
+            assert lse[0, 0, i] == pytest.approx(math.log(sum(wts[:hi])), abs=1e-14)
+
+
+# ---------------------------------------------------------------------------
+# The streamed recurrence equals the plain definition
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("bq,bk", [(1, 1), (4, 3), (16, 16), (7, 64), (64, 5)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_streamed_equals_definition(bq, bk, causal):
+    B, H, N, d = 3, 2, 45, 8
+    rng = np.random.default_rng(200 + bq * 7 + bk)
+    q = rng.standard_normal((B, H, N, d)) * 3
+    k = rng.standard_normal((B, H, N, d))
+    v = rng.standard_normal((B, H, N, d))
+    key_len = np.array([45, 0, 11])  # full, empty, and ragged
+    o1, l1 = oracle.attention(q, k, v, 0.35, causal=causal, key_len=key_len)
+    o2, l2 = oracle.streamed_attention(q, k, v, 0.35, causal=causal, key_len=key_len,
+                                       block_q=bq, block_k=bk)
+    assert np.allclose(o1, o2, atol=1e-12, rtol=0)
+    fin = np.isfinite(l1)
+    assert np.array_equal(fin, np.isfinite(l2))
+    assert np.allclose(l1[fin], l2[fin], atol=1e-12)
+    assert np.all(o2[~fin] == 0)
+
+
+def test_streamed_dominant_key_in_last_block():
+    """A much larger score arriving in the last block forces a large rescale."""
+    B, H, N, d = 1, 1, 64, 4
+    rng = np.random.default_rng(300)
+    q = rng.standard_normal((B, H, N, d))
+    k = rng.standard_normal((B, H, N, d))
+    v = rng.standard_normal((B, H, N, d))
+    k[0, 0, N - 1] = 30.0 * q[0, 0].mean(axis=0) / np.linalg.norm(q[0, 0].mean(axis=0))
+    o1, l1 = oracle.attention(q, k, v, 1.0)
+    o2, l2 = oracle.streamed_attention(q, k, v, 1.0, block_q=16, block_k=8)
+    assert np.allclose(o1, o2, atol=1e-12) and np.allclose(l1, l2, atol=1e-12)
+
+
+def test_fully_masked_block_summary_merge():
+    A = oracle.block_summary([-math.inf, -math.inf], [1.0, 2.0])
+    assert A[0] == -math.inf and A[1] == 0.0 and A[2][0] == 0.0
+    B = oracle.block_summary([0.0, math.log(3)], [2.0, 6.0])
+    M = oracle.merge_summaries(A, B)
+    assert oracle.finalize_summary(M)[0][0] == pytest.approx(5.0, abs=1e-14)
+    E = oracle.merge_summaries(A, A)
+    o, lse = oracle.finalize_summary(E)
+    assert o[0] == 0.0 and lse == -math.inf
+
+
+# ---------------------------------------------------------------------------
+# Planted mistakes: each plausible error in the oracle fails some pin above.
+# The mistakes are planted by wrapping the oracle (never the HIP path).
+# ---------------------------------------------------------------------------
+
+def _pin_suite(attn):
+    """Returns the names of the pins that `attn` (same signature as
+    oracle.attention) fails."""
+    failed = []
+    ex = GOLD["example_two_ways"]
+    s = logs(ex["scores"])
+    n = len(s)
+    o, _ = attn(np.ones((1, 1, n, 1)), as_bhnd(s), as_bhnd(ex["values"]), 1.0)
+    if abs(o[0, 0, -1, 0] - 17 / 6) > 1e-12:
+        failed.append("two_ways")
+    B, H, N, d = 1, 1, 9, 3
+    rng = np.random.default_rng(0)
+    q = rng.standard_normal((B, H, N, d))
+    k = rng.standard_normal((B, H, N, d))
+    v = rng.standard_normal((B, H, N, d))
+    for causal, L in itertools.product((False, True), (N, 4)):
+        o, lse = attn(q, k, v, 0.6, causal=causal, key_len=np.array([L]))
+        O, LSE = brute(q[0, 0].tolist(), k[0, 0].tolist(), v[0, 0].tolist(), 0.6, causal, L)
+        if not np.allclose(o[0, 0], np.array(O), atol=1e-12):
+            failed.append(f"brute_{causal}_{L}")
+    return failed
+
+
+def test_pins_pass_on_oracle():
+    assert _pin_suite(oracle.attention) == []
+
+
+@pytest.mark.parametrize("mistake", ["dropped_scale", "transposed_qk", "flipped_causal",
+                                     "unmasked_padding_rows", "wrong_value_operand"])
+def test_planted_mistakes_are_caught(mistake):
+    def attn(q, k, v, scale, causal=False, key_len=None, rows=None):
+        if mistake == "dropped_scale":
+            return oracle.attention(q, k, v, 1.0, causal, key_len, rows)
+        if mistake == "transposed_qk":
+            return oracle.attention(k, q, v, scale, causal, key_len, rows)
+        if mistake == "flipped_causal":
+            # j >= i instead of j <= i: reverse the sequence on both sides
+            o, l = oracle.attention(q[:, :, ::-1], k[:, :, ::-1], v[:, :, ::-1], scale, causal,
+                                    None if key_len is None else key_len, rows)
+            return o[:, :, ::-1], l[:, :, ::-1]
+        if mistake == "unmasked_padding_rows":
+            o, l = oracle.attention(q, k, v, scale, causal, key_len, rows)
+            # padding rows computed as if they were ordinary rows
+            N = q.shape[2]
+            o2, l2 = oracle.attention(q, k, v, scale, causal,
+                                      None if key_len is None else np.full_like(key_len, N), rows)
+            L = N if key_len is None else int(key_len[0])
+            o[:, :, L:] = o2[:, :, L:]
+            return o, l
+        if mistake == "wrong_value_operand":
+            return oracle.attention(q, k, k, scale, causal, key_len, rows)
+        raise AssertionError(mistake)
+
+    assert _pin_suite(attn) != []
