@@ -1,0 +1,248 @@
+"""Throughput of the fused attention forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--no-cpu-baseline] [--no-naive]
+
+A step is one fa_forward call over the whole workload (every batch, head and
+query row), with Q, K, V already resident in device memory.  Default
+workload: 32 heads, N = 8192, d = 128, causal, bf16 (the shape the pages use
+for the 4 GiB score-matrix example).  Prints one JSON line.
+
+Throughput counts useful work only: 4*d flops per visible (query, key) pair
+(two products of 2*d flops each); the masked half of a causal problem is
+not counted.  `roofline` relates the fused kernel's average duration,
+measured with HIP events on the stream it is launched on, to the bf16 dense
+MFMA peak of MI355X.  `cpu_baseline` times the fp64 CPU oracle on a bounded
+sample of query rows of the same workload on this host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA, 2.4 GHz
+PEAK_F32_TFLOPS = 157.3     # MI355X fp32 matrix
+PEAK_HBM_GBS = 8000.0
+DEFAULT_WORKLOAD = "h32_n8192_d128_causal_bf16"
+KERNEL_SOURCES = ["fa_fwd_bf16.hip", "fa_fwd_f32.hip", "fa_device.hpp", "fa_internal.hpp"]
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "io_aware_exact_forward_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary,
+    if it was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    ent = rec.get(workload)
+    if not ent or ent.get("kernel_hash") != kernel_hash():
+        return None
+    return ent.get("hbm_bytes_per_launch")
+
+
+def to_device(inp, dev):
+    import numpy as np
+    import torch
+    if inp.wl.dtype == "bf16":
+        conv = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+    else:
+        conv = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    kl = None if inp.key_len is None else torch.from_numpy(inp.key_len).to(dev)
+    return conv(inp.q), conv(inp.k), conv(inp.v), kl
+
+
+def cpu_baseline(inp, wl, o_dev, lse_dev, target_s: float):
+    """Time the fp64 oracle on a seeded sample of query rows (all heads)."""
+    import numpy as np
+    import oracle
+    from io_aware_exact_forward_amd import workloads as W
+    B, H, N, d = inp.q.shape
+    qx, kx, vx = inp.exact("q"), inp.exact("k"), inp.exact("v")
+    # calibrate: one small chunk to estimate the per-row cost
+    rng = np.random.default_rng(4242)
+    probe = np.sort(rng.choice(N, min(N, 64), replace=False))
+    t0 = time.perf_counter()
+    oracle.attention(qx[:1, :1], kx[:1, :1], vx[:1, :1], wl.scale, causal=wl.causal,
+                     key_len=None if inp.key_len is None else inp.key_len[:1], rows=probe)
+    per_row = (time.perf_counter() - t0) / len(probe)
+    rows_per_head = int(max(8, min(N, target_s / max(per_row, 1e-9) / (B * H))))
+    rows = np.stack([np.sort(rng.choice(N, rows_per_head, replace=False)) for _ in range(H)])
+    t0 = time.perf_counter()
+    o_ref, lse_ref = oracle.attention(qx, kx, vx, wl.scale, causal=wl.causal, key_len=inp.key_len,
+                                      rows=rows)
+    dt = time.perf_counter() - t0
+    # useful flops in the sample: 4*d per visible pair
+    lens = np.full(B, N) if inp.key_len is None else np.clip(inp.key_len, 0, N)
+    pairs = 0
+    for b in range(B):
+        L = int(lens[b])
+        for h in range(H):
+            r = rows[h]
+            r = r[r < L]
+            pairs += int((r + 1).sum()) if wl.causal else len(r) * L
+    flops = 4.0 * d * pairs
+    # agreement of the device output on the sampled rows (context only)
+    og = np.stack([o_dev[:, h, rows[h]] for h in range(H)], axis=1)
+    err = float(np.nanmax(np.abs(og - o_ref))) if og.size else 0.0
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"{rows_per_head} seeded query rows per head x {B * H} (batch, head) pairs "
+                  f"({rows_per_head * B * H} rows of {B * H * N}); fp64 numpy, whole score rows "
+                  f"materialised; {dt:.1f} s",
+        "seconds": dt,
+        "host_threads_available": len(os.sched_getaffinity(0)),
+        "sample_rows_max_abs_err_vs_device": err,
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-naive", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the attention forward "
+              f"shards by (batch, head) with no communication, so there is no multi-GPU step "
+              f"to time here.", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import io_aware_exact_forward_amd as fa
+    from io_aware_exact_forward_amd import _lib
+    from io_aware_exact_forward_amd import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    if not os.path.exists(_lib.lib_path()):
+        from io_aware_exact_forward_amd import build as _b
+        _b.build()
+    fa.load()
+
+    wl = W.workload(args.workload)
+    inp = W.make_inputs(wl)
+    dev = torch.device("cuda:0")
+    q, k, v, kl = to_device(inp, dev)
+    B, H, N, d = wl.B, wl.H, wl.N, wl.d
+    out = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    pairs = W.valid_pairs(N, wl.causal, inp.key_len, B) * H
+    flops = 4.0 * d * pairs
+    esz = 2 if wl.dtype == "bf16" else 4
+    lens = [N] * B if inp.key_len is None else [max(0, min(int(x), N)) for x in inp.key_len]
+    compulsory = sum(3 * H * L * d * esz for L in lens) + B * H * N * d * esz + B * H * N * 4
+
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(args.warmup):
+        fa.forward(q, k, v, scale=wl.scale, causal=wl.causal, key_len=kl, out=out, lse=lse)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    t_wall = time.perf_counter()
+    start.record(stream)
+    for _ in range(args.steps):
+        fa.forward(q, k, v, scale=wl.scale, causal=wl.causal, key_len=kl, out=out, lse=lse)
+    end.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms = start.elapsed_time(end) / args.steps
+    tflops = flops / (ms * 1e-3) / 1e12
+    peak = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_F32_TFLOPS
+
+    result = {
+        "metric": "attention fwd TFLOP/s (bf16, 1 GPU) and % of MFMA peak; HBM bytes vs N*d bound",
+        "value": tflops,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": dict(wl.describe(), useful_flops=flops, compulsory_hbm_bytes=compulsory,
+                       parallelism="single GPU"),
+        "roofline": {
+            "bound": "mfma",
+            "achieved": tflops,
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": tflops / peak,
+            "traffic": stored_traffic(wl.name),
+            "kernel": "fa_fwd_bf16_kernel" if wl.dtype == "bf16" else "fa_fwd_f32_kernel",
+            "kernel_hash": kernel_hash(),
+        },
+        "wall_s_timed_region": t_wall,
+    }
+
+    if not args.no_naive:
+        need = fa.fa_naive_workspace_bytes(B, H, N, fa.FA_DTYPE_BF16 if wl.dtype == "bf16" else fa.FA_DTYPE_F32)
+        free = torch.cuda.mem_get_info(dev)[0]
+        if need < 0.8 * free:
+            ws = torch.empty(need, dtype=torch.uint8, device=dev)
+            fa.naive_forward(q, k, v, scale=wl.scale, causal=wl.causal, key_len=kl, workspace=ws)
+            torch.cuda.synchronize()
+            nsteps = 3
+            s0 = torch.cuda.Event(enable_timing=True)
+            s1 = torch.cuda.Event(enable_timing=True)
+            s0.record(stream)
+            for _ in range(nsteps):
+                fa.naive_forward(q, k, v, scale=wl.scale, causal=wl.causal, key_len=kl, workspace=ws)
+            s1.record(stream)
+            torch.cuda.synchronize()
+            nms = s0.elapsed_time(s1) / nsteps
+            result["naive_baseline"] = {"ms_per_step": nms, "tflops_useful": flops / (nms * 1e-3) / 1e12,
+                                        "workspace_bytes": need, "speedup_of_fused": nms / ms}
+            del ws
+            torch.cuda.empty_cache()
+
+    if not args.no_cpu_baseline:
+        o_host = out
+        if wl.dtype == "bf16":
+            o_np = W.bf16_decode(o_host.view(torch.int16).cpu().numpy().view(np.uint16))
+        else:
+            o_np = o_host.cpu().numpy().astype(np.float64)
+        result["cpu_baseline"] = cpu_baseline(inp, wl, o_np, lse.cpu().numpy(), args.cpu_seconds)
+
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

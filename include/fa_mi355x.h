@@ -1,0 +1,138 @@
+/*
+ * fa_mi355x.h -- C ABI of the MI355X (gfx950) exact attention forward.
+ *
+ * The operation is exact scaled dot-product attention with an additive mask,
+ *     O = softmax(scale * Q K^T + M) V,
+ * softmax taken over keys for each query row, as defined on the pages
+ * "FlashAttention: Exact Attention as an IO-Aware Streaming Computation"
+ * (section "Problem setting") and "FlashAttention" (glossary, section "Move
+ * less data", which adds the optional additive mask M).  Besides O the call
+ * writes one log-sum-exp per query row, the compact per-row normalisation
+ * record that "IO-aware exact attention" (section "Backward recomputation")
+ * keeps instead of the probability matrix.
+ *
+ * fa_forward computes it tile by tile with a running maximum, denominator and
+ * unnormalised numerator per query row ("FlashAttention: Exact Attention as
+ * an IO-Aware Streaming Computation", section "Mathematical structure";
+ * "IO-aware exact attention", section "One tiled forward-pass iteration"):
+ * no N x N score or probability matrix is ever written to device memory.
+ *
+ * fa_naive_forward computes the same result along the materialised dataflow
+ * the pages contrast it with ("IO-aware exact attention", section "Traffic in
+ * the materialized implementation"): S = scale Q K^T is written to device
+ * memory, a softmax pass reads S and writes P, and a third pass computes
+ * O = P V.  It exists to measure the N^2 traffic the fused kernel removes.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  Layout   q, k, v, o: [B, H, N, d] row-major, d innermost, contiguous.
+ *           lse: [B, H, N] float32, natural-log units.
+ *           key_len_mask: [B] int32 or NULL.
+ *  Dtypes   FA_DTYPE_BF16: q, k, v, o are bfloat16; arithmetic is bf16 matrix
+ *           products with fp32 accumulation and fp32 softmax state; the
+ *           probabilities enter the second product rounded to bf16
+ *           (nearest-even) and O is rounded to bf16 (nearest-even).
+ *           FA_DTYPE_F32: q, k, v, o are float32; everything is fp32.
+ *  Head dim d in {64, 128}.
+ *  Sizes    B, H, N >= 0.  If any is 0 there is nothing to do: the call
+ *           returns FA_OK without touching memory (pointers may be NULL).
+ *           B*H*N*d must be below 2^62 and the number of 128-row query tiles
+ *           times B*H below 2^31.
+ *  Mask M   causal != 0: key j is visible to query i only if j <= i.
+ *           key_len_mask != NULL: L_b = clamp(key_len_mask[b], 0, N); keys
+ *           j >= L_b are masked and query rows i >= L_b are padding.
+ *           A row with no visible key (only padding rows) gets O = 0 and
+ *           LSE = -inf; this is the explicit fully-masked handling the
+ *           glossary's section "Why a tile can be discarded" asks for.
+ *  Scale    used as given (any finite value; the usual choice is 1/sqrt(d)).
+ *  Memory   every pointer is device memory owned by the caller, on the
+ *           device current for the calling thread.  q, k, v, o must be
+ *           16-byte aligned; lse, key_len_mask 4-byte aligned.  o and lse
+ *           must not overlap q, k, v, key_len_mask or each other.  The
+ *           library keeps no per-call state and allocates no memory.
+ *  Stream   stream is a hipStream_t (NULL = the legacy default stream).
+ *           Work is enqueued asynchronously; the call returns once it is
+ *           enqueued.  A device fault surfaces at the caller's next
+ *           synchronisation on that stream.
+ *  Errors   arguments are validated on the host before any HIP call; a bad
+ *           argument returns a negative fa_status_t and writes nothing.  A
+ *           launch failure returns FA_ERR_HIP.  No C++ exception crosses
+ *           this interface.  Calls are thread-safe.
+ */
+#ifndef FA_MI355X_H
+#define FA_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FA_DTYPE_BF16 = 0,
+  FA_DTYPE_F32 = 1
+} fa_dtype_t;
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_NULL = -1,        /* a required pointer is NULL                       */
+  FA_ERR_SHAPE = -2,       /* B, H or N negative, or sizes overflow            */
+  FA_ERR_HEAD_DIM = -3,    /* d not in {64, 128}                               */
+  FA_ERR_DTYPE = -4,       /* dtype not an fa_dtype_t                          */
+  FA_ERR_ALIGN = -5,       /* a pointer is not aligned as required             */
+  FA_ERR_SCALE = -6,       /* scale is NaN or infinite                         */
+  FA_ERR_ALIAS = -7,       /* an output overlaps an input or the other output */
+  FA_ERR_WORKSPACE = -8,   /* naive path: workspace NULL or too small          */
+  FA_ERR_HIP = -9          /* the HIP runtime reported an error at launch      */
+} fa_status_t;
+
+/*
+ * Fused attention forward (the streamed tile-by-tile computation).
+ *   q, k, v      inputs [B, H, N, d] of `dtype`.
+ *   o            output [B, H, N, d] of `dtype`; every element is written.
+ *   lse          output [B, H, N] float32; every element is written:
+ *                LSE_i = ln sum_{visible j} exp(scale * q_i . k_j), or -inf.
+ *   scale        multiplies Q K^T before the mask is added.
+ *   causal       0 or non-zero, see the mask convention above.
+ *   key_len_mask device int32 [B] or NULL.
+ *   stream       hipStream_t to enqueue on.
+ * Returns FA_OK or a negative fa_status_t.
+ */
+int fa_forward(const void* q, const void* k, const void* v, void* o, float* lse,
+               int B, int H, int N, int d, float scale, int causal,
+               const int32_t* key_len_mask, int dtype, void* stream);
+
+/*
+ * Bytes of device workspace fa_naive_forward needs: the materialised score
+ * and probability matrices, B*H*N*N elements each, stored in `dtype`, each
+ * rounded up to 256 bytes.  Returns 0 for invalid arguments.
+ */
+size_t fa_naive_workspace_bytes(int B, int H, int N, int dtype);
+
+/*
+ * Materialised three-pass attention forward, same arguments and results as
+ * fa_forward plus a caller-owned device workspace of at least
+ * fa_naive_workspace_bytes(B, H, N, dtype) bytes (256-byte aligned).  The
+ * workspace must not overlap any other argument.  S and P are stored in
+ * `dtype` (bf16 for bf16 inputs), so results differ from fa_forward by the
+ * extra rounding of S.
+ */
+int fa_naive_forward(const void* q, const void* k, const void* v, void* o, float* lse,
+                     int B, int H, int N, int d, float scale, int causal,
+                     const int32_t* key_len_mask, int dtype,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char* fa_status_string(int status);
+
+/* ABI version of this header: (major << 16) | minor. */
+int fa_abi_version(void);
+
+#define FA_ABI_VERSION ((1 << 16) | 0)
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_MI355X_H */

@@ -1,0 +1,90 @@
+"""Exact attention forward for MI355X (gfx950): fused HIP kernels behind a C ABI.
+
+The C entry points (include/fa_mi355x.h) are exposed under their own names by
+``io_aware_exact_forward_amd._lib``; ``forward`` and ``naive_forward`` below
+are conveniences that take torch tensors (torch only provides device memory
+and the stream), allocate the outputs and call those entry points.  Nothing
+here computes attention itself.
+"""
+from __future__ import annotations
+
+import math
+
+from ._lib import (  # noqa: F401
+    FA_DTYPE_BF16,
+    FA_DTYPE_F32,
+    FAError,
+    check,
+    fa_abi_version,
+    fa_forward,
+    fa_naive_forward,
+    fa_naive_workspace_bytes,
+    fa_status_string,
+    load,
+)
+
+__all__ = [
+    "forward", "naive_forward", "fa_forward", "fa_naive_forward", "fa_naive_workspace_bytes",
+    "fa_status_string", "fa_abi_version", "FAError", "FA_DTYPE_BF16", "FA_DTYPE_F32",
+]
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return FA_DTYPE_BF16
+    if t.dtype == torch.float32:
+        return FA_DTYPE_F32
+    raise FAError(-4, f"unsupported dtype {t.dtype}")
+
+
+def _prepare(q, k, v, scale, key_len):
+    import torch
+    if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
+        raise FAError(-2, f"q, k, v must share the shape [B, H, N, d]; got {tuple(q.shape)}, "
+                          f"{tuple(k.shape)}, {tuple(v.shape)}")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise FAError(-4, "q, k, v must share one dtype")
+    for t in (q, k, v):
+        if not t.is_cuda or not t.is_contiguous():
+            raise FAError(-1, "q, k, v must be contiguous device tensors")
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    kl = 0
+    if key_len is not None:
+        if key_len.dtype != torch.int32 or not key_len.is_cuda or key_len.numel() != B:
+            raise FAError(-1, "key_len must be a device int32 tensor of B elements")
+        kl = key_len.contiguous().data_ptr()
+    return B, H, N, d, float(scale), kl
+
+
+def forward(q, k, v, *, scale=None, causal=False, key_len=None, out=None, lse=None):
+    """O, LSE = fa_forward(...) on torch's current stream of q's device."""
+    import torch
+    B, H, N, d, scale, kl = _prepare(q, k, v, scale, key_len)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    check(fa_forward(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                     B, H, N, d, scale, int(bool(causal)), kl, _dtype_code(q), stream))
+    return out, lse
+
+
+def naive_forward(q, k, v, *, scale=None, causal=False, key_len=None, workspace=None):
+    """Materialised three-pass baseline (S and P stored in device memory)."""
+    import torch
+    B, H, N, d, scale, kl = _prepare(q, k, v, scale, key_len)
+    dt = _dtype_code(q)
+    need = fa_naive_workspace_bytes(B, H, N, dt)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    out = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    check(fa_naive_forward(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                           lse.data_ptr(), B, H, N, d, scale, int(bool(causal)), kl, dt,
+                           workspace.data_ptr(), workspace.numel(), stream))
+    return out, lse

@@ -1,0 +1,108 @@
+"""ctypes binding of libfa_mi355x.so: the C entry points under their C names.
+
+Argument marshalling only.  Every call goes to the HIP library; there is no
+other implementation behind these names, and a missing library raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+from . import build as _build
+
+FA_DTYPE_BF16 = 0
+FA_DTYPE_F32 = 1
+
+_STATUS_NAMES = {
+    0: "FA_OK", -1: "FA_ERR_NULL", -2: "FA_ERR_SHAPE", -3: "FA_ERR_HEAD_DIM",
+    -4: "FA_ERR_DTYPE", -5: "FA_ERR_ALIGN", -6: "FA_ERR_SCALE", -7: "FA_ERR_ALIAS",
+    -8: "FA_ERR_WORKSPACE", -9: "FA_ERR_HIP",
+}
+
+# Every symbol the header declares, with its ctypes signature.
+_SIGNATURES = {
+    "fa_forward": (ctypes.c_int, [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float, ctypes.c_int,
+        ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]),
+    "fa_naive_workspace_bytes": (ctypes.c_size_t, [
+        ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int]),
+    "fa_naive_forward": (ctypes.c_int, [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float, ctypes.c_int,
+        ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "fa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "fa_abi_version": (ctypes.c_int, []),
+}
+
+_lock = threading.Lock()
+_lib = None
+
+
+class FAError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{_STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+def lib_path() -> str:
+    return _build.lib_path()
+
+
+def load() -> ctypes.CDLL:
+    """Load the built library (building it first only if none is built)."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        path = lib_path()
+        if not os.path.exists(path):
+            _build.build()
+        if not os.path.exists(path):
+            raise FAError(-9, f"HIP library {path} is missing and could not be built")
+        lib = ctypes.CDLL(path)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+        return lib
+
+
+def exported_symbols() -> list[str]:
+    return list(_SIGNATURES)
+
+
+def status_string(status: int) -> str:
+    return load().fa_status_string(int(status)).decode()
+
+
+def check(status: int) -> None:
+    if status != 0:
+        raise FAError(status, status_string(status))
+
+
+def fa_forward(q, k, v, o, lse, B, H, N, d, scale, causal, key_len_mask, dtype, stream) -> int:
+    """Raw C call; pointers and the stream are integers (0 = NULL)."""
+    return load().fa_forward(q, k, v, o, lse, B, H, N, d, scale, int(causal),
+                             key_len_mask or None, dtype, stream or None)
+
+
+def fa_naive_workspace_bytes(B, H, N, dtype) -> int:
+    return load().fa_naive_workspace_bytes(B, H, N, dtype)
+
+
+def fa_naive_forward(q, k, v, o, lse, B, H, N, d, scale, causal, key_len_mask, dtype,
+                     workspace, workspace_bytes, stream) -> int:
+    return load().fa_naive_forward(q, k, v, o, lse, B, H, N, d, scale, int(causal),
+                                   key_len_mask or None, dtype, workspace, workspace_bytes,
+                                   stream or None)
+
+
+def fa_status_string(status) -> str:
+    return status_string(status)
+
+
+def fa_abi_version() -> int:
+    return load().fa_abi_version()

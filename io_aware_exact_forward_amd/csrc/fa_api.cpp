@@ -1,0 +1,214 @@
+// C ABI of the attention forward library: argument validation, kernel
+// selection and launch.  Declared and documented in include/fa_mi355x.h.
+#include "fa_mi355x.h"
+
+#include <hip/hip_runtime.h>
+#include <rocblas/rocblas.h>
+
+#include <climits>
+#include <cmath>
+#include <cstdint>
+#include <mutex>
+
+#include "fa_internal.hpp"
+
+namespace {
+
+constexpr int64_t kMaxElems = int64_t(1) << 62;
+
+struct Shape {
+  int64_t elems = 0;  // B*H*N*d
+  int64_t rows = 0;   // B*H*N
+  int esz = 0;        // bytes per q/k/v/o element
+};
+
+bool is_aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+bool overlaps(const void* a, int64_t na, const void* b, int64_t nb) {
+  if (!a || !b || na <= 0 || nb <= 0) return false;
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+  return a0 < b0 + static_cast<uintptr_t>(nb) && b0 < a0 + static_cast<uintptr_t>(na);
+}
+
+// Checks that do not look at pointers.  Sets *empty when there is no work.
+int check_scalars(int B, int H, int N, int d, float scale, int dtype, Shape* s, bool* empty) {
+  if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_F32) return FA_ERR_DTYPE;
+  if (d != 64 && d != 128) return FA_ERR_HEAD_DIM;
+  if (B < 0 || H < 0 || N < 0) return FA_ERR_SHAPE;
+  if (!std::isfinite(scale)) return FA_ERR_SCALE;
+  const double c = std::fabs(static_cast<double>(scale)) * 1.4426950408889634;
+  if (!std::isfinite(static_cast<float>(c))) return FA_ERR_SCALE;
+  *empty = (B == 0 || H == 0 || N == 0);
+  if (*empty) return FA_OK;
+  const int64_t bh = int64_t(B) * H;
+  if (bh > INT_MAX) return FA_ERR_SHAPE;
+  const int64_t rows = bh * N;
+  if (rows > kMaxElems / d) return FA_ERR_SHAPE;
+  const int64_t qtiles = (int64_t(N) + fa::kQueryTile - 1) / fa::kQueryTile;
+  if (qtiles * bh > INT_MAX) return FA_ERR_SHAPE;
+  s->rows = rows;
+  s->elems = rows * d;
+  s->esz = dtype == FA_DTYPE_BF16 ? 2 : 4;
+  return FA_OK;
+}
+
+int check_pointers(const void* q, const void* k, const void* v, void* o, float* lse,
+                   const int32_t* key_len, int B, const Shape& s) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  if (!is_aligned(q, 16) || !is_aligned(k, 16) || !is_aligned(v, 16) || !is_aligned(o, 16))
+    return FA_ERR_ALIGN;
+  if (!is_aligned(lse, 4) || (key_len && !is_aligned(key_len, 4))) return FA_ERR_ALIGN;
+  const int64_t nb = s.elems * s.esz;
+  const int64_t nl = s.rows * 4;
+  const int64_t nk = key_len ? int64_t(B) * 4 : 0;
+  for (const void* in : {q, k, v}) {
+    if (overlaps(o, nb, in, nb) || overlaps(lse, nl, in, nb)) return FA_ERR_ALIAS;
+  }
+  if (overlaps(o, nb, lse, nl) || overlaps(o, nb, key_len, nk) || overlaps(lse, nl, key_len, nk))
+    return FA_ERR_ALIAS;
+  return FA_OK;
+}
+
+fa::FwdParams make_params(const void* q, const void* k, const void* v, void* o, float* lse,
+                          int B, int H, int N, float scale, const int32_t* key_len, int dtype) {
+  fa::FwdParams p{};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  p.key_len = key_len;
+  p.B = B;
+  p.H = H;
+  p.N = N;
+  p.n_qtiles = (N + fa::kQueryTile - 1) / fa::kQueryTile;
+  // exp(x) = exp2(x * log2 e): the kernels keep scores in log2 units.
+  p.c = static_cast<float>(std::fabs(static_cast<double>(scale)) * 1.4426950408889634);
+  // A negative scale is applied by negating Q (exact) and using |scale|.
+  p.q_sign = std::signbit(scale) && scale != 0.f
+                 ? (dtype == FA_DTYPE_BF16 ? 0x80008000u : 0x80000000u)
+                 : 0u;
+  return p;
+}
+
+size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// One rocBLAS handle per device for the materialised path's two products.
+std::mutex g_blas_mu;
+rocblas_handle g_blas[64] = {};
+
+}  // namespace
+
+extern "C" int fa_forward(const void* q, const void* k, const void* v, void* o, float* lse,
+                          int B, int H, int N, int d, float scale, int causal,
+                          const int32_t* key_len_mask, int dtype, void* stream) {
+  Shape s;
+  bool empty = false;
+  int st = check_scalars(B, H, N, d, scale, dtype, &s, &empty);
+  if (st != FA_OK || empty) return st;
+  st = check_pointers(q, k, v, o, lse, key_len_mask, B, s);
+  if (st != FA_OK) return st;
+  const fa::FwdParams p = make_params(q, k, v, o, lse, B, H, N, scale, key_len_mask, dtype);
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  const hipError_t e = dtype == FA_DTYPE_BF16 ? fa::launch_fwd_bf16(p, d, causal != 0, hs)
+                                              : fa::launch_fwd_f32(p, d, causal != 0, hs);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+extern "C" size_t fa_naive_workspace_bytes(int B, int H, int N, int dtype) {
+  Shape s;
+  bool empty = false;
+  if (check_scalars(B, H, N, 64, 1.f, dtype, &s, &empty) != FA_OK || empty) return 0;
+  const size_t esz = dtype == FA_DTYPE_BF16 ? 2 : 4;
+  const size_t mat = size_t(B) * size_t(H) * size_t(N) * size_t(N) * esz;
+  return 2 * round256(mat);
+}
+
+extern "C" int fa_naive_forward(const void* q, const void* k, const void* v, void* o, float* lse,
+                                int B, int H, int N, int d, float scale, int causal,
+                                const int32_t* key_len_mask, int dtype, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  Shape s;
+  bool empty = false;
+  int st = check_scalars(B, H, N, d, scale, dtype, &s, &empty);
+  if (st != FA_OK || empty) return st;
+  st = check_pointers(q, k, v, o, lse, key_len_mask, B, s);
+  if (st != FA_OK) return st;
+  const size_t need = fa_naive_workspace_bytes(B, H, N, dtype);
+  if (!workspace || workspace_bytes < need || !is_aligned(workspace, 256)) return FA_ERR_WORKSPACE;
+  {
+    const int64_t nb = s.elems * s.esz, nw = static_cast<int64_t>(need);
+    if (overlaps(workspace, nw, q, nb) || overlaps(workspace, nw, k, nb) ||
+        overlaps(workspace, nw, v, nb) || overlaps(workspace, nw, o, nb) ||
+        overlaps(workspace, nw, lse, s.rows * 4) ||
+        overlaps(workspace, nw, key_len_mask, key_len_mask ? int64_t(B) * 4 : 0))
+      return FA_ERR_ALIAS;
+  }
+  if (int64_t(N) * N > (int64_t(1) << 62) / (int64_t(B) * H)) return FA_ERR_SHAPE;
+
+  const bool bf16 = dtype == FA_DTYPE_BF16;
+  const size_t mat = need / 2;
+  void* smat = workspace;
+  void* pmat = static_cast<char*>(workspace) + mat;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return FA_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_blas_mu);
+  if (!g_blas[dev] && rocblas_create_handle(&g_blas[dev]) != rocblas_status_success) {
+    g_blas[dev] = nullptr;
+    return FA_ERR_HIP;
+  }
+  rocblas_handle hb = g_blas[dev];
+  if (rocblas_set_stream(hb, hs) != rocblas_status_success) return FA_ERR_HIP;
+  const rocblas_datatype t = bf16 ? rocblas_datatype_bf16_r : rocblas_datatype_f32_r;
+  const float alpha_s = scale, one = 1.f, zero = 0.f;
+  const int bh = B * H;
+  const rocblas_stride snd = int64_t(N) * d, snn = int64_t(N) * N;
+
+  // Pass 1: S = scale * Q K^T for every (b, h).  Column-major view: the
+  // row-major [N, N] S is S^T = K Q^T with K^T, Q^T stored as [d, N].
+  rocblas_status bs = rocblas_gemm_strided_batched_ex(
+      hb, rocblas_operation_transpose, rocblas_operation_none, N, N, d, &alpha_s, k, t, d, snd,
+      q, t, d, snd, &zero, smat, t, N, snn, smat, t, N, snn, bh, rocblas_datatype_f32_r,
+      rocblas_gemm_algo_standard, 0, 0);
+  if (bs != rocblas_status_success) return FA_ERR_HIP;
+
+  // Pass 2: P = softmax(S + M) row by row, plus LSE.
+  fa::NaiveSoftmaxParams sp{};
+  sp.s = smat;
+  sp.p = pmat;
+  sp.lse = lse;
+  sp.key_len = key_len_mask;
+  sp.B = B;
+  sp.H = H;
+  sp.N = N;
+  sp.causal = causal != 0;
+  if (fa::launch_naive_softmax(sp, bf16, hs) != hipSuccess) return FA_ERR_HIP;
+
+  // Pass 3: O = P V.  Column-major: O^T [d, N] = V^T [d, N] * P^T [N, N].
+  bs = rocblas_gemm_strided_batched_ex(
+      hb, rocblas_operation_none, rocblas_operation_none, d, N, N, &one, v, t, d, snd, pmat, t, N,
+      snn, &zero, o, t, d, snd, o, t, d, snd, bh, rocblas_datatype_f32_r,
+      rocblas_gemm_algo_standard, 0, 0);
+  if (bs != rocblas_status_success) return FA_ERR_HIP;
+  return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+extern "C" const char* fa_status_string(int status) {
+  switch (status) {
+    case FA_OK: return "ok";
+    case FA_ERR_NULL: return "a required pointer is NULL";
+    case FA_ERR_SHAPE: return "B, H or N is negative or the sizes overflow";
+    case FA_ERR_HEAD_DIM: return "head dimension must be 64 or 128";
+    case FA_ERR_DTYPE: return "dtype must be FA_DTYPE_BF16 or FA_DTYPE_F32";
+    case FA_ERR_ALIGN: return "a pointer is misaligned (q, k, v, o: 16 bytes; lse, key_len: 4)";
+    case FA_ERR_SCALE: return "scale must be finite";
+    case FA_ERR_ALIAS: return "an output overlaps an input or another output";
+    case FA_ERR_WORKSPACE: return "workspace is NULL, misaligned or too small";
+    case FA_ERR_HIP: return "the HIP runtime reported an error";
+    default: return "unknown status";
+  }
+}
+
+extern "C" int fa_abi_version(void) { return FA_ABI_VERSION; }

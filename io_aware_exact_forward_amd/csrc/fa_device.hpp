@@ -1,0 +1,64 @@
+// Device-side helpers shared by the gfx950 attention kernels: vector types,
+// the 32x32 MFMA wrappers, wave-half exchanges and bf16 packing.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInf = -__builtin_huge_valf();
+
+// D(32x32, fp32) += A(32x16, bf16) * B(16x32, bf16).
+// Operand layout on a 64-lane wave: lane l holds row (A) / column (B)
+// l % 32 and eight consecutive k values starting at 8 * (l / 32).
+// Accumulator layout: lane l holds column l % 32; register r holds row
+// 8 * (r / 4) + 4 * (l / 32) + r % 4.
+__device__ __forceinline__ f32x16 mfma_32x32x16_bf16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// D(32x32, fp32) += A(32x2, fp32) * B(2x32, fp32); lane l holds k = l / 32.
+__device__ __forceinline__ f32x16 mfma_32x32x2_f32(float a, float b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+// Row of the 32x32 accumulator held by register r of a lane in half h.
+__device__ __forceinline__ constexpr int acc_row(int r, int h) {
+  return 8 * (r >> 2) + 4 * h + (r & 3);
+}
+
+// Combine a value with the one held by the lane 32 apart (the other half of
+// the wave).  v_permlane32_swap exchanges the two halves between a pair of
+// registers; applying it to two copies of x leaves x of lane l%32 in one
+// result and x of lane 32 + l%32 in the other, in every lane.
+__device__ __forceinline__ float halves_max(float x) {
+  uint32_t u = __builtin_bit_cast(uint32_t, x);
+  auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1]));
+}
+
+__device__ __forceinline__ float halves_sum(float x) {
+  uint32_t u = __builtin_bit_cast(uint32_t, x);
+  auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
+}
+
+// Two fp32 -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2 v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+}  // namespace fa

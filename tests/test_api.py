@@ -1,0 +1,134 @@
+"""Host-side checks of the C ABI: the library loads, exports every declared
+symbol, and rejects bad arguments before any HIP call.
+
+None of these calls launches work: every argument set below fails host
+validation (or is empty), so they run on a machine without a GPU.
+"""
+import os
+import re
+
+import pytest
+
+import io_aware_exact_forward_amd as fa
+from io_aware_exact_forward_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa_mi355x.h")
+
+OK, NULL, SHAPE, HEAD_DIM, DTYPE, ALIGN, SCALE, ALIAS, WORKSPACE, HIP = 0, -1, -2, -3, -4, -5, -6, -7, -8, -9
+BF16, F32 = fa.FA_DTYPE_BF16, fa.FA_DTYPE_F32
+
+# Fake, aligned, non-overlapping "device" addresses: never dereferenced,
+# because every call below fails validation first.
+A = 1 << 40
+Q, K, V, O, L, KL, WS = (A + i * (1 << 34) for i in range(7))
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\**(fa_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_expected_entry_points():
+    assert declared_functions() == sorted(
+        ["fa_forward", "fa_naive_workspace_bytes", "fa_naive_forward", "fa_status_string",
+         "fa_abi_version"])
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    lib = fa.load()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert set(_lib.exported_symbols()) == set(declared_functions())
+    assert fa.fa_abi_version() == (1 << 16)
+
+
+def test_status_strings():
+    for st in (OK, NULL, SHAPE, HEAD_DIM, DTYPE, ALIGN, SCALE, ALIAS, WORKSPACE, HIP):
+        s = fa.fa_status_string(st)
+        assert isinstance(s, str) and s
+    assert fa.fa_status_string(12345) == "unknown status"
+
+
+def call(q=Q, k=K, v=V, o=O, lse=L, B=1, H=2, N=64, d=64, scale=0.125, causal=0, kl=0,
+         dtype=BF16, stream=0):
+    return fa.fa_forward(q, k, v, o, lse, B, H, N, d, scale, causal, kl, dtype, stream)
+
+
+def test_bad_dtype_and_head_dim():
+    assert call(dtype=2) == DTYPE
+    assert call(dtype=-1) == DTYPE
+    for d in (0, 32, 96, 256, -64):
+        assert call(d=d) == HEAD_DIM
+        assert call(d=d, dtype=F32) == HEAD_DIM
+
+
+def test_bad_shapes():
+    assert call(B=-1) == SHAPE
+    assert call(H=-1) == SHAPE
+    assert call(N=-5) == SHAPE
+    # B*H*N*d beyond 2^62 elements
+    assert call(B=2 ** 31 - 1, H=2 ** 31 - 1, N=2 ** 31 - 1) == SHAPE
+
+
+def test_bad_scale():
+    for s in (float("nan"), float("inf"), -float("inf"), 3e38):
+        assert call(scale=s) == SCALE
+
+
+def test_empty_problem_is_a_no_op():
+    # nothing to do: returns OK without touching the (NULL) pointers
+    for B, H, N in ((0, 2, 64), (1, 0, 64), (1, 2, 0)):
+        assert call(q=0, k=0, v=0, o=0, lse=0, B=B, H=H, N=N) == OK
+        assert fa.fa_naive_forward(0, 0, 0, 0, 0, B, H, N, 64, 1.0, 0, 0, BF16, 0, 0, 0) == OK
+
+
+def test_null_pointers():
+    for field in ("q", "k", "v", "o", "lse"):
+        assert call(**{field: 0}) == NULL
+
+
+def test_misaligned_pointers():
+    for field in ("q", "k", "v", "o"):
+        assert call(**{field: locals_default(field) + 8}) == ALIGN
+    assert call(lse=L + 2) == ALIGN
+    assert call(kl=KL + 1) == ALIGN
+
+
+def locals_default(field):
+    return {"q": Q, "k": K, "v": V, "o": O, "lse": L}[field]
+
+
+def test_aliasing_outputs():
+    assert call(o=Q) == ALIAS
+    assert call(o=V + 64) == ALIAS          # partial overlap
+    assert call(lse=K) == ALIAS
+    assert call(lse=O + 1024) == ALIAS
+    assert call(kl=O + 16) == ALIAS
+    # inputs may alias each other (self-attention on one buffer)
+    # -> validation passes; not called here because it would launch
+
+
+def test_naive_workspace_size():
+    # S and P, B*H*N*N each, in the input dtype
+    assert fa.fa_naive_workspace_bytes(1, 32, 8192, BF16) == 2 * 32 * 8192 * 8192 * 2
+    assert fa.fa_naive_workspace_bytes(1, 1, 3, F32) == 2 * 256
+    assert fa.fa_naive_workspace_bytes(1, 1, 3, 7) == 0
+    assert fa.fa_naive_workspace_bytes(-1, 1, 3, BF16) == 0
+
+
+def test_naive_workspace_errors():
+    need = fa.fa_naive_workspace_bytes(1, 2, 64, BF16)
+    args = (Q, K, V, O, L, 1, 2, 64, 64, 0.125, 0, 0, BF16)
+    assert fa.fa_naive_forward(*args, 0, need, 0) == WORKSPACE
+    assert fa.fa_naive_forward(*args, WS, need - 1, 0) == WORKSPACE
+    assert fa.fa_naive_forward(*args, WS + 16, need, 0) == WORKSPACE
+    assert fa.fa_naive_forward(*args, Q, need, 0) == ALIAS
+
+
+def test_python_wrapper_rejects_host_tensors():
+    import torch
+    x = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
+    with pytest.raises(fa.FAError):
+        fa.forward(x, x, x)
