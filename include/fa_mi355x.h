@@ -36,8 +36,9 @@
  *  Head dim d in {64, 128}.
  *  Sizes    B, H, N >= 0.  If any is 0 there is nothing to do: the call
  *           returns FA_OK without touching memory (pointers may be NULL).
- *           B*H*N*d must be below 2^62 and the number of 128-row query tiles
- *           times B*H below 2^31.
+ *           B*H*N*d must be below 2^62, the number of 128-row query tiles
+ *           times B*H below 2^31, and one (batch, head) slice of q
+ *           (N*d elements) at most 2^31 - 1 bytes.
  *  Mask M   causal != 0: key j is visible to query i only if j <= i.
  *           key_len_mask != NULL: L_b = clamp(key_len_mask[b], 0, N); keys
  *           j >= L_b are masked and query rows i >= L_b are padding.

@@ -46,6 +46,8 @@ int check_scalars(int B, int H, int N, int d, float scale, int dtype, Shape* s, 
   if (rows > kMaxElems / d) return FA_ERR_SHAPE;
   const int64_t qtiles = (int64_t(N) + fa::kQueryTile - 1) / fa::kQueryTile;
   if (qtiles * bh > INT_MAX) return FA_ERR_SHAPE;
+  // byte offsets within one (batch, head) slice are 32-bit in the kernels
+  if (int64_t(N) * d * (dtype == FA_DTYPE_BF16 ? 2 : 4) > INT_MAX) return FA_ERR_SHAPE;
   s->rows = rows;
   s->elems = rows * d;
   s->esz = dtype == FA_DTYPE_BF16 ? 2 : 4;

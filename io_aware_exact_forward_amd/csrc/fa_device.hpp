@@ -8,6 +8,7 @@
 namespace fa {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -60,5 +61,29 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+// 16 bytes per lane from global memory straight into LDS (buffer_load ...
+// lds): lane l of the wave writes lds_base + 16*l.  The source is the raw
+// buffer [base, base + nbytes); a lane whose offset lies past nbytes reads
+// zeros, which are written to LDS like any other data.  The resource is built
+// here, in a device-only helper, so that kernels using it keep a host stub.
+__device__ __forceinline__ void load_lds_16(const void* base, uint32_t nbytes, void* lds_base,
+                                            uint32_t offset) {
+  const __amdgpu_buffer_rsrc_t rsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)nbytes, 0x00020000);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)lds_base, 16, offset, 0, 0, 0);
+}
+
+// Transpose read of 4 bf16 (ds_read_b64_tr_b16).  Within each group of 16
+// lanes, lane r supplies an 8-byte address; lane i receives element i % 4 of
+// the chunks addressed by lanes i/4, i/4 + 4, i/4 + 8 and i/4 + 12, in that
+// order.  With lane r pointing at row r/4, columns 4*(r%4) .. +3 of a
+// 4 x 16 block, lane i therefore receives column i of rows 0..3.
+__device__ __forceinline__ bf16x4 lds_read_tr16(const void* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p);
+}
 
 }  // namespace fa

@@ -8,16 +8,31 @@
 // iteration").  Score tiles live only in registers; only O and the per-row
 // log-sum-exp are written.
 //
-// Work split: 4 waves x 32 query rows.  Each wave computes the transposed
-// score tile S^T = K Q^T on 32x32x16 bf16 MFMA so that every lane holds one
-// query row's scores (column l % 32 of the accumulator); row maxima and sums
-// are then in-lane reductions plus one exchange between the two wave halves.
-// The probabilities are packed to bf16 in place and are already in the
-// B-operand layout of the second product O^T = V^T P^T, provided V^T is laid
-// out in LDS with the key order the accumulator rows use (bits 2 and 3 of
-// the key index swapped within each group of 16).  O^T keeps one query row
-// per lane as well, so the exp2(m_old - m_new) rescale is one multiply per
+// Data movement.  K and V tiles go from HBM straight into LDS with buffer
+// loads (no register staging).  The buffer range is the sequence's valid
+// keys, so rows past the end arrive as zeros.  Both tiles are row-major
+// [key][dim] with the 16-byte chunks of each row permuted by an XOR of the
+// row index, which makes the fragment reads below free of bank conflicts.
+//
+// Products.  Each wave computes the transposed score tile S^T = K Q^T on
+// 32x32x16 bf16 MFMA (K fragments from LDS, Q fragments resident in
+// registers), so that each lane holds the scores of one query row: row max
+// and row sum are in-lane reductions plus one exchange between the two wave
+// halves.  The probabilities are packed to bf16 in place; that packing is
+// already the B operand of O^T = V^T P^T.  The matching V^T operand comes from
+// the row-major V tile through transpose reads (ds_read_b64_tr_b16), which
+// hand each lane one head-dim column across four consecutive keys.  O^T keeps
+// one query row per lane, so rescaling the numerator is one multiply per
 // register.
+//
+// Reference maximum.  Scores are exponentiated against a per-row reference
+// value.  It is raised to the running maximum only when some row's block
+// maximum exceeds it by more than kRescaleSlack (log2 units); otherwise the
+// old reference stays and exponentials may reach 2^kRescaleSlack.  The
+// denominator and numerator always share the reference, so o = a / l is
+// unchanged: this is the glossary page's observation ("Why a tile can be
+// discarded") that any common reference maximum preserves the exponential
+// sums, and it skips most rescales of the accumulator.
 //
 // Causal tiles run heaviest first; consecutive workgroups cycle over
 // (batch, head) so all tiles of a head land on one XCD when B*H is a
@@ -28,32 +43,43 @@
 namespace fa {
 namespace {
 
+constexpr float kRescaleSlack = 8.0f;
+
 template <int D>
 struct Bf16Cfg {
   static constexpr int BQ = kQueryTile;          // query rows per workgroup
   static constexpr int BK = D == 128 ? 64 : 128; // keys per streamed tile
-  static constexpr int KS = D + 8;               // K row stride in LDS (elements)
-  static constexpr int VS = BK + 8;              // V^T row stride in LDS (elements)
-  static constexpr int K_ELEMS = BK * KS;
-  static constexpr int V_ELEMS = D * VS;
-  static constexpr int STAGE = K_ELEMS + V_ELEMS;  // one K tile + one V^T tile
-  static constexpr int DCH = D / 8;              // 16-byte chunks per row
-  static constexpr int K_LOADS = BK * DCH / 256; // 16-byte K loads per thread
+  static constexpr int ROW_BYTES = D * 2;
+  static constexpr int CPR = D / 8;              // 16-byte chunks per row
+  static constexpr int TILE_BYTES = BK * ROW_BYTES;  // one K or V tile (16 KiB)
+  static constexpr int STAGE_BYTES = 2 * TILE_BYTES; // K tile + V tile
+  static constexpr int LOADS = TILE_BYTES / 1024 / 4; // 1 KiB loads per wave per tile
   static constexpr int NB = BK / 32;             // 32-key blocks per tile
   static constexpr int ND = D / 32;              // 32-wide slices of the head dim
-  static_assert(K_LOADS * 256 == BK * DCH, "K tile must split evenly over 256 threads");
-  static_assert((BK / 4) * DCH == 256, "one V task (4 keys x 8 dims) per thread");
+  static_assert(LOADS * 4 * 1024 == TILE_BYTES, "tile must split into 1 KiB wave loads");
 };
 
-// Position of key kk (0 <= kk < BK) inside a V^T row: bits 2 and 3 swapped.
-__device__ __forceinline__ int vt_pos(int kk) {
-  return (kk & ~12) | ((kk & 4) << 1) | ((kk & 8) >> 1);
+// Physical 16-byte chunk of logical chunk c in row `row` of a K tile.  Reads
+// of one chunk by 16 consecutive rows then touch 16 distinct bank groups.
+template <int D>
+__device__ __forceinline__ int k_chunk(int row, int c) {
+  return D == 128 ? (c ^ (row & 15)) : (c ^ ((row >> 1) & 7));
+}
+
+// Physical 16-byte chunk of logical chunk c in row `row` of a V tile.  A
+// transpose read covers 4 consecutive keys x 32 dims per half wave (and 8
+// keys x 16 dims per 16-lane pair); this permutation spreads both over all
+// banks.
+template <int D>
+__device__ __forceinline__ int v_chunk(int row, int c) {
+  return D == 128 ? (c ^ (4 * (row & 3) + 2 * ((row >> 2) & 1)))
+                  : (c ^ (4 * ((row >> 1) & 1) + 2 * ((row >> 2) & 1)));
 }
 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256, 2) void fa_fwd_bf16_kernel(FwdParams p) {
   using C = Bf16Cfg<D>;
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * C::STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * C::STAGE_BYTES];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -82,8 +108,6 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_bf16_kernel(FwdParams p) {
 
   const int64_t base = (int64_t)bh * N * D;
   const uint16_t* __restrict__ qg = (const uint16_t*)p.q + base;
-  const uint16_t* __restrict__ kg = (const uint16_t*)p.k + base;
-  const uint16_t* __restrict__ vg = (const uint16_t*)p.v + base;
 
   const int qw0 = q0 + 32 * wave;  // first query row of this wave
   const int qrow = qw0 + l32;      // the query row this lane owns
@@ -98,77 +122,67 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_bf16_kernel(FwdParams p) {
     qf[kk] = __builtin_bit_cast(bf16x8, w);
   }
 
-  // ---- K/V tile staging: global -> registers -> LDS -----------------------
-  u32x4 kreg[C::K_LOADS];
-  u32x4 vreg[4];
-  const int vg_g = tid / C::DCH;  // V task: keys 4*vg_g .. +3
-  const int vg_ch = tid % C::DCH; //         dims 8*vg_ch .. +7
-
-  auto load_tile = [&](int kv0) {
+  // ---- K/V tile loads: HBM -> LDS, range-checked ---------------------------
+  // Buffer range = the valid keys of this (batch, head): loads beyond it
+  // return zeros, so padded keys contribute exact zeros to both products.
+  const uint32_t valid_bytes = (uint32_t)kv_lim * C::ROW_BYTES;
+  const void* kbase = (const uint16_t*)p.k + base;
+  const void* vbase = (const uint16_t*)p.v + base;
+  // Per-lane source offsets within a tile (bytes): load i of this wave fills
+  // LDS chunks [(4 i + wave) * 64, +64); lane l fills chunk (4 i + wave)*64 + l.
+  uint32_t koff[C::LOADS], voff[C::LOADS];
 #pragma unroll
-    for (int i = 0; i < C::K_LOADS; ++i) {
-      const int lin = i * 256 + tid;
-      const int row = lin / C::DCH, ch = lin % C::DCH;
-      const int key = kv0 + row;
-      u32x4 w = {0u, 0u, 0u, 0u};
-      if (key < kv_lim) w = *(const u32x4*)(kg + (int64_t)key * D + 8 * ch);
-      kreg[i] = w;
-    }
+  for (int i = 0; i < C::LOADS; ++i) {
+    const int pch = (4 * i + wave) * 64 + lane;  // physical chunk index in the tile
+    const int row = pch / C::CPR, phys = pch % C::CPR;
+    koff[i] = row * C::ROW_BYTES + 16 * k_chunk<D>(row, phys);  // XOR is its own inverse
+    voff[i] = row * C::ROW_BYTES + 16 * v_chunk<D>(row, phys);
+  }
+  auto load_tile = [&](int kv0, int stage) {
+    uint8_t* ks = lds + stage * C::STAGE_BYTES;
+    uint8_t* vs = ks + C::TILE_BYTES;
+    const uint32_t tile_off = (uint32_t)kv0 * C::ROW_BYTES;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int key = kv0 + 4 * vg_g + i;
-      u32x4 w = {0u, 0u, 0u, 0u};
-      if (key < kv_lim) w = *(const u32x4*)(vg + (int64_t)key * D + 8 * vg_ch);
-      vreg[i] = w;
-    }
-  };
-
-  auto store_tile = [&](int stage) {
-    uint16_t* ks = lds + stage * C::STAGE;
-    uint16_t* vt = ks + C::K_ELEMS;
-#pragma unroll
-    for (int i = 0; i < C::K_LOADS; ++i) {
-      const int lin = i * 256 + tid;
-      const int row = lin / C::DCH, ch = lin % C::DCH;
-      *(u32x4*)(ks + row * C::KS + 8 * ch) = kreg[i];
-    }
-    // V^T: for each of the 8 dims, the 4 keys' values form one 8-byte store.
-    const int pos = vt_pos(4 * vg_g);
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const uint32_t a0 = vreg[0][w], a1 = vreg[1][w], a2 = vreg[2][w], a3 = vreg[3][w];
-      u32x2 ev = {(a0 & 0xffffu) | (a1 << 16), (a2 & 0xffffu) | (a3 << 16)};
-      u32x2 od = {(a0 >> 16) | (a1 & 0xffff0000u), (a2 >> 16) | (a3 & 0xffff0000u)};
-      *(u32x2*)(vt + (8 * vg_ch + 2 * w) * C::VS + pos) = ev;
-      *(u32x2*)(vt + (8 * vg_ch + 2 * w + 1) * C::VS + pos) = od;
+    for (int i = 0; i < C::LOADS; ++i) {
+      const int blk = (4 * i + wave) * 1024;
+      // the whole offset goes in the per-lane operand: the range check
+      // covers that operand (not the scalar one)
+      load_lds_16(kbase, valid_bytes, ks + blk, koff[i] + tile_off);
+      load_lds_16(vbase, valid_bytes, vs + blk, voff[i] + tile_off);
     }
   };
+
+  // Fragment addresses within a tile (bytes), independent of the tile.
+  // K: lane reads row 32*bb + l32, logical chunk 2*kk + h.
+  // V: transpose read t4 of block (bb, half) for dim slice db: lanes in a
+  // 16-lane group read 4 keys x 16 dims; lane r reads key +r/4, dims +4*(r%4).
+  const int r16 = lane & 15, g16 = (lane >> 4) & 1;
 
   // ---- running state (one query row per lane) -----------------------------
   f32x16 o_acc[C::ND];
 #pragma unroll
   for (int i = 0; i < C::ND; ++i) o_acc[i] = f32x16{};
-  float m_run = kNegInf;  // running max of scale*log2(e)*s
-  float l_run = 0.f;      // this lane's part of the denominator
+  float m_ref = kNegInf;  // reference maximum of scale*log2(e)*s
+  float l_run = 0.f;      // this lane's part of the fp32 denominator
+  float lp_run = 0.f;     // the same over the bf16-rounded probabilities
   const float c = p.c;
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-  if (ntiles > 0) {
-    load_tile(0);
-    store_tile(0);
-  }
+  if (ntiles > 0) load_tile(0, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
   for (int t = 0; t < ntiles; ++t) {
     const int kv0 = t * C::BK;
-    if (t + 1 < ntiles) load_tile(kv0 + C::BK);  // prefetch, consumed after compute
+    if (t + 1 < ntiles) load_tile(kv0 + C::BK, (t + 1) & 1);  // lands during compute
 
-    const uint16_t* ks = lds + (t & 1) * C::STAGE;
-    const uint16_t* vt = ks + C::K_ELEMS;
+    const uint8_t* ks = lds + (t & 1) * C::STAGE_BYTES;
+    const uint8_t* vs = ks + C::TILE_BYTES;
 
     // Waves whose rows see no key of this tile skip it (wave-uniform).
     const bool skip = (CAUSAL && kv0 > qw0 + 31) || (qw0 >= kv_lim);
     if (!skip) {
-      // S^T = K Q^T for this tile: NB accumulators of 32 keys x 32 queries.
+      // S^T = K Q^T: NB accumulators of 32 keys x 32 queries.
       f32x16 s[C::NB];
 #pragma unroll
       for (int bb = 0; bb < C::NB; ++bb) s[bb] = f32x16{};
@@ -176,7 +190,9 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_bf16_kernel(FwdParams p) {
       for (int kk = 0; kk < D / 16; ++kk) {
 #pragma unroll
         for (int bb = 0; bb < C::NB; ++bb) {
-          const bf16x8 kf = *(const bf16x8*)(ks + (32 * bb + l32) * C::KS + 16 * kk + 8 * h);
+          const int row = 32 * bb + l32;
+          const bf16x8 kf =
+              *(const bf16x8*)(ks + row * C::ROW_BYTES + 16 * k_chunk<D>(row, 2 * kk + h));
           s[bb] = mfma_32x32x16_bf16(kf, qf[kk], s[bb]);
         }
       }
@@ -193,25 +209,30 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_bf16_kernel(FwdParams p) {
             const int key = kv0 + 32 * bb + acc_row(r, h);
             const bool vis = key < kv_lim && (!CAUSAL || key <= qrow);
             s[bb][r] = vis ? s[bb][r] : kNegInf;
-            mx = fmaxf(mx, s[bb][r]);
           }
-      } else {
-#pragma unroll
-        for (int bb = 0; bb < C::NB; ++bb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[bb][r]);
       }
+#pragma unroll
+      for (int bb = 0; bb < C::NB; ++bb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[bb][r]);
       mx = halves_max(mx);
 
-      // New reference maximum (log2 units); -inf - (-inf) never evaluated.
+      // Raise the reference maximum only when some row outgrew it by more
+      // than the slack (wave-uniform decision; -inf - (-inf) never formed).
       const float m_blk = (mx == kNegInf) ? kNegInf : mx * c;
-      const float m_new = fmaxf(m_run, m_blk);
-      const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-      const float alpha = fast_exp2(m_run - m_use);
-      m_run = m_new;
+      const bool grow = m_blk > m_ref + kRescaleSlack;
+      if (__any(grow)) {
+        const float m_new = fmaxf(m_ref, m_blk);
+        const float alpha = (m_ref == kNegInf) ? 0.f : fast_exp2(m_ref - m_new);
+        m_ref = m_new;
+        l_run *= alpha;
+        lp_run *= alpha;
+#pragma unroll
+        for (int i = 0; i < C::ND; ++i) o_acc[i] *= alpha;
+      }
+      const float neg_m = (m_ref == kNegInf) ? 0.f : -m_ref;
 
-      // P = exp2(c*s - m_use); masked entries are exactly 0.
-      float lsum = 0.f;
+      // P = exp2(c*s - m_ref), masked entries exactly 0, packed to bf16.
       bf16x8 pf[C::NB][2];
 #pragma unroll
       for (int bb = 0; bb < C::NB; ++bb) {
@@ -221,47 +242,62 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_bf16_kernel(FwdParams p) {
 #pragma unroll
           for (int t8 = 0; t8 < 8; ++t8) {
             const float sv = s[bb][8 * half + t8];
-            float pv = fast_exp2(__builtin_fmaf(sv, c, -m_use));
+            float pv = fast_exp2(__builtin_fmaf(sv, c, neg_m));
             if (masked) pv = (sv == kNegInf) ? 0.f : pv;
             e[t8] = pv;
-            lsum += pv;
           }
-          u32x4 w = {pack_bf16x2(e[0], e[1]), pack_bf16x2(e[2], e[3]),
-                     pack_bf16x2(e[4], e[5]), pack_bf16x2(e[6], e[7])};
-          pf[bb][half] = __builtin_bit_cast(bf16x8, w);
+          // Two denominators.  l_run sums the fp32 values and feeds the
+          // log-sum-exp (the bf16-rounded sum is off by up to 2^-9 relative
+          // on rows with few keys).  lp_run sums the bf16 values the second
+          // product multiplies, so a / lp_run is an exact convex combination
+          // of V rows under those weights; a dominant key is then reproduced
+          // without the 2^-9 error of its rounded weight.  (The pairs are
+          // built as bf16x2 values and fed to the dot product directly:
+          // taking them as bit casts of u32x4 elements made this compiler
+          // read the first element for all four dot products.)
+          bf16x2 pr[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            l_run += e[2 * j] + e[2 * j + 1];
+            pr[j] = bf16x2{(__bf16)e[2 * j], (__bf16)e[2 * j + 1]};
+            lp_run = __builtin_amdgcn_fdot2_f32_bf16(pr[j], ones, lp_run, false);
+          }
+          pf[bb][half] = bf16x8{pr[0][0], pr[0][1], pr[1][0], pr[1][1],
+                                pr[2][0], pr[2][1], pr[3][0], pr[3][1]};
         }
       }
-      l_run = alpha * l_run + lsum;
 
-      // a <- alpha * a, skipped when no row's maximum moved (exact).
-      if (__any(alpha != 1.f)) {
-#pragma unroll
-        for (int i = 0; i < C::ND; ++i) o_acc[i] *= alpha;
-      }
-
-      // O^T += V^T P^T.
+      // O^T += V^T P^T; V^T fragments by transpose reads of the V tile.
 #pragma unroll
       for (int db = 0; db < C::ND; ++db) {
+        const int dim = 32 * db + 16 * g16 + 4 * (r16 & 3);
+        const int cdim = dim >> 3, sub = (dim & 7) * 2;
 #pragma unroll
         for (int bb = 0; bb < C::NB; ++bb) {
 #pragma unroll
           for (int half = 0; half < 2; ++half) {
-            const bf16x8 vf =
-                *(const bf16x8*)(vt + (32 * db + l32) * C::VS + 32 * bb + 16 * half + 8 * h);
+            const int key0 = 32 * bb + 16 * half + 4 * h + (r16 >> 2);
+            const int key1 = key0 + 8;
+            const bf16x4 v0 = lds_read_tr16(vs + key0 * C::ROW_BYTES + 16 * v_chunk<D>(key0, cdim) + sub);
+            const bf16x4 v1 = lds_read_tr16(vs + key1 * C::ROW_BYTES + 16 * v_chunk<D>(key1, cdim) + sub);
+            const bf16x8 vf = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
             o_acc[db] = mfma_32x32x16_bf16(vf, pf[bb][half], o_acc[db]);
           }
         }
       }
     }
 
-    if (t + 1 < ntiles) store_tile((t + 1) & 1);
+    // The next tile's loads must have landed, and every wave must be done
+    // with this stage, before anyone reads the next stage or refills this one.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   }
 
   // ---- epilogue: o = a / l, LSE = ln(2) * (m + log2 l) ---------------------
   const float l_tot = halves_sum(l_run);
+  const float lp_tot = halves_sum(lp_run);
   const bool valid = qrow < kv_lim;  // rows at or beyond the length are padding
-  const float inv = valid ? 1.f / l_tot : 0.f;
+  const float inv = valid ? 1.f / lp_tot : 0.f;
   if (qrow < N) {
     uint16_t* og = (uint16_t*)p.o + base + (int64_t)qrow * D;
 #pragma unroll
@@ -277,7 +313,7 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_bf16_kernel(FwdParams p) {
       }
     }
     if (h == 0) {
-      p.lse[(int64_t)bh * N + qrow] = valid ? (m_run + __log2f(l_tot)) * kLn2 : kNegInf;
+      p.lse[(int64_t)bh * N + qrow] = valid ? (m_ref + __log2f(l_tot)) * kLn2 : kNegInf;
     }
   }
 }
