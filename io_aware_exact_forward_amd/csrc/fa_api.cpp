@@ -7,7 +7,9 @@
 
 #include <climits>
 #include <cmath>
+#include <algorithm>
 #include <cstdint>
+#include <limits>
 #include <mutex>
 
 #include "fa_internal.hpp"
@@ -84,8 +86,12 @@ fa::FwdParams make_params(const void* q, const void* k, const void* v, void* o, 
   p.H = H;
   p.N = N;
   p.n_qtiles = (N + fa::kQueryTile - 1) / fa::kQueryTile;
-  // exp(x) = exp2(x * log2 e): the kernels keep scores in log2 units.
-  p.c = static_cast<float>(std::fabs(static_cast<double>(scale)) * 1.4426950408889634);
+  // exp(x) = exp2(x * log2 e): the kernels keep scores in log2 units.  c is
+  // kept >= the smallest normal float so that a masked score (-inf) times c
+  // is -inf, never NaN; for scale = 0 that changes no exp2 result, since
+  // |s| * FLT_MIN is far below 2^-24 for any finite score s.
+  p.c = std::max(static_cast<float>(std::fabs(static_cast<double>(scale)) * 1.4426950408889634),
+                 std::numeric_limits<float>::min());
   // A negative scale is applied by negating Q (exact) and using |scale|.
   p.q_sign = std::signbit(scale) && scale != 0.f
                  ? (dtype == FA_DTYPE_BF16 ? 0x80008000u : 0x80000000u)

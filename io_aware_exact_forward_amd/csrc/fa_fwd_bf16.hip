@@ -45,6 +45,11 @@ namespace {
 
 constexpr float kRescaleSlack = 8.0f;
 
+template <int S>
+struct StageTag {
+  static constexpr int value = S;
+};
+
 template <int D>
 struct Bf16Cfg {
   static constexpr int BQ = kQueryTile;          // query rows per workgroup
@@ -82,7 +87,9 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_bf16_kernel(FwdParams p) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * C::STAGE_BYTES];
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  // wave index as a scalar (it is uniform), so LDS destinations of the
+  // direct loads are computed on the scalar unit
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int h = lane >> 5;
@@ -101,6 +108,9 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_bf16_kernel(FwdParams p) {
     const int L = p.key_len[b];
     kv_lim = L < 0 ? 0 : (L > N ? N : L);
   }
+  // uniform across the workgroup; keep it (and all that derives from it,
+  // such as the buffer ranges) in scalar registers
+  kv_lim = __builtin_amdgcn_readfirstlane(kv_lim);
   int n_kv = kv_lim;
   if (CAUSAL) n_kv = min(n_kv, q0 + C::BQ);
   if (q0 >= kv_lim) n_kv = 0;  // every row of the tile is padding
@@ -141,12 +151,12 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_bf16_kernel(FwdParams p) {
   auto load_tile = [&](int kv0, int stage) {
     uint8_t* ks = lds + stage * C::STAGE_BYTES;
     uint8_t* vs = ks + C::TILE_BYTES;
-    const uint32_t tile_off = (uint32_t)kv0 * C::ROW_BYTES;
+    const uint32_t tile_off = __builtin_amdgcn_readfirstlane(kv0 * C::ROW_BYTES);
 #pragma unroll
     for (int i = 0; i < C::LOADS; ++i) {
       const int blk = (4 * i + wave) * 1024;
-      // the whole offset goes in the per-lane operand: the range check
-      // covers that operand (not the scalar one)
+      // The whole offset goes in the per-lane operand: the range check
+      // covers that operand (not the scalar one).
       load_lds_16(kbase, valid_bytes, ks + blk, koff[i] + tile_off);
       load_lds_16(vbase, valid_bytes, vs + blk, voff[i] + tile_off);
     }
@@ -172,11 +182,15 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_bf16_kernel(FwdParams p) {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
-  for (int t = 0; t < ntiles; ++t) {
+  // One streamed tile, read from LDS stage S.  S is a compile-time constant
+  // (the loop below alternates the two instantiations), so every LDS read
+  // address is a per-lane base plus an immediate offset.
+  auto step = [&](const int t, auto stage_tag) {
+    constexpr int S = decltype(stage_tag)::value;
     const int kv0 = t * C::BK;
-    if (t + 1 < ntiles) load_tile(kv0 + C::BK, (t + 1) & 1);  // lands during compute
+    if (t + 1 < ntiles) load_tile(kv0 + C::BK, S ^ 1);  // lands during compute
 
-    const uint8_t* ks = lds + (t & 1) * C::STAGE_BYTES;
+    const uint8_t* ks = lds + S * C::STAGE_BYTES;
     const uint8_t* vs = ks + C::TILE_BYTES;
 
     // Waves whose rows see no key of this tile skip it (wave-uniform).
@@ -232,7 +246,7 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_bf16_kernel(FwdParams p) {
       }
       const float neg_m = (m_ref == kNegInf) ? 0.f : -m_ref;
 
-      // P = exp2(c*s - m_ref), masked entries exactly 0, packed to bf16.
+      // P = exp2(c*s - m_ref), packed to bf16.
       bf16x8 pf[C::NB][2];
 #pragma unroll
       for (int bb = 0; bb < C::NB; ++bb) {
@@ -241,10 +255,8 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_bf16_kernel(FwdParams p) {
           float e[8];
 #pragma unroll
           for (int t8 = 0; t8 < 8; ++t8) {
-            const float sv = s[bb][8 * half + t8];
-            float pv = fast_exp2(__builtin_fmaf(sv, c, neg_m));
-            if (masked) pv = (sv == kNegInf) ? 0.f : pv;
-            e[t8] = pv;
+            // masked scores are -inf and c > 0, so they give exactly 0
+            e[t8] = fast_exp2(__builtin_fmaf(s[bb][8 * half + t8], c, neg_m));
           }
           // Two denominators.  l_run sums the fp32 values and feeds the
           // log-sum-exp (the bf16-rounded sum is off by up to 2^-9 relative
@@ -291,6 +303,10 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_bf16_kernel(FwdParams p) {
     // with this stage, before anyone reads the next stage or refills this one.
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
+  };
+  for (int t = 0; t < ntiles; t += 2) {
+    step(t, StageTag<0>{});
+    if (t + 1 < ntiles) step(t + 1, StageTag<1>{});
   }
 
   // ---- epilogue: o = a / l, LSE = ln(2) * (m + log2 l) ---------------------
