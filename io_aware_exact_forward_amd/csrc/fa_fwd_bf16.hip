@@ -1,29 +1,31 @@
 // Fused attention forward for bf16 Q/K/V on gfx950 (CDNA4).
 //
-// One workgroup owns a tile of 128 query rows of one (batch, head) and keeps,
-// per row, the running maximum m, denominator l and unnormalised numerator a
-// of "FlashAttention: Exact Attention as an IO-Aware Streaming Computation"
-// (section "Mathematical structure"), while key/value tiles stream through
-// LDS ("IO-aware exact attention", section "One tiled forward-pass
-// iteration").  Score tiles live only in registers; only O and the per-row
-// log-sum-exp are written.
+// One workgroup owns a tile of 32*WAVES query rows of one (batch, head) and
+// keeps, per row, the running maximum m, denominator l and unnormalised
+// numerator a of "FlashAttention: Exact Attention as an IO-Aware Streaming
+// Computation" (section "Mathematical structure"), while key/value tiles
+// stream through LDS ("IO-aware exact attention", section "One tiled
+// forward-pass iteration").  Score tiles live only in registers; only O and
+// the per-row log-sum-exp are written.
 //
 // Data movement.  K and V tiles go from HBM straight into LDS with buffer
-// loads (no register staging).  The buffer range is the sequence's valid
-// keys, so rows past the end arrive as zeros.  Both tiles are row-major
-// [key][dim] with the 16-byte chunks of each row permuted by an XOR of the
-// row index, which makes the fragment reads below free of bank conflicts.
+// loads (no register staging), through a ring of NSTAGE LDS stages: the
+// loads for tile t + NSTAGE - 1 are issued while tile t is computed.  The
+// buffer range is the sequence's valid keys, so rows past the end arrive as
+// zeros.  Both tiles are row-major [key][dim] with the 16-byte chunks of each
+// row permuted by an XOR of the row index, which makes the fragment reads
+// below free of bank conflicts.
 //
-// Products.  Each wave computes the transposed score tile S^T = K Q^T on
-// 32x32x16 bf16 MFMA (K fragments from LDS, Q fragments resident in
-// registers), so that each lane holds the scores of one query row: row max
-// and row sum are in-lane reductions plus one exchange between the two wave
-// halves.  The probabilities are packed to bf16 in place; that packing is
-// already the B operand of O^T = V^T P^T.  The matching V^T operand comes from
-// the row-major V tile through transpose reads (ds_read_b64_tr_b16), which
-// hand each lane one head-dim column across four consecutive keys.  O^T keeps
-// one query row per lane, so rescaling the numerator is one multiply per
-// register.
+// Products.  Each wave (32 query rows) computes the transposed score tile
+// S^T = K Q^T on 32x32x16 bf16 MFMA (K fragments from LDS, Q fragments
+// resident in registers), so that each lane holds the scores of one query
+// row: row max and row sum are in-lane reductions plus one exchange between
+// the two wave halves.  The probabilities are packed to bf16 in place; that
+// packing is already the B operand of O^T = V^T P^T.  The matching V^T
+// operand comes from the row-major V tile through transpose reads
+// (ds_read_b64_tr_b16), which hand each lane one head-dim column across four
+// consecutive keys.  O^T keeps one query row per lane, so rescaling the
+// numerator is one multiply per register.
 //
 // Reference maximum.  Scores are exponentiated against a per-row reference
 // value.  It is raised to the running maximum only when some row's block
@@ -50,18 +52,22 @@ struct StageTag {
   static constexpr int value = S;
 };
 
-template <int D>
+template <int D, int WAVES, int NSTAGE>
 struct Bf16Cfg {
-  static constexpr int BQ = kQueryTile;          // query rows per workgroup
+  static constexpr int BQ = 32 * WAVES;          // query rows per workgroup
   static constexpr int BK = D == 128 ? 64 : 128; // keys per streamed tile
   static constexpr int ROW_BYTES = D * 2;
   static constexpr int CPR = D / 8;              // 16-byte chunks per row
   static constexpr int TILE_BYTES = BK * ROW_BYTES;  // one K or V tile (16 KiB)
   static constexpr int STAGE_BYTES = 2 * TILE_BYTES; // K tile + V tile
-  static constexpr int LOADS = TILE_BYTES / 1024 / 4; // 1 KiB loads per wave per tile
+  static constexpr int LDS_BYTES = NSTAGE * STAGE_BYTES;
+  static constexpr int LOADS = TILE_BYTES / 1024 / WAVES;  // 1 KiB loads per wave per tensor
+  static constexpr int LOADS_PER_TILE = 2 * LOADS;         // K and V, per wave
   static constexpr int NB = BK / 32;             // 32-key blocks per tile
   static constexpr int ND = D / 32;              // 32-wide slices of the head dim
-  static_assert(LOADS * 4 * 1024 == TILE_BYTES, "tile must split into 1 KiB wave loads");
+  static_assert(LOADS * WAVES * 1024 == TILE_BYTES, "tile must split into 1 KiB wave loads");
+  static_assert(NSTAGE >= 2 && NSTAGE <= 4, "2..4 LDS stages");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS capacity");
 };
 
 // Physical 16-byte chunk of logical chunk c in row `row` of a K tile.  Reads
@@ -81,10 +87,27 @@ __device__ __forceinline__ int v_chunk(int row, int c) {
                   : (c ^ (4 * ((row >> 1) & 1) + 2 * ((row >> 2) & 1)));
 }
 
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 2) void fa_fwd_bf16_kernel(FwdParams p) {
-  using C = Bf16Cfg<D>;
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * C::STAGE_BYTES];
+// Wait until at most n of this wave's vector-memory operations are in
+// flight (they complete in issue order).  n is one of the few values the
+// stage ring can need.
+__device__ __forceinline__ void wait_vmem(int n) {
+  switch (n) {
+    case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+    case 2: asm volatile("s_waitcnt vmcnt(2)" ::: "memory"); break;
+    case 4: asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); break;
+    case 6: asm volatile("s_waitcnt vmcnt(6)" ::: "memory"); break;
+    case 8: asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); break;
+    case 12: asm volatile("s_waitcnt vmcnt(12)" ::: "memory"); break;
+    case 16: asm volatile("s_waitcnt vmcnt(16)" ::: "memory"); break;
+    default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+  }
+}
+
+template <int D, bool CAUSAL, int WAVES, int NSTAGE>
+__global__ __launch_bounds__(64 * WAVES, (WAVES == 4 && NSTAGE == 2) ? 2 : 1)
+void fa_fwd_bf16_kernel(FwdParams p) {
+  using C = Bf16Cfg<D, WAVES, NSTAGE>;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[C::LDS_BYTES];
 
   const int tid = threadIdx.x;
   // wave index as a scalar (it is uniform), so LDS destinations of the
@@ -139,11 +162,11 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_bf16_kernel(FwdParams p) {
   const void* kbase = (const uint16_t*)p.k + base;
   const void* vbase = (const uint16_t*)p.v + base;
   // Per-lane source offsets within a tile (bytes): load i of this wave fills
-  // LDS chunks [(4 i + wave) * 64, +64); lane l fills chunk (4 i + wave)*64 + l.
+  // the 1 KiB LDS block WAVES*i + wave; lane l fills its 16-byte chunk l.
   uint32_t koff[C::LOADS], voff[C::LOADS];
 #pragma unroll
   for (int i = 0; i < C::LOADS; ++i) {
-    const int pch = (4 * i + wave) * 64 + lane;  // physical chunk index in the tile
+    const int pch = (WAVES * i + wave) * 64 + lane;  // physical chunk index in the tile
     const int row = pch / C::CPR, phys = pch % C::CPR;
     koff[i] = row * C::ROW_BYTES + 16 * k_chunk<D>(row, phys);  // XOR is its own inverse
     voff[i] = row * C::ROW_BYTES + 16 * v_chunk<D>(row, phys);
@@ -154,7 +177,7 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_bf16_kernel(FwdParams p) {
     const uint32_t tile_off = __builtin_amdgcn_readfirstlane(kv0 * C::ROW_BYTES);
 #pragma unroll
     for (int i = 0; i < C::LOADS; ++i) {
-      const int blk = (4 * i + wave) * 1024;
+      const int blk = (WAVES * i + wave) * 1024;
       // The whole offset goes in the per-lane operand: the range check
       // covers that operand (not the scalar one).
       load_lds_16(kbase, valid_bytes, ks + blk, koff[i] + tile_off);
@@ -162,10 +185,8 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_bf16_kernel(FwdParams p) {
     }
   };
 
-  // Fragment addresses within a tile (bytes), independent of the tile.
-  // K: lane reads row 32*bb + l32, logical chunk 2*kk + h.
-  // V: transpose read t4 of block (bb, half) for dim slice db: lanes in a
-  // 16-lane group read 4 keys x 16 dims; lane r reads key +r/4, dims +4*(r%4).
+  // V transpose reads: in each 16-lane group, lane r reads key +r/4 and
+  // dims +4*(r%4), so lane r receives dim r of four consecutive keys.
   const int r16 = lane & 15, g16 = (lane >> 4) & 1;
 
   // ---- running state (one query row per lane) -----------------------------
@@ -178,135 +199,145 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_bf16_kernel(FwdParams p) {
   const float c = p.c;
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-  if (ntiles > 0) load_tile(0, 0);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
+  // Prologue: the first NSTAGE - 1 tiles.
+#pragma unroll
+  for (int s = 0; s < NSTAGE - 1; ++s)
+    if (s < ntiles) load_tile(s * C::BK, s);
 
-  // One streamed tile, read from LDS stage S.  S is a compile-time constant
-  // (the loop below alternates the two instantiations), so every LDS read
-  // address is a per-lane base plus an immediate offset.
+  // One streamed tile, read from LDS stage S (a compile-time constant: the
+  // loop below cycles through the NSTAGE instantiations, so every LDS read
+  // address is a per-lane base plus an immediate offset).
   auto step = [&](const int t, auto stage_tag) {
     constexpr int S = decltype(stage_tag)::value;
     const int kv0 = t * C::BK;
-    if (t + 1 < ntiles) load_tile(kv0 + C::BK, S ^ 1);  // lands during compute
+
+    // Tile t has landed once at most the loads of the tiles issued after
+    // it are still in flight; after the barrier every wave's part has
+    // landed and every wave is done with tile t - 1, whose stage is refilled.
+    const int later = min(NSTAGE - 2, ntiles - 1 - t);
+    wait_vmem(later * C::LOADS_PER_TILE);
+    __syncthreads();
+    if (t + NSTAGE - 1 < ntiles) load_tile(kv0 + (NSTAGE - 1) * C::BK, (S + NSTAGE - 1) % NSTAGE);
 
     const uint8_t* ks = lds + S * C::STAGE_BYTES;
     const uint8_t* vs = ks + C::TILE_BYTES;
 
     // Waves whose rows see no key of this tile skip it (wave-uniform).
     const bool skip = (CAUSAL && kv0 > qw0 + 31) || (qw0 >= kv_lim);
-    if (!skip) {
-      // S^T = K Q^T: NB accumulators of 32 keys x 32 queries.
-      f32x16 s[C::NB];
-#pragma unroll
-      for (int bb = 0; bb < C::NB; ++bb) s[bb] = f32x16{};
-#pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) {
-#pragma unroll
-        for (int bb = 0; bb < C::NB; ++bb) {
-          const int row = 32 * bb + l32;
-          const bf16x8 kf =
-              *(const bf16x8*)(ks + row * C::ROW_BYTES + 16 * k_chunk<D>(row, 2 * kk + h));
-          s[bb] = mfma_32x32x16_bf16(kf, qf[kk], s[bb]);
-        }
-      }
+    if (skip) return;
 
-      // Element masks only where the tile crosses the diagonal or the
-      // sequence end (wave-uniform test).
-      const bool masked = (CAUSAL && kv0 + C::BK - 1 > qw0) || (kv0 + C::BK > kv_lim);
-      float mx = kNegInf;
-      if (masked) {
+    // S^T = K Q^T: NB accumulators of 32 keys x 32 queries.
+    f32x16 s[C::NB];
 #pragma unroll
-        for (int bb = 0; bb < C::NB; ++bb)
+    for (int bb = 0; bb < C::NB; ++bb) s[bb] = f32x16{};
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = kv0 + 32 * bb + acc_row(r, h);
-            const bool vis = key < kv_lim && (!CAUSAL || key <= qrow);
-            s[bb][r] = vis ? s[bb][r] : kNegInf;
-          }
+    for (int kk = 0; kk < D / 16; ++kk) {
+#pragma unroll
+      for (int bb = 0; bb < C::NB; ++bb) {
+        const int row = 32 * bb + l32;
+        const bf16x8 kf =
+            *(const bf16x8*)(ks + row * C::ROW_BYTES + 16 * k_chunk<D>(row, 2 * kk + h));
+        s[bb] = mfma_32x32x16_bf16(kf, qf[kk], s[bb]);
       }
+    }
+
+    // Element masks only where the tile crosses the diagonal or the
+    // sequence end (wave-uniform test).
+    const bool masked = (CAUSAL && kv0 + C::BK - 1 > qw0) || (kv0 + C::BK > kv_lim);
+    if (masked) {
 #pragma unroll
       for (int bb = 0; bb < C::NB; ++bb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[bb][r]);
-      mx = halves_max(mx);
-
-      // Raise the reference maximum only when some row outgrew it by more
-      // than the slack (wave-uniform decision; -inf - (-inf) never formed).
-      const float m_blk = (mx == kNegInf) ? kNegInf : mx * c;
-      const bool grow = m_blk > m_ref + kRescaleSlack;
-      if (__any(grow)) {
-        const float m_new = fmaxf(m_ref, m_blk);
-        const float alpha = (m_ref == kNegInf) ? 0.f : fast_exp2(m_ref - m_new);
-        m_ref = m_new;
-        l_run *= alpha;
-        lp_run *= alpha;
+        for (int r = 0; r < 16; ++r) {
+          const int key = kv0 + 32 * bb + acc_row(r, h);
+          const bool vis = key < kv_lim && (!CAUSAL || key <= qrow);
+          s[bb][r] = vis ? s[bb][r] : kNegInf;
+        }
+    }
+    // Row maximum: four independent partial maxima, then the wave halves.
+    float m4[4] = {kNegInf, kNegInf, kNegInf, kNegInf};
 #pragma unroll
-        for (int i = 0; i < C::ND; ++i) o_acc[i] *= alpha;
-      }
-      const float neg_m = (m_ref == kNegInf) ? 0.f : -m_ref;
+    for (int bb = 0; bb < C::NB; ++bb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) m4[r & 3] = fmaxf(m4[r & 3], s[bb][r]);
+    const float mx = halves_max(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3])));
 
-      // P = exp2(c*s - m_ref), packed to bf16.
-      bf16x8 pf[C::NB][2];
+    // Raise the reference maximum only when some row outgrew it by more
+    // than the slack (wave-uniform decision; -inf - (-inf) never formed).
+    const float m_blk = (mx == kNegInf) ? kNegInf : mx * c;
+    const bool grow = m_blk > m_ref + kRescaleSlack;
+    if (__any(grow)) {
+      const float m_new = fmaxf(m_ref, m_blk);
+      const float alpha = (m_ref == kNegInf) ? 0.f : fast_exp2(m_ref - m_new);
+      m_ref = m_new;
+      l_run *= alpha;
+      lp_run *= alpha;
+#pragma unroll
+      for (int i = 0; i < C::ND; ++i) o_acc[i] *= alpha;
+    }
+    const float neg_m = (m_ref == kNegInf) ? 0.f : -m_ref;
+
+    // P = exp2(c*s - m_ref), packed to bf16.
+    bf16x8 pf[C::NB][2];
+#pragma unroll
+    for (int bb = 0; bb < C::NB; ++bb) {
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        float e[8];
+#pragma unroll
+        for (int t8 = 0; t8 < 8; ++t8)
+          // masked scores are -inf and c > 0, so they give exactly 0
+          e[t8] = fast_exp2(__builtin_fmaf(s[bb][8 * half + t8], c, neg_m));
+        // Two denominators.  l_run sums the fp32 values and feeds the
+        // log-sum-exp (the bf16-rounded sum is off by up to 2^-9 relative
+        // on rows with few keys).  lp_run sums the bf16 values the second
+        // product multiplies, so a / lp_run is an exact convex combination
+        // of V rows under those weights; a dominant key is then reproduced
+        // without the 2^-9 error of its rounded weight.  (The pairs are
+        // built as bf16x2 values and fed to the dot product directly:
+        // taking them as bit casts of u32x4 elements made this compiler
+        // read the first element for all four dot products.)
+        bf16x2 pr[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          l_run += e[2 * j] + e[2 * j + 1];
+          pr[j] = bf16x2{(__bf16)e[2 * j], (__bf16)e[2 * j + 1]};
+          lp_run = __builtin_amdgcn_fdot2_f32_bf16(pr[j], ones, lp_run, false);
+        }
+        pf[bb][half] = bf16x8{pr[0][0], pr[0][1], pr[1][0], pr[1][1],
+                              pr[2][0], pr[2][1], pr[3][0], pr[3][1]};
+      }
+    }
+
+    // O^T += V^T P^T; V^T fragments by transpose reads of the V tile.
+#pragma unroll
+    for (int db = 0; db < C::ND; ++db) {
+      const int dim = 32 * db + 16 * g16 + 4 * (r16 & 3);
+      const int cdim = dim >> 3, sub = (dim & 7) * 2;
 #pragma unroll
       for (int bb = 0; bb < C::NB; ++bb) {
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
-          float e[8];
-#pragma unroll
-          for (int t8 = 0; t8 < 8; ++t8) {
-            // masked scores are -inf and c > 0, so they give exactly 0
-            e[t8] = fast_exp2(__builtin_fmaf(s[bb][8 * half + t8], c, neg_m));
-          }
-          // Two denominators.  l_run sums the fp32 values and feeds the
-          // log-sum-exp (the bf16-rounded sum is off by up to 2^-9 relative
-          // on rows with few keys).  lp_run sums the bf16 values the second
-          // product multiplies, so a / lp_run is an exact convex combination
-          // of V rows under those weights; a dominant key is then reproduced
-          // without the 2^-9 error of its rounded weight.  (The pairs are
-          // built as bf16x2 values and fed to the dot product directly:
-          // taking them as bit casts of u32x4 elements made this compiler
-          // read the first element for all four dot products.)
-          bf16x2 pr[4];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            l_run += e[2 * j] + e[2 * j + 1];
-            pr[j] = bf16x2{(__bf16)e[2 * j], (__bf16)e[2 * j + 1]};
-            lp_run = __builtin_amdgcn_fdot2_f32_bf16(pr[j], ones, lp_run, false);
-          }
-          pf[bb][half] = bf16x8{pr[0][0], pr[0][1], pr[1][0], pr[1][1],
-                                pr[2][0], pr[2][1], pr[3][0], pr[3][1]};
-        }
-      }
-
-      // O^T += V^T P^T; V^T fragments by transpose reads of the V tile.
-#pragma unroll
-      for (int db = 0; db < C::ND; ++db) {
-        const int dim = 32 * db + 16 * g16 + 4 * (r16 & 3);
-        const int cdim = dim >> 3, sub = (dim & 7) * 2;
-#pragma unroll
-        for (int bb = 0; bb < C::NB; ++bb) {
-#pragma unroll
-          for (int half = 0; half < 2; ++half) {
-            const int key0 = 32 * bb + 16 * half + 4 * h + (r16 >> 2);
-            const int key1 = key0 + 8;
-            const bf16x4 v0 = lds_read_tr16(vs + key0 * C::ROW_BYTES + 16 * v_chunk<D>(key0, cdim) + sub);
-            const bf16x4 v1 = lds_read_tr16(vs + key1 * C::ROW_BYTES + 16 * v_chunk<D>(key1, cdim) + sub);
-            const bf16x8 vf = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-            o_acc[db] = mfma_32x32x16_bf16(vf, pf[bb][half], o_acc[db]);
-          }
+          const int key0 = 32 * bb + 16 * half + 4 * h + (r16 >> 2);
+          const int key1 = key0 + 8;
+          const bf16x4 v0 = lds_read_tr16(vs + key0 * C::ROW_BYTES + 16 * v_chunk<D>(key0, cdim) + sub);
+          const bf16x4 v1 = lds_read_tr16(vs + key1 * C::ROW_BYTES + 16 * v_chunk<D>(key1, cdim) + sub);
+          const bf16x8 vf = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+          o_acc[db] = mfma_32x32x16_bf16(vf, pf[bb][half], o_acc[db]);
         }
       }
     }
-
-    // The next tile's loads must have landed, and every wave must be done
-    // with this stage, before anyone reads the next stage or refills this one.
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
   };
-  for (int t = 0; t < ntiles; t += 2) {
+
+  for (int t = 0; t < ntiles; t += NSTAGE) {
     step(t, StageTag<0>{});
     if (t + 1 < ntiles) step(t + 1, StageTag<1>{});
+    if constexpr (NSTAGE > 2) {
+      if (t + 2 < ntiles) step(t + 2, StageTag<2>{});
+    }
+    if constexpr (NSTAGE > 3) {
+      if (t + 3 < ntiles) step(t + 3, StageTag<3>{});
+    }
   }
 
   // ---- epilogue: o = a / l, LSE = ln(2) * (m + log2 l) ---------------------
@@ -334,19 +365,32 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_bf16_kernel(FwdParams p) {
   }
 }
 
+template <int D, bool CAUSAL, int WAVES, int NSTAGE>
+hipError_t launch_cfg(FwdParams p, hipStream_t stream) {
+  using C = Bf16Cfg<D, WAVES, NSTAGE>;
+  p.n_qtiles = (p.N + C::BQ - 1) / C::BQ;
+  const dim3 grid((unsigned)((int64_t)p.n_qtiles * p.B * p.H));
+  hipLaunchKernelGGL((fa_fwd_bf16_kernel<D, CAUSAL, WAVES, NSTAGE>), grid, dim3(64 * WAVES), 0,
+                     stream, p);
+  return hipGetLastError();
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_d(const FwdParams& p, hipStream_t stream) {
+  // 256-row tiles (8 waves, one workgroup per CU, 3-stage ring) when there
+  // are enough of them to fill the chip twice over; 128-row tiles (4 waves,
+  // two workgroups per CU, 2 stages) otherwise.  (Measured on MI355X at
+  // N = 8192, d = 128: 3 stages are a few percent ahead of 2 and 4.)
+  const int64_t big_tiles = (int64_t)p.B * p.H * ((p.N + 255) / 256);
+  if (big_tiles >= 512) return launch_cfg<D, CAUSAL, 8, 3>(p, stream);
+  return launch_cfg<D, CAUSAL, 4, 2>(p, stream);
+}
+
 }  // namespace
 
 hipError_t launch_fwd_bf16(const FwdParams& p, int d, bool causal, hipStream_t stream) {
-  const dim3 grid((unsigned)(p.n_qtiles * p.B * p.H));
-  const dim3 block(256);
-  if (d == 128) {
-    if (causal) hipLaunchKernelGGL((fa_fwd_bf16_kernel<128, true>), grid, block, 0, stream, p);
-    else hipLaunchKernelGGL((fa_fwd_bf16_kernel<128, false>), grid, block, 0, stream, p);
-  } else {
-    if (causal) hipLaunchKernelGGL((fa_fwd_bf16_kernel<64, true>), grid, block, 0, stream, p);
-    else hipLaunchKernelGGL((fa_fwd_bf16_kernel<64, false>), grid, block, 0, stream, p);
-  }
-  return hipGetLastError();
+  if (d == 128) return causal ? launch_d<128, true>(p, stream) : launch_d<128, false>(p, stream);
+  return causal ? launch_d<64, true>(p, stream) : launch_d<64, false>(p, stream);
 }
 
 }  // namespace fa
