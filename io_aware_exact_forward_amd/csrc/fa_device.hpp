@@ -5,6 +5,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+#include <utility>
+
 namespace fa {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -84,6 +87,59 @@ __device__ __forceinline__ void load_lds_16(const void* base, uint32_t nbytes, v
 // 4 x 16 block, lane i therefore receives column i of rows 0..3.
 __device__ __forceinline__ bf16x4 lds_read_tr16(const void* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p);
+}
+
+// The same transpose read issued as an instruction the compiler does not
+// track: it inserts no wait for it (in particular no wait for unrelated
+// buffer->LDS loads still in flight, which it cannot tell apart), and the
+// caller must wait for the result with lds_wait before using it.
+template <int OFFSET>
+__device__ __forceinline__ bf16x4 lds_read_tr16_async(const void* p) {
+  static_assert(OFFSET >= 0 && OFFSET < 65536, "ds offset field");
+  bf16x4 r;
+  const uint32_t a = (uint32_t)(uintptr_t)(lds_void*)p;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(a), "i"(OFFSET));
+  return r;
+}
+
+// Wait until at most N of this wave's LDS operations are outstanding (they
+// complete in order).  The eight values are passed through the wait, so
+// everything the compiler schedules after it that uses them sees them
+// complete.
+template <int N>
+__device__ __forceinline__ void lds_wait8(bf16x4 (&v)[8]) {
+  static_assert(N >= 0 && N < 16, "lgkmcnt field");
+  asm volatile("s_waitcnt lgkmcnt(%8)"
+               : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]),
+                 "+v"(v[6]), "+v"(v[7])
+               : "i"(N));
+}
+
+// Calls f(std::integral_constant<int, I>{}) for I = 0 .. N-1, so that the
+// body can use I as a compile-time constant (for instruction immediates).
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// Workgroup barrier without a memory fence.  The caller makes its own
+// memory operations complete (with the waits above) before arriving; the
+// fence __syncthreads() adds would also wait for prefetches that are meant
+// to stay in flight across the barrier.
+__device__ __forceinline__ void barrier_no_fence() {
+  asm volatile("s_barrier" ::: "memory");
+}
+
+// Wait until at most N of this wave's vector-memory operations (loads,
+// including buffer->LDS loads) are in flight; they complete in issue order.
+template <int N>
+__device__ __forceinline__ void vmem_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt field");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"i"(N) : "memory");
 }
 
 }  // namespace fa

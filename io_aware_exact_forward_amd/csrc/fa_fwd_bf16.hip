@@ -87,22 +87,6 @@ __device__ __forceinline__ int v_chunk(int row, int c) {
                   : (c ^ (4 * ((row >> 1) & 1) + 2 * ((row >> 2) & 1)));
 }
 
-// Wait until at most n of this wave's vector-memory operations are in
-// flight (they complete in issue order).  n is one of the few values the
-// stage ring can need.
-__device__ __forceinline__ void wait_vmem(int n) {
-  switch (n) {
-    case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
-    case 2: asm volatile("s_waitcnt vmcnt(2)" ::: "memory"); break;
-    case 4: asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); break;
-    case 6: asm volatile("s_waitcnt vmcnt(6)" ::: "memory"); break;
-    case 8: asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); break;
-    case 12: asm volatile("s_waitcnt vmcnt(12)" ::: "memory"); break;
-    case 16: asm volatile("s_waitcnt vmcnt(16)" ::: "memory"); break;
-    default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
-  }
-}
-
 template <int D, bool CAUSAL, int WAVES, int NSTAGE>
 __global__ __launch_bounds__(64 * WAVES, (WAVES == 4 && NSTAGE == 2) ? 2 : 1)
 void fa_fwd_bf16_kernel(FwdParams p) {
@@ -186,8 +170,18 @@ void fa_fwd_bf16_kernel(FwdParams p) {
   };
 
   // V transpose reads: in each 16-lane group, lane r reads key +r/4 and
-  // dims +4*(r%4), so lane r receives dim r of four consecutive keys.
+  // dims +4*(r%4), so lane r receives dim r of four consecutive keys.  The
+  // swizzle chunk of such a read depends on the lane and the head-dim slice
+  // only (not on which 8-key group of the tile is read), so each slice has
+  // one per-lane byte offset.
   const int r16 = lane & 15, g16 = (lane >> 4) & 1;
+  uint32_t v_lane_off[C::ND];
+#pragma unroll
+  for (int db = 0; db < C::ND; ++db) {
+    const int key = 4 * h + (r16 >> 2);
+    const int dim = 32 * db + 16 * g16 + 4 * (r16 & 3);
+    v_lane_off[db] = key * C::ROW_BYTES + 16 * v_chunk<D>(key, dim >> 3) + (dim & 7) * 2;
+  }
 
   // ---- running state (one query row per lane) -----------------------------
   f32x16 o_acc[C::ND];
@@ -214,9 +208,11 @@ void fa_fwd_bf16_kernel(FwdParams p) {
     // Tile t has landed once at most the loads of the tiles issued after
     // it are still in flight; after the barrier every wave's part has
     // landed and every wave is done with tile t - 1, whose stage is refilled.
-    const int later = min(NSTAGE - 2, ntiles - 1 - t);
-    wait_vmem(later * C::LOADS_PER_TILE);
-    __syncthreads();
+    const int later = min(NSTAGE - 2, ntiles - 1 - t);  // 0 .. NSTAGE - 2 (uniform)
+    if (NSTAGE > 3 && later >= 2) vmem_wait<(NSTAGE > 3 ? 2 : 0) * C::LOADS_PER_TILE>();
+    else if (later >= 1) vmem_wait<C::LOADS_PER_TILE>();
+    else vmem_wait<0>();
+    barrier_no_fence();
     if (t + NSTAGE - 1 < ntiles) load_tile(kv0 + (NSTAGE - 1) * C::BK, (S + NSTAGE - 1) % NSTAGE);
 
     const uint8_t* ks = lds + S * C::STAGE_BYTES;
@@ -309,24 +305,44 @@ void fa_fwd_bf16_kernel(FwdParams p) {
       }
     }
 
-    // O^T += V^T P^T; V^T fragments by transpose reads of the V tile.
+    // O^T += V^T P^T; V^T fragments by transpose reads of the V tile, four
+    // MFMAs (eight reads) per group with the next group's reads in flight.
+    // Lane bases per head-dim slice; the key offsets of a read are
+    // immediates, since the swizzle chunk depends on the lane only.
+    constexpr int NM = C::ND * C::NB * 2;  // MFMAs per tile
+    constexpr int NG = NM / 4;             // groups of four
+    uint32_t vbase_db[C::ND];
 #pragma unroll
-    for (int db = 0; db < C::ND; ++db) {
-      const int dim = 32 * db + 16 * g16 + 4 * (r16 & 3);
-      const int cdim = dim >> 3, sub = (dim & 7) * 2;
-#pragma unroll
-      for (int bb = 0; bb < C::NB; ++bb) {
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          const int key0 = 32 * bb + 16 * half + 4 * h + (r16 >> 2);
-          const int key1 = key0 + 8;
-          const bf16x4 v0 = lds_read_tr16(vs + key0 * C::ROW_BYTES + 16 * v_chunk<D>(key0, cdim) + sub);
-          const bf16x4 v1 = lds_read_tr16(vs + key1 * C::ROW_BYTES + 16 * v_chunk<D>(key1, cdim) + sub);
-          const bf16x8 vf = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-          o_acc[db] = mfma_32x32x16_bf16(vf, pf[bb][half], o_acc[db]);
-        }
+    for (int db = 0; db < C::ND; ++db)
+      vbase_db[db] = (uint32_t)(uintptr_t)(lds_void*)(vs) + v_lane_off[db];
+    bf16x4 vr[2][8];
+    auto issue = [&](auto gc, bf16x4 (&dst)[8]) {
+      constexpr int g = decltype(gc)::value;
+      static_for<8>([&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        constexpr int m = 4 * g + i / 2;                    // MFMA index
+        constexpr int db = m / (2 * C::NB), bb = (m / 2) % C::NB, half = m % 2;
+        constexpr int off = (32 * bb + 16 * half + 8 * (i % 2)) * C::ROW_BYTES;
+        dst[i] = lds_read_tr16_async<off>((const void*)(uintptr_t)vbase_db[db]);
+      });
+    };
+    issue(std::integral_constant<int, 0>{}, vr[0]);
+    static_for<NG>([&](auto gc) {
+      constexpr int g = decltype(gc)::value;
+      if constexpr (g + 1 < NG) {
+        issue(std::integral_constant<int, g + 1>{}, vr[(g + 1) & 1]);
+        lds_wait8<8>(vr[g & 1]);  // group g complete; g + 1 may be in flight
+      } else {
+        lds_wait8<0>(vr[g & 1]);
       }
-    }
+      static_for<4>([&](auto jc) {
+        constexpr int m = 4 * g + decltype(jc)::value;
+        constexpr int db = m / (2 * C::NB), bb = (m / 2) % C::NB, half = m % 2;
+        const bf16x4 v0 = vr[g & 1][2 * (m % 4)], v1 = vr[g & 1][2 * (m % 4) + 1];
+        const bf16x8 vf = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+        o_acc[db] = mfma_32x32x16_bf16(vf, pf[bb][half], o_acc[db]);
+      });
+    });
   };
 
   for (int t = 0; t < ntiles; t += NSTAGE) {
