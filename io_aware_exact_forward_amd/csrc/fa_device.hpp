@@ -94,16 +94,31 @@ __device__ __forceinline__ bf16x4 lds_read_tr16(const void* p) {
 // buffer->LDS loads still in flight, which it cannot tell apart), and the
 // caller must wait for the result with lds_wait before using it.
 template <int OFFSET>
-__device__ __forceinline__ bf16x4 lds_read_tr16_async(const void* p) {
-  static_assert(OFFSET >= 0 && OFFSET < 65536, "ds offset field");
+__device__ __forceinline__ bf16x4 lds_read_tr16_async(uint32_t addr) {
+  static_assert(OFFSET >= 0 && OFFSET < 65536 && OFFSET % 8 == 0, "ds offset field");
   bf16x4 r;
-  const uint32_t a = (uint32_t)(uintptr_t)(lds_void*)p;
-  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(a), "i"(OFFSET));
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFFSET));
+  return r;
+}
+
+// LDS byte address of a pointer into the workgroup's shared memory.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(lds_void*)p;
+}
+
+// 16-byte LDS read (ds_read_b128) at addr + OFFSET, untracked like the
+// transpose read above: wait for it with lds_wait before use.  addr must be
+// 16-byte aligned.
+template <int OFFSET>
+__device__ __forceinline__ bf16x8 lds_read_b128_async(uint32_t addr) {
+  static_assert(OFFSET >= 0 && OFFSET < 65536 && OFFSET % 16 == 0, "ds offset field");
+  bf16x8 r;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFFSET));
   return r;
 }
 
 // Wait until at most N of this wave's LDS operations are outstanding (they
-// complete in order).  The eight values are passed through the wait, so
+// complete in order).  The values are passed through the wait, so
 // everything the compiler schedules after it that uses them sees them
 // complete.
 template <int N>
@@ -113,6 +128,11 @@ __device__ __forceinline__ void lds_wait8(bf16x4 (&v)[8]) {
                : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]),
                  "+v"(v[6]), "+v"(v[7])
                : "i"(N));
+}
+template <int N>
+__device__ __forceinline__ void lds_wait4(bf16x8 (&v)[4]) {
+  static_assert(N >= 0 && N < 16, "lgkmcnt field");
+  asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]) : "i"(N));
 }
 
 // Calls f(std::integral_constant<int, I>{}) for I = 0 .. N-1, so that the
@@ -129,9 +149,13 @@ __device__ __forceinline__ void static_for(F&& f) {
 // Workgroup barrier without a memory fence.  The caller makes its own
 // memory operations complete (with the waits above) before arriving; the
 // fence __syncthreads() adds would also wait for prefetches that are meant
-// to stay in flight across the barrier.
+// to stay in flight across the barrier.  The scheduling barriers keep the
+// compiler from moving any instruction (MFMAs included, which the memory
+// clobber does not hold) across it.
 __device__ __forceinline__ void barrier_no_fence() {
+  __builtin_amdgcn_sched_barrier(0);
   asm volatile("s_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 // Wait until at most N of this wave's vector-memory operations (loads,

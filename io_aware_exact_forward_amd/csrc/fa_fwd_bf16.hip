@@ -87,7 +87,7 @@ __device__ __forceinline__ int v_chunk(int row, int c) {
                   : (c ^ (4 * ((row >> 1) & 1) + 2 * ((row >> 2) & 1)));
 }
 
-template <int D, bool CAUSAL, int WAVES, int NSTAGE>
+template <int D, bool CAUSAL, int WAVES, int NSTAGE, bool PINGPONG>
 __global__ __launch_bounds__(64 * WAVES, (WAVES == 4 && NSTAGE == 2) ? 2 : 1)
 void fa_fwd_bf16_kernel(FwdParams p) {
   using C = Bf16Cfg<D, WAVES, NSTAGE>;
@@ -155,7 +155,9 @@ void fa_fwd_bf16_kernel(FwdParams p) {
     koff[i] = row * C::ROW_BYTES + 16 * k_chunk<D>(row, phys);  // XOR is its own inverse
     voff[i] = row * C::ROW_BYTES + 16 * v_chunk<D>(row, phys);
   }
-  auto load_tile = [&](int kv0, int stage) {
+  // With nbytes = 0 every lane is out of range: the stage is filled with
+  // zeros and no memory is read.
+  auto load_tile_n = [&](int kv0, int stage, uint32_t nbytes) __attribute__((always_inline)) {
     uint8_t* ks = lds + stage * C::STAGE_BYTES;
     uint8_t* vs = ks + C::TILE_BYTES;
     const uint32_t tile_off = __builtin_amdgcn_readfirstlane(kv0 * C::ROW_BYTES);
@@ -164,24 +166,13 @@ void fa_fwd_bf16_kernel(FwdParams p) {
       const int blk = (WAVES * i + wave) * 1024;
       // The whole offset goes in the per-lane operand: the range check
       // covers that operand (not the scalar one).
-      load_lds_16(kbase, valid_bytes, ks + blk, koff[i] + tile_off);
-      load_lds_16(vbase, valid_bytes, vs + blk, voff[i] + tile_off);
+      load_lds_16(kbase, nbytes, ks + blk, koff[i] + tile_off);
+      load_lds_16(vbase, nbytes, vs + blk, voff[i] + tile_off);
     }
   };
-
-  // V transpose reads: in each 16-lane group, lane r reads key +r/4 and
-  // dims +4*(r%4), so lane r receives dim r of four consecutive keys.  The
-  // swizzle chunk of such a read depends on the lane and the head-dim slice
-  // only (not on which 8-key group of the tile is read), so each slice has
-  // one per-lane byte offset.
-  const int r16 = lane & 15, g16 = (lane >> 4) & 1;
-  uint32_t v_lane_off[C::ND];
-#pragma unroll
-  for (int db = 0; db < C::ND; ++db) {
-    const int key = 4 * h + (r16 >> 2);
-    const int dim = 32 * db + 16 * g16 + 4 * (r16 & 3);
-    v_lane_off[db] = key * C::ROW_BYTES + 16 * v_chunk<D>(key, dim >> 3) + (dim & 7) * 2;
-  }
+  auto load_tile = [&](int kv0, int stage) __attribute__((always_inline)) {
+    load_tile_n(kv0, stage, valid_bytes);
+  };
 
   // ---- running state (one query row per lane) -----------------------------
   f32x16 o_acc[C::ND];
@@ -193,50 +184,62 @@ void fa_fwd_bf16_kernel(FwdParams p) {
   const float c = p.c;
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-  // Prologue: the first NSTAGE - 1 tiles.
+  // Waves whose rows see no key of the tile at kv0 skip it (wave-uniform).
+  auto skip_tile = [&](const int kv0) __attribute__((always_inline)) {
+    return (CAUSAL && kv0 > qw0 + 31) || (qw0 >= kv_lim);
+  };
+
+  // ---- LDS fragment reads ---------------------------------------------------
+  // Both products read their LDS operands in groups of four MFMAs' worth,
+  // issued one group ahead of the MFMAs that use them (untracked reads with
+  // explicit waits; LDS operations of a wave complete in order).
+  //
+  // K fragment (kk, bb): row 32*bb + l32 of the tile, logical chunk 2*kk + h.
+  // The swizzle depends on the row only through l32, so each kk has one
+  // per-lane offset and bb is an immediate.
+  uint32_t k_lane_off[D / 16];
 #pragma unroll
-  for (int s = 0; s < NSTAGE - 1; ++s)
-    if (s < ntiles) load_tile(s * C::BK, s);
+  for (int kk = 0; kk < D / 16; ++kk)
+    k_lane_off[kk] = l32 * C::ROW_BYTES + 16 * k_chunk<D>(l32, 2 * kk + h);
+  constexpr int KG = (D / 16) * C::NB / 4;  // K read groups per tile (4 reads each)
+  auto k_issue = [&](auto gc, const uint32_t kbase, bf16x8 (&dst)[4])
+      __attribute__((always_inline)) {
+    constexpr int g = decltype(gc)::value;
+    static_for<4>([&](auto jc) __attribute__((always_inline)) {
+      constexpr int i = 4 * g + decltype(jc)::value;
+      constexpr int kk = i / C::NB, bb = i % C::NB;
+      dst[decltype(jc)::value] =
+          lds_read_b128_async<bb * 32 * C::ROW_BYTES>(kbase + k_lane_off[kk]);
+    });
+  };
+  bf16x8 kr[2][4];
 
-  // One streamed tile, read from LDS stage S (a compile-time constant: the
-  // loop below cycles through the NSTAGE instantiations, so every LDS read
-  // address is a per-lane base plus an immediate offset).
-  auto step = [&](const int t, auto stage_tag) {
-    constexpr int S = decltype(stage_tag)::value;
-    const int kv0 = t * C::BK;
-
-    // Tile t has landed once at most the loads of the tiles issued after
-    // it are still in flight; after the barrier every wave's part has
-    // landed and every wave is done with tile t - 1, whose stage is refilled.
-    const int later = min(NSTAGE - 2, ntiles - 1 - t);  // 0 .. NSTAGE - 2 (uniform)
-    if (NSTAGE > 3 && later >= 2) vmem_wait<(NSTAGE > 3 ? 2 : 0) * C::LOADS_PER_TILE>();
-    else if (later >= 1) vmem_wait<C::LOADS_PER_TILE>();
-    else vmem_wait<0>();
-    barrier_no_fence();
-    if (t + NSTAGE - 1 < ntiles) load_tile(kv0 + (NSTAGE - 1) * C::BK, (S + NSTAGE - 1) % NSTAGE);
-
-    const uint8_t* ks = lds + S * C::STAGE_BYTES;
-    const uint8_t* vs = ks + C::TILE_BYTES;
-
-    // Waves whose rows see no key of this tile skip it (wave-uniform).
-    const bool skip = (CAUSAL && kv0 > qw0 + 31) || (qw0 >= kv_lim);
-    if (skip) return;
-
-    // S^T = K Q^T: NB accumulators of 32 keys x 32 queries.
-    f32x16 s[C::NB];
+  // S^T = K Q^T for the K tile at kbase: NB accumulators of 32 keys x 32
+  // queries.  K group 0 must already be in flight (k_issue into kr[0]).
+  auto compute_s = [&](const uint32_t kbase, f32x16 (&s)[C::NB]) __attribute__((always_inline)) {
 #pragma unroll
     for (int bb = 0; bb < C::NB; ++bb) s[bb] = f32x16{};
-#pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
-#pragma unroll
-      for (int bb = 0; bb < C::NB; ++bb) {
-        const int row = 32 * bb + l32;
-        const bf16x8 kf =
-            *(const bf16x8*)(ks + row * C::ROW_BYTES + 16 * k_chunk<D>(row, 2 * kk + h));
-        s[bb] = mfma_32x32x16_bf16(kf, qf[kk], s[bb]);
+    static_for<KG>([&](auto gc) __attribute__((always_inline)) {
+      constexpr int g = decltype(gc)::value;
+      if constexpr (g + 1 < KG) {
+        k_issue(std::integral_constant<int, g + 1>{}, kbase, kr[(g + 1) & 1]);
+        lds_wait4<4>(kr[g & 1]);
+      } else {
+        lds_wait4<0>(kr[g & 1]);
       }
-    }
+      static_for<4>([&](auto jc) __attribute__((always_inline)) {
+        constexpr int i = 4 * g + decltype(jc)::value;
+        constexpr int kk = i / C::NB, bb = i % C::NB;
+        s[bb] = mfma_32x32x16_bf16(kr[g & 1][decltype(jc)::value], qf[kk], s[bb]);
+      });
+    });
+  };
 
+  // Scores of the tile at kv0 -> bf16 probabilities (the B operand of the
+  // second product), with the running reference maximum and denominators
+  // brought up to date.
+  auto softmax = [&](const int kv0, f32x16 (&s)[C::NB], bf16x8 (&pf)[C::NB][2])
+      __attribute__((always_inline)) {
     // Element masks only where the tile crosses the diagonal or the
     // sequence end (wave-uniform test).
     const bool masked = (CAUSAL && kv0 + C::BK - 1 > qw0) || (kv0 + C::BK > kv_lim);
@@ -274,7 +277,6 @@ void fa_fwd_bf16_kernel(FwdParams p) {
     const float neg_m = (m_ref == kNegInf) ? 0.f : -m_ref;
 
     // P = exp2(c*s - m_ref), packed to bf16.
-    bf16x8 pf[C::NB][2];
 #pragma unroll
     for (int bb = 0; bb < C::NB; ++bb) {
 #pragma unroll
@@ -284,76 +286,232 @@ void fa_fwd_bf16_kernel(FwdParams p) {
         for (int t8 = 0; t8 < 8; ++t8)
           // masked scores are -inf and c > 0, so they give exactly 0
           e[t8] = fast_exp2(__builtin_fmaf(s[bb][8 * half + t8], c, neg_m));
-        // Two denominators.  l_run sums the fp32 values and feeds the
-        // log-sum-exp (the bf16-rounded sum is off by up to 2^-9 relative
-        // on rows with few keys).  lp_run sums the bf16 values the second
-        // product multiplies, so a / lp_run is an exact convex combination
-        // of V rows under those weights; a dominant key is then reproduced
-        // without the 2^-9 error of its rounded weight.  (The pairs are
-        // built as bf16x2 values and fed to the dot product directly:
-        // taking them as bit casts of u32x4 elements made this compiler
-        // read the first element for all four dot products.)
+        // l_run sums the fp32 values and feeds the log-sum-exp; the sum of
+        // the bf16-rounded values (lp_run, for o) is taken in the second
+        // product's step.
         bf16x2 pr[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           l_run += e[2 * j] + e[2 * j + 1];
           pr[j] = bf16x2{(__bf16)e[2 * j], (__bf16)e[2 * j + 1]};
-          lp_run = __builtin_amdgcn_fdot2_f32_bf16(pr[j], ones, lp_run, false);
         }
         pf[bb][half] = bf16x8{pr[0][0], pr[0][1], pr[1][0], pr[1][1],
                               pr[2][0], pr[2][1], pr[3][0], pr[3][1]};
       }
     }
+  };
 
-    // O^T += V^T P^T; V^T fragments by transpose reads of the V tile, four
-    // MFMAs (eight reads) per group with the next group's reads in flight.
-    // Lane bases per head-dim slice; the key offsets of a read are
-    // immediates, since the swizzle chunk depends on the lane only.
-    constexpr int NM = C::ND * C::NB * 2;  // MFMAs per tile
-    constexpr int NG = NM / 4;             // groups of four
-    uint32_t vbase_db[C::ND];
+  // O^T += V^T P^T.  V^T fragments come from transpose reads of the V tile,
+  // eight reads (four MFMAs) per group.  In each 16-lane group, lane r
+  // reads key +r/4 and dims +4*(r%4), so lane r receives dim r of four
+  // consecutive keys; the swizzle chunk of such a read depends on the lane
+  // and the head-dim slice only, so each slice has one per-lane offset and
+  // the key offsets are immediates.
+  uint32_t v_lane_off[C::ND];
 #pragma unroll
-    for (int db = 0; db < C::ND; ++db)
-      vbase_db[db] = (uint32_t)(uintptr_t)(lds_void*)(vs) + v_lane_off[db];
-    bf16x4 vr[2][8];
-    auto issue = [&](auto gc, bf16x4 (&dst)[8]) {
+  for (int db = 0; db < C::ND; ++db) {
+    const int r16 = lane & 15, g16 = (lane >> 4) & 1;
+    const int key = 4 * h + (r16 >> 2);
+    const int dim = 32 * db + 16 * g16 + 4 * (r16 & 3);
+    v_lane_off[db] = key * C::ROW_BYTES + 16 * v_chunk<D>(key, dim >> 3) + (dim & 7) * 2;
+  }
+  constexpr int VG = C::ND * C::NB * 2 / 4;  // V read groups per tile (8 reads each)
+  auto v_issue = [&](auto gc, const uint32_t vbase, bf16x4 (&dst)[8])
+      __attribute__((always_inline)) {
+    constexpr int g = decltype(gc)::value;
+    static_for<8>([&](auto ic) __attribute__((always_inline)) {
+      constexpr int i = decltype(ic)::value;
+      constexpr int m = 4 * g + i / 2;  // MFMA index
+      constexpr int db = m / (2 * C::NB), bb = (m / 2) % C::NB, half = m % 2;
+      constexpr int off = (32 * bb + 16 * half + 8 * (i % 2)) * C::ROW_BYTES;
+      dst[i] = lds_read_tr16_async<off>(vbase + v_lane_off[db]);
+    });
+  };
+  bf16x4 vr[2][8];
+
+  // The second product for the V tile at vbase, V group 0 already in flight
+  // (v_issue into vr[0]).  With chain_k, K group 0 of the tile at kbase is
+  // issued behind the last V group, so the first product can follow without
+  // waiting for LDS.
+  auto pv = [&](const uint32_t vbase, const bf16x8 (&pf)[C::NB][2], auto chain_tag,
+                const uint32_t kbase) __attribute__((always_inline)) {
+    constexpr bool chain_k = decltype(chain_tag)::value;
+    static_for<VG>([&](auto gc) __attribute__((always_inline)) {
       constexpr int g = decltype(gc)::value;
-      static_for<8>([&](auto ic) {
-        constexpr int i = decltype(ic)::value;
-        constexpr int m = 4 * g + i / 2;                    // MFMA index
-        constexpr int db = m / (2 * C::NB), bb = (m / 2) % C::NB, half = m % 2;
-        constexpr int off = (32 * bb + 16 * half + 8 * (i % 2)) * C::ROW_BYTES;
-        dst[i] = lds_read_tr16_async<off>((const void*)(uintptr_t)vbase_db[db]);
-      });
-    };
-    issue(std::integral_constant<int, 0>{}, vr[0]);
-    static_for<NG>([&](auto gc) {
-      constexpr int g = decltype(gc)::value;
-      if constexpr (g + 1 < NG) {
-        issue(std::integral_constant<int, g + 1>{}, vr[(g + 1) & 1]);
+      if constexpr (g + 1 < VG) {
+        v_issue(std::integral_constant<int, g + 1>{}, vbase, vr[(g + 1) & 1]);
         lds_wait8<8>(vr[g & 1]);  // group g complete; g + 1 may be in flight
+      } else if constexpr (chain_k) {
+        k_issue(std::integral_constant<int, 0>{}, kbase, kr[0]);
+        lds_wait8<4>(vr[g & 1]);
       } else {
         lds_wait8<0>(vr[g & 1]);
       }
-      static_for<4>([&](auto jc) {
+      static_for<4>([&](auto jc) __attribute__((always_inline)) {
         constexpr int m = 4 * g + decltype(jc)::value;
         constexpr int db = m / (2 * C::NB), bb = (m / 2) % C::NB, half = m % 2;
         const bf16x4 v0 = vr[g & 1][2 * (m % 4)], v1 = vr[g & 1][2 * (m % 4) + 1];
         const bf16x8 vf = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
         o_acc[db] = mfma_32x32x16_bf16(vf, pf[bb][half], o_acc[db]);
       });
+      // lp_run, the sum of the bf16 weights the product multiplies, so that
+      // a / lp_run is an exact convex combination of V rows under those
+      // weights (a dominant key is then reproduced without the 2^-9 error
+      // of its rounded weight).  The dot products run on the matrix pipe:
+      // here they slot in between this wave's own MFMAs, where in the
+      // softmax step each would wait for a whole MFMA of the other wave
+      // sharing the SIMD.  Group g sums 2*NB/NG of the weight vectors.
+      constexpr int PER = 2 * C::NB / VG;
+      static_for<PER>([&](auto ic) __attribute__((always_inline)) {
+        constexpr int f = g * PER + decltype(ic)::value;
+        const bf16x8 w = pf[f / 2][f % 2];
+        static_for<4>([&](auto jc) __attribute__((always_inline)) {
+          constexpr int j = decltype(jc)::value;
+          lp_run = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{w[2 * j], w[2 * j + 1]}, ones, lp_run,
+                                                   false);
+        });
+      });
+      // keeps the compiler from sinking the sum into the softmax step
+      asm volatile("" : "+v"(lp_run));
     });
   };
 
-  for (int t = 0; t < ntiles; t += NSTAGE) {
-    step(t, StageTag<0>{});
-    if (t + 1 < ntiles) step(t + 1, StageTag<1>{});
-    if constexpr (NSTAGE > 2) {
-      if (t + 2 < ntiles) step(t + 2, StageTag<2>{});
+  f32x16 s[C::NB];
+  bf16x8 pf[C::NB][2];
+  const uint32_t lds0 = lds_addr(lds);
+  constexpr auto G0 = std::integral_constant<int, 0>{};
+
+  if constexpr (!PINGPONG) {
+    // ---- lockstep schedule: every wave runs S, softmax and PV of a tile
+    // between two barriers -------------------------------------------------
+#pragma unroll
+    for (int st = 0; st < NSTAGE - 1; ++st)
+      if (st < ntiles) load_tile(st * C::BK, st);
+
+    // One streamed tile, read from LDS stage S (a compile-time constant:
+    // the loop below cycles through the NSTAGE instantiations).
+    auto step = [&](const int t, auto stage_tag) __attribute__((always_inline)) {
+      constexpr int S = decltype(stage_tag)::value;
+      const int kv0 = t * C::BK;
+      // Tile t has landed once at most the loads of the tiles issued after
+      // it are still in flight; after the barrier every wave's part has
+      // landed and every wave is done with tile t - 1, whose stage is
+      // refilled.
+      const int later = min(NSTAGE - 2, ntiles - 1 - t);  // 0 .. NSTAGE - 2 (uniform)
+      if (NSTAGE > 3 && later >= 2) vmem_wait<(NSTAGE > 3 ? 2 : 0) * C::LOADS_PER_TILE>();
+      else if (later >= 1) vmem_wait<C::LOADS_PER_TILE>();
+      else vmem_wait<0>();
+      barrier_no_fence();
+      if (t + NSTAGE - 1 < ntiles) load_tile(kv0 + (NSTAGE - 1) * C::BK, (S + NSTAGE - 1) % NSTAGE);
+      if (skip_tile(kv0)) return;
+      uint32_t kbase = lds0 + S * C::STAGE_BYTES;
+      asm volatile("" : "+s"(kbase));  // see the ping-pong schedule
+      k_issue(G0, kbase, kr[0]);
+      compute_s(kbase, s);
+      softmax(kv0, s, pf);
+      v_issue(G0, kbase + C::TILE_BYTES, vr[0]);
+      pv(kbase + C::TILE_BYTES, pf, std::false_type{}, 0u);
+    };
+    for (int t = 0; t < ntiles; t += NSTAGE) {
+      step(t, StageTag<0>{});
+      if (t + 1 < ntiles) step(t + 1, StageTag<1>{});
+      if constexpr (NSTAGE > 2) {
+        if (t + 2 < ntiles) step(t + 2, StageTag<2>{});
+      }
+      if constexpr (NSTAGE > 3) {
+        if (t + 3 < ntiles) step(t + 3, StageTag<3>{});
+      }
     }
-    if constexpr (NSTAGE > 3) {
-      if (t + 3 < ntiles) step(t + 3, StageTag<3>{});
+  } else {
+    // ---- ping-pong schedule ----------------------------------------------
+    // The two waves that share a SIMD belong to different groups (waves
+    // 0-3 and 4-7; the hardware deals a workgroup's waves to the four SIMDs
+    // in turn).  Each wave alternates an MFMA phase (PV of tile t - 1, then
+    // S of tile t) with a softmax phase (tile t, VALU only), and the second
+    // group runs one phase behind the first: while one wave of a SIMD keeps
+    // the matrix core busy, the other has the vector ALU to itself.  Every
+    // phase starts at a workgroup barrier (a barrier only counts arrivals,
+    // so the two groups may arrive from different points of their loop).
+    // Since a phase lasts as long as its slowest wave, waves do not skip
+    // tiles their rows cannot see here: the scores come out masked and the
+    // probabilities zero.
+    //
+    // LDS ring of four stages.  Tile t is read by the MFMA phases that start
+    // at barriers 2t and 2t+1 (its K) and 2t+2 and 2t+3 (its V); the loads
+    // of tile t + 2 are issued at the start of a wave's MFMA phase t, into
+    // the stage of tile t - 2, whose last reader finished at barrier 2t.
+    // Past the last tile those loads are zero fills (an empty buffer
+    // range), so every MFMA phase issues the same number of loads.  Before
+    // the barrier that opens its softmax phase t, each wave waits for its
+    // own loads of tile t + 1, leaving only those of tile t + 2 in flight,
+    // so tile t + 1 is complete at barrier 2t+2, where the first group's
+    // MFMA phase t + 1 starts.  The V reads of PV of tile t - 1 may start
+    // before the barrier: that tile is complete since barrier 2t-2 and its
+    // stage is refilled only after barrier 2t+2.
+    //
+    // Fragment reads run ahead of their MFMAs untracked by the compiler, so
+    // no control-flow join (where the compiler may copy registers) lies
+    // between a read and its wait: each phase below is straight-line code.
+    static_assert(WAVES == 8 && NSTAGE == 4, "ping-pong needs 8 waves and 4 stages");
+    const int grp = wave >> 2;
+    if (0 < ntiles) load_tile(0, 0);
+    if (1 < ntiles) load_tile(C::BK, 1);
+    if (1 < ntiles) vmem_wait<C::LOADS_PER_TILE>();
+    else vmem_wait<0>();
+    if (grp == 1) barrier_no_fence();  // the second group's idle first phase
+
+    auto k_stage = [&](const int t) __attribute__((always_inline)) {
+      return lds0 + (uint32_t)(t & 3) * C::STAGE_BYTES;
+    };
+    auto v_stage = [&](const int t) __attribute__((always_inline)) {
+      return lds0 + (uint32_t)(t & 3) * C::STAGE_BYTES + C::TILE_BYTES;
+    };
+    // Opens MFMA phase t: barrier, then the loads of tile t + 2.  The wave
+    // in its MFMA phase takes issue priority over its partner in softmax:
+    // otherwise the older of the two waves wins the arbitration whatever
+    // it runs, and the matrix core idles whenever that is the VALU wave.
+    auto open_phase = [&](const int t) __attribute__((always_inline)) {
+      barrier_no_fence();
+      __builtin_amdgcn_s_setprio(1);
+      const uint32_t nb = t + 2 < ntiles ? valid_bytes : 0u;
+      load_tile_n((t + 2) * C::BK, (t + 2) & 3, __builtin_amdgcn_readfirstlane(nb));
+    };
+    // Closes MFMA phase t < ntiles and runs softmax phase t.
+    auto softmax_phase = [&](const int t) __attribute__((always_inline)) {
+      vmem_wait<C::LOADS_PER_TILE>();  // this wave's loads of tile t + 1
+      __builtin_amdgcn_s_setprio(0);
+      barrier_no_fence();
+      softmax(t * C::BK, s, pf);
+    };
+
+    if (ntiles > 0) {
+      // phase 0: S of tile 0 only
+      open_phase(0);
+      const uint32_t kb = k_stage(0);
+      k_issue(G0, kb, kr[0]);
+      compute_s(kb, s);
+      softmax_phase(0);
+      for (int t = 1; t < ntiles; ++t) {
+        const uint32_t vb = v_stage(t - 1), kb2 = k_stage(t);
+        v_issue(G0, vb, vr[0]);
+        open_phase(t);
+        pv(vb, pf, std::true_type{}, kb2);
+        compute_s(kb2, s);
+        softmax_phase(t);
+      }
+      // last phase: PV of the last tile only
+      const uint32_t vb = v_stage(ntiles - 1);
+      v_issue(G0, vb, vr[0]);
+      open_phase(ntiles);
+      pv(vb, pf, std::false_type{}, 0u);
+    } else {
+      barrier_no_fence();  // the one MFMA phase, with nothing to do
     }
+    __builtin_amdgcn_s_setprio(0);
+    // Both groups pass 2 * ntiles + 2 barriers: the first group's last one.
+    if (grp == 0) barrier_no_fence();
+    // No load into LDS may still be in flight when the workgroup ends.
+    vmem_wait<0>();
   }
 
   // ---- epilogue: o = a / l, LSE = ln(2) * (m + log2 l) ---------------------
@@ -381,13 +539,13 @@ void fa_fwd_bf16_kernel(FwdParams p) {
   }
 }
 
-template <int D, bool CAUSAL, int WAVES, int NSTAGE>
+template <int D, bool CAUSAL, int WAVES, int NSTAGE, bool PINGPONG>
 hipError_t launch_cfg(FwdParams p, hipStream_t stream) {
   using C = Bf16Cfg<D, WAVES, NSTAGE>;
   p.n_qtiles = (p.N + C::BQ - 1) / C::BQ;
   const dim3 grid((unsigned)((int64_t)p.n_qtiles * p.B * p.H));
-  hipLaunchKernelGGL((fa_fwd_bf16_kernel<D, CAUSAL, WAVES, NSTAGE>), grid, dim3(64 * WAVES), 0,
-                     stream, p);
+  hipLaunchKernelGGL((fa_fwd_bf16_kernel<D, CAUSAL, WAVES, NSTAGE, PINGPONG>), grid,
+                     dim3(64 * WAVES), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -398,8 +556,8 @@ hipError_t launch_d(const FwdParams& p, hipStream_t stream) {
   // two workgroups per CU, 2 stages) otherwise.  (Measured on MI355X at
   // N = 8192, d = 128: 3 stages are a few percent ahead of 2 and 4.)
   const int64_t big_tiles = (int64_t)p.B * p.H * ((p.N + 255) / 256);
-  if (big_tiles >= 512) return launch_cfg<D, CAUSAL, 8, 3>(p, stream);
-  return launch_cfg<D, CAUSAL, 4, 2>(p, stream);
+  if (big_tiles >= 512) return launch_cfg<D, CAUSAL, 8, 4, true>(p, stream);
+  return launch_cfg<D, CAUSAL, 4, 2, false>(p, stream);
 }
 
 }  // namespace
