@@ -28,13 +28,13 @@
 // numerator is one multiply per register.
 //
 // Reference maximum.  Scores are exponentiated against a per-row reference
-// value.  It is raised to the running maximum only when some row's block
-// maximum exceeds it by more than kRescaleSlack (log2 units); otherwise the
-// old reference stays and exponentials may reach 2^kRescaleSlack.  The
-// denominator and numerator always share the reference, so o = a / l is
-// unchanged: this is the glossary page's observation ("Why a tile can be
-// discarded") that any common reference maximum preserves the exponential
-// sums, and it skips most rescales of the accumulator.
+// value, which is raised to the running maximum only when a tile's weights
+// against the old one would exceed kWeightBound (the test is on the sums
+// the denominator needs anyway, so the common path computes no row
+// maximum).  The denominator and numerator always share the reference, so
+// o = a / l is unchanged: this is the glossary page's observation ("Why a
+// tile can be discarded") that any common reference maximum preserves the
+// exponential sums, and it skips most rescales of the accumulator.
 //
 // Causal tiles run heaviest first; consecutive workgroups cycle over
 // (batch, head) so all tiles of a head land on one XCD when B*H is a
@@ -45,7 +45,9 @@
 namespace fa {
 namespace {
 
-constexpr float kRescaleSlack = 8.0f;
+// Bound on one lane's sum of the weights of a tile (and so on each weight)
+// before the reference maximum is raised: weights stay below 2^16.
+constexpr float kWeightBound = 65536.0f;
 
 template <int S>
 struct StageTag {
@@ -215,7 +217,8 @@ void fa_fwd_bf16_kernel(FwdParams p) {
   bf16x8 kr[2][4];
 
   // S^T = K Q^T for the K tile at kbase: NB accumulators of 32 keys x 32
-  // queries.  K group 0 must already be in flight (k_issue into kr[0]).
+  // queries.  K group 0 must already be in flight (k_issue into kr[0]); each
+  // later group is issued one group ahead.
   auto compute_s = [&](const uint32_t kbase, f32x16 (&s)[C::NB]) __attribute__((always_inline)) {
 #pragma unroll
     for (int bb = 0; bb < C::NB; ++bb) s[bb] = f32x16{};
@@ -238,7 +241,49 @@ void fa_fwd_bf16_kernel(FwdParams p) {
   // Scores of the tile at kv0 -> bf16 probabilities (the B operand of the
   // second product), with the running reference maximum and denominators
   // brought up to date.
-  auto softmax = [&](const int kv0, f32x16 (&s)[C::NB], bf16x8 (&pf)[C::NB][2])
+  // P = exp2(c*s + neg_m), packed to bf16 into pf (the B operand of the
+  // second product); returns this lane's sum of the fp32 values, which feeds
+  // the log-sum-exp (the sum of the bf16-rounded values, lp_run, for o is
+  // taken in the second product's step).
+  auto exp_pack = [&](f32x16 (&s)[C::NB], bf16x8 (&pf)[C::NB][2], const float neg_m)
+      __attribute__((always_inline)) {
+    float part[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int bb = 0; bb < C::NB; ++bb) {
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        float e[8];
+#pragma unroll
+        for (int t8 = 0; t8 < 8; ++t8)
+          // masked scores are -inf and c > 0, so they give exactly 0
+          e[t8] = fast_exp2(__builtin_fmaf(s[bb][8 * half + t8], c, neg_m));
+        bf16x2 pr[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          part[j] += e[2 * j] + e[2 * j + 1];
+          pr[j] = bf16x2{(__bf16)e[2 * j], (__bf16)e[2 * j + 1]};
+        }
+        pf[bb][half] = bf16x8{pr[0][0], pr[0][1], pr[1][0], pr[1][1],
+                              pr[2][0], pr[2][1], pr[3][0], pr[3][1]};
+      }
+    }
+    return (part[0] + part[1]) + (part[2] + part[3]);
+  };
+
+  // Scores of the tile at kv0 -> bf16 probabilities, with the reference
+  // maximum and the fp32 denominator brought up to date.  mid() runs after
+  // the masking, before the exponentials.
+  //
+  // The weights are first taken against the current reference.  Each
+  // weight of a lane is at most the lane's sum, so a sum within
+  // kWeightBound bounds them all and the tile is accepted as it is; inf and
+  // NaN fail that test.  Only otherwise (and for a row's first tile, when
+  // the reference is still -inf) does the wave find the tile's row maxima,
+  // raise the reference to the running maximum, rescale its state and redo
+  // the exponentials.  The reference therefore moves only when some weight
+  // would exceed the bound, and the row maximum costs nothing on the
+  // common path.
+  auto softmax = [&](const int kv0, f32x16 (&s)[C::NB], bf16x8 (&pf)[C::NB][2], auto&& mid)
       __attribute__((always_inline)) {
     // Element masks only where the tile crosses the diagonal or the
     // sequence end (wave-uniform test).
@@ -253,19 +298,23 @@ void fa_fwd_bf16_kernel(FwdParams p) {
           s[bb][r] = vis ? s[bb][r] : kNegInf;
         }
     }
-    // Row maximum: four independent partial maxima, then the wave halves.
-    float m4[4] = {kNegInf, kNegInf, kNegInf, kNegInf};
+    mid();
+    bool slow = __any(m_ref == kNegInf);
+    float lt = 0.f;
+    if (!slow) {
+      lt = exp_pack(s, pf, -m_ref);
+      slow = __any(!(lt <= kWeightBound));
+    }
+    if (slow) {
+      // Row maximum: four independent partial maxima, then the wave halves.
+      float m4[4] = {kNegInf, kNegInf, kNegInf, kNegInf};
 #pragma unroll
-    for (int bb = 0; bb < C::NB; ++bb)
+      for (int bb = 0; bb < C::NB; ++bb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) m4[r & 3] = fmaxf(m4[r & 3], s[bb][r]);
-    const float mx = halves_max(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3])));
-
-    // Raise the reference maximum only when some row outgrew it by more
-    // than the slack (wave-uniform decision; -inf - (-inf) never formed).
-    const float m_blk = (mx == kNegInf) ? kNegInf : mx * c;
-    const bool grow = m_blk > m_ref + kRescaleSlack;
-    if (__any(grow)) {
+        for (int r = 0; r < 16; ++r) m4[r & 3] = fmaxf(m4[r & 3], s[bb][r]);
+      const float mx = halves_max(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3])));
+      // -inf - (-inf) is never formed
+      const float m_blk = (mx == kNegInf) ? kNegInf : mx * c;
       const float m_new = fmaxf(m_ref, m_blk);
       const float alpha = (m_ref == kNegInf) ? 0.f : fast_exp2(m_ref - m_new);
       m_ref = m_new;
@@ -273,32 +322,9 @@ void fa_fwd_bf16_kernel(FwdParams p) {
       lp_run *= alpha;
 #pragma unroll
       for (int i = 0; i < C::ND; ++i) o_acc[i] *= alpha;
+      lt = exp_pack(s, pf, (m_ref == kNegInf) ? 0.f : -m_ref);
     }
-    const float neg_m = (m_ref == kNegInf) ? 0.f : -m_ref;
-
-    // P = exp2(c*s - m_ref), packed to bf16.
-#pragma unroll
-    for (int bb = 0; bb < C::NB; ++bb) {
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        float e[8];
-#pragma unroll
-        for (int t8 = 0; t8 < 8; ++t8)
-          // masked scores are -inf and c > 0, so they give exactly 0
-          e[t8] = fast_exp2(__builtin_fmaf(s[bb][8 * half + t8], c, neg_m));
-        // l_run sums the fp32 values and feeds the log-sum-exp; the sum of
-        // the bf16-rounded values (lp_run, for o) is taken in the second
-        // product's step.
-        bf16x2 pr[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          l_run += e[2 * j] + e[2 * j + 1];
-          pr[j] = bf16x2{(__bf16)e[2 * j], (__bf16)e[2 * j + 1]};
-        }
-        pf[bb][half] = bf16x8{pr[0][0], pr[0][1], pr[1][0], pr[1][1],
-                              pr[2][0], pr[2][1], pr[3][0], pr[3][1]};
-      }
-    }
+    l_run += lt;
   };
 
   // O^T += V^T P^T.  V^T fragments come from transpose reads of the V tile,
@@ -376,6 +402,49 @@ void fa_fwd_bf16_kernel(FwdParams p) {
     });
   };
 
+  // The second product from V fragments already in flight in vpre (all
+  // groups, issued in that order), followed by KPRE more LDS reads.  A wave
+  // has at most 15 LDS operations outstanding (the issue of a 16th waits),
+  // so a count above 15 is the same as 15: those outstanding are always the
+  // most recent ones.
+  bf16x4 vpre[VG][8];
+  // Groups [G0, G1) of the V fragments, issued at this point of the code.
+  auto v_issue_range = [&](const uint32_t vbase, auto g0_tag, auto g1_tag)
+      __attribute__((always_inline)) {
+    static_for<VG>([&](auto gc) __attribute__((always_inline)) {
+      if constexpr (decltype(gc)::value >= decltype(g0_tag)::value &&
+                    decltype(gc)::value < decltype(g1_tag)::value)
+        v_issue(gc, vbase, vpre[gc]);
+    });
+    __builtin_amdgcn_sched_barrier(0);  // issued here, ahead of the work that follows
+  };
+  auto pv_pre = [&](const bf16x8 (&pf)[C::NB][2], auto kpre_tag) __attribute__((always_inline)) {
+    constexpr int KPRE = decltype(kpre_tag)::value;
+    static_for<VG>([&](auto gc) __attribute__((always_inline)) {
+      constexpr int g = decltype(gc)::value;
+      constexpr int later = 8 * (VG - 1 - g) + KPRE;
+      lds_wait8<(later > 15 ? 15 : later)>(vpre[g]);
+      static_for<4>([&](auto jc) __attribute__((always_inline)) {
+        constexpr int m = 4 * g + decltype(jc)::value;
+        constexpr int db = m / (2 * C::NB), bb = (m / 2) % C::NB, half = m % 2;
+        const bf16x4 v0 = vpre[g][2 * (m % 4)], v1 = vpre[g][2 * (m % 4) + 1];
+        const bf16x8 vf = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+        o_acc[db] = mfma_32x32x16_bf16(vf, pf[bb][half], o_acc[db]);
+      });
+      constexpr int PER = 2 * C::NB / VG;
+      static_for<PER>([&](auto ic) __attribute__((always_inline)) {
+        constexpr int f = g * PER + decltype(ic)::value;
+        const bf16x8 w = pf[f / 2][f % 2];
+        static_for<4>([&](auto jc) __attribute__((always_inline)) {
+          constexpr int j = decltype(jc)::value;
+          lp_run = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{w[2 * j], w[2 * j + 1]}, ones, lp_run,
+                                                   false);
+        });
+      });
+      asm volatile("" : "+v"(lp_run));
+    });
+  };
+
   f32x16 s[C::NB];
   bf16x8 pf[C::NB][2];
   const uint32_t lds0 = lds_addr(lds);
@@ -408,7 +477,7 @@ void fa_fwd_bf16_kernel(FwdParams p) {
       asm volatile("" : "+s"(kbase));  // see the ping-pong schedule
       k_issue(G0, kbase, kr[0]);
       compute_s(kbase, s);
-      softmax(kv0, s, pf);
+      softmax(kv0, s, pf, [] {});
       v_issue(G0, kbase + C::TILE_BYTES, vr[0]);
       pv(kbase + C::TILE_BYTES, pf, std::false_type{}, 0u);
     };
@@ -476,34 +545,46 @@ void fa_fwd_bf16_kernel(FwdParams p) {
       const uint32_t nb = t + 2 < ntiles ? valid_bytes : 0u;
       load_tile_n((t + 2) * C::BK, (t + 2) & 3, __builtin_amdgcn_readfirstlane(nb));
     };
-    // Closes MFMA phase t < ntiles and runs softmax phase t.
+    // Closes MFMA phase t < ntiles and runs softmax phase t.  The V
+    // fragments of tile t (complete since barrier 2t) are read during the
+    // softmax, where this wave's SIMD has LDS bandwidth to spare, so the
+    // MFMA phase that multiplies them reads only K.  Half of them are issued
+    // before the softmax and half before its exponentials (a wave stalls
+    // once it has 15 LDS reads outstanding).
     auto softmax_phase = [&](const int t) __attribute__((always_inline)) {
       vmem_wait<C::LOADS_PER_TILE>();  // this wave's loads of tile t + 1
       __builtin_amdgcn_s_setprio(0);
       barrier_no_fence();
-      softmax(t * C::BK, s, pf);
+      const uint32_t vb = v_stage(t);
+      v_issue_range(vb, G0, std::integral_constant<int, VG / 2>{});
+      softmax(t * C::BK, s, pf, [&] {
+        v_issue_range(vb, std::integral_constant<int, VG / 2>{}, std::integral_constant<int, VG>{});
+      });
     };
+    constexpr auto K4 = std::integral_constant<int, 4>{};
+    constexpr auto K0 = std::integral_constant<int, 0>{};
 
+    // The loop runs from a softmax phase to the following MFMA phase, so the
+    // V reads issued in the one and waited for in the other never cross the
+    // loop's back edge.
     if (ntiles > 0) {
-      // phase 0: S of tile 0 only
+      // MFMA phase 0: S of tile 0 only
       open_phase(0);
       const uint32_t kb = k_stage(0);
       k_issue(G0, kb, kr[0]);
       compute_s(kb, s);
-      softmax_phase(0);
       for (int t = 1; t < ntiles; ++t) {
-        const uint32_t vb = v_stage(t - 1), kb2 = k_stage(t);
-        v_issue(G0, vb, vr[0]);
+        softmax_phase(t - 1);
+        const uint32_t kb2 = k_stage(t);
         open_phase(t);
-        pv(vb, pf, std::true_type{}, kb2);
+        k_issue(G0, kb2, kr[0]);
+        pv_pre(pf, K4);
         compute_s(kb2, s);
-        softmax_phase(t);
       }
-      // last phase: PV of the last tile only
-      const uint32_t vb = v_stage(ntiles - 1);
-      v_issue(G0, vb, vr[0]);
+      softmax_phase(ntiles - 1);
+      // last MFMA phase: PV of the last tile only
       open_phase(ntiles);
-      pv(vb, pf, std::false_type{}, 0u);
+      pv_pre(pf, K0);
     } else {
       barrier_no_fence();  // the one MFMA phase, with nothing to do
     }
