@@ -214,26 +214,35 @@ void fa_fwd_bf16_kernel(FwdParams p) {
           lds_read_b128_async<bb * 32 * C::ROW_BYTES>(kbase + k_lane_off[kk]);
     });
   };
-  bf16x8 kr[2][4];
+  bf16x8 kr[KG][4];
 
   // S^T = K Q^T for the K tile at kbase: NB accumulators of 32 keys x 32
-  // queries.  K group 0 must already be in flight (k_issue into kr[0]); each
-  // later group is issued one group ahead.
-  auto compute_s = [&](const uint32_t kbase, f32x16 (&s)[C::NB]) __attribute__((always_inline)) {
+  // queries.  With PRE = 1, K group 0 must already be in flight (k_issue
+  // into kr[0]) and each later group is issued one group ahead; with
+  // PRE = KG all groups are already in flight, in order, in kr[g].
+  auto compute_s = [&](const uint32_t kbase, f32x16 (&s)[C::NB], auto pre_tag)
+      __attribute__((always_inline)) {
+    constexpr int PRE = decltype(pre_tag)::value;
+    static_assert(PRE == 1 || PRE == KG, "chained or all in flight");
 #pragma unroll
     for (int bb = 0; bb < C::NB; ++bb) s[bb] = f32x16{};
     static_for<KG>([&](auto gc) __attribute__((always_inline)) {
       constexpr int g = decltype(gc)::value;
-      if constexpr (g + 1 < KG) {
-        k_issue(std::integral_constant<int, g + 1>{}, kbase, kr[(g + 1) & 1]);
-        lds_wait4<4>(kr[g & 1]);
+      constexpr int buf = PRE == 1 ? (g & 1) : g;
+      if constexpr (PRE == 1) {
+        if constexpr (g + 1 < KG) {
+          k_issue(std::integral_constant<int, g + 1>{}, kbase, kr[(g + 1) & 1]);
+          lds_wait4<4>(kr[buf]);
+        } else {
+          lds_wait4<0>(kr[buf]);
+        }
       } else {
-        lds_wait4<0>(kr[g & 1]);
+        lds_wait4<4 * (KG - 1 - g)>(kr[buf]);
       }
       static_for<4>([&](auto jc) __attribute__((always_inline)) {
         constexpr int i = 4 * g + decltype(jc)::value;
         constexpr int kk = i / C::NB, bb = i % C::NB;
-        s[bb] = mfma_32x32x16_bf16(kr[g & 1][decltype(jc)::value], qf[kk], s[bb]);
+        s[bb] = mfma_32x32x16_bf16(kr[buf][decltype(jc)::value], qf[kk], s[bb]);
       });
     });
   };
@@ -418,11 +427,15 @@ void fa_fwd_bf16_kernel(FwdParams p) {
     });
     __builtin_amdgcn_sched_barrier(0);  // issued here, ahead of the work that follows
   };
-  auto pv_pre = [&](const bf16x8 (&pf)[C::NB][2], auto kpre_tag) __attribute__((always_inline)) {
+  // KPRE reads were issued after the V groups, before this call; after(g)
+  // runs behind the MFMAs of group g and issues KPER reads (g < VG - 1).
+  auto pv_pre = [&](const bf16x8 (&pf)[C::NB][2], auto kpre_tag, auto kper_tag, auto&& after)
+      __attribute__((always_inline)) {
     constexpr int KPRE = decltype(kpre_tag)::value;
+    constexpr int KPER = decltype(kper_tag)::value;
     static_for<VG>([&](auto gc) __attribute__((always_inline)) {
       constexpr int g = decltype(gc)::value;
-      constexpr int later = 8 * (VG - 1 - g) + KPRE;
+      constexpr int later = 8 * (VG - 1 - g) + KPRE + KPER * g;
       lds_wait8<(later > 15 ? 15 : later)>(vpre[g]);
       static_for<4>([&](auto jc) __attribute__((always_inline)) {
         constexpr int m = 4 * g + decltype(jc)::value;
@@ -442,6 +455,7 @@ void fa_fwd_bf16_kernel(FwdParams p) {
         });
       });
       asm volatile("" : "+v"(lp_run));
+      after(gc);
     });
   };
 
@@ -476,7 +490,7 @@ void fa_fwd_bf16_kernel(FwdParams p) {
       uint32_t kbase = lds0 + S * C::STAGE_BYTES;
       asm volatile("" : "+s"(kbase));  // see the ping-pong schedule
       k_issue(G0, kbase, kr[0]);
-      compute_s(kbase, s);
+      compute_s(kbase, s, std::integral_constant<int, 1>{});
       softmax(kv0, s, pf, [] {});
       v_issue(G0, kbase + C::TILE_BYTES, vr[0]);
       pv(kbase + C::TILE_BYTES, pf, std::false_type{}, 0u);
@@ -542,6 +556,8 @@ void fa_fwd_bf16_kernel(FwdParams p) {
     auto open_phase = [&](const int t) __attribute__((always_inline)) {
       barrier_no_fence();
       __builtin_amdgcn_s_setprio(1);
+    };
+    auto issue_loads = [&](const int t) __attribute__((always_inline)) {
       const uint32_t nb = t + 2 < ntiles ? valid_bytes : 0u;
       load_tile_n((t + 2) * C::BK, (t + 2) & 3, __builtin_amdgcn_readfirstlane(nb));
     };
@@ -563,6 +579,8 @@ void fa_fwd_bf16_kernel(FwdParams p) {
     };
     constexpr auto K4 = std::integral_constant<int, 4>{};
     constexpr auto K0 = std::integral_constant<int, 0>{};
+    constexpr auto PRE1 = std::integral_constant<int, 1>{};
+    constexpr auto PREALL = std::integral_constant<int, KG>{};
 
     // The loop runs from a softmax phase to the following MFMA phase, so the
     // V reads issued in the one and waited for in the other never cross the
@@ -570,21 +588,32 @@ void fa_fwd_bf16_kernel(FwdParams p) {
     if (ntiles > 0) {
       // MFMA phase 0: S of tile 0 only
       open_phase(0);
+      issue_loads(0);
       const uint32_t kb = k_stage(0);
       k_issue(G0, kb, kr[0]);
-      compute_s(kb, s);
+      compute_s(kb, s, PRE1);
       for (int t = 1; t < ntiles; ++t) {
         softmax_phase(t - 1);
         const uint32_t kb2 = k_stage(t);
+        // PV of tile t - 1 starts right at the barrier (its V fragments
+        // are in registers); the tile loads and the K groups of tile t
+        // are issued behind its MFMA groups, one K group each, so that
+        // all of K is in registers when the first product starts.
         open_phase(t);
         k_issue(G0, kb2, kr[0]);
-        pv_pre(pf, K4);
-        compute_s(kb2, s);
+        pv_pre(pf, K4, K4, [&](auto gc) __attribute__((always_inline)) {
+          constexpr int g = decltype(gc)::value;
+          if constexpr (g == 0) issue_loads(t);
+          if constexpr (g + 1 < KG && g + 1 < VG)
+            k_issue(std::integral_constant<int, g + 1>{}, kb2, kr[g + 1]);
+        });
+        compute_s(kb2, s, PREALL);
       }
       softmax_phase(ntiles - 1);
       // last MFMA phase: PV of the last tile only
       open_phase(ntiles);
-      pv_pre(pf, K0);
+      issue_loads(ntiles);
+      pv_pre(pf, K0, K0, [](auto) {});
     } else {
       barrier_no_fence();  // the one MFMA phase, with nothing to do
     }
