@@ -509,39 +509,43 @@ void fa_fwd_bf16_kernel(FwdParams p) {
     // ---- ping-pong schedule ----------------------------------------------
     // The two waves that share a SIMD belong to different groups (waves
     // 0-3 and 4-7; the hardware deals a workgroup's waves to the four SIMDs
-    // in turn).  Each wave alternates an MFMA phase (PV of tile t - 1, then
-    // S of tile t) with a softmax phase (tile t, VALU only), and the second
+    // in turn).  Each wave alternates an MFMA phase t (PV of tile t - 1,
+    // then S of tile t) with a softmax phase t (VALU only), and the second
     // group runs one phase behind the first: while one wave of a SIMD keeps
-    // the matrix core busy, the other has the vector ALU to itself.  Every
-    // phase starts at a workgroup barrier (a barrier only counts arrivals,
-    // so the two groups may arrive from different points of their loop).
-    // Since a phase lasts as long as its slowest wave, waves do not skip
-    // tiles their rows cannot see here: the scores come out masked and the
-    // probabilities zero.
+    // the matrix core busy, the other has the vector ALU to itself.  The
+    // MFMA phase runs at raised issue priority: otherwise the older of the
+    // two waves wins the arbitration whatever it runs, and the matrix core
+    // idles whenever that is the VALU wave.  Since phases overlap across the
+    // groups, waves do not skip tiles their rows cannot see here: the scores
+    // come out masked and the probabilities zero.
     //
-    // LDS ring of four stages.  Tile t is read by the MFMA phases that start
-    // at barriers 2t and 2t+1 (its K) and 2t+2 and 2t+3 (its V); the loads
-    // of tile t + 2 are issued at the start of a wave's MFMA phase t, into
-    // the stage of tile t - 2, whose last reader finished at barrier 2t.
-    // Past the last tile those loads are zero fills (an empty buffer
-    // range), so every MFMA phase issues the same number of loads.  Before
-    // the barrier that opens its softmax phase t, each wave waits for its
-    // own loads of tile t + 1, leaving only those of tile t + 2 in flight,
-    // so tile t + 1 is complete at barrier 2t+2, where the first group's
-    // MFMA phase t + 1 starts.  The V reads of PV of tile t - 1 may start
-    // before the barrier: that tile is complete since barrier 2t-2 and its
-    // stage is refilled only after barrier 2t+2.
+    // One workgroup barrier per tile.  Barrier t opens the first group's
+    // MFMA phase t and the second group's softmax phase t - 1 (a barrier
+    // only counts arrivals, so the groups may arrive from different points
+    // of their code); that offset is all that pairs the phases.  Before
+    // barrier t each wave waits for its own loads of tile t, so the tile is
+    // complete at barrier t.
+    //
+    // LDS ring of four stages.  Every MFMA phase t issues the loads of tile
+    // t + 2 (past the last tile a zero fill, an empty buffer range) into the
+    // stage of tile t - 2.  Its last readers are the PV products of the MFMA
+    // phases t - 1, which both groups finish before barrier t, and the
+    // refill is issued after it.  K of tile t is read in MFMA phases t
+    // (after barrier t); V of tile t is read in softmax phases t (after
+    // barrier t) and waited for in MFMA phases t + 1, before barrier t + 2,
+    // after which its stage is refilled.
     //
     // Fragment reads run ahead of their MFMAs untracked by the compiler, so
     // no control-flow join (where the compiler may copy registers) lies
-    // between a read and its wait: each phase below is straight-line code.
+    // between a read and its wait: each group runs its own straight-line
+    // copy of the loop, in which a softmax phase and the MFMA phase that
+    // multiplies its V fragments fall in one iteration.
     static_assert(WAVES == 8 && NSTAGE == 4, "ping-pong needs 8 waves and 4 stages");
     const int grp = wave >> 2;
     if (0 < ntiles) load_tile(0, 0);
     if (1 < ntiles) load_tile(C::BK, 1);
     if (1 < ntiles) vmem_wait<C::LOADS_PER_TILE>();
     else vmem_wait<0>();
-    if (grp == 1) barrier_no_fence();  // the second group's idle first phase
 
     auto k_stage = [&](const int t) __attribute__((always_inline)) {
       return lds0 + (uint32_t)(t & 3) * C::STAGE_BYTES;
@@ -549,28 +553,17 @@ void fa_fwd_bf16_kernel(FwdParams p) {
     auto v_stage = [&](const int t) __attribute__((always_inline)) {
       return lds0 + (uint32_t)(t & 3) * C::STAGE_BYTES + C::TILE_BYTES;
     };
-    // Opens MFMA phase t: barrier, then the loads of tile t + 2.  The wave
-    // in its MFMA phase takes issue priority over its partner in softmax:
-    // otherwise the older of the two waves wins the arbitration whatever
-    // it runs, and the matrix core idles whenever that is the VALU wave.
-    auto open_phase = [&](const int t) __attribute__((always_inline)) {
-      barrier_no_fence();
-      __builtin_amdgcn_s_setprio(1);
-    };
     auto issue_loads = [&](const int t) __attribute__((always_inline)) {
       const uint32_t nb = t + 2 < ntiles ? valid_bytes : 0u;
       load_tile_n((t + 2) * C::BK, (t + 2) & 3, __builtin_amdgcn_readfirstlane(nb));
     };
-    // Closes MFMA phase t < ntiles and runs softmax phase t.  The V
-    // fragments of tile t (complete since barrier 2t) are read during the
-    // softmax, where this wave's SIMD has LDS bandwidth to spare, so the
-    // MFMA phase that multiplies them reads only K.  Half of them are issued
-    // before the softmax and half before its exponentials (a wave stalls
-    // once it has 15 LDS reads outstanding).
+    // Softmax phase t.  The V fragments of tile t are read here, where
+    // this wave's SIMD has LDS bandwidth to spare, so the MFMA phase that
+    // multiplies them reads only K.  Half of them are issued before the
+    // softmax and half before its exponentials (a wave stalls once it has
+    // 15 LDS reads outstanding).
     auto softmax_phase = [&](const int t) __attribute__((always_inline)) {
-      vmem_wait<C::LOADS_PER_TILE>();  // this wave's loads of tile t + 1
       __builtin_amdgcn_s_setprio(0);
-      barrier_no_fence();
       const uint32_t vb = v_stage(t);
       v_issue_range(vb, G0, std::integral_constant<int, VG / 2>{});
       softmax(t * C::BK, s, pf, [&] {
@@ -581,45 +574,49 @@ void fa_fwd_bf16_kernel(FwdParams p) {
     constexpr auto K0 = std::integral_constant<int, 0>{};
     constexpr auto PRE1 = std::integral_constant<int, 1>{};
     constexpr auto PREALL = std::integral_constant<int, KG>{};
-
-    // The loop runs from a softmax phase to the following MFMA phase, so the
-    // V reads issued in the one and waited for in the other never cross the
-    // loop's back edge.
-    if (ntiles > 0) {
-      // MFMA phase 0: S of tile 0 only
-      open_phase(0);
-      issue_loads(0);
-      const uint32_t kb = k_stage(0);
+    // MFMA phase 0 < t < ntiles.  PV of tile t - 1 starts right away (its
+    // V fragments are in flight or in registers); the tile loads and the K
+    // groups of tile t are issued behind its MFMA groups, one K group each,
+    // so that all of K is in registers when the first product starts.
+    auto mfma_phase = [&](const int t) __attribute__((always_inline)) {
+      __builtin_amdgcn_s_setprio(1);
+      const uint32_t kb = k_stage(t);
       k_issue(G0, kb, kr[0]);
-      compute_s(kb, s, PRE1);
+      pv_pre(pf, K4, K4, [&](auto gc) __attribute__((always_inline)) {
+        constexpr int g = decltype(gc)::value;
+        if constexpr (g == 0) issue_loads(t);
+        if constexpr (g + 1 < KG && g + 1 < VG)
+          k_issue(std::integral_constant<int, g + 1>{}, kb, kr[g + 1]);
+      });
+      compute_s(kb, s, PREALL);
+    };
+    auto run = [&](auto grp_tag) __attribute__((always_inline)) {
+      constexpr bool first = decltype(grp_tag)::value == 0;
+      barrier_no_fence();  // barrier 0
+      if (ntiles == 0) return;
+      // MFMA phase 0: S of tile 0 only
+      __builtin_amdgcn_s_setprio(1);
+      issue_loads(0);
+      k_issue(G0, k_stage(0), kr[0]);
+      compute_s(k_stage(0), s, PRE1);
       for (int t = 1; t < ntiles; ++t) {
-        softmax_phase(t - 1);
-        const uint32_t kb2 = k_stage(t);
-        // PV of tile t - 1 starts right at the barrier (its V fragments
-        // are in registers); the tile loads and the K groups of tile t
-        // are issued behind its MFMA groups, one K group each, so that
-        // all of K is in registers when the first product starts.
-        open_phase(t);
-        k_issue(G0, kb2, kr[0]);
-        pv_pre(pf, K4, K4, [&](auto gc) __attribute__((always_inline)) {
-          constexpr int g = decltype(gc)::value;
-          if constexpr (g == 0) issue_loads(t);
-          if constexpr (g + 1 < KG && g + 1 < VG)
-            k_issue(std::integral_constant<int, g + 1>{}, kb2, kr[g + 1]);
-        });
-        compute_s(kb2, s, PREALL);
+        if constexpr (first) softmax_phase(t - 1);
+        vmem_wait<C::LOADS_PER_TILE>();  // this wave's loads of tile t
+        barrier_no_fence();              // barrier t
+        if constexpr (!first) softmax_phase(t - 1);
+        mfma_phase(t);
       }
-      softmax_phase(ntiles - 1);
+      if constexpr (first) softmax_phase(ntiles - 1);
+      barrier_no_fence();  // barrier ntiles
+      if constexpr (!first) softmax_phase(ntiles - 1);
       // last MFMA phase: PV of the last tile only
-      open_phase(ntiles);
+      __builtin_amdgcn_s_setprio(1);
       issue_loads(ntiles);
       pv_pre(pf, K0, K0, [](auto) {});
-    } else {
-      barrier_no_fence();  // the one MFMA phase, with nothing to do
-    }
+    };
+    if (grp == 0) run(std::integral_constant<int, 0>{});
+    else run(std::integral_constant<int, 1>{});
     __builtin_amdgcn_s_setprio(0);
-    // Both groups pass 2 * ntiles + 2 barriers: the first group's last one.
-    if (grp == 0) barrier_no_fence();
     // No load into LDS may still be in flight when the workgroup ends.
     vmem_wait<0>();
   }
