@@ -244,6 +244,9 @@ void fa_fwd_bf16_kernel(FwdParams p) {
         constexpr int kk = i / C::NB, bb = i % C::NB;
         s[bb] = mfma_32x32x16_bf16(kr[buf][decltype(jc)::value], qf[kk], s[bb]);
       });
+      // each group's MFMAs stay between its wait and the next one (the
+      // compiler would otherwise gather the waits ahead of all MFMAs)
+      __builtin_amdgcn_sched_barrier(0);
     });
   };
 
@@ -433,6 +436,24 @@ void fa_fwd_bf16_kernel(FwdParams p) {
       __attribute__((always_inline)) {
     constexpr int KPRE = decltype(kpre_tag)::value;
     constexpr int KPER = decltype(kper_tag)::value;
+    // lp_run, the sum of the bf16 weights the product multiplies, so that
+    // a / lp_run is an exact convex combination of V rows under those
+    // weights (a dominant key is then reproduced without the 2^-9 error
+    // of its rounded weight).  The dot products run on the matrix pipe:
+    // here, back to back ahead of this wave's own MFMAs (interleaved with
+    // them, each one costs the pipe a turnaround; in the softmax step each
+    // would wait for a whole MFMA of the other wave sharing the SIMD).
+    static_for<2 * C::NB>([&](auto fc) __attribute__((always_inline)) {
+      constexpr int f = decltype(fc)::value;
+      const bf16x8 w = pf[f / 2][f % 2];
+      static_for<4>([&](auto jc) __attribute__((always_inline)) {
+        constexpr int j = decltype(jc)::value;
+        lp_run = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{w[2 * j], w[2 * j + 1]}, ones, lp_run,
+                                                 false);
+      });
+    });
+    asm volatile("" : "+v"(lp_run));  // keeps the sum here
+    __builtin_amdgcn_sched_barrier(0);
     static_for<VG>([&](auto gc) __attribute__((always_inline)) {
       constexpr int g = decltype(gc)::value;
       constexpr int later = 8 * (VG - 1 - g) + KPRE + KPER * g;
@@ -444,18 +465,8 @@ void fa_fwd_bf16_kernel(FwdParams p) {
         const bf16x8 vf = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
         o_acc[db] = mfma_32x32x16_bf16(vf, pf[bb][half], o_acc[db]);
       });
-      constexpr int PER = 2 * C::NB / VG;
-      static_for<PER>([&](auto ic) __attribute__((always_inline)) {
-        constexpr int f = g * PER + decltype(ic)::value;
-        const bf16x8 w = pf[f / 2][f % 2];
-        static_for<4>([&](auto jc) __attribute__((always_inline)) {
-          constexpr int j = decltype(jc)::value;
-          lp_run = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{w[2 * j], w[2 * j + 1]}, ones, lp_run,
-                                                   false);
-        });
-      });
-      asm volatile("" : "+v"(lp_run));
       after(gc);
+      __builtin_amdgcn_sched_barrier(0);  // keeps the group's MFMAs here
     });
   };
 
