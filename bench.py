@@ -33,7 +33,8 @@ PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA, 2.4 GHz
 PEAK_F32_TFLOPS = 157.3     # MI355X fp32 matrix
 PEAK_HBM_GBS = 8000.0
 DEFAULT_WORKLOAD = "h32_n8192_d128_causal_bf16"
-KERNEL_SOURCES = ["fa_fwd_bf16.hip", "fa_fwd_f32.hip", "fa_device.hpp", "fa_internal.hpp"]
+KERNEL_SOURCES = ["fa_fwd_bf16.hip", "fa_fwd_f32.hip", "fa_bf16_tiles.hpp",
+                  "fa_device.hpp", "fa_internal.hpp"]
 
 
 def kernel_hash() -> str:

@@ -39,6 +39,7 @@
 // Causal tiles run heaviest first; consecutive workgroups cycle over
 // (batch, head) so all tiles of a head land on one XCD when B*H is a
 // multiple of 8 (workgroups are dealt round-robin to the 8 XCDs).
+#include "fa_bf16_tiles.hpp"
 #include "fa_device.hpp"
 #include "fa_internal.hpp"
 
@@ -48,6 +49,12 @@ namespace {
 // Bound on one lane's sum of the weights of a tile (and so on each weight)
 // before the reference maximum is raised: weights stay below 2^16.
 constexpr float kWeightBound = 65536.0f;
+
+// LDS stages of the ping-pong schedule (4 x 32 KiB).  Five fit in 160 KiB
+// but the extra address state spills registers at 8 waves per CU and
+// measured slower.
+constexpr int kPingPongStages = 4;
+
 
 template <int S>
 struct StageTag {
@@ -68,26 +75,9 @@ struct Bf16Cfg {
   static constexpr int NB = BK / 32;             // 32-key blocks per tile
   static constexpr int ND = D / 32;              // 32-wide slices of the head dim
   static_assert(LOADS * WAVES * 1024 == TILE_BYTES, "tile must split into 1 KiB wave loads");
-  static_assert(NSTAGE >= 2 && NSTAGE <= 4, "2..4 LDS stages");
+  static_assert(NSTAGE >= 2 && NSTAGE <= 5, "2..5 LDS stages");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS capacity");
 };
-
-// Physical 16-byte chunk of logical chunk c in row `row` of a K tile.  Reads
-// of one chunk by 16 consecutive rows then touch 16 distinct bank groups.
-template <int D>
-__device__ __forceinline__ int k_chunk(int row, int c) {
-  return D == 128 ? (c ^ (row & 15)) : (c ^ ((row >> 1) & 7));
-}
-
-// Physical 16-byte chunk of logical chunk c in row `row` of a V tile.  A
-// transpose read covers 4 consecutive keys x 32 dims per half wave (and 8
-// keys x 16 dims per 16-lane pair); this permutation spreads both over all
-// banks.
-template <int D>
-__device__ __forceinline__ int v_chunk(int row, int c) {
-  return D == 128 ? (c ^ (4 * (row & 3) + 2 * ((row >> 2) & 1)))
-                  : (c ^ (4 * ((row >> 1) & 1) + 2 * ((row >> 2) & 1)));
-}
 
 template <int D, bool CAUSAL, int WAVES, int NSTAGE, bool PINGPONG>
 __global__ __launch_bounds__(64 * WAVES, (WAVES == 4 && NSTAGE == 2) ? 2 : 1)
@@ -551,35 +541,37 @@ void fa_fwd_bf16_kernel(FwdParams p) {
     // between a read and its wait: each group runs its own straight-line
     // copy of the loop, in which a softmax phase and the MFMA phase that
     // multiplies its V fragments fall in one iteration.
-    static_assert(WAVES == 8 && NSTAGE == 4, "ping-pong needs 8 waves and 4 stages");
+    static_assert(WAVES == 8 && NSTAGE >= 4, "ping-pong needs 8 waves and 4 or more stages");
+    constexpr int LA = NSTAGE - 2;  // tiles loaded ahead of the one being multiplied
     const int grp = wave >> 2;
-    if (0 < ntiles) load_tile(0, 0);
-    if (1 < ntiles) load_tile(C::BK, 1);
-    if (1 < ntiles) vmem_wait<C::LOADS_PER_TILE>();
-    else vmem_wait<0>();
-
+    auto stage_of = [&](const int t) __attribute__((always_inline)) {
+      return (uint32_t)(NSTAGE == 4 ? (t & 3) : t % NSTAGE);
+    };
     auto k_stage = [&](const int t) __attribute__((always_inline)) {
-      return lds0 + (uint32_t)(t & 3) * C::STAGE_BYTES;
+      return lds0 + stage_of(t) * C::STAGE_BYTES;
     };
     auto v_stage = [&](const int t) __attribute__((always_inline)) {
-      return lds0 + (uint32_t)(t & 3) * C::STAGE_BYTES + C::TILE_BYTES;
+      return lds0 + stage_of(t) * C::STAGE_BYTES + C::TILE_BYTES;
     };
-    auto issue_loads = [&](const int t) __attribute__((always_inline)) {
-      const uint32_t nb = t + 2 < ntiles ? valid_bytes : 0u;
-      load_tile_n((t + 2) * C::BK, (t + 2) & 3, __builtin_amdgcn_readfirstlane(nb));
+    // Loads of tile u (a zero fill at or past the last tile, so that every
+    // wave always has the same number of loads in flight).
+    auto load_ahead = [&](const int u) __attribute__((always_inline)) {
+      const uint32_t nb = u < ntiles ? valid_bytes : 0u;
+      load_tile_n(u * C::BK, stage_of(u), __builtin_amdgcn_readfirstlane(nb));
     };
-    // Softmax phase t.  The V fragments of tile t are read here, where
+    auto issue_loads = [&](const int t) __attribute__((always_inline)) { load_ahead(t + LA); };
+#pragma unroll
+    for (int u = 0; u < LA; ++u) load_ahead(u);
+    vmem_wait<(LA - 1) * C::LOADS_PER_TILE>();  // tile 0
+    // Softmax phase t.  The V fragments of tile t are read at its end, where
     // this wave's SIMD has LDS bandwidth to spare, so the MFMA phase that
-    // multiplies them reads only K.  Half of them are issued before the
-    // softmax and half before its exponentials (a wave stalls once it has
-    // 15 LDS reads outstanding).
+    // multiplies them reads only K.  (Issued after the exponentials, when
+    // the score registers are free: issued earlier they cost 15 registers
+    // more at the peak and ran no faster.)
     auto softmax_phase = [&](const int t) __attribute__((always_inline)) {
       __builtin_amdgcn_s_setprio(0);
-      const uint32_t vb = v_stage(t);
-      v_issue_range(vb, G0, std::integral_constant<int, VG / 2>{});
-      softmax(t * C::BK, s, pf, [&] {
-        v_issue_range(vb, std::integral_constant<int, VG / 2>{}, std::integral_constant<int, VG>{});
-      });
+      softmax(t * C::BK, s, pf, [] {});
+      v_issue_range(v_stage(t), G0, std::integral_constant<int, VG>{});
     };
     constexpr auto K4 = std::integral_constant<int, 4>{};
     constexpr auto K0 = std::integral_constant<int, 0>{};
@@ -612,7 +604,7 @@ void fa_fwd_bf16_kernel(FwdParams p) {
       compute_s(k_stage(0), s, PRE1);
       for (int t = 1; t < ntiles; ++t) {
         if constexpr (first) softmax_phase(t - 1);
-        vmem_wait<C::LOADS_PER_TILE>();  // this wave's loads of tile t
+        vmem_wait<(LA - 1) * C::LOADS_PER_TILE>();  // this wave's loads of tile t
         barrier_no_fence();              // barrier t
         if constexpr (!first) softmax_phase(t - 1);
         mfma_phase(t);
@@ -674,7 +666,7 @@ hipError_t launch_d(const FwdParams& p, hipStream_t stream) {
   // two workgroups per CU, 2 stages) otherwise.  (Measured on MI355X at
   // N = 8192, d = 128: 3 stages are a few percent ahead of 2 and 4.)
   const int64_t big_tiles = (int64_t)p.B * p.H * ((p.N + 255) / 256);
-  if (big_tiles >= 512) return launch_cfg<D, CAUSAL, 8, 4, true>(p, stream);
+  if (big_tiles >= 512) return launch_cfg<D, CAUSAL, 8, kPingPongStages, true>(p, stream);
   return launch_cfg<D, CAUSAL, 4, 2, false>(p, stream);
 }
 
