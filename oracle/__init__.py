@@ -11,4 +11,5 @@ from .attention import (  # noqa: F401
     merge_summaries,
     finalize_summary,
     streamed_attention,
+    split_attention,
 )

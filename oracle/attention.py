@@ -34,15 +34,25 @@ notes of the repository):
     requires explicit handling of fully masked blocks];
   * LSE is the natural-log log-sum-exp of the row's scaled, masked scores,
     the "compact per-row normalization information" of P2 "Backward
-    recomputation".
+    recomputation";
+  * with Nq query rows against Nk keys (decode and chunked prefill, the
+    serving regimes of P2 "Exercise" and "Common errors"), the keys are a
+    cache holding L_b = clamp(key_len[b], 0, Nk) valid entries (Nk without a
+    length) and the query rows, when end aligned, are that sequence's last
+    Nq positions: row i sits at key position p = i + L_b - Nq.  Keys j >= L_b
+    are hidden, causal also hides j > p, and no row is padding; a row that
+    sees no key (L_b = 0, or p < 0 under causal) gets O = 0, LSE = -inf.
+    Without a length and with Nq = Nk this is the square case unchanged.
 
 Pins (tests/test_oracle.py): the two worked examples of P3 with every printed
 intermediate value, closed forms (uniform scores, causal running means,
 single visible key, dominant key), invariants (convex hull, shift and
 permutation invariance), scipy's softmax on the unmasked case, pure-Python
 brute force with exact summation on tiny inputs, and agreement between the
-plain definition and the streamed recurrence.  No function here is parity
-unpinned.
+plain definition and the streamed recurrence.  The Nq != Nk reading is pinned
+by brute force with positions on tiny inputs, by the last Nq rows of the
+square problem (causal and padded) and by decode rows against scipy's
+softmax over the visible keys.  No function here is parity unpinned.
 """
 from __future__ import annotations
 
@@ -55,6 +65,7 @@ __all__ = [
     "merge_summaries",
     "finalize_summary",
     "streamed_attention",
+    "split_attention",
 ]
 
 NEG_INF = -np.inf
@@ -66,23 +77,24 @@ def _clamped_length(key_len, b: int, N: int) -> int:
     return int(min(max(int(key_len[b]), 0), N))
 
 
-def visible_mask(rows: np.ndarray, N: int, L: int, causal: bool) -> np.ndarray:
-    """Boolean [R, N]: key j visible to query rows[r].
+def visible_mask(rows: np.ndarray, N: int, L: int, causal: bool, pos_off: int = 0) -> np.ndarray:
+    """Boolean [R, N]: key j (of N keys) visible to query rows[r].
 
-    Visible iff j < L, rows[r] < L and (not causal or j <= rows[r]).
-    This is the support of the additive mask M of [P3 "Move less data"]:
-    M = 0 where visible, -inf elsewhere.
+    The query row sits at key position p = rows[r] + pos_off.  Key j is
+    visible iff j < L, p < L and (not causal or j <= p).  This is the support
+    of the additive mask M of [P3 "Move less data"]: M = 0 where visible,
+    -inf elsewhere.
     """
-    rows = np.asarray(rows, dtype=np.int64)
+    p = np.asarray(rows, dtype=np.int64)[:, None] + int(pos_off)
     j = np.arange(N, dtype=np.int64)[None, :]
-    i = rows[:, None]
-    vis = (j < L) & (i < L)
+    vis = (j < L) & (p < L)
     if causal:
-        vis &= j <= i
+        vis &= j <= p
     return vis
 
 
-def attention(q, k, v, scale, causal=False, key_len=None, rows=None, chunk_rows=256):
+def attention(q, k, v, scale, causal=False, key_len=None, rows=None, chunk_rows=256,
+              end_aligned=False):
     """Plain definition: O = softmax(scale * Q K^T + M) V, and per-row LSE.
 
     [P1 "Problem setting"] defines O = softmax(Q K^T / sqrt(d)) V; [P3 "Move
@@ -93,17 +105,20 @@ def attention(q, k, v, scale, causal=False, key_len=None, rows=None, chunk_rows=
     row, then O = P V.  The usual max shift inside softmax changes nothing
     mathematically (softmax is shift invariant, [P4]).
 
-    q, k, v: float64 arrays [B, H, N, d] (v may have its own last dim).
+    q: float64 array [B, H, Nq, d]; k, v: [B, H, Nk, d] (v may have its own
+    last dim).  Query row i sits at key position i, or with end_aligned at
+    i + L_b - Nq, where no row is padding (see the module notes).
     rows: None (all rows), or int array [R], [H, R] or [B, H, R] of query rows.
-    Returns (o [B, H, R, dv], lse [B, H, R]) with R = N when rows is None.
+    Returns (o [B, H, R, dv], lse [B, H, R]) with R = Nq when rows is None.
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
-    B, H, N, _ = q.shape
+    B, H, Nq, _ = q.shape
+    N = k.shape[2]  # keys
     dv = v.shape[-1]
     if rows is None:
-        rows_bh = np.broadcast_to(np.arange(N, dtype=np.int64), (B, H, N))
+        rows_bh = np.broadcast_to(np.arange(Nq, dtype=np.int64), (B, H, Nq))
     else:
         r = np.asarray(rows, dtype=np.int64)
         if r.ndim == 1:
@@ -116,17 +131,18 @@ def attention(q, k, v, scale, causal=False, key_len=None, rows=None, chunk_rows=
     lse = np.full((B, H, R), NEG_INF, dtype=np.float64)
     for b in range(B):
         L = _clamped_length(key_len, b, N)
+        pos_off = L - Nq if end_aligned else 0
         for h in range(H):
             for r0 in range(0, R, chunk_rows):
                 rr = rows_bh[b, h, r0:r0 + chunk_rows]
                 # S = scale * Q K^T for whole rows (all N keys).
                 s = scale * (q[b, h, rr, :] @ k[b, h].T)
-                vis = visible_mask(rr, N, L, causal)
+                vis = visible_mask(rr, N, L, causal, pos_off)
                 live = vis.any(axis=1)
                 # Additive mask: -inf where not visible.
                 s = np.where(vis, s, NEG_INF)
                 # Row maximum over visible keys (0 for rows with none).
-                m = np.where(live, s.max(axis=1), 0.0)
+                m = np.where(live, s.max(axis=1, initial=NEG_INF), 0.0)
                 w = np.where(vis, np.exp(s - m[:, None]), 0.0)
                 ell = w.sum(axis=1)
                 # P = softmax(S + M), materialised for these rows.
@@ -256,4 +272,44 @@ def streamed_attention(q, k, v, scale, causal=False, key_len=None,
                 o[b, h, rows] = np.divide(a, ell[:, None], out=np.zeros_like(a), where=pos[:, None])
                 with np.errstate(divide="ignore"):
                     lse[b, h, rows] = np.where(pos, m + np.log(np.where(pos, ell, 1.0)), NEG_INF)
+    return o, lse
+
+
+# ---------------------------------------------------------------------------
+# Key ranges merged by their summaries [P3 "Why a tile can be discarded",
+# "One row, checked two ways", "Practice: can you average block outputs?"]
+# ---------------------------------------------------------------------------
+
+def split_attention(q, k, v, scale, causal=False, key_len=None, split_keys=128,
+                    end_aligned=True):
+    """Each query row's keys cut into consecutive ranges of split_keys keys;
+    every range is summarised on its own (block_summary over the row's masked
+    scores in that range), the summaries are merged left to right with
+    merge_summaries, and the merged summary is finalised.  Row by row, for
+    small inputs.  Positions and masks are those of ``attention`` (end
+    aligned by default, the decode convention).
+
+    Returns (o [B, H, Nq, dv], lse [B, H, Nq]).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    B, H, Nq, _ = q.shape
+    N = k.shape[2]
+    dv = v.shape[-1]
+    o = np.zeros((B, H, Nq, dv))
+    lse = np.full((B, H, Nq), NEG_INF)
+    for b in range(B):
+        L = _clamped_length(key_len, b, N)
+        pos_off = L - Nq if end_aligned else 0
+        for h in range(H):
+            vis = visible_mask(np.arange(Nq), N, L, causal, pos_off)
+            s_all = scale * (q[b, h] @ k[b, h].T)
+            for i in range(Nq):
+                s_row = np.where(vis[i], s_all[i], NEG_INF)
+                acc = (NEG_INF, 0.0, np.zeros(dv))
+                for k0 in range(0, N, split_keys):
+                    part = block_summary(s_row[k0:k0 + split_keys], v[b, h, k0:k0 + split_keys])
+                    acc = merge_summaries(acc, part)
+                o[b, h, i], lse[b, h, i] = finalize_summary(acc)
     return o, lse

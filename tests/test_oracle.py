@@ -8,7 +8,8 @@ scipy's softmax on the unmasked case, pure-Python brute force with exact
 summation and no max shift on tiny inputs, and equality of the plain
 definition with the streamed (m, l, a) recurrence.  The last block plants
 plausible mistakes (dropped scale, transposed operand, flipped causal
-direction, unmasked padding, unrescaled merge) and checks that a pin fails.
+direction, unmasked padding, wrong value operand, query rows of a key cache
+placed at the wrong positions) and checks that a pin fails.
 """
 import itertools
 import json
@@ -324,17 +325,20 @@ def test_matches_scipy_softmax_unmasked():
     assert np.allclose(lse, scipy.special.logsumexp(s, axis=-1), atol=1e-13)
 
 
-def brute(q, k, v, scale, causal, L):
+def brute(q, k, v, scale, causal, L, end_aligned=False):
     """Direct definition with exact summation and no max shift, pure Python.
 
-    q, k, v: nested lists [N][d]; returns (o [N][d], lse [N]).
+    q: nested list [Nq][d]; k, v: [Nk][d].  Query row i sits at key position
+    p = i, or p = i + L - Nq when end_aligned; key j is visible iff j < L,
+    p < L and (not causal or j <= p).  Returns (o [Nq][dv], lse [Nq]).
     """
-    N = len(q)
+    Nq, Nk = len(q), len(k)
     d = len(q[0])
-    dv = len(v[0])
+    dv = len(v[0]) if Nk else 1
     O, LSE = [], []
-    for i in range(N):
-        keys = [j for j in range(N) if j < L and i < L and (not causal or j <= i)]
+    for i in range(Nq):
+        p = i + (L - Nq if end_aligned else 0)
+        keys = [j for j in range(Nk) if j < L and p < L and (not causal or j <= p)]
         if not keys:
             O.append([0.0] * dv)
             LSE.append(-math.inf)
@@ -380,6 +384,116 @@ def test_brute_force_exact_rationals():
             exact = Fraction(sum(w * x for w, x in zip(wts[:hi], vals[:hi])), sum(wts[:hi]))
             assert o[0, 0, i, 0] == pytest.approx(float(exact), abs=1e-14)
             assert lse[0, 0, i] == pytest.approx(math.log(sum(wts[:hi])), abs=1e-14)
+
+
+# ---------------------------------------------------------------------------
+# Query rows at the end of a longer key cache (decode, chunked prefill)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("Nq,Nk,d", [(1, 1, 2), (1, 6, 3), (3, 7, 2), (6, 3, 2), (4, 4, 3), (2, 0, 2)])
+def test_brute_force_end_aligned(Nq, Nk, d):
+    rng = np.random.default_rng(700 + 10 * Nq + Nk)
+    q = rng.standard_normal((1, 1, Nq, d))
+    k = rng.standard_normal((1, 1, Nk, d))
+    v = rng.standard_normal((1, 1, Nk, d + 1))
+    for causal, L in itertools.product((False, True), range(0, Nk + 2)):
+        o, lse = oracle.attention(q, k, v, 0.8, causal=causal, key_len=np.array([L]), end_aligned=True)
+        O, LSE = brute(q[0, 0].tolist(), k[0, 0].tolist(), v[0, 0].tolist(), 0.8, causal,
+                       min(L, Nk), end_aligned=True)
+        assert np.allclose(o[0, 0], np.array(O).reshape(Nq, -1)[:, :d + 1], atol=1e-13), (causal, L)
+        for a, b in zip(lse[0, 0], LSE):
+            assert (a == b == -math.inf) or abs(a - b) < 1e-13, (causal, L)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_end_aligned_without_length_is_square_when_nq_equals_nk(causal):
+    B, H, N, d = 2, 2, 33, 5
+    q, k, v = rand((B, H, N, d), 710), rand((B, H, N, d), 711), rand((B, H, N, d), 712)
+    o1, l1 = oracle.attention(q, k, v, 0.3, causal=causal)
+    o2, l2 = oracle.attention(q, k, v, 0.3, causal=causal, end_aligned=True)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def test_decode_rows_are_softmax_over_cached_keys():
+    """Nq = 1 at position L - 1 sees exactly the first L keys, causal or not:
+    scipy's softmax and logsumexp over those scores."""
+    B, H, Nk, d = 4, 3, 50, 8
+    q, k, v = rand((B, H, 1, d), 720), rand((B, H, Nk, d), 721), rand((B, H, Nk, d), 722)
+    key_len = np.array([50, 1, 0, 17])
+    for causal in (False, True):
+        o, lse = oracle.attention(q, k, v, 0.4, causal=causal, key_len=key_len, end_aligned=True)
+        for b, L in enumerate(key_len):
+            for h in range(H):
+                if L == 0:
+                    assert np.all(o[b, h] == 0) and lse[b, h, 0] == -math.inf
+                    continue
+                s = 0.4 * k[b, h, :L] @ q[b, h, 0]
+                assert np.allclose(o[b, h, 0], scipy.special.softmax(s) @ v[b, h, :L], atol=1e-14)
+                assert abs(lse[b, h, 0] - scipy.special.logsumexp(s)) < 1e-13
+
+
+@pytest.mark.parametrize("Nq", [1, 6, 23, 40])
+def test_end_aligned_rows_match_square_problem(Nq):
+    """Causal: row i at p = i + L - Nq equals row p of the square causal
+    problem over the first L keys (whose other query rows are arbitrary);
+    rows with p < 0 see nothing.  Non-causal: every row is the softmax over
+    the first L keys."""
+    B, H, Nk, d = 3, 2, 30, 4
+    q, k, v = rand((B, H, Nq, d), 730), rand((B, H, Nk, d), 731), rand((B, H, Nk, d), 732)
+    key_len = np.array([30, 11, 0])
+    oc, lc = oracle.attention(q, k, v, 0.5, causal=True, key_len=key_len, end_aligned=True)
+    on, ln_ = oracle.attention(q, k, v, 0.5, causal=False, key_len=key_len, end_aligned=True)
+    rng = np.random.default_rng(733)
+    for b, L in enumerate(key_len):
+        for h in range(H):
+            for i in range(Nq):
+                p = i + L - Nq
+                if L == 0 or p < 0:
+                    assert np.all(oc[b, h, i] == 0) and lc[b, h, i] == -math.inf
+                    if L == 0:
+                        assert np.all(on[b, h, i] == 0) and ln_[b, h, i] == -math.inf
+                    continue
+                qs = rng.standard_normal((1, 1, L, d))
+                qs[0, 0, p] = q[b, h, i]
+                o_sq, l_sq = oracle.attention(qs, k[b:b + 1, h:h + 1, :L], v[b:b + 1, h:h + 1, :L],
+                                              0.5, causal=True)
+                assert np.allclose(oc[b, h, i], o_sq[0, 0, p], atol=1e-14)
+                assert abs(lc[b, h, i] - l_sq[0, 0, p]) < 1e-13
+            for i in range(Nq):
+                if L == 0:
+                    continue
+                s = 0.5 * k[b, h, :L] @ q[b, h, i]
+                assert np.allclose(on[b, h, i], scipy.special.softmax(s) @ v[b, h, :L], atol=1e-14)
+
+
+@pytest.mark.parametrize("split_keys", [1, 3, 8, 16, 64])
+@pytest.mark.parametrize("causal", [False, True])
+def test_split_ranges_merged_equal_definition(split_keys, causal):
+    """Key ranges summarised separately and merged (including ranges that
+    are wholly masked) give the plain definition."""
+    B, H, Nq, Nk, d = 3, 2, 9, 37, 4
+    q, k, v = rand((B, H, Nq, d), 740, 2.0), rand((B, H, Nk, d), 741), rand((B, H, Nk, d), 742)
+    key_len = np.array([37, 5, 0])
+    o1, l1 = oracle.attention(q, k, v, 0.6, causal=causal, key_len=key_len, end_aligned=True)
+    o2, l2 = oracle.split_attention(q, k, v, 0.6, causal=causal, key_len=key_len,
+                                    split_keys=split_keys)
+    assert np.allclose(o1, o2, atol=1e-13, rtol=0)
+    fin = np.isfinite(l1)
+    assert np.array_equal(fin, np.isfinite(l2))
+    assert np.allclose(l1[fin], l2[fin], atol=1e-13)
+
+
+def test_split_average_of_block_outputs_is_wrong():
+    """Averaging the ranges' normalised outputs (the error the glossary page
+    warns about) differs from the merged result."""
+    rng = np.random.default_rng(750)
+    q = rng.standard_normal((1, 1, 1, 4)) * 3
+    k = rng.standard_normal((1, 1, 8, 4))
+    v = rng.standard_normal((1, 1, 8, 2))
+    o, _ = oracle.split_attention(q, k, v, 1.0, split_keys=4)
+    parts = [oracle.attention(q, k[:, :, a:a + 4], v[:, :, a:a + 4], 1.0, end_aligned=True)[0]
+             for a in (0, 4)]
+    assert not np.allclose(o, 0.5 * (parts[0] + parts[1]), atol=1e-3)
 
 
 # ---------------------------------------------------------------------------
@@ -454,6 +568,20 @@ def _pin_suite(attn):
         O, LSE = brute(q[0, 0].tolist(), k[0, 0].tolist(), v[0, 0].tolist(), 0.6, causal, L)
         if not np.allclose(o[0, 0], np.array(O), atol=1e-12):
             failed.append(f"brute_{causal}_{L}")
+    # three query rows at the end of a nine-key cache holding 7 (then 2) keys
+    qd = rng.standard_normal((B, H, 3, d))
+    for causal, L in itertools.product((False, True), (7, 2)):
+        try:
+            o, lse = attn(qd, k, v, 0.6, causal=causal, key_len=np.array([L]), end_aligned=True)
+            ok = o.shape == (1, 1, 3, d)
+        except (ValueError, IndexError):
+            ok = False
+        if ok:
+            O, LSE = brute(qd[0, 0].tolist(), k[0, 0].tolist(), v[0, 0].tolist(), 0.6, causal, L,
+                           end_aligned=True)
+            ok = np.allclose(o[0, 0], np.array(O), atol=1e-12)
+        if not ok:
+            failed.append(f"brute_end_{causal}_{L}")
     return failed
 
 
@@ -462,29 +590,43 @@ def test_pins_pass_on_oracle():
 
 
 @pytest.mark.parametrize("mistake", ["dropped_scale", "transposed_qk", "flipped_causal",
-                                     "unmasked_padding_rows", "wrong_value_operand"])
+                                     "unmasked_padding_rows", "wrong_value_operand",
+                                     "start_aligned_cache_rows", "rows_aligned_to_capacity"])
 def test_planted_mistakes_are_caught(mistake):
-    def attn(q, k, v, scale, causal=False, key_len=None, rows=None):
+    def attn(q, k, v, scale, causal=False, key_len=None, rows=None, end_aligned=False):
+        ea = end_aligned
         if mistake == "dropped_scale":
-            return oracle.attention(q, k, v, 1.0, causal, key_len, rows)
+            return oracle.attention(q, k, v, 1.0, causal, key_len, rows, end_aligned=ea)
         if mistake == "transposed_qk":
-            return oracle.attention(k, q, v, scale, causal, key_len, rows)
+            return oracle.attention(k, q, v, scale, causal, key_len, rows, end_aligned=ea)
         if mistake == "flipped_causal":
             # j >= i instead of j <= i: reverse the sequence on both sides
             o, l = oracle.attention(q[:, :, ::-1], k[:, :, ::-1], v[:, :, ::-1], scale, causal,
-                                    None if key_len is None else key_len, rows)
+                                    None if key_len is None else key_len, rows, end_aligned=ea)
             return o[:, :, ::-1], l[:, :, ::-1]
         if mistake == "unmasked_padding_rows":
-            o, l = oracle.attention(q, k, v, scale, causal, key_len, rows)
+            o, l = oracle.attention(q, k, v, scale, causal, key_len, rows, end_aligned=ea)
             # padding rows computed as if they were ordinary rows
             N = q.shape[2]
             o2, l2 = oracle.attention(q, k, v, scale, causal,
-                                      None if key_len is None else np.full_like(key_len, N), rows)
+                                      None if key_len is None else np.full_like(key_len, N), rows,
+                                      end_aligned=ea)
             L = N if key_len is None else int(key_len[0])
             o[:, :, L:] = o2[:, :, L:]
             return o, l
         if mistake == "wrong_value_operand":
-            return oracle.attention(q, k, k, scale, causal, key_len, rows)
+            return oracle.attention(q, k, k, scale, causal, key_len, rows, end_aligned=ea)
+        if mistake == "start_aligned_cache_rows":
+            # query row i at position i whatever the cache holds
+            return oracle.attention(q, k, v, scale, causal, key_len, rows)
+        if mistake == "rows_aligned_to_capacity":
+            # row i at i + Nk - Nq, ignoring the sequence's own length
+            if not ea:
+                return oracle.attention(q, k, v, scale, causal, key_len, rows)
+            Nq, Nk = q.shape[2], k.shape[2]
+            qp = np.zeros(q.shape[:2] + (Nk, q.shape[3]))
+            qp[:, :, Nk - Nq:] = q
+            return oracle.attention(qp, k, v, scale, causal, key_len, rows=np.arange(Nk - Nq, Nk))
         raise AssertionError(mistake)
 
     assert _pin_suite(attn) != []
