@@ -3,6 +3,10 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                     [--no-cpu-baseline] [--no-naive]
 
+With --workload decode_b8_h32_k16384_d128_bf16 a step is instead one
+fa_forward_split call (a decode step: one query row per sequence and head),
+and the roofline is HBM bandwidth.
+
 A step is one fa_forward call over the whole workload (every batch, head and
 query row), with Q, K, V already resident in device memory.  Default
 workload: 32 heads, N = 8192, d = 128, causal, bf16 (the shape the pages use
@@ -33,7 +37,7 @@ PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA, 2.4 GHz
 PEAK_F32_TFLOPS = 157.3     # MI355X fp32 matrix
 PEAK_HBM_GBS = 8000.0
 DEFAULT_WORKLOAD = "h32_n8192_d128_causal_bf16"
-KERNEL_SOURCES = ["fa_fwd_bf16.hip", "fa_fwd_f32.hip", "fa_bf16_tiles.hpp",
+KERNEL_SOURCES = ["fa_fwd_bf16.hip", "fa_fwd_f32.hip", "fa_merge.hip", "fa_bf16_tiles.hpp",
                   "fa_device.hpp", "fa_internal.hpp"]
 
 
@@ -123,6 +127,109 @@ def cpu_baseline(inp, wl, o_dev, lse_dev, target_s: float):
     }
 
 
+def bench_decode(args) -> int:
+    """Decode: one query row per (sequence, head) against its key cache,
+    through fa_forward_split with the library's own range count.  A step is
+    one call (the range kernel and the merge).  Bound by HBM: the algorithmic
+    bytes are each sequence's valid K and V rows read once plus q, o and LSE."""
+    import numpy as np
+    import torch
+
+    import io_aware_exact_forward_amd as fa
+    import oracle
+    from io_aware_exact_forward_amd import workloads as W
+
+    wl = W.DECODE_WORKLOADS[args.workload]
+    inp = W.decode_inputs(wl)
+    dev = torch.device("cuda:0")
+    q, k, v, kl = to_device(inp, dev)
+    B, H, Nk, d = wl.B, wl.H, wl.Nk, wl.d
+    lens = [int(x) for x in np.clip(inp.key_len, 0, Nk)]
+    flops = 4.0 * d * H * sum(lens)
+    algo_bytes = sum(H * (2 * L * d * 2 + 2 * d * 2 + 4) for L in lens)
+    ws_bytes = fa.fa_split_workspace_bytes(B, H, 1, Nk, d, 0)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    out = torch.empty_like(q)
+    lse = torch.empty((B, H, 1), dtype=torch.float32, device=dev)
+
+    def step():
+        fa.forward_split(q, k, v, scale=wl.scale, causal=True, key_len=kl, num_splits=0,
+                         workspace=ws, out=out, lse=lse)
+
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    t_wall = time.perf_counter()
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms = start.elapsed_time(end) / args.steps
+    gbs = algo_bytes / (ms * 1e-3) / 1e9
+    result = {
+        "metric": "attention fwd TFLOP/s (bf16, 1 GPU); decode step, HBM-bound",
+        "value": flops / (ms * 1e-3) / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": dict(wl.describe(), key_lens=lens, useful_flops=flops,
+                       algorithmic_hbm_bytes=algo_bytes, workspace_bytes=ws_bytes,
+                       parallelism="single GPU"),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": gbs,
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": gbs / PEAK_HBM_GBS,
+            "traffic": stored_traffic(wl.name),
+            "kernel": "fa_fwd_bf16_kernel + merge_kernel (one call; both inside the events)",
+            "kernel_hash": kernel_hash(),
+        },
+        "wall_s_timed_region": t_wall,
+    }
+    if not args.no_cpu_baseline:
+        # the oracle on whole (sequence, head) rows, as many as fit the time budget
+        qx, kx, vx = inp.exact("q"), inp.exact("k"), inp.exact("v")
+        pairs, done, t0 = 0, 0, time.perf_counter()
+        for b in range(B):
+            for h in range(H):
+                oracle.attention(qx[b:b + 1, h:h + 1], kx[b:b + 1, h:h + 1], vx[b:b + 1, h:h + 1],
+                                 wl.scale, causal=True, key_len=inp.key_len[b:b + 1],
+                                 end_aligned=True)
+                pairs += lens[b]
+                done += 1
+                if time.perf_counter() - t0 > args.cpu_seconds:
+                    break
+            if time.perf_counter() - t0 > args.cpu_seconds:
+                break
+        dt = time.perf_counter() - t0
+        try:
+            from threadpoolctl import threadpool_info
+            threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        except Exception:
+            threads = len(os.sched_getaffinity(0))
+        result["cpu_baseline"] = {
+            "value": 4.0 * d * pairs / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{done} of {B * H} (sequence, head) decode rows, fp64 numpy; {dt:.1f} s",
+            "seconds": dt,
+        }
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -130,7 +237,9 @@ def main() -> int:
     # the engine clock ramps up over the first ~0.1-0.3 s of sustained work:
     # the default warm-up covers that so the timed steps see steady state
     ap.add_argument("--warmup", type=int, default=300)
-    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD,
+                    help="a square workload name, or decode_b8_h32_k16384_d128_bf16 (one query "
+                         "row per sequence and head against its key cache, split over key ranges)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-naive", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -169,6 +278,8 @@ def main() -> int:
         print(json.dumps({"copy_probe_bytes": n, "copies": 3}), flush=True)
         return 0
 
+    if args.workload in W.DECODE_WORKLOADS:
+        return bench_decode(args)
     wl = W.workload(args.workload)
     inp = W.make_inputs(wl)
     dev = torch.device("cuda:0")

@@ -84,7 +84,7 @@ typedef enum {
   FA_ERR_ALIGN = -5,       /* a pointer is not aligned as required             */
   FA_ERR_SCALE = -6,       /* scale is NaN or infinite                         */
   FA_ERR_ALIAS = -7,       /* an output overlaps an input or the other output */
-  FA_ERR_WORKSPACE = -8,   /* naive path: workspace NULL or too small          */
+  FA_ERR_WORKSPACE = -8,   /* workspace NULL, misaligned or too small          */
   FA_ERR_HIP = -9          /* the HIP runtime reported an error at launch      */
 } fa_status_t;
 
@@ -124,13 +124,63 @@ int fa_naive_forward(const void* q, const void* k, const void* v, void* o, float
                      const int32_t* key_len_mask, int dtype,
                      void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Split-KV attention forward: Nq query rows against Nk key rows, with the
+ * keys of every query tile divided into ranges that separate workgroups
+ * compute, each leaving a normalised partial output and its log-sum-exp in
+ * the workspace; a second kernel combines them with the block-summary rule
+ * of the page "FlashAttention" (sections "Why a tile can be discarded" and
+ * "One row, checked two ways": each block's denominator and numerator are
+ * expressed against a common reference maximum, then added).  It is for the
+ * shapes where one workgroup per query tile leaves the device idle -- few
+ * query rows against many keys (decode), or few (batch, head) pairs at long
+ * Nk -- which "IO-aware exact attention" (section "Common errors") names as
+ * needing a different schedule.
+ *   q, o         [B, H, Nq, d] of `dtype`; k, v [B, H, Nk, d]; lse [B, H, Nq].
+ *   Positions    L_b = clamp(key_len_mask[b], 0, Nk), or Nk when key_len_mask
+ *                is NULL: sequence b holds keys 0 .. L_b - 1 and its query
+ *                rows are the last Nq positions of that sequence, row i at key
+ *                position p = i + L_b - Nq (decode: Nq = 1 sits at L_b - 1).
+ *                Without key_len_mask and with Nq = Nk this is position i, and
+ *                the call computes what fa_forward computes (up to the order
+ *                of the additions).
+ *   Mask         keys j >= L_b are never visible; causal != 0 also hides keys
+ *                j > p.  No row is padding: every row sees keys 0 .. L_b - 1
+ *                (0 .. min(p, L_b - 1) if causal).  A row that sees no key
+ *                (L_b = 0, or p < 0 under causal, which needs Nq > L_b) gets
+ *                O = 0 and LSE = -inf.
+ *   dtype        FA_DTYPE_BF16 only (FA_ERR_DTYPE otherwise).
+ *   num_splits   key ranges per query tile, >= 1, or 0 to let the library
+ *                choose enough ranges to fill the device.  Ranges are whole
+ *                128-key blocks, so fewer ranges than asked may be used.
+ *   workspace    device memory, 256-byte aligned, of at least
+ *                fa_split_workspace_bytes(B, H, Nq, Nk, d, num_splits) bytes,
+ *                overlapping no other argument: fp32 partial outputs
+ *                [ranges, B, H, Nq, d] and their log-sum-exp [ranges, B, H, Nq].
+ *                When a single range is used it is not touched (NULL and 0 are
+ *                then accepted).
+ *   Sizes        B, H, Nq, Nk >= 0 (nothing to do if B, H or Nq is 0; Nk = 0
+ *                gives O = 0, LSE = -inf, and k, v may then be NULL); one
+ *                (batch, head) slice of q and of
+ *                k at most 2^31 - 1 bytes; num_splits <= 65536.
+ * Enqueues two kernels on `stream` (one when a single range is used).  The
+ * remaining conventions (alignment, aliasing, errors, streams) are those of
+ * fa_forward; a workspace that is NULL, misaligned or too small returns
+ * FA_ERR_WORKSPACE.
+ */
+size_t fa_split_workspace_bytes(int B, int H, int Nq, int Nk, int d, int num_splits);
+int fa_forward_split(const void* q, const void* k, const void* v, void* o, float* lse,
+                     int B, int H, int Nq, int Nk, int d, float scale, int causal,
+                     const int32_t* key_len_mask, int dtype, int num_splits,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* fa_status_string(int status);
 
 /* ABI version of this header: (major << 16) | minor. */
 int fa_abi_version(void);
 
-#define FA_ABI_VERSION ((1 << 16) | 0)
+#define FA_ABI_VERSION ((1 << 16) | 1)
 
 #ifdef __cplusplus
 }

@@ -1,8 +1,8 @@
 """Exact attention forward for MI355X (gfx950): fused HIP kernels behind a C ABI.
 
 The C entry points (include/fa_mi355x.h) are exposed under their own names by
-``io_aware_exact_forward_amd._lib``; ``forward`` and ``naive_forward`` below
-are conveniences that take torch tensors (torch only provides device memory
+``io_aware_exact_forward_amd._lib``; ``forward``, ``forward_split`` and
+``naive_forward`` below are conveniences that take torch tensors (torch only provides device memory
 and the stream), allocate the outputs and call those entry points.  Nothing
 here computes attention itself.
 """
@@ -17,14 +17,17 @@ from ._lib import (  # noqa: F401
     check,
     fa_abi_version,
     fa_forward,
+    fa_forward_split,
     fa_naive_forward,
     fa_naive_workspace_bytes,
+    fa_split_workspace_bytes,
     fa_status_string,
     load,
 )
 
 __all__ = [
-    "forward", "naive_forward", "fa_forward", "fa_naive_forward", "fa_naive_workspace_bytes",
+    "forward", "forward_split", "naive_forward", "fa_forward", "fa_forward_split",
+    "fa_split_workspace_bytes", "fa_naive_forward", "fa_naive_workspace_bytes",
     "fa_status_string", "fa_abi_version", "FAError", "FA_DTYPE_BF16", "FA_DTYPE_F32",
 ]
 
@@ -87,4 +90,43 @@ def naive_forward(q, k, v, *, scale=None, causal=False, key_len=None, workspace=
     check(fa_naive_forward(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                            lse.data_ptr(), B, H, N, d, scale, int(bool(causal)), kl, dt,
                            workspace.data_ptr(), workspace.numel(), stream))
+    return out, lse
+
+
+def forward_split(q, k, v, *, scale=None, causal=False, key_len=None, num_splits=0,
+                  workspace=None, out=None, lse=None):
+    """O, LSE = fa_forward_split(...): q [B, H, Nq, d] against k, v [B, H, Nk, d]
+    (query row i at key position i + Nk - Nq), keys split into ranges that are
+    merged by their log-sum-exp.  num_splits = 0 lets the library choose."""
+    import torch
+    if q.dim() != 4 or k.dim() != 4 or k.shape != v.shape or q.shape[:2] != k.shape[:2] \
+            or q.shape[3] != k.shape[3]:
+        raise FAError(-2, f"q [B, H, Nq, d] and k, v [B, H, Nk, d] expected; got "
+                          f"{tuple(q.shape)}, {tuple(k.shape)}, {tuple(v.shape)}")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise FAError(-4, "q, k, v must share one dtype")
+    for t in (q, k, v):
+        if not t.is_cuda or not t.is_contiguous():
+            raise FAError(-1, "q, k, v must be contiguous device tensors")
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    kl = 0
+    if key_len is not None:
+        if key_len.dtype != torch.int32 or not key_len.is_cuda or key_len.numel() != B:
+            raise FAError(-1, "key_len must be a device int32 tensor of B elements")
+        kl = key_len.contiguous().data_ptr()
+    need = fa_split_workspace_bytes(B, H, Nq, Nk, d, num_splits)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    ws, wsb = (0, 0) if workspace is None else (workspace.data_ptr(), workspace.numel())
+    check(fa_forward_split(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                           lse.data_ptr(), B, H, Nq, Nk, d, float(scale), int(bool(causal)), kl,
+                           _dtype_code(q), int(num_splits), ws, wsb, stream))
     return out, lse

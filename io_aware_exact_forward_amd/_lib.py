@@ -32,6 +32,13 @@ _SIGNATURES = {
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
         ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float, ctypes.c_int,
         ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "fa_split_workspace_bytes": (ctypes.c_size_t, [
+        ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int]),
+    "fa_forward_split": (ctypes.c_int, [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float,
+        ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+        ctypes.c_size_t, ctypes.c_void_p]),
     "fa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "fa_abi_version": (ctypes.c_int, []),
 }
@@ -98,6 +105,17 @@ def fa_naive_forward(q, k, v, o, lse, B, H, N, d, scale, causal, key_len_mask, d
     return load().fa_naive_forward(q, k, v, o, lse, B, H, N, d, scale, int(causal),
                                    key_len_mask or None, dtype, workspace, workspace_bytes,
                                    stream or None)
+
+
+def fa_split_workspace_bytes(B, H, Nq, Nk, d, num_splits) -> int:
+    return load().fa_split_workspace_bytes(B, H, Nq, Nk, d, num_splits)
+
+
+def fa_forward_split(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, key_len_mask, dtype,
+                     num_splits, workspace, workspace_bytes, stream) -> int:
+    return load().fa_forward_split(q, k, v, o, lse, B, H, Nq, Nk, d, scale, int(causal),
+                                   key_len_mask or None, dtype, num_splits, workspace or None,
+                                   workspace_bytes, stream or None)
 
 
 def fa_status_string(status) -> str:

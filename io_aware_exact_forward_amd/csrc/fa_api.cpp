@@ -85,7 +85,13 @@ fa::FwdParams make_params(const void* q, const void* k, const void* v, void* o, 
   p.B = B;
   p.H = H;
   p.N = N;
+  p.Nk = N;
+  p.end_aligned = 0;
   p.n_qtiles = (N + fa::kQueryTile - 1) / fa::kQueryTile;
+  p.splits = 1;
+  p.split_keys = static_cast<int>(std::min<int64_t>((int64_t(N) + 127) / 128 * 128, INT_MAX - 127));
+  p.o_part = nullptr;
+  p.lse_part = nullptr;
   // exp(x) = exp2(x * log2 e): the kernels keep scores in log2 units.  c is
   // kept >= the smallest normal float so that a masked score (-inf) times c
   // is -inf, never NaN; for scale = 0 that changes no exp2 result, since
@@ -100,6 +106,73 @@ fa::FwdParams make_params(const void* q, const void* k, const void* v, void* o, 
 }
 
 size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// ---- split-KV -----------------------------------------------------------------
+
+constexpr int kMaxSplits = 65536;
+constexpr int kSplitBlock = 128;  // keys: ranges are whole blocks of this size
+
+struct SplitShape {
+  int64_t bh = 0;
+  int64_t rows = 0;      // B*H*Nq
+  int64_t kv_elems = 0;  // B*H*Nk*d
+  int splits = 1;        // ranges actually used
+  int split_keys = kSplitBlock;
+};
+
+// Ranges are whole 128-key blocks.  With num_splits = 0: enough ranges that
+// 128-row query tiles times ranges reach 512 workgroups (two per CU).
+void plan_split(int B, int H, int Nq, int Nk, int num_splits, SplitShape* sp) {
+  const int64_t kblocks = (int64_t(Nk) + kSplitBlock - 1) / kSplitBlock;
+  if (kblocks == 0) {
+    sp->splits = 1;
+    sp->split_keys = kSplitBlock;
+    return;
+  }
+  int64_t want = num_splits;
+  if (want == 0) {
+    const int64_t tiles = int64_t(B) * H * ((int64_t(Nq) + fa::kQueryTile - 1) / fa::kQueryTile);
+    want = tiles > 0 ? (512 + tiles - 1) / tiles : 1;
+  }
+  want = std::max<int64_t>(1, std::min<int64_t>(want, kblocks));
+  const int64_t per = (kblocks + want - 1) / want;  // blocks per range
+  sp->splits = static_cast<int>((kblocks + per - 1) / per);
+  sp->split_keys = static_cast<int>(per * kSplitBlock);
+}
+
+int check_split_scalars(int B, int H, int Nq, int Nk, int d, float scale, int dtype,
+                        int num_splits, SplitShape* sp, bool* empty) {
+  if (dtype != FA_DTYPE_BF16) return FA_ERR_DTYPE;
+  if (d != 64 && d != 128) return FA_ERR_HEAD_DIM;
+  if (B < 0 || H < 0 || Nq < 0 || Nk < 0 || num_splits < 0 || num_splits > kMaxSplits)
+    return FA_ERR_SHAPE;
+  if (!std::isfinite(scale)) return FA_ERR_SCALE;
+  const double c = std::fabs(static_cast<double>(scale)) * 1.4426950408889634;
+  if (!std::isfinite(static_cast<float>(c))) return FA_ERR_SCALE;
+  *empty = (B == 0 || H == 0 || Nq == 0);
+  if (*empty) return FA_OK;
+  const int64_t bh = int64_t(B) * H;
+  if (bh > INT_MAX) return FA_ERR_SHAPE;
+  if (bh * Nq > kMaxElems / d || bh * Nk > kMaxElems / d) return FA_ERR_SHAPE;
+  // byte offsets within one (batch, head) slice are 32-bit in the kernels
+  if (int64_t(Nq) * d * 2 > INT_MAX || int64_t(Nk) * d * 2 > INT_MAX) return FA_ERR_SHAPE;
+  plan_split(B, H, Nq, Nk, num_splits, sp);
+  const int64_t qtiles = (int64_t(Nq) + fa::kQueryTile - 1) / fa::kQueryTile;
+  if (qtiles * bh * sp->splits > INT_MAX) return FA_ERR_SHAPE;
+  sp->bh = bh;
+  sp->rows = bh * Nq;
+  sp->kv_elems = bh * Nk * d;
+  return FA_OK;
+}
+
+size_t split_part_bytes(const SplitShape& sp, int d) {
+  return round256(size_t(sp.splits) * size_t(sp.rows) * size_t(d) * sizeof(float));
+}
+
+size_t split_workspace(const SplitShape& sp, int d) {
+  if (sp.splits <= 1) return 0;
+  return split_part_bytes(sp, d) + round256(size_t(sp.splits) * size_t(sp.rows) * sizeof(float));
+}
 
 // One rocBLAS handle per device for the materialised path's two products.
 std::mutex g_blas_mu;
@@ -203,13 +276,76 @@ extern "C" int fa_naive_forward(const void* q, const void* k, const void* v, voi
   return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+extern "C" size_t fa_split_workspace_bytes(int B, int H, int Nq, int Nk, int d, int num_splits) {
+  SplitShape sp;
+  bool empty = false;
+  if (check_split_scalars(B, H, Nq, Nk, d, 1.f, FA_DTYPE_BF16, num_splits, &sp, &empty) != FA_OK ||
+      empty)
+    return 0;
+  return split_workspace(sp, d);
+}
+
+extern "C" int fa_forward_split(const void* q, const void* k, const void* v, void* o, float* lse,
+                                int B, int H, int Nq, int Nk, int d, float scale, int causal,
+                                const int32_t* key_len_mask, int dtype, int num_splits,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  SplitShape sp;
+  bool empty = false;
+  int st = check_split_scalars(B, H, Nq, Nk, d, scale, dtype, num_splits, &sp, &empty);
+  if (st != FA_OK || empty) return st;
+  // an empty cache (Nk = 0) is never read: k and v may then be NULL
+  if (!q || !o || !lse || (Nk > 0 && (!k || !v))) return FA_ERR_NULL;
+  if (!is_aligned(q, 16) || !is_aligned(k, 16) || !is_aligned(v, 16) || !is_aligned(o, 16))
+    return FA_ERR_ALIGN;
+  if (!is_aligned(lse, 4) || (key_len_mask && !is_aligned(key_len_mask, 4))) return FA_ERR_ALIGN;
+  const int64_t nq = sp.rows * d * 2, nkv = sp.kv_elems * 2, nl = sp.rows * 4;
+  const int64_t nkl = key_len_mask ? int64_t(B) * 4 : 0;
+  if (overlaps(o, nq, q, nq) || overlaps(o, nq, k, nkv) || overlaps(o, nq, v, nkv) ||
+      overlaps(lse, nl, q, nq) || overlaps(lse, nl, k, nkv) || overlaps(lse, nl, v, nkv) ||
+      overlaps(o, nq, lse, nl) || overlaps(o, nq, key_len_mask, nkl) ||
+      overlaps(lse, nl, key_len_mask, nkl))
+    return FA_ERR_ALIAS;
+  const size_t need = split_workspace(sp, d);
+  if (need > 0) {
+    if (!workspace || workspace_bytes < need || !is_aligned(workspace, 256)) return FA_ERR_WORKSPACE;
+    const int64_t nw = static_cast<int64_t>(need);
+    if (overlaps(workspace, nw, q, nq) || overlaps(workspace, nw, k, nkv) ||
+        overlaps(workspace, nw, v, nkv) || overlaps(workspace, nw, o, nq) ||
+        overlaps(workspace, nw, lse, nl) || overlaps(workspace, nw, key_len_mask, nkl))
+      return FA_ERR_ALIAS;
+  }
+
+  fa::FwdParams p = make_params(q, k, v, o, lse, B, H, Nq, scale, key_len_mask, dtype);
+  p.Nk = Nk;
+  p.end_aligned = 1;
+  p.splits = sp.splits;
+  p.split_keys = sp.split_keys;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (sp.splits > 1) {
+    p.o_part = static_cast<float*>(workspace);
+    p.lse_part = reinterpret_cast<float*>(static_cast<char*>(workspace) + split_part_bytes(sp, d));
+  }
+  if (fa::launch_fwd_bf16(p, d, causal != 0, hs) != hipSuccess) return FA_ERR_HIP;
+  if (sp.splits > 1) {
+    fa::MergeParams mp{};
+    mp.o_part = p.o_part;
+    mp.lse_part = p.lse_part;
+    mp.o = o;
+    mp.lse = lse;
+    mp.rows = sp.rows;
+    mp.splits = sp.splits;
+    if (fa::launch_merge(mp, d, true, hs) != hipSuccess) return FA_ERR_HIP;
+  }
+  return FA_OK;
+}
+
 extern "C" const char* fa_status_string(int status) {
   switch (status) {
     case FA_OK: return "ok";
     case FA_ERR_NULL: return "a required pointer is NULL";
     case FA_ERR_SHAPE: return "B, H or N is negative or the sizes overflow";
     case FA_ERR_HEAD_DIM: return "head dimension must be 64 or 128";
-    case FA_ERR_DTYPE: return "dtype must be FA_DTYPE_BF16 or FA_DTYPE_F32";
+    case FA_ERR_DTYPE: return "dtype not supported by this entry point";
     case FA_ERR_ALIGN: return "a pointer is misaligned (q, k, v, o: 16 bytes; lse, key_len: 4)";
     case FA_ERR_SCALE: return "scale must be finite";
     case FA_ERR_ALIAS: return "an output overlaps an input or another output";

@@ -94,32 +94,50 @@ void fa_fwd_bf16_kernel(FwdParams p) {
   const int h = lane >> 5;
 
   // ---- tile assignment ----------------------------------------------------
+  // Workgroup = (key range, (batch, head), query tile); consecutive ids
+  // take consecutive key ranges, then cycle over (batch, head).
   const int BH = p.B * p.H;
-  const int x = blockIdx.x;
+  int x = blockIdx.x;
+  const int split = x % p.splits;
+  x /= p.splits;
   const int bh = x % BH;
   int qt = x / BH;
   if (CAUSAL) qt = p.n_qtiles - 1 - qt;  // heaviest tiles first
   const int b = bh / p.H;
-  const int N = p.N;
+  const int N = p.N;    // query rows
+  const int Nk = p.Nk;  // key rows
   const int q0 = qt * C::BQ;
-  int kv_lim = N;
+  int kv_lim = Nk;
   if (p.key_len) {
     const int L = p.key_len[b];
-    kv_lim = L < 0 ? 0 : (L > N ? N : L);
+    kv_lim = L < 0 ? 0 : (L > Nk ? Nk : L);
   }
   // uniform across the workgroup; keep it (and all that derives from it,
   // such as the buffer ranges) in scalar registers
   kv_lim = __builtin_amdgcn_readfirstlane(kv_lim);
+  // Query row i sits at key position i + off: i itself, or, with the rows
+  // aligned to the end of the sequence's keys, i + L_b - N (then no row is
+  // padding).
+  const int off = p.end_aligned ? kv_lim - N : 0;
+  // Keys this query tile can see: below the length and, if causal, at or
+  // before the position of its last row.
   int n_kv = kv_lim;
-  if (CAUSAL) n_kv = min(n_kv, q0 + C::BQ);
-  if (q0 >= kv_lim) n_kv = 0;  // every row of the tile is padding
-  const int ntiles = (n_kv + C::BK - 1) / C::BK;
+  if (CAUSAL) n_kv = min(n_kv, max(0, q0 + C::BQ + off));
+  if (q0 + off >= kv_lim) n_kv = 0;  // every row of the tile is padding
+  // This workgroup's key range; ranges are whole tiles, so only the
+  // sequence end and the diagonal need element masks.
+  const int kv_first = split * p.split_keys;
+  const int kv_last = min(n_kv, kv_first + p.split_keys);
+  const int ntiles = kv_last > kv_first ? (kv_last - kv_first + C::BK - 1) / C::BK : 0;
 
-  const int64_t base = (int64_t)bh * N * D;
+  const int64_t base = (int64_t)bh * N * D;     // Q, O
+  const int64_t kvbase = (int64_t)bh * Nk * D;  // K, V
   const uint16_t* __restrict__ qg = (const uint16_t*)p.q + base;
 
   const int qw0 = q0 + 32 * wave;  // first query row of this wave
   const int qrow = qw0 + l32;      // the query row this lane owns
+  const int qwpos = qw0 + off;     // key position of the wave's first row
+  const int qpos = qrow + off;     // key position of this lane's row
 
   // ---- Q fragments (B operand of S^T = K Q^T) -----------------------------
   bf16x8 qf[D / 16];
@@ -135,8 +153,8 @@ void fa_fwd_bf16_kernel(FwdParams p) {
   // Buffer range = the valid keys of this (batch, head): loads beyond it
   // return zeros, so padded keys contribute exact zeros to both products.
   const uint32_t valid_bytes = (uint32_t)kv_lim * C::ROW_BYTES;
-  const void* kbase = (const uint16_t*)p.k + base;
-  const void* vbase = (const uint16_t*)p.v + base;
+  const void* kbase = (const uint16_t*)p.k + kvbase;
+  const void* vbase = (const uint16_t*)p.v + kvbase;
   // Per-lane source offsets within a tile (bytes): load i of this wave fills
   // the 1 KiB LDS block WAVES*i + wave; lane l fills its 16-byte chunk l.
   uint32_t koff[C::LOADS], voff[C::LOADS];
@@ -178,7 +196,7 @@ void fa_fwd_bf16_kernel(FwdParams p) {
 
   // Waves whose rows see no key of the tile at kv0 skip it (wave-uniform).
   auto skip_tile = [&](const int kv0) __attribute__((always_inline)) {
-    return (CAUSAL && kv0 > qw0 + 31) || (qw0 >= kv_lim);
+    return (CAUSAL && kv0 > qwpos + 31) || (qwpos >= kv_lim) || (qw0 >= N);
   };
 
   // ---- LDS fragment reads ---------------------------------------------------
@@ -289,14 +307,14 @@ void fa_fwd_bf16_kernel(FwdParams p) {
       __attribute__((always_inline)) {
     // Element masks only where the tile crosses the diagonal or the
     // sequence end (wave-uniform test).
-    const bool masked = (CAUSAL && kv0 + C::BK - 1 > qw0) || (kv0 + C::BK > kv_lim);
+    const bool masked = (CAUSAL && kv0 + C::BK - 1 > qwpos) || (kv0 + C::BK > kv_lim);
     if (masked) {
 #pragma unroll
       for (int bb = 0; bb < C::NB; ++bb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = kv0 + 32 * bb + acc_row(r, h);
-          const bool vis = key < kv_lim && (!CAUSAL || key <= qrow);
+          const bool vis = key < kv_lim && (!CAUSAL || key <= qpos);
           s[bb][r] = vis ? s[bb][r] : kNegInf;
         }
     }
@@ -470,13 +488,13 @@ void fa_fwd_bf16_kernel(FwdParams p) {
     // between two barriers -------------------------------------------------
 #pragma unroll
     for (int st = 0; st < NSTAGE - 1; ++st)
-      if (st < ntiles) load_tile(st * C::BK, st);
+      if (st < ntiles) load_tile(kv_first + st * C::BK, st);
 
     // One streamed tile, read from LDS stage S (a compile-time constant:
     // the loop below cycles through the NSTAGE instantiations).
     auto step = [&](const int t, auto stage_tag) __attribute__((always_inline)) {
       constexpr int S = decltype(stage_tag)::value;
-      const int kv0 = t * C::BK;
+      const int kv0 = kv_first + t * C::BK;
       // Tile t has landed once at most the loads of the tiles issued after
       // it are still in flight; after the barrier every wave's part has
       // landed and every wave is done with tile t - 1, whose stage is
@@ -557,7 +575,7 @@ void fa_fwd_bf16_kernel(FwdParams p) {
     // wave always has the same number of loads in flight).
     auto load_ahead = [&](const int u) __attribute__((always_inline)) {
       const uint32_t nb = u < ntiles ? valid_bytes : 0u;
-      load_tile_n(u * C::BK, stage_of(u), __builtin_amdgcn_readfirstlane(nb));
+      load_tile_n(kv_first + u * C::BK, stage_of(u), __builtin_amdgcn_readfirstlane(nb));
     };
     auto issue_loads = [&](const int t) __attribute__((always_inline)) { load_ahead(t + LA); };
 #pragma unroll
@@ -570,7 +588,7 @@ void fa_fwd_bf16_kernel(FwdParams p) {
     // more at the peak and ran no faster.)
     auto softmax_phase = [&](const int t) __attribute__((always_inline)) {
       __builtin_amdgcn_s_setprio(0);
-      softmax(t * C::BK, s, pf, [] {});
+      softmax(kv_first + t * C::BK, s, pf, [] {});
       v_issue_range(v_stage(t), G0, std::integral_constant<int, VG>{});
     };
     constexpr auto K4 = std::integral_constant<int, 4>{};
@@ -625,26 +643,45 @@ void fa_fwd_bf16_kernel(FwdParams p) {
   }
 
   // ---- epilogue: o = a / l, LSE = ln(2) * (m + log2 l) ---------------------
+  // Rows at or beyond the key length are padding (o = 0, LSE = -inf); so is
+  // a row that saw no key in this workgroup's range.
   const float l_tot = halves_sum(l_run);
   const float lp_tot = halves_sum(lp_run);
-  const bool valid = qrow < kv_lim;  // rows at or beyond the length are padding
+  const bool valid = qpos < kv_lim && lp_tot > 0.f;
   const float inv = valid ? 1.f / lp_tot : 0.f;
+  const float lse_row = valid ? (m_ref + __log2f(l_tot)) * kLn2 : kNegInf;
   if (qrow < N) {
-    uint16_t* og = (uint16_t*)p.o + base + (int64_t)qrow * D;
+    if (p.o_part) {
+      // one key range of several: fp32 partial result and its log-sum-exp
+      const int64_t prow = ((int64_t)split * BH + bh) * N + qrow;
+      float* og = p.o_part + prow * D;
 #pragma unroll
-    for (int db = 0; db < C::ND; ++db) {
+      for (int db = 0; db < C::ND; ++db) {
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int d0 = 32 * db + 8 * g + 4 * h;
-        float y[4];
+        for (int g = 0; g < 4; ++g) {
+          const int d0 = 32 * db + 8 * g + 4 * h;
+          f32x4 y;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) y[e] = valid ? o_acc[db][4 * g + e] * inv : 0.f;
-        u32x2 w = {pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
-        *(u32x2*)(og + d0) = w;
+          for (int e = 0; e < 4; ++e) y[e] = valid ? o_acc[db][4 * g + e] * inv : 0.f;
+          *(f32x4*)(og + d0) = y;
+        }
       }
-    }
-    if (h == 0) {
-      p.lse[(int64_t)bh * N + qrow] = valid ? (m_ref + __log2f(l_tot)) * kLn2 : kNegInf;
+      if (h == 0) p.lse_part[prow] = lse_row;
+    } else {
+      uint16_t* og = (uint16_t*)p.o + base + (int64_t)qrow * D;
+#pragma unroll
+      for (int db = 0; db < C::ND; ++db) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int d0 = 32 * db + 8 * g + 4 * h;
+          float y[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) y[e] = valid ? o_acc[db][4 * g + e] * inv : 0.f;
+          u32x2 w = {pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
+          *(u32x2*)(og + d0) = w;
+        }
+      }
+      if (h == 0) p.lse[(int64_t)bh * N + qrow] = lse_row;
     }
   }
 }
@@ -653,7 +690,7 @@ template <int D, bool CAUSAL, int WAVES, int NSTAGE, bool PINGPONG>
 hipError_t launch_cfg(FwdParams p, hipStream_t stream) {
   using C = Bf16Cfg<D, WAVES, NSTAGE>;
   p.n_qtiles = (p.N + C::BQ - 1) / C::BQ;
-  const dim3 grid((unsigned)((int64_t)p.n_qtiles * p.B * p.H));
+  const dim3 grid((unsigned)((int64_t)p.n_qtiles * p.B * p.H * p.splits));
   hipLaunchKernelGGL((fa_fwd_bf16_kernel<D, CAUSAL, WAVES, NSTAGE, PINGPONG>), grid,
                      dim3(64 * WAVES), 0, stream, p);
   return hipGetLastError();
@@ -661,12 +698,13 @@ hipError_t launch_cfg(FwdParams p, hipStream_t stream) {
 
 template <int D, bool CAUSAL>
 hipError_t launch_d(const FwdParams& p, hipStream_t stream) {
-  // 256-row tiles (8 waves, one workgroup per CU, 3-stage ring) when there
-  // are enough of them to fill the chip twice over; 128-row tiles (4 waves,
-  // two workgroups per CU, 2 stages) otherwise.  (Measured on MI355X at
-  // N = 8192, d = 128: 3 stages are a few percent ahead of 2 and 4.)
-  const int64_t big_tiles = (int64_t)p.B * p.H * ((p.N + 255) / 256);
-  if (big_tiles >= 512) return launch_cfg<D, CAUSAL, 8, kPingPongStages, true>(p, stream);
+  // 256-row tiles (8 waves, one workgroup per CU, ping-pong schedule) when
+  // the query tiles are full and there are enough workgroups to fill the
+  // chip twice over; 128-row tiles (4 waves, two workgroups per CU, lockstep
+  // schedule, which skips rows past the end) otherwise.
+  const int64_t big_tiles = (int64_t)p.B * p.H * ((p.N + 255) / 256) * p.splits;
+  if (p.N >= 256 && big_tiles >= 512)
+    return launch_cfg<D, CAUSAL, 8, kPingPongStages, true>(p, stream);
   return launch_cfg<D, CAUSAL, 4, 2, false>(p, stream);
 }
 

@@ -9,16 +9,32 @@ namespace fa {
 
 // Everything a forward kernel needs, passed by value as one kernel argument.
 struct FwdParams {
-  const void* q;
-  const void* k;
-  const void* v;
-  void* o;
-  float* lse;
+  const void* q;           // [B, H, N, d]
+  const void* k;           // [B, H, Nk, d]
+  const void* v;           // [B, H, Nk, d]
+  void* o;                 // [B, H, N, d] (unused when o_part is set)
+  float* lse;              // [B, H, N]    (unused when o_part is set)
   const int32_t* key_len;  // device [B] or nullptr
-  int B, H, N;
+  int B, H, N;             // N: query rows
+  int Nk;                  // key rows
+  int end_aligned;         // 0: query row i sits at key position i; 1: at i + L_b - N
   int n_qtiles;            // ceil(N / query-tile rows)
+  int splits;              // key ranges per (batch, head, query tile), >= 1
+  int split_keys;          // keys per range, a multiple of 128
+  float* o_part;           // [splits, B, H, N, d] fp32 partial outputs, or nullptr
+  float* lse_part;         // [splits, B, H, N] their log-sum-exp
   float c;                 // |scale| * log2(e): scores enter exp2 in log2 units
   uint32_t q_sign;         // sign bits xor-ed into Q when scale < 0 (0 otherwise)
+};
+
+// Merge of split partial results into the final output.
+struct MergeParams {
+  const float* o_part;     // [splits, rows, d]
+  const float* lse_part;   // [splits, rows]
+  void* o;                 // [rows, d] in the input dtype
+  float* lse;              // [rows]
+  int64_t rows;            // B * H * N
+  int splits;
 };
 
 // Parameters of the materialised (three-pass) path's softmax pass.
@@ -37,5 +53,6 @@ constexpr int kQueryTile = 128;
 hipError_t launch_fwd_bf16(const FwdParams& p, int d, bool causal, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdParams& p, int d, bool causal, hipStream_t stream);
 hipError_t launch_naive_softmax(const NaiveSoftmaxParams& p, bool bf16, hipStream_t stream);
+hipError_t launch_merge(const MergeParams& p, int d, bool bf16, hipStream_t stream);
 
 }  // namespace fa

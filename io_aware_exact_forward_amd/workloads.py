@@ -35,6 +35,11 @@ __all__ = [
     "bf16_decode",
     "make_inputs",
     "valid_pairs",
+    "cache_inputs",
+    "decode_inputs",
+    "DecodeWorkload",
+    "DECODE_WORKLOADS",
+    "Inputs",
 ]
 
 
@@ -179,6 +184,66 @@ def random_inputs(B, H, N, d, dtype, seed, *, q_mult=1.0, key_len=None):
     wl = Workload(f"random_b{B}_h{H}_n{N}_d{d}_{dtype}", B, H, N, d, dtype, False,
                   1.0 / math.sqrt(d), seed, q_mult=q_mult)
     return Inputs(wl, q, k, v, kl, None)
+
+
+def cache_inputs(B, H, Nq, Nk, d, seed, *, q_mult=1.0, key_len=None):
+    """Query rows against a longer key cache (same recipe, bf16): q [B, H, Nq, d]
+    is drawn first, then k and v [B, H, Nk, d]."""
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((B, H, Nq, d), dtype=np.float32)
+    k = rng.standard_normal((B, H, Nk, d), dtype=np.float32)
+    v = rng.standard_normal((B, H, Nk, d), dtype=np.float32)
+    if q_mult != 1.0:
+        q *= np.float32(q_mult)
+    kl = None if key_len is None else np.asarray(key_len, dtype=np.int32)
+    wl = Workload(f"cache_b{B}_h{H}_q{Nq}_k{Nk}_d{d}_bf16", B, H, Nk, d, "bf16", False,
+                  1.0 / math.sqrt(d), seed, q_mult=q_mult)
+    return Inputs(wl, bf16_encode(q), bf16_encode(k), bf16_encode(v), kl, None)
+
+
+@dataclasses.dataclass(frozen=True)
+class DecodeWorkload:
+    """One query row per (sequence, head) against a key cache of Nk rows
+    whose per-sequence lengths are uniform on [1, Nk]; causal, bf16."""
+    name: str
+    B: int
+    H: int
+    Nk: int
+    d: int
+    seed: int
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+    def describe(self) -> dict:
+        return {"workload": self.name, "B": self.B, "H": self.H, "Nq": 1, "Nk": self.Nk,
+                "d": self.d, "dtype": "bf16", "causal": True, "scale": self.scale,
+                "key_len": "per sequence, uniform on [1, Nk]"}
+
+
+DECODE_WORKLOADS = {
+    # decode step of 8 sequences x 32 heads, d = 128, caches of up to 16384 keys
+    "decode_b8_h32_k16384_d128_bf16": DecodeWorkload(
+        "decode_b8_h32_k16384_d128_bf16", 8, 32, 16384, 128, 1006),
+}
+
+
+def decode_inputs(wl: DecodeWorkload, *, B=None, H=None, Nk=None, seed=None) -> "Inputs":
+    """q [B, H, 1, d], then k, v [B, H, Nk, d], then key lengths (same recipe);
+    keyword overrides give smaller variants."""
+    B = wl.B if B is None else B
+    H = wl.H if H is None else H
+    Nk = wl.Nk if Nk is None else Nk
+    seed = wl.seed if seed is None else seed
+    d = wl.d
+    rng = np.random.default_rng(seed)
+    q = bf16_encode(rng.standard_normal((B, H, 1, d), dtype=np.float32))
+    k = bf16_encode(rng.standard_normal((B, H, Nk, d), dtype=np.float32))
+    v = bf16_encode(rng.standard_normal((B, H, Nk, d), dtype=np.float32))
+    kl = rng.integers(1, Nk, size=B, endpoint=True, dtype=np.int64).astype(np.int32)
+    sq = Workload(wl.name, B, H, Nk, d, "bf16", True, wl.scale, seed, ragged=True)
+    return Inputs(sq, q, k, v, kl, None)
 
 
 def valid_pairs(N: int, causal: bool, key_len=None, B: int = 1) -> int:

@@ -32,8 +32,8 @@ def declared_functions():
 
 def test_header_declares_expected_entry_points():
     assert declared_functions() == sorted(
-        ["fa_forward", "fa_naive_workspace_bytes", "fa_naive_forward", "fa_status_string",
-         "fa_abi_version"])
+        ["fa_forward", "fa_naive_workspace_bytes", "fa_naive_forward", "fa_split_workspace_bytes",
+         "fa_forward_split", "fa_status_string", "fa_abi_version"])
 
 
 def test_library_loads_and_exports_every_declared_symbol():
@@ -41,7 +41,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     for name in declared_functions():
         assert hasattr(lib, name), name
     assert set(_lib.exported_symbols()) == set(declared_functions())
-    assert fa.fa_abi_version() == (1 << 16)
+    assert fa.fa_abi_version() == (1 << 16) | 1
 
 
 def test_status_strings():
@@ -132,3 +132,85 @@ def test_python_wrapper_rejects_host_tensors():
     x = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
     with pytest.raises(fa.FAError):
         fa.forward(x, x, x)
+
+
+# ---- split-KV entry point -------------------------------------------------------
+
+def split_call(q=Q, k=K, v=V, o=O, lse=L, B=1, H=2, Nq=64, Nk=1024, d=64, scale=0.125, causal=0,
+               kl=0, dtype=BF16, num_splits=4, ws=WS, wsb=1 << 30, stream=0):
+    return fa.fa_forward_split(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, kl, dtype,
+                               num_splits, ws, wsb, stream)
+
+
+def test_split_workspace_size():
+    # fp32 partial outputs [ranges, B*H*Nq, d] then their LSE [ranges, B*H*Nq],
+    # each rounded up to 256 bytes; ranges are whole 128-key blocks
+    assert fa.fa_split_workspace_bytes(1, 2, 64, 1024, 64, 4) == 4 * 128 * 64 * 4 + 4 * 128 * 4
+    # one range: no workspace
+    assert fa.fa_split_workspace_bytes(1, 2, 64, 1024, 64, 1) == 0
+    # automatic: 2 query tiles -> as many ranges as 128-key blocks (8)
+    assert fa.fa_split_workspace_bytes(1, 2, 64, 1024, 64, 0) == 8 * 128 * 64 * 4 + 8 * 128 * 4
+    # more ranges asked than blocks: one block per range
+    assert fa.fa_split_workspace_bytes(1, 2, 64, 1024, 64, 100) == 8 * 128 * 64 * 4 + 8 * 128 * 4
+    # 8 blocks in 3 ranges of 3, 3, 2 blocks; d = 128; one decode row per head
+    assert fa.fa_split_workspace_bytes(2, 3, 1, 1000, 128, 3) == 3 * 6 * 128 * 4 + 256
+    # many query tiles: the automatic choice stays at one range
+    assert fa.fa_split_workspace_bytes(1, 32, 8192, 8192, 128, 0) == 0
+    # no keys, empty problems and invalid arguments: 0
+    assert fa.fa_split_workspace_bytes(1, 2, 64, 0, 64, 4) == 0
+    assert fa.fa_split_workspace_bytes(0, 2, 64, 1024, 64, 4) == 0
+    assert fa.fa_split_workspace_bytes(-1, 2, 64, 1024, 64, 4) == 0
+    assert fa.fa_split_workspace_bytes(1, 2, 64, 1024, 96, 4) == 0
+    assert fa.fa_split_workspace_bytes(1, 2, 64, 1024, 64, -1) == 0
+    assert fa.fa_split_workspace_bytes(1, 2, 64, 1024, 64, 65537) == 0
+
+
+def test_split_bad_arguments():
+    assert split_call(dtype=F32) == DTYPE
+    assert split_call(dtype=3) == DTYPE
+    assert split_call(d=96) == HEAD_DIM
+    for bad in (dict(B=-1), dict(H=-1), dict(Nq=-1), dict(Nk=-1), dict(num_splits=-1),
+                dict(num_splits=65537)):
+        assert split_call(**bad) == SHAPE, bad
+    # one (batch, head) slice above 2^31 - 1 bytes
+    assert split_call(Nq=1 << 24, d=128) == SHAPE
+    assert split_call(Nk=1 << 24, d=128) == SHAPE
+    for s in (float("nan"), float("inf"), 3e38):
+        assert split_call(scale=s) == SCALE
+
+
+def test_split_empty_is_a_no_op():
+    for B, H, Nq in ((0, 2, 64), (1, 0, 64), (1, 2, 0)):
+        assert split_call(q=0, k=0, v=0, o=0, lse=0, B=B, H=H, Nq=Nq, ws=0, wsb=0) == OK
+
+
+def test_split_pointer_checks():
+    for field in ("q", "k", "v", "o", "lse"):
+        assert split_call(**{field: 0}) == NULL
+    for field, val in (("q", Q + 8), ("k", K + 8), ("v", V + 8), ("o", O + 8), ("lse", L + 2),
+                       ("kl", KL + 1)):
+        assert split_call(**{field: val}) == ALIGN, field
+    assert split_call(o=Q) == ALIAS
+    assert split_call(lse=V + 4) == ALIAS
+    assert split_call(o=L) == ALIAS
+
+
+def test_split_workspace_errors():
+    need = fa.fa_split_workspace_bytes(1, 2, 64, 1024, 64, 4)
+    assert need > 0
+    assert split_call(ws=0, wsb=need) == WORKSPACE
+    assert split_call(wsb=need - 1) == WORKSPACE
+    assert split_call(ws=WS + 16, wsb=need) == WORKSPACE   # 256-byte alignment
+    assert split_call(ws=Q, wsb=need) == ALIAS
+    assert split_call(ws=O - 256, wsb=need) == ALIAS          # tail overlaps the output
+    assert split_call(ws=KL, wsb=need, kl=KL + need - 4) == ALIAS
+
+
+def test_python_split_wrapper_rejects_bad_tensors():
+    import torch
+    x = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
+    with pytest.raises(fa.FAError):
+        fa.forward_split(x, x, x)
+    y = torch.zeros(1, 2, 4, 64, dtype=torch.bfloat16)
+    with pytest.raises(fa.FAError):
+        fa.forward_split(x, y, y)   # heads differ
