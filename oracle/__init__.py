@@ -1,4 +1,4 @@
-"""fp64 CPU oracle for the attention forward pass.
+"""fp64 CPU oracle for the attention forward pass and its gradients.
 
 TEST INFRASTRUCTURE ONLY: imported by the tests, by the smoke check of the
 repository's graft entry point and by the benchmark's CPU-baseline leg, never
@@ -13,3 +13,4 @@ from .attention import (  # noqa: F401
     streamed_attention,
     split_attention,
 )
+from .backward import attention_backward  # noqa: F401
