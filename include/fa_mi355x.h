@@ -174,13 +174,37 @@ int fa_forward_split(const void* q, const void* k, const void* v, void* o, float
                      const int32_t* key_len_mask, int dtype, int num_splits,
                      void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Attention backward by recomputation ("IO-aware exact attention", section
+ * "Backward recomputation"): the gradients dQ, dK, dV of the loss
+ * sum(dO * O) for O = fa_forward(q, k, v, ...), rebuilt from the inputs, the
+ * forward's output o and its log-sum-exp lse, without storing any N x N
+ * matrix.  With P the masked softmax, D_i = dO_i . O_i:
+ *   dV = P^T dO,  dS = P * (dO V^T - D),  dQ = scale * dS K,  dK = scale * dS^T Q.
+ *   q, k, v, o, dout, dq, dk, dv  [B, H, N, d] of `dtype`; lse [B, H, N] fp32 as
+ *                written by fa_forward with the same scale, causal and key_len_mask.
+ *   Masks        those of fa_forward; padding rows and keys at or beyond L_b get
+ *                zero gradients (their dO and lse entries are not read).
+ *   dtype        FA_DTYPE_BF16 only; d = 64 only (FA_ERR_HEAD_DIM otherwise).
+ *   workspace    device memory, 256-byte aligned, of at least
+ *                fa_backward_workspace_bytes(B, H, N, d, dtype) bytes (fp32 D,
+ *                [B, H, N]); it and dq, dk, dv overlap no input and no other output.
+ * Enqueues two kernels on `stream` (dQ and D, then dK and dV).  Validation,
+ * alignment and error conventions are those of fa_forward.
+ */
+size_t fa_backward_workspace_bytes(int B, int H, int N, int d, int dtype);
+int fa_backward(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                const void* dout, void* dq, void* dk, void* dv, int B, int H, int N, int d,
+                float scale, int causal, const int32_t* key_len_mask, int dtype,
+                void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* fa_status_string(int status);
 
 /* ABI version of this header: (major << 16) | minor. */
 int fa_abi_version(void);
 
-#define FA_ABI_VERSION ((1 << 16) | 1)
+#define FA_ABI_VERSION ((1 << 16) | 2)
 
 #ifdef __cplusplus
 }

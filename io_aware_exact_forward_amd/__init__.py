@@ -1,8 +1,8 @@
 """Exact attention forward for MI355X (gfx950): fused HIP kernels behind a C ABI.
 
 The C entry points (include/fa_mi355x.h) are exposed under their own names by
-``io_aware_exact_forward_amd._lib``; ``forward``, ``forward_split`` and
-``naive_forward`` below are conveniences that take torch tensors (torch only provides device memory
+``io_aware_exact_forward_amd._lib``; ``forward``, ``forward_split``,
+``backward`` and ``naive_forward`` below are conveniences that take torch tensors (torch only provides device memory
 and the stream), allocate the outputs and call those entry points.  Nothing
 here computes attention itself.
 """
@@ -16,6 +16,8 @@ from ._lib import (  # noqa: F401
     FAError,
     check,
     fa_abi_version,
+    fa_backward,
+    fa_backward_workspace_bytes,
     fa_forward,
     fa_forward_split,
     fa_naive_forward,
@@ -26,7 +28,8 @@ from ._lib import (  # noqa: F401
 )
 
 __all__ = [
-    "forward", "forward_split", "naive_forward", "fa_forward", "fa_forward_split",
+    "forward", "forward_split", "backward", "naive_forward", "fa_forward", "fa_forward_split",
+    "fa_backward", "fa_backward_workspace_bytes",
     "fa_split_workspace_bytes", "fa_naive_forward", "fa_naive_workspace_bytes",
     "fa_status_string", "fa_abi_version", "FAError", "FA_DTYPE_BF16", "FA_DTYPE_F32",
 ]
@@ -130,3 +133,38 @@ def forward_split(q, k, v, *, scale=None, causal=False, key_len=None, num_splits
                            lse.data_ptr(), B, H, Nq, Nk, d, float(scale), int(bool(causal)), kl,
                            _dtype_code(q), int(num_splits), ws, wsb, stream))
     return out, lse
+
+
+def backward(q, k, v, o, lse, dout, *, scale=None, causal=False, key_len=None, workspace=None,
+             dq=None, dk=None, dv=None):
+    """dQ, dK, dV = fa_backward(...): gradients of sum(dout * O) for the forward
+    result (o, lse) of the same q, k, v, scale, causal and key_len."""
+    import torch
+    for t in (q, k, v, o, dout):
+        if t.dim() != 4 or t.shape != q.shape or t.dtype != q.dtype:
+            raise FAError(-2, "q, k, v, o, dout must share one [B, H, N, d] shape and dtype")
+        if not t.is_cuda or not t.is_contiguous():
+            raise FAError(-1, "q, k, v, o, dout must be contiguous device tensors")
+    B, H, N, d = q.shape
+    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_cuda:
+        raise FAError(-2, "lse must be a device float32 tensor [B, H, N]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    kl = 0
+    if key_len is not None:
+        if key_len.dtype != torch.int32 or not key_len.is_cuda or key_len.numel() != B:
+            raise FAError(-1, "key_len must be a device int32 tensor of B elements")
+        kl = key_len.data_ptr()
+    dt = _dtype_code(q)
+    if workspace is None:
+        need = fa_backward_workspace_bytes(B, H, N, d, dt)
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    check(fa_backward(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                      dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d,
+                      float(scale), int(bool(causal)), kl, dt, workspace.data_ptr(),
+                      workspace.numel(), stream))
+    return dq, dk, dv

@@ -39,6 +39,13 @@ _SIGNATURES = {
         ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float,
         ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
         ctypes.c_size_t, ctypes.c_void_p]),
+    "fa_backward_workspace_bytes": (ctypes.c_size_t, [
+        ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int]),
+    "fa_backward": (ctypes.c_int, [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float, ctypes.c_int,
+        ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
     "fa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "fa_abi_version": (ctypes.c_int, []),
 }
@@ -116,6 +123,17 @@ def fa_forward_split(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, key_len_ma
     return load().fa_forward_split(q, k, v, o, lse, B, H, Nq, Nk, d, scale, int(causal),
                                    key_len_mask or None, dtype, num_splits, workspace or None,
                                    workspace_bytes, stream or None)
+
+
+def fa_backward_workspace_bytes(B, H, N, d, dtype) -> int:
+    return load().fa_backward_workspace_bytes(B, H, N, d, dtype)
+
+
+def fa_backward(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, d, scale, causal, key_len_mask,
+                dtype, workspace, workspace_bytes, stream) -> int:
+    return load().fa_backward(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, d, scale, int(causal),
+                              key_len_mask or None, dtype, workspace or None, workspace_bytes,
+                              stream or None)
 
 
 def fa_status_string(status) -> str:

@@ -339,6 +339,77 @@ extern "C" int fa_forward_split(const void* q, const void* k, const void* v, voi
   return FA_OK;
 }
 
+extern "C" size_t fa_backward_workspace_bytes(int B, int H, int N, int d, int dtype) {
+  Shape s;
+  bool empty = false;
+  if (dtype != FA_DTYPE_BF16 || d != 64) return 0;
+  if (check_scalars(B, H, N, d, 1.f, dtype, &s, &empty) != FA_OK || empty) return 0;
+  return round256(size_t(s.rows) * sizeof(float));
+}
+
+extern "C" int fa_backward(const void* q, const void* k, const void* v, const void* o,
+                           const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                           int B, int H, int N, int d, float scale, int causal,
+                           const int32_t* key_len_mask, int dtype, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  if (dtype != FA_DTYPE_BF16) return FA_ERR_DTYPE;
+  if (d != 64) return FA_ERR_HEAD_DIM;
+  Shape s;
+  bool empty = false;
+  int st = check_scalars(B, H, N, d, scale, dtype, &s, &empty);
+  if (st != FA_OK || empty) return st;
+  const void* ins[] = {q, k, v, o, dout};
+  void* outs[] = {dq, dk, dv};
+  for (const void* x : ins)
+    if (!x) return FA_ERR_NULL;
+  for (void* x : outs)
+    if (!x) return FA_ERR_NULL;
+  if (!lse) return FA_ERR_NULL;
+  for (const void* x : ins)
+    if (!is_aligned(x, 16)) return FA_ERR_ALIGN;
+  for (void* x : outs)
+    if (!is_aligned(x, 16)) return FA_ERR_ALIGN;
+  if (!is_aligned(lse, 4) || (key_len_mask && !is_aligned(key_len_mask, 4))) return FA_ERR_ALIGN;
+  const int64_t nb = s.elems * s.esz, nl = s.rows * 4, nk = key_len_mask ? int64_t(B) * 4 : 0;
+  const size_t need = round256(size_t(s.rows) * sizeof(float));
+  if (!workspace || workspace_bytes < need || !is_aligned(workspace, 256)) return FA_ERR_WORKSPACE;
+  const int64_t nw = static_cast<int64_t>(need);
+  // the outputs (and the workspace) overlap no input and no other output
+  struct Region { const void* p; int64_t n; };
+  const Region written[] = {{dq, nb}, {dk, nb}, {dv, nb}, {workspace, nw}};
+  const Region read[] = {{q, nb}, {k, nb}, {v, nb}, {o, nb}, {dout, nb}, {lse, nl},
+                         {key_len_mask, nk}};
+  for (int i = 0; i < 4; ++i) {
+    for (const Region& r : read)
+      if (overlaps(written[i].p, written[i].n, r.p, r.n)) return FA_ERR_ALIAS;
+    for (int j = i + 1; j < 4; ++j)
+      if (overlaps(written[i].p, written[i].n, written[j].p, written[j].n)) return FA_ERR_ALIAS;
+  }
+
+  fa::BwdParams p{};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.dout = dout;
+  p.lse = lse;
+  p.dq = dq;
+  p.dk = dk;
+  p.dv = dv;
+  p.dvec = static_cast<float*>(workspace);
+  p.key_len = key_len_mask;
+  p.B = B;
+  p.H = H;
+  p.N = N;
+  p.n_qtiles = (N + 127) / 128;
+  p.n_ktiles = (N + 127) / 128;
+  p.scale = scale;
+  p.c2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
+  if (fa::launch_bwd_bf16(p, d, causal != 0, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return FA_ERR_HIP;
+  return FA_OK;
+}
+
 extern "C" const char* fa_status_string(int status) {
   switch (status) {
     case FA_OK: return "ok";

@@ -1,0 +1,453 @@
+// Attention backward for bf16 Q/K/V on gfx950 (CDNA4), by recomputation.
+//
+// "IO-aware exact attention" (section "Backward recomputation") keeps only
+// the inputs, the output and a per-row normalisation record from the
+// forward pass and rebuilds score and probability blocks while dQ, dK and dV
+// accumulate, so nothing N x N is stored.  The record here is the forward's
+// natural-log LSE: P_ij = exp(scale * q_i . k_j - LSE_i) is exact
+// recomputation of the forward's probabilities.  With the upstream gradient
+// dO and D_i = dO_i . O_i the gradients of the loss sum(dO * O) are
+//   dV = P^T dO,  dS = P * (dO V^T - D),  dQ = scale dS K,  dK = scale dS^T Q.
+//
+// Two kernels, neither with atomics:
+//  * fa_bwd_dq_kernel, one workgroup per 128 query rows (a wave per 32
+//    rows), streams key/value tiles like the forward: S^T = K Q^T and
+//    dP^T = V dO^T with Q and dO resident in registers, then
+//    dQ^T += K^T dS^T.  It also computes D_i (each lane holds half of its
+//    row of O and dO) and leaves it in the workspace.
+//  * fa_bwd_dkdv_kernel, one workgroup per 128 keys (a wave per 32 keys),
+//    streams query tiles with their LSE and D: S = Q K^T and dP = dO V^T
+//    with K and V resident, then dV^T += dO^T P and dK^T += Q^T dS.
+// Every product is a 32x32x16 bf16 MFMA with fp32 accumulation; P and dS are
+// rounded to bf16 only as MFMA operands.  The transposed operands (K^T,
+// dO^T, Q^T) come from row-major LDS tiles through transpose reads
+// (ds_read_b64_tr_b16), with the contraction index permuted to match the
+// register layout of P and dS, exactly as the forward reads V^T.
+//
+// Tiles go global -> registers -> LDS (two stages, one workgroup barrier
+// per tile).  Rows and keys at or beyond a sequence's length are loaded as
+// zeros and masked, so they contribute nothing, and their gradients are 0.
+#include "fa_bf16_tiles.hpp"
+#include "fa_device.hpp"
+#include "fa_internal.hpp"
+
+namespace fa {
+namespace {
+
+template <int D>
+struct BwdCfg {
+  static constexpr int ROW_BYTES = 2 * D;
+  static constexpr int CPR = D / 8;   // 16-byte chunks per row
+  static constexpr int ND = D / 32;   // 32-wide head-dim slices (accumulator blocks)
+  static constexpr int KD = D / 16;   // 16-wide head-dim chunks (MFMA k steps)
+};
+
+// Byte offset of logical chunk c of row r in a tile stored with the
+// transpose-friendly chunk permutation (read both plainly and transposed).
+template <int D>
+__device__ __forceinline__ int toff_t(int r, int c) {
+  return r * BwdCfg<D>::ROW_BYTES + 16 * v_chunk<D>(r, c);
+}
+// The same for tiles only read plainly.
+template <int D>
+__device__ __forceinline__ int toff_p(int r, int c) {
+  return r * BwdCfg<D>::ROW_BYTES + 16 * k_chunk<D>(r, c);
+}
+
+__device__ __forceinline__ bf16x8 lds_b128(const uint8_t* base, int off) {
+  return *(const bf16x8*)(base + off);
+}
+
+// A operand of an MFMA whose contraction runs over 16 rows of a row-major
+// tile (rows r0 .. r0+15 of the tile at `t`), for head-dim slice db: lane l
+// receives dim 32*db + l%32 of rows {r0 + 4h + 0..3, r0 + 8 + 4h + 0..3}
+// (h = l/32), which is the order in which the accumulator layout holds the
+// 16 rows of one MFMA's worth of P or dS.
+template <int D>
+__device__ __forceinline__ bf16x8 tr_operand(const uint8_t* t, int r0, int db, int lane) {
+  const int r16 = lane & 15, g16 = (lane >> 4) & 1, h = lane >> 5;
+  const int dim = 32 * db + 16 * g16 + 4 * (r16 & 3);
+  const int ra = r0 + 4 * h + (r16 >> 2);
+  const int rb = ra + 8;
+  const bf16x4 x = lds_read_tr16(t + toff_t<D>(ra, dim >> 3) + (dim & 7) * 2);
+  const bf16x4 y = lds_read_tr16(t + toff_t<D>(rb, dim >> 3) + (dim & 7) * 2);
+  return bf16x8{x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
+}
+
+// Eight accumulator registers (one MFMA's worth of rows) -> bf16 B operand.
+__device__ __forceinline__ bf16x8 pack8(const float* x) {
+  return bf16x8{(__bf16)x[0], (__bf16)x[1], (__bf16)x[2], (__bf16)x[3],
+                (__bf16)x[4], (__bf16)x[5], (__bf16)x[6], (__bf16)x[7]};
+}
+
+// Row of a 16-byte bf16 chunk -> fp32 dot product of two chunks.
+__device__ __forceinline__ float dot8(u32x4 a, u32x4 b) {
+  const bf16x8 x = __builtin_bit_cast(bf16x8, a), y = __builtin_bit_cast(bf16x8, b);
+  float s = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) s += (float)x[e] * (float)y[e];
+  return s;
+}
+
+__device__ __forceinline__ int seq_len(const BwdParams& p, int b) {
+  int L = p.N;
+  if (p.key_len) {
+    const int x = p.key_len[b];
+    L = x < 0 ? 0 : (x > p.N ? p.N : x);
+  }
+  return __builtin_amdgcn_readfirstlane(L);
+}
+
+// ---------------------------------------------------------------------------
+// dQ (and D): one workgroup per 128 query rows of one (batch, head)
+// ---------------------------------------------------------------------------
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256, 2) void fa_bwd_dq_kernel(BwdParams p) {
+  using C = BwdCfg<D>;
+  constexpr int BQ = 128, BK = 64, NB = BK / 32;
+  constexpr int TILE = BK * C::ROW_BYTES;
+  constexpr int LPT = BK * C::CPR / 256;  // 16-byte chunks per thread per tensor
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2][2 * TILE];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, l32 = lane & 31, h = lane >> 5;
+  const int BH = p.B * p.H;
+  const int bh = blockIdx.x % BH;
+  int qt = blockIdx.x / BH;
+  if (CAUSAL) qt = p.n_qtiles - 1 - qt;  // heaviest tiles first
+  const int b = bh / p.H;
+  const int N = p.N;
+  const int L = seq_len(p, b);
+  const int q0 = qt * BQ;
+  int n_kv = L;
+  if (CAUSAL) n_kv = min(n_kv, q0 + BQ);
+  if (q0 >= L) n_kv = 0;
+  const int ntiles = (n_kv + BK - 1) / BK;
+
+  const int64_t base = (int64_t)bh * N * D;
+  const uint16_t* qg = (const uint16_t*)p.q + base;
+  const uint16_t* kg = (const uint16_t*)p.k + base;
+  const uint16_t* vg = (const uint16_t*)p.v + base;
+  const uint16_t* og = (const uint16_t*)p.o + base;
+  const uint16_t* dog = (const uint16_t*)p.dout + base;
+
+  const int qw0 = q0 + 32 * wave;
+  const int row = qw0 + l32;
+  const bool row_ok = row < L;
+
+  // Q and dO of this lane's row (half of the head dim, B-operand layout),
+  // and D = dO . O over the whole row.
+  bf16x8 qf[C::KD], dof[C::KD];
+  float dsum = 0.f;
+#pragma unroll
+  for (int kk = 0; kk < C::KD; ++kk) {
+    u32x4 wq = {0u, 0u, 0u, 0u}, wd = {0u, 0u, 0u, 0u}, wo = {0u, 0u, 0u, 0u};
+    if (row_ok) {
+      const int64_t off = (int64_t)row * D + 16 * kk + 8 * h;
+      wq = *(const u32x4*)(qg + off);
+      wd = *(const u32x4*)(dog + off);
+      wo = *(const u32x4*)(og + off);
+    }
+    qf[kk] = __builtin_bit_cast(bf16x8, wq);
+    dof[kk] = __builtin_bit_cast(bf16x8, wd);
+    dsum += dot8(wd, wo);
+  }
+  const float dval = halves_sum(dsum);
+  const float lse2 = row_ok ? p.lse[(int64_t)bh * N + row] * kLog2e : 0.f;
+  if (h == 0 && row < N) p.dvec[(int64_t)bh * N + row] = row_ok ? dval : 0.f;
+
+  f32x16 dq[C::ND];
+#pragma unroll
+  for (int i = 0; i < C::ND; ++i) dq[i] = f32x16{};
+
+  // K tile: read plainly (S^T) and transposed (dQ^T); V tile: plainly (dP^T).
+  u32x4 kst[LPT], vst[LPT];
+  auto load_regs = [&](int kv0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < LPT; ++i) {
+      const int c = tid + 256 * i, r = c / C::CPR, lc = c % C::CPR;
+      const int key = kv0 + r;
+      u32x4 a = {0u, 0u, 0u, 0u}, v = {0u, 0u, 0u, 0u};
+      if (key < L) {
+        a = *(const u32x4*)(kg + (int64_t)key * D + 8 * lc);
+        v = *(const u32x4*)(vg + (int64_t)key * D + 8 * lc);
+      }
+      kst[i] = a;
+      vst[i] = v;
+    }
+  };
+  auto store_lds = [&](int st) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < LPT; ++i) {
+      const int c = tid + 256 * i, r = c / C::CPR, lc = c % C::CPR;
+      *(u32x4*)(&lds[st][toff_t<D>(r, lc)]) = kst[i];
+      *(u32x4*)(&lds[st][TILE + toff_p<D>(r, lc)]) = vst[i];
+    }
+  };
+
+  auto compute = [&](int st, int kv0) __attribute__((always_inline)) {
+    // keys all after the wave's last row, or the wave's rows all padding
+    if ((CAUSAL && kv0 > qw0 + 31) || qw0 >= L) return;
+    const uint8_t* kt = lds[st];
+    const uint8_t* vt = lds[st] + TILE;
+    f32x16 s[NB], dp[NB];
+#pragma unroll
+    for (int bb = 0; bb < NB; ++bb) {
+      s[bb] = f32x16{};
+      dp[bb] = f32x16{};
+      const int kr = 32 * bb + l32;
+#pragma unroll
+      for (int kk = 0; kk < C::KD; ++kk) {
+        s[bb] = mfma_32x32x16_bf16(lds_b128(kt, toff_t<D>(kr, 2 * kk + h)), qf[kk], s[bb]);
+        dp[bb] = mfma_32x32x16_bf16(lds_b128(vt, toff_p<D>(kr, 2 * kk + h)), dof[kk], dp[bb]);
+      }
+    }
+    // P^T and dS^T: lane = query row, register r of block bb = key 32bb + acc_row(r, h)
+    bf16x8 dsb[NB][2];
+#pragma unroll
+    for (int bb = 0; bb < NB; ++bb) {
+      float ds[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = kv0 + 32 * bb + acc_row(r, h);
+        const bool vis = row_ok && key < L && (!CAUSAL || key <= row);
+        const float pr = vis ? fast_exp2(__builtin_fmaf(s[bb][r], p.c2, -lse2)) : 0.f;
+        ds[r] = pr * (dp[bb][r] - dval);
+      }
+      dsb[bb][0] = pack8(ds);
+      dsb[bb][1] = pack8(ds + 8);
+    }
+    // dQ^T += K^T dS^T
+#pragma unroll
+    for (int db = 0; db < C::ND; ++db)
+#pragma unroll
+      for (int bb = 0; bb < NB; ++bb)
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+          dq[db] = mfma_32x32x16_bf16(tr_operand<D>(kt, 32 * bb + 16 * m, db, lane), dsb[bb][m], dq[db]);
+  };
+
+  if (ntiles > 0) {
+    load_regs(0);
+    store_lds(0);
+    __syncthreads();
+    for (int t = 0; t < ntiles; ++t) {
+      const bool more = t + 1 < ntiles;
+      if (more) load_regs((t + 1) * BK);
+      compute(t & 1, t * BK);
+      if (more) store_lds((t + 1) & 1);
+      __syncthreads();
+    }
+  }
+
+  // dQ = scale * (dQ^T)^T: lane = row, register r of slice db = dim 32db + acc_row(r, h)
+  if (row < N) {
+    uint16_t* dqg = (uint16_t*)p.dq + base + (int64_t)row * D;
+#pragma unroll
+    for (int db = 0; db < C::ND; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = 32 * db + 8 * g + 4 * h;
+        const f32x16& a = dq[db];
+        u32x2 w = {pack_bf16x2(p.scale * a[4 * g], p.scale * a[4 * g + 1]),
+                   pack_bf16x2(p.scale * a[4 * g + 2], p.scale * a[4 * g + 3])};
+        *(u32x2*)(dqg + d0) = w;
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV: one workgroup per 128 keys of one (batch, head)
+// ---------------------------------------------------------------------------
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256, 2) void fa_bwd_dkdv_kernel(BwdParams p) {
+  using C = BwdCfg<D>;
+  constexpr int BKW = 128, BQ = 64, NQB = BQ / 32;
+  constexpr int TILE = BQ * C::ROW_BYTES;
+  constexpr int LPT = BQ * C::CPR / 256;
+  // [stage][Q tile | dO tile | LSE2 (BQ floats) | D (BQ floats)]
+  constexpr int STAGE = 2 * TILE + 2 * BQ * 4;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2][STAGE];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, l32 = lane & 31, h = lane >> 5;
+  const int BH = p.B * p.H;
+  const int bh = blockIdx.x % BH;
+  const int kt_idx = blockIdx.x / BH;  // causal: lower key tiles see more rows: heaviest first
+  const int b = bh / p.H;
+  const int N = p.N;
+  const int L = seq_len(p, b);
+  const int k0 = kt_idx * BKW;
+  const int kw0 = k0 + 32 * wave;
+  const int key = kw0 + l32;
+  const bool key_ok = key < L;
+
+  const int64_t base = (int64_t)bh * N * D;
+  const uint16_t* qg = (const uint16_t*)p.q + base;
+  const uint16_t* kg = (const uint16_t*)p.k + base;
+  const uint16_t* vg = (const uint16_t*)p.v + base;
+  const uint16_t* dog = (const uint16_t*)p.dout + base;
+  const float* lseg = p.lse + (int64_t)bh * N;
+  const float* dvg = p.dvec + (int64_t)bh * N;
+
+  bf16x8 kf[C::KD], vf[C::KD];
+#pragma unroll
+  for (int kk = 0; kk < C::KD; ++kk) {
+    u32x4 a = {0u, 0u, 0u, 0u}, v = {0u, 0u, 0u, 0u};
+    if (key_ok) {
+      const int64_t off = (int64_t)key * D + 16 * kk + 8 * h;
+      a = *(const u32x4*)(kg + off);
+      v = *(const u32x4*)(vg + off);
+    }
+    kf[kk] = __builtin_bit_cast(bf16x8, a);
+    vf[kk] = __builtin_bit_cast(bf16x8, v);
+  }
+
+  f32x16 dk[C::ND], dv[C::ND];
+#pragma unroll
+  for (int i = 0; i < C::ND; ++i) {
+    dk[i] = f32x16{};
+    dv[i] = f32x16{};
+  }
+
+  // Query tiles that see any key of this workgroup: rows >= k0 if causal,
+  // below the sequence length.
+  const int qfirst = (k0 < L) ? (CAUSAL ? (k0 / BQ) : 0) : 0;
+  const int qend = (k0 < L) ? (L + BQ - 1) / BQ : 0;
+
+  u32x4 qst[LPT], dst[LPT];
+  float aux = 0.f;  // LSE2 (threads 0..BQ-1) or D (threads BQ..2BQ-1) of one row
+  auto load_regs = [&](int q0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < LPT; ++i) {
+      const int c = tid + 256 * i, r = c / C::CPR, lc = c % C::CPR;
+      const int qr = q0 + r;
+      u32x4 a = {0u, 0u, 0u, 0u}, d = {0u, 0u, 0u, 0u};
+      if (qr < L) {
+        a = *(const u32x4*)(qg + (int64_t)qr * D + 8 * lc);
+        d = *(const u32x4*)(dog + (int64_t)qr * D + 8 * lc);
+      }
+      qst[i] = a;
+      dst[i] = d;
+    }
+    if (tid < 2 * BQ) {
+      const int qr = q0 + (tid % BQ);
+      aux = 0.f;
+      if (qr < L) aux = tid < BQ ? lseg[qr] * kLog2e : dvg[qr];
+    }
+  };
+  auto store_lds = [&](int st) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < LPT; ++i) {
+      const int c = tid + 256 * i, r = c / C::CPR, lc = c % C::CPR;
+      *(u32x4*)(&lds[st][toff_t<D>(r, lc)]) = qst[i];
+      *(u32x4*)(&lds[st][TILE + toff_t<D>(r, lc)]) = dst[i];
+    }
+    if (tid < 2 * BQ) *(float*)(&lds[st][2 * TILE + 4 * tid]) = aux;
+  };
+
+  auto compute = [&](int st, int q0) __attribute__((always_inline)) {
+    // rows all before the wave's first key, or the wave's keys all padding
+    if ((CAUSAL && q0 + BQ - 1 < kw0) || kw0 >= L) return;
+    const uint8_t* qt = lds[st];
+    const uint8_t* dt = lds[st] + TILE;
+    const float* lse2 = (const float*)(lds[st] + 2 * TILE);
+    const float* dd = lse2 + BQ;
+    bf16x8 pb[NQB][2], dsb[NQB][2];
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+      f32x16 s = f32x16{}, dp = f32x16{};
+      const int qr = 32 * qb + l32;
+#pragma unroll
+      for (int kk = 0; kk < C::KD; ++kk) {
+        s = mfma_32x32x16_bf16(lds_b128(qt, toff_t<D>(qr, 2 * kk + h)), kf[kk], s);
+        dp = mfma_32x32x16_bf16(lds_b128(dt, toff_t<D>(qr, 2 * kk + h)), vf[kk], dp);
+      }
+      // lane = key, register r = row 32qb + acc_row(r, h)
+      float pr[16], ds[16];
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int r0 = 32 * qb + 8 * q4 + 4 * h;  // four consecutive rows
+        const f32x4 l4 = *(const f32x4*)(lse2 + r0);
+        const f32x4 d4 = *(const f32x4*)(dd + r0);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int r = 4 * q4 + t;
+          const int qrow = q0 + r0 + t;
+          const bool vis = key_ok && qrow < L && (!CAUSAL || key <= qrow);
+          pr[r] = vis ? fast_exp2(__builtin_fmaf(s[r], p.c2, -l4[t])) : 0.f;
+          ds[r] = pr[r] * (dp[r] - d4[t]);
+        }
+      }
+      pb[qb][0] = pack8(pr);
+      pb[qb][1] = pack8(pr + 8);
+      dsb[qb][0] = pack8(ds);
+      dsb[qb][1] = pack8(ds + 8);
+    }
+    // dV^T += dO^T P, dK^T += Q^T dS
+#pragma unroll
+    for (int db = 0; db < C::ND; ++db)
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+          dv[db] = mfma_32x32x16_bf16(tr_operand<D>(dt, 32 * qb + 16 * m, db, lane), pb[qb][m], dv[db]);
+          dk[db] = mfma_32x32x16_bf16(tr_operand<D>(qt, 32 * qb + 16 * m, db, lane), dsb[qb][m], dk[db]);
+        }
+  };
+
+  if (qend > qfirst) {
+    load_regs(qfirst * BQ);
+    store_lds(0);
+    __syncthreads();
+    for (int t = qfirst; t < qend; ++t) {
+      const bool more = t + 1 < qend;
+      if (more) load_regs((t + 1) * BQ);
+      compute((t - qfirst) & 1, t * BQ);
+      if (more) store_lds((t + 1 - qfirst) & 1);
+      __syncthreads();
+    }
+  }
+
+  // dK = scale * (dK^T)^T, dV = (dV^T)^T: lane = key, register r of slice db = dim
+  if (key < N) {
+    uint16_t* dkg = (uint16_t*)p.dk + base + (int64_t)key * D;
+    uint16_t* dvg2 = (uint16_t*)p.dv + base + (int64_t)key * D;
+#pragma unroll
+    for (int db = 0; db < C::ND; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = 32 * db + 8 * g + 4 * h;
+        const f32x16& a = dk[db];
+        const f32x16& v = dv[db];
+        u32x2 wk = {pack_bf16x2(p.scale * a[4 * g], p.scale * a[4 * g + 1]),
+                    pack_bf16x2(p.scale * a[4 * g + 2], p.scale * a[4 * g + 3])};
+        u32x2 wv = {pack_bf16x2(v[4 * g], v[4 * g + 1]), pack_bf16x2(v[4 * g + 2], v[4 * g + 3])};
+        *(u32x2*)(dkg + d0) = wk;
+        *(u32x2*)(dvg2 + d0) = wv;
+      }
+  }
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_bwd(const BwdParams& p, hipStream_t stream) {
+  const int BH = p.B * p.H;
+  hipLaunchKernelGGL((fa_bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)((int64_t)p.n_qtiles * BH)),
+                     dim3(256), 0, stream, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)((int64_t)p.n_ktiles * BH)),
+                     dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_bwd_bf16(const BwdParams& p, int d, bool causal, hipStream_t stream) {
+  if (d != 64) return hipErrorInvalidValue;
+  return causal ? launch_bwd<64, true>(p, stream) : launch_bwd<64, false>(p, stream);
+}
+
+}  // namespace fa

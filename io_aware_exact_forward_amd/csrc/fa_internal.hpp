@@ -47,6 +47,26 @@ struct NaiveSoftmaxParams {
   int causal;
 };
 
+// Everything the two backward kernels need.
+struct BwdParams {
+  const void* q;           // [B, H, N, d] bf16
+  const void* k;
+  const void* v;
+  const void* o;           // forward output
+  const void* dout;        // upstream gradient dO
+  const float* lse;        // [B, H, N] forward log-sum-exp (natural log)
+  void* dq;                // [B, H, N, d] bf16 outputs
+  void* dk;
+  void* dv;
+  float* dvec;             // [B, H, N] workspace: D_i = dO_i . O_i
+  const int32_t* key_len;  // device [B] or nullptr
+  int B, H, N;
+  int n_qtiles;            // ceil(N / 128): workgroups per (b, h) of the dQ kernel
+  int n_ktiles;            // ceil(N / 128): workgroups per (b, h) of the dK/dV kernel
+  float scale;             // signed
+  float c2;                // scale * log2(e), signed
+};
+
 // Query rows per workgroup of the fused kernels.
 constexpr int kQueryTile = 128;
 
@@ -54,5 +74,6 @@ hipError_t launch_fwd_bf16(const FwdParams& p, int d, bool causal, hipStream_t s
 hipError_t launch_fwd_f32(const FwdParams& p, int d, bool causal, hipStream_t stream);
 hipError_t launch_naive_softmax(const NaiveSoftmaxParams& p, bool bf16, hipStream_t stream);
 hipError_t launch_merge(const MergeParams& p, int d, bool bf16, hipStream_t stream);
+hipError_t launch_bwd_bf16(const BwdParams& p, int d, bool causal, hipStream_t stream);
 
 }  // namespace fa

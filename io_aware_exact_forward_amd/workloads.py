@@ -40,6 +40,7 @@ __all__ = [
     "DecodeWorkload",
     "DECODE_WORKLOADS",
     "Inputs",
+    "grad_inputs",
 ]
 
 
@@ -244,6 +245,24 @@ def decode_inputs(wl: DecodeWorkload, *, B=None, H=None, Nk=None, seed=None) -> 
     kl = rng.integers(1, Nk, size=B, endpoint=True, dtype=np.int64).astype(np.int32)
     sq = Workload(wl.name, B, H, Nk, d, "bf16", True, wl.scale, seed, ragged=True)
     return Inputs(sq, q, k, v, kl, None)
+
+
+def grad_inputs(B, H, N, d, seed, *, q_mult=1.0, key_len=None):
+    """Inputs of a backward pass (same recipe, bf16): Q, K, V, then the
+    upstream gradient dO, each [B, H, N, d] standard normal.  Returns the
+    Inputs of Q, K, V and the bf16 bits of dO."""
+    rng = np.random.default_rng(seed)
+    shape = (B, H, N, d)
+    q = rng.standard_normal(shape, dtype=np.float32)
+    k = rng.standard_normal(shape, dtype=np.float32)
+    v = rng.standard_normal(shape, dtype=np.float32)
+    do = rng.standard_normal(shape, dtype=np.float32)
+    if q_mult != 1.0:
+        q *= np.float32(q_mult)
+    kl = None if key_len is None else np.asarray(key_len, dtype=np.int32)
+    wl = Workload(f"grad_b{B}_h{H}_n{N}_d{d}_bf16", B, H, N, d, "bf16", False,
+                  1.0 / math.sqrt(d), seed, q_mult=q_mult)
+    return Inputs(wl, bf16_encode(q), bf16_encode(k), bf16_encode(v), kl, None), bf16_encode(do)
 
 
 def valid_pairs(N: int, causal: bool, key_len=None, B: int = 1) -> int:

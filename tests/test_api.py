@@ -33,7 +33,8 @@ def declared_functions():
 def test_header_declares_expected_entry_points():
     assert declared_functions() == sorted(
         ["fa_forward", "fa_naive_workspace_bytes", "fa_naive_forward", "fa_split_workspace_bytes",
-         "fa_forward_split", "fa_status_string", "fa_abi_version"])
+         "fa_forward_split", "fa_backward_workspace_bytes", "fa_backward", "fa_status_string",
+         "fa_abi_version"])
 
 
 def test_library_loads_and_exports_every_declared_symbol():
@@ -41,7 +42,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     for name in declared_functions():
         assert hasattr(lib, name), name
     assert set(_lib.exported_symbols()) == set(declared_functions())
-    assert fa.fa_abi_version() == (1 << 16) | 1
+    assert fa.fa_abi_version() == (1 << 16) | 2
 
 
 def test_status_strings():
@@ -214,3 +215,48 @@ def test_python_split_wrapper_rejects_bad_tensors():
     y = torch.zeros(1, 2, 4, 64, dtype=torch.bfloat16)
     with pytest.raises(fa.FAError):
         fa.forward_split(x, y, y)   # heads differ
+
+
+# ---- backward entry point -------------------------------------------------------
+
+DQ, DK, DV, DO, OO = (A + (7 + i) * (1 << 34) for i in range(5))
+
+
+def bwd_call(q=Q, k=K, v=V, o=OO, lse=L, do=DO, dq=DQ, dk=DK, dv=DV, B=1, H=2, N=64, d=64,
+             scale=0.125, causal=0, kl=0, dtype=BF16, ws=WS, wsb=1 << 20, stream=0):
+    return fa.fa_backward(q, k, v, o, lse, do, dq, dk, dv, B, H, N, d, scale, causal, kl, dtype,
+                          ws, wsb, stream)
+
+
+def test_backward_workspace_size():
+    # fp32 D per row, rounded up to 256 bytes
+    assert fa.fa_backward_workspace_bytes(2, 16, 4096, 64, BF16) == 2 * 16 * 4096 * 4
+    assert fa.fa_backward_workspace_bytes(1, 1, 3, 64, BF16) == 256
+    assert fa.fa_backward_workspace_bytes(1, 1, 3, 64, F32) == 0
+    assert fa.fa_backward_workspace_bytes(1, 1, 3, 128, BF16) == 0
+    assert fa.fa_backward_workspace_bytes(0, 1, 3, 64, BF16) == 0
+
+
+def test_backward_bad_arguments():
+    assert bwd_call(dtype=F32) == DTYPE
+    assert bwd_call(d=128) == HEAD_DIM
+    assert bwd_call(N=-1) == SHAPE
+    assert bwd_call(scale=float("nan")) == SCALE
+    for field in ("q", "k", "v", "o", "lse", "do", "dq", "dk", "dv"):
+        assert bwd_call(**{field: 0}) == NULL, field
+    for field, val in (("q", Q + 8), ("dk", DK + 8), ("do", DO + 2), ("lse", L + 2)):
+        assert bwd_call(**{field: val}) == ALIGN, field
+    assert bwd_call(ws=0) == WORKSPACE
+    assert bwd_call(wsb=64) == WORKSPACE
+    assert bwd_call(ws=WS + 16) == WORKSPACE
+    assert bwd_call(dq=Q) == ALIAS
+    assert bwd_call(dk=DQ + 64) == ALIAS
+    assert bwd_call(dv=OO) == ALIAS
+    assert bwd_call(ws=DO) == ALIAS
+    assert bwd_call(ws=DV) == ALIAS
+
+
+def test_backward_empty_is_a_no_op():
+    for B, H, N in ((0, 2, 64), (1, 0, 64), (1, 2, 0)):
+        assert bwd_call(q=0, k=0, v=0, o=0, lse=0, do=0, dq=0, dk=0, dv=0, ws=0, wsb=0,
+                        B=B, H=H, N=N) == OK

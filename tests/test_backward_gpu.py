@@ -1,0 +1,140 @@
+"""GPU parity of the backward (fa_backward) against the fp64 gradient oracle.
+
+Each case runs the HIP forward (fa_forward) for O and LSE, then the HIP
+backward, and compares dQ, dK and dV element by element with
+oracle.attention_backward on the same exact bf16 inputs.
+
+Tolerance, per gradient tensor G (relative to the tensor's own scale, since
+gradient magnitudes differ between dQ, dK and dV): max |G - G_ref| <= 2e-2 *
+max |G_ref| and mean |G - G_ref| <= 1.5e-2 * mean |G_ref|.  The kernel's
+roundings: the results are stored in bf16 (up to 2^-8 relative per element,
+about 2e-3 of the mean magnitude on average, which dominates the measured
+mean errors of 2-4e-3 once rows have tens of keys); P and dS enter their
+products as bf16 (2^-9 relative per term), and D is formed from the bf16
+forward output, so it is off by up to 2^-8 * sum_d |dO_d O_d|.  The last two
+are relative to the terms of a row, not to its sum: each row of dS sums to
+zero, so when a row has very few keys dQ and dK are differences of nearly
+equal terms, and with two keys the dS rounding (~2^-9 of each term, ~4e-3 of
+the difference) and the D error (~4e-3) add to the output rounding: ~1e-2 of
+the mean magnitude, which the bound covers with 50 % margin.  Padding rows
+and keys past a sequence's length must have exactly zero gradients.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from io_aware_exact_forward_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+TOL_MAX, TOL_MEAN = 2e-2, 1.5e-2
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def dev(a):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to("cuda:0")
+
+
+def host(t):
+    import torch
+    return W.bf16_decode(t.view(torch.int16).cpu().numpy().view(np.uint16), np.float64)
+
+
+def run(inp, do_bits, causal, scale):
+    import torch
+    import io_aware_exact_forward_amd as fa
+    q, k, v, do = dev(inp.q), dev(inp.k), dev(inp.v), dev(do_bits)
+    kl = None if inp.key_len is None else torch.from_numpy(inp.key_len).to("cuda:0")
+    o, lse = fa.forward(q, k, v, scale=scale, causal=causal, key_len=kl)
+    dq, dk, dv = fa.backward(q, k, v, o, lse, do, scale=scale, causal=causal, key_len=kl)
+    torch.cuda.synchronize()
+    return host(dq), host(dk), host(dv)
+
+
+def check(inp, do_bits, causal, scale, got, label, heads=None):
+    qx, kx, vx = inp.exact("q"), inp.exact("k"), inp.exact("v")
+    dox = W.bf16_decode(do_bits, np.float64)
+    if heads is not None:
+        qx, kx, vx, dox = (x[:, heads] for x in (qx, kx, vx, dox))
+        got = tuple(g[:, heads] for g in got)
+    ref = oracle.attention_backward(qx, kx, vx, dox, scale, causal=causal, key_len=inp.key_len)[:3]
+    stats = {"label": label}
+    for name, g, r in zip(("dq", "dk", "dv"), got, ref):
+        assert np.all(np.isfinite(g)), f"{label} {name}: non-finite"
+        err = np.abs(g - r)
+        scale_max, scale_mean = float(np.abs(r).max()), float(np.abs(r).mean())
+        stats[name] = (float(err.max()) / max(scale_max, 1e-30), float(err.mean()) / max(scale_mean, 1e-30))
+        if scale_max > 0:
+            assert err.max() <= TOL_MAX * scale_max, f"{label} {name}: max err {err.max():.3g} vs {scale_max:.3g}"
+            assert err.mean() <= TOL_MEAN * scale_mean, f"{label} {name}: mean err {err.mean():.3g} vs {scale_mean:.3g}"
+        else:
+            assert np.all(g == 0), f"{label} {name}: expected zeros"
+    # exact zeros where no pair is visible
+    if inp.key_len is not None:
+        N = qx.shape[2]
+        for b, L in enumerate(np.clip(inp.key_len, 0, N)):
+            for g in got:
+                assert np.all(g[b, :, L:] == 0.0), f"{label}: nonzero gradient past the length"
+    say(stats)
+    return stats
+
+
+CASES = [
+    # (B, H, N, key_len, q_mult, seed)
+    (1, 2, 300, None, 1.0, 9301),
+    (2, 2, 1000, [1000, 437], 1.0, 9302),
+    (1, 3, 129, None, 1.0, 9303),
+    (2, 1, 64, [64, 1], 1.0, 9304),
+    (1, 2, 513, None, 4.0, 9305),      # peaky rows
+    (3, 1, 200, [0, 17, 200], 1.0, 9306),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: f"b{c[0]}h{c[1]}n{c[2]}")
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_against_oracle(case, causal):
+    B, H, N, key_len, q_mult, seed = case
+    say("case", case, "causal", causal)
+    inp, do = W.grad_inputs(B, H, N, 64, seed, q_mult=q_mult, key_len=key_len)
+    got = run(inp, do, causal, 0.125)
+    check(inp, do, causal, 0.125, got, f"{case} causal={causal}")
+
+
+@pytest.mark.parametrize("N", [1, 2, 17, 64, 65, 127, 128, 129, 255])
+def test_backward_edge_sizes(N):
+    for causal in (False, True):
+        inp, do = W.grad_inputs(1, 2, N, 64, 9400 + N)
+        got = run(inp, do, causal, 0.125)
+        check(inp, do, causal, 0.125, got, f"N={N} causal={causal}")
+
+
+def test_backward_negative_and_zero_scale():
+    inp, do = W.grad_inputs(1, 2, 190, 64, 9501)
+    for scale in (-0.1, 0.0):
+        for causal in (False, True):
+            got = run(inp, do, causal, scale)
+            check(inp, do, causal, scale, got, f"scale={scale} causal={causal}")
+
+
+def test_backward_is_deterministic():
+    import torch
+    inp, do = W.grad_inputs(2, 4, 777, 64, 9502)
+    a = run(inp, do, True, 0.125)
+    b = run(inp, do, True, 0.125)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_full_size_sampled_heads(causal):
+    """The pages' backward workload at its largest length (batch 2, 16 heads,
+    d = 64, N = 4096): every element of three heads against the oracle."""
+    inp, do = W.grad_inputs(2, 16, 4096, 64, 9600)
+    say("full size", causal)
+    got = run(inp, do, causal, 0.125)
+    check(inp, do, causal, 0.125, got, f"b2h16n4096 causal={causal}", heads=[0, 9, 15])
