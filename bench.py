@@ -5,7 +5,8 @@
 
 With --workload decode_b8_h32_k16384_d128_bf16 a step is instead one
 fa_forward_split call (a decode step: one query row per sequence and head),
-and the roofline is HBM bandwidth.
+and the roofline is HBM bandwidth.  With --workload bwd_b2_h16_n4096_d64_bf16
+a step is one fa_backward call (gradients of all heads).
 
 A step is one fa_forward call over the whole workload (every batch, head and
 query row), with Q, K, V already resident in device memory.  Default
@@ -37,19 +38,25 @@ PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA, 2.4 GHz
 PEAK_F32_TFLOPS = 157.3     # MI355X fp32 matrix
 PEAK_HBM_GBS = 8000.0
 DEFAULT_WORKLOAD = "h32_n8192_d128_causal_bf16"
-KERNEL_SOURCES = ["fa_fwd_bf16.hip", "fa_fwd_f32.hip", "fa_merge.hip", "fa_bf16_tiles.hpp",
-                  "fa_device.hpp", "fa_internal.hpp"]
+# Sources of the kernels each kind of workload runs (their hash tags stored
+# counter readings, which are reported only for the source they were taken on).
+HEADERS = ["fa_bf16_tiles.hpp", "fa_device.hpp", "fa_internal.hpp"]
+KERNEL_SOURCES = {
+    "forward": ["fa_fwd_bf16.hip", "fa_fwd_f32.hip"] + HEADERS,
+    "split": ["fa_fwd_bf16.hip", "fa_merge.hip"] + HEADERS,
+    "backward": ["fa_bwd_bf16.hip"] + HEADERS,
+}
 
 
-def kernel_hash() -> str:
+def kernel_hash(kind: str = "forward") -> str:
     h = hashlib.sha256()
-    for name in KERNEL_SOURCES:
+    for name in KERNEL_SOURCES[kind]:
         with open(os.path.join(ROOT, "io_aware_exact_forward_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def stored_traffic(workload: str):
+def stored_traffic(workload: str, kind: str = "forward"):
     """HBM bytes per launch from the committed rocprofv3 counter summary,
     if it was taken on the current kernel source; else None."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
@@ -59,7 +66,7 @@ def stored_traffic(workload: str):
     except (OSError, ValueError):
         return None
     ent = rec.get(workload)
-    if not ent or ent.get("kernel_hash") != kernel_hash():
+    if not ent or ent.get("kernel_hash") != kernel_hash(kind):
         return None
     return ent.get("hbm_bytes_per_launch")
 
@@ -193,9 +200,9 @@ def bench_decode(args) -> int:
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": gbs / PEAK_HBM_GBS,
-            "traffic": stored_traffic(wl.name),
+            "traffic": stored_traffic(wl.name, "split"),
             "kernel": "fa_fwd_bf16_kernel + merge_kernel (one call; both inside the events)",
-            "kernel_hash": kernel_hash(),
+            "kernel_hash": kernel_hash("split"),
         },
         "wall_s_timed_region": t_wall,
     }
@@ -230,6 +237,150 @@ def bench_decode(args) -> int:
     return 0
 
 
+def bench_backward(args) -> int:
+    """Backward: one fa_backward call (the dQ and the dK/dV kernels) over the
+    whole workload, with Q, K, V, O, LSE and dO resident.  Useful work is
+    10*d flops per visible pair (the five products of the gradient: S, dV,
+    dP, dQ, dK); the kernels also recompute S and dP once more."""
+    import numpy as np
+    import torch
+
+    import io_aware_exact_forward_amd as fa
+    import oracle
+    from io_aware_exact_forward_amd import workloads as W
+
+    wl = W.BWD_WORKLOADS[args.workload]
+    B, H, N, d = wl.B, wl.H, wl.N, wl.d
+    if args.n:
+        N = args.n
+    inp, do_bits = W.grad_inputs(B, H, N, d, wl.seed)
+    dev = torch.device("cuda:0")
+    q, k, v, _ = to_device(inp, dev)
+    dout = torch.from_numpy(np.ascontiguousarray(do_bits).view(np.int16)).view(torch.bfloat16).to(dev)
+    o, lse = fa.forward(q, k, v, scale=wl.scale, causal=wl.causal)
+    ws = torch.empty(fa.fa_backward_workspace_bytes(B, H, N, d, fa.FA_DTYPE_BF16), dtype=torch.uint8,
+                     device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    pairs = W.valid_pairs(N, wl.causal, None, B) * H
+    flops = 10.0 * d * pairs
+
+    def step():
+        fa.backward(q, k, v, o, lse, dout, scale=wl.scale, causal=wl.causal, workspace=ws,
+                    dq=dq, dk=dk, dv=dv)
+
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    t_wall = time.perf_counter()
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms = start.elapsed_time(end) / args.steps
+    tflops = flops / (ms * 1e-3) / 1e12
+    result = {
+        "metric": "attention bwd TFLOP/s (bf16, 1 GPU; useful 10*d flops per visible pair)",
+        "value": tflops,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": dict(wl.describe(), N=N, useful_flops=flops,
+                       workspace_bytes=ws.numel(), parallelism="single GPU"),
+        "roofline": {
+            "bound": "mfma",
+            "achieved": tflops,
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": tflops / PEAK_BF16_TFLOPS,
+            "traffic": stored_traffic(wl.name, "backward") if N == wl.N else None,
+            "kernel": "fa_bwd_dq_kernel + fa_bwd_dkdv_kernel (one call; both inside the events)",
+            "kernel_hash": kernel_hash("backward"),
+        },
+        "wall_s_timed_region": t_wall,
+    }
+    # Stored-state comparison (the N x N matrices in HBM): latency and peak
+    # allocated memory of both paths, each measured from the same resident
+    # inputs and outputs.
+    if not args.no_naive:
+        def peak_of(fn, ws_bytes):
+            torch.cuda.synchronize()
+            torch.cuda.reset_peak_memory_stats(dev)
+            base = torch.cuda.memory_allocated(dev)
+            w = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+            fn(w)
+            torch.cuda.synchronize()
+            s0 = torch.cuda.Event(enable_timing=True)
+            s1 = torch.cuda.Event(enable_timing=True)
+            s0.record(stream)
+            for _ in range(args.steps):
+                fn(w)
+            s1.record(stream)
+            torch.cuda.synchronize()
+            peak = torch.cuda.max_memory_allocated(dev) - base
+            del w
+            torch.cuda.empty_cache()
+            return s0.elapsed_time(s1) / args.steps, peak
+        fused_ms, fused_peak = peak_of(
+            lambda w: fa.backward(q, k, v, o, lse, dout, scale=wl.scale, causal=wl.causal,
+                                  workspace=w, dq=dq, dk=dk, dv=dv), ws.numel())
+        need = fa.fa_naive_workspace_bytes(B, H, N, fa.FA_DTYPE_BF16)
+        if need < 0.8 * torch.cuda.mem_get_info(dev)[0]:
+            naive_ms, naive_peak = peak_of(
+                lambda w: fa.naive_backward(q, k, v, o, lse, dout, scale=wl.scale,
+                                            causal=wl.causal, workspace=w, dq=dq, dk=dk, dv=dv),
+                need)
+            resident = sum(t.numel() * t.element_size() for t in (q, k, v, o, lse, dout, dq, dk, dv))
+            result["stored_state_comparison"] = {
+                "recompute_ms": fused_ms, "stored_state_ms": naive_ms,
+                "speedup_of_recompute": naive_ms / fused_ms,
+                "resident_tensor_bytes": resident,
+                "recompute_extra_peak_bytes": fused_peak, "stored_state_extra_peak_bytes": naive_peak,
+                "note": "extra peak = allocation peak above the resident inputs and outputs "
+                        "(the workspace: D per row, vs S/P and dP/dS matrices)",
+            }
+    if not args.no_cpu_baseline:
+        qx, kx, vx = inp.exact("q"), inp.exact("k"), inp.exact("v")
+        dox = W.bf16_decode(do_bits, np.float64)
+        t0, done = time.perf_counter(), 0
+        for b in range(B):
+            for h in range(H):
+                oracle.attention_backward(qx[b:b + 1, h:h + 1], kx[b:b + 1, h:h + 1],
+                                          vx[b:b + 1, h:h + 1], dox[b:b + 1, h:h + 1], wl.scale,
+                                          causal=wl.causal)
+                done += 1
+                if time.perf_counter() - t0 > args.cpu_seconds:
+                    break
+            if time.perf_counter() - t0 > args.cpu_seconds:
+                break
+        dt = time.perf_counter() - t0
+        try:
+            from threadpoolctl import threadpool_info
+            threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        except Exception:
+            threads = len(os.sched_getaffinity(0))
+        result["cpu_baseline"] = {
+            "value": flops / (B * H) * done / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{done} of {B * H} (batch, head) slices, fp64 numpy gradients with P "
+                      f"materialised; {dt:.1f} s",
+            "seconds": dt,
+        }
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -238,8 +389,11 @@ def main() -> int:
     # the default warm-up covers that so the timed steps see steady state
     ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD,
-                    help="a square workload name, or decode_b8_h32_k16384_d128_bf16 (one query "
-                         "row per sequence and head against its key cache, split over key ranges)")
+                    help="a square workload name, decode_b8_h32_k16384_d128_bf16 (one query "
+                         "row per sequence and head against its key cache, split over key ranges) "
+                         "or bwd_b2_h16_n4096_d64_bf16 (the backward pass)")
+    ap.add_argument("--n", type=int, default=0,
+                    help="backward workload only: another sequence length (512 .. 4096)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-naive", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -280,6 +434,8 @@ def main() -> int:
 
     if args.workload in W.DECODE_WORKLOADS:
         return bench_decode(args)
+    if args.workload in W.BWD_WORKLOADS:
+        return bench_backward(args)
     wl = W.workload(args.workload)
     inp = W.make_inputs(wl)
     dev = torch.device("cuda:0")

@@ -198,6 +198,23 @@ int fa_backward(const void* q, const void* k, const void* v, const void* o, cons
                 float scale, int causal, const int32_t* key_len_mask, int dtype,
                 void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Stored-state backward: the same gradients as fa_backward, computed the
+ * conventional way with the N x N matrices in HBM (S and then P in the first
+ * half of the workspace, dP and then dS in the second), by five rocBLAS
+ * products and two row passes -- the comparison path of "IO-aware exact
+ * attention" (section "Measure stored-state and recomputed attention
+ * backward").  P and dS are stored in bf16, so results are slightly less
+ * accurate than fa_backward's.  Arguments as fa_backward; dtype
+ * FA_DTYPE_BF16; d = 64 or 128; the workspace is fa_naive_workspace_bytes(B, H, N,
+ * dtype) bytes, 256-byte aligned (o is validated but not read: D is formed
+ * from the stored P and dP).
+ */
+int fa_naive_backward(const void* q, const void* k, const void* v, const void* o,
+                      const float* lse, const void* dout, void* dq, void* dk, void* dv, int B,
+                      int H, int N, int d, float scale, int causal, const int32_t* key_len_mask,
+                      int dtype, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* fa_status_string(int status);
 

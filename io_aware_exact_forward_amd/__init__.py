@@ -20,6 +20,7 @@ from ._lib import (  # noqa: F401
     fa_backward_workspace_bytes,
     fa_forward,
     fa_forward_split,
+    fa_naive_backward,
     fa_naive_forward,
     fa_naive_workspace_bytes,
     fa_split_workspace_bytes,
@@ -29,7 +30,7 @@ from ._lib import (  # noqa: F401
 
 __all__ = [
     "forward", "forward_split", "backward", "naive_forward", "fa_forward", "fa_forward_split",
-    "fa_backward", "fa_backward_workspace_bytes",
+    "fa_backward", "fa_backward_workspace_bytes", "fa_naive_backward", "naive_backward",
     "fa_split_workspace_bytes", "fa_naive_forward", "fa_naive_workspace_bytes",
     "fa_status_string", "fa_abi_version", "FAError", "FA_DTYPE_BF16", "FA_DTYPE_F32",
 ]
@@ -135,8 +136,16 @@ def forward_split(q, k, v, *, scale=None, causal=False, key_len=None, num_splits
     return out, lse
 
 
+def naive_backward(q, k, v, o, lse, dout, *, scale=None, causal=False, key_len=None,
+                   workspace=None, dq=None, dk=None, dv=None):
+    """The stored-state backward (fa_naive_backward): same gradients as
+    ``backward``, with the N x N matrices in the workspace."""
+    return backward(q, k, v, o, lse, dout, scale=scale, causal=causal, key_len=key_len,
+                    workspace=workspace, dq=dq, dk=dk, dv=dv, _naive=True)
+
+
 def backward(q, k, v, o, lse, dout, *, scale=None, causal=False, key_len=None, workspace=None,
-             dq=None, dk=None, dv=None):
+             dq=None, dk=None, dv=None, _naive=False):
     """dQ, dK, dV = fa_backward(...): gradients of sum(dout * O) for the forward
     result (o, lse) of the same q, k, v, scale, causal and key_len."""
     import torch
@@ -157,14 +166,16 @@ def backward(q, k, v, o, lse, dout, *, scale=None, causal=False, key_len=None, w
         kl = key_len.data_ptr()
     dt = _dtype_code(q)
     if workspace is None:
-        need = fa_backward_workspace_bytes(B, H, N, d, dt)
+        need = (fa_naive_workspace_bytes(B, H, N, dt) if _naive
+                else fa_backward_workspace_bytes(B, H, N, d, dt))
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
     stream = torch.cuda.current_stream(q.device).cuda_stream
-    check(fa_backward(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
-                      dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d,
-                      float(scale), int(bool(causal)), kl, dt, workspace.data_ptr(),
-                      workspace.numel(), stream))
+    fn = fa_naive_backward if _naive else fa_backward
+    check(fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+             dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d,
+             float(scale), int(bool(causal)), kl, dt, workspace.data_ptr(), workspace.numel(),
+             stream))
     return dq, dk, dv

@@ -46,6 +46,11 @@ _SIGNATURES = {
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
         ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float, ctypes.c_int,
         ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "fa_naive_backward": (ctypes.c_int, [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float, ctypes.c_int,
+        ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
     "fa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "fa_abi_version": (ctypes.c_int, []),
 }
@@ -134,6 +139,13 @@ def fa_backward(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, d, scale, causal, ke
     return load().fa_backward(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, d, scale, int(causal),
                               key_len_mask or None, dtype, workspace or None, workspace_bytes,
                               stream or None)
+
+
+def fa_naive_backward(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, d, scale, causal,
+                      key_len_mask, dtype, workspace, workspace_bytes, stream) -> int:
+    return load().fa_naive_backward(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, d, scale,
+                                    int(causal), key_len_mask or None, dtype, workspace or None,
+                                    workspace_bytes, stream or None)
 
 
 def fa_status_string(status) -> str:

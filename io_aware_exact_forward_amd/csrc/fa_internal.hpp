@@ -67,6 +67,16 @@ struct BwdParams {
   float c2;                // scale * log2(e), signed
 };
 
+// Row passes of the stored-state (materialised) backward.
+struct NaiveBwdParams {
+  void* sp;                // [B*H, N, N] bf16: S on entry, P after the first pass
+  void* dpds;              // [B*H, N, N] bf16: dP on entry, dS after the second pass
+  const float* lse;        // [B*H, N]
+  const int32_t* key_len;  // device [B] or nullptr
+  int B, H, N;
+  int causal;
+};
+
 // Query rows per workgroup of the fused kernels.
 constexpr int kQueryTile = 128;
 
@@ -75,5 +85,7 @@ hipError_t launch_fwd_f32(const FwdParams& p, int d, bool causal, hipStream_t st
 hipError_t launch_naive_softmax(const NaiveSoftmaxParams& p, bool bf16, hipStream_t stream);
 hipError_t launch_merge(const MergeParams& p, int d, bool bf16, hipStream_t stream);
 hipError_t launch_bwd_bf16(const BwdParams& p, int d, bool causal, hipStream_t stream);
+hipError_t launch_naive_bwd_p(const NaiveBwdParams& p, hipStream_t stream);
+hipError_t launch_naive_bwd_ds(const NaiveBwdParams& p, hipStream_t stream);
 
 }  // namespace fa

@@ -41,6 +41,7 @@ __all__ = [
     "DECODE_WORKLOADS",
     "Inputs",
     "grad_inputs",
+    "BWD_WORKLOADS",
 ]
 
 
@@ -245,6 +246,15 @@ def decode_inputs(wl: DecodeWorkload, *, B=None, H=None, Nk=None, seed=None) -> 
     kl = rng.integers(1, Nk, size=B, endpoint=True, dtype=np.int64).astype(np.int32)
     sq = Workload(wl.name, B, H, Nk, d, "bf16", True, wl.scale, seed, ragged=True)
     return Inputs(sq, q, k, v, kl, None)
+
+
+# The backward exercise of "IO-aware exact attention" (section "Measure
+# stored-state and recomputed attention backward"): batch 2, 16 heads,
+# d = 64, lengths 512 .. 4096; the named workload is its longest length.
+BWD_WORKLOADS = {
+    "bwd_b2_h16_n4096_d64_bf16": Workload(
+        "bwd_b2_h16_n4096_d64_bf16", 2, 16, 4096, 64, "bf16", False, 1.0 / 8.0, 1007),
+}
 
 
 def grad_inputs(B, H, N, d, seed, *, q_mult=1.0, key_len=None):

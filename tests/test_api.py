@@ -33,8 +33,8 @@ def declared_functions():
 def test_header_declares_expected_entry_points():
     assert declared_functions() == sorted(
         ["fa_forward", "fa_naive_workspace_bytes", "fa_naive_forward", "fa_split_workspace_bytes",
-         "fa_forward_split", "fa_backward_workspace_bytes", "fa_backward", "fa_status_string",
-         "fa_abi_version"])
+         "fa_forward_split", "fa_backward_workspace_bytes", "fa_backward", "fa_naive_backward",
+         "fa_status_string", "fa_abi_version"])
 
 
 def test_library_loads_and_exports_every_declared_symbol():
@@ -260,3 +260,22 @@ def test_backward_empty_is_a_no_op():
     for B, H, N in ((0, 2, 64), (1, 0, 64), (1, 2, 0)):
         assert bwd_call(q=0, k=0, v=0, o=0, lse=0, do=0, dq=0, dk=0, dv=0, ws=0, wsb=0,
                         B=B, H=H, N=N) == OK
+
+
+def test_naive_backward_bad_arguments():
+    def nb(**kw):
+        a = dict(q=Q, k=K, v=V, o=OO, lse=L, do=DO, dq=DQ, dk=DK, dv=DV, B=1, H=2, N=64, d=64,
+                 scale=0.125, causal=0, kl=0, dtype=BF16, ws=WS,
+                 wsb=fa.fa_naive_workspace_bytes(1, 2, 64, BF16), stream=0)
+        a.update(kw)
+        return fa.fa_naive_backward(a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"], a["dq"],
+                                    a["dk"], a["dv"], a["B"], a["H"], a["N"], a["d"], a["scale"],
+                                    a["causal"], a["kl"], a["dtype"], a["ws"], a["wsb"], a["stream"])
+    assert nb(dtype=F32) == DTYPE
+    assert nb(d=96) == HEAD_DIM
+    assert nb(dq=0) == NULL
+    assert nb(dk=DK + 4) == ALIGN
+    assert nb(ws=0) == WORKSPACE
+    assert nb(wsb=100) == WORKSPACE
+    assert nb(dv=K) == ALIAS
+    assert nb(B=0, q=0, k=0, v=0, o=0, lse=0, do=0, dq=0, dk=0, dv=0, ws=0, wsb=0) == OK
