@@ -12,5 +12,7 @@ from .attention import (  # noqa: F401
     finalize_summary,
     streamed_attention,
     split_attention,
+    expand_kv_heads,
+    varlen_attention,
 )
 from .backward import attention_backward  # noqa: F401

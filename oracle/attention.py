@@ -52,7 +52,10 @@ brute force with exact summation on tiny inputs, and agreement between the
 plain definition and the streamed recurrence.  The Nq != Nk reading is pinned
 by brute force with positions on tiny inputs, by the last Nq rows of the
 square problem (causal and padded) and by decode rows against scipy's
-softmax over the visible keys.  No function here is parity unpinned.
+softmax over the visible keys.  Grouped key/value heads are pinned by a
+closed form (value rows that name their head) and varlen batches by the
+padded problem with per-sequence lengths and by brute force with a key
+cache.  No function here is parity unpinned.
 """
 from __future__ import annotations
 
@@ -66,6 +69,8 @@ __all__ = [
     "finalize_summary",
     "streamed_attention",
     "split_attention",
+    "expand_kv_heads",
+    "varlen_attention",
 ]
 
 NEG_INF = -np.inf
@@ -312,4 +317,46 @@ def split_attention(q, k, v, scale, causal=False, key_len=None, split_keys=128,
                     part = block_summary(s_row[k0:k0 + split_keys], v[b, h, k0:k0 + split_keys])
                     acc = merge_summaries(acc, part)
                 o[b, h, i], lse[b, h, i] = finalize_summary(acc)
+    return o, lse
+
+
+# ---------------------------------------------------------------------------
+# Shared key/value heads and packed variable-length batches ("IO-aware exact
+# attention", section "Why implementations form a family": grouped heads and
+# variable-length packing change the data access, not the result)
+# ---------------------------------------------------------------------------
+
+def expand_kv_heads(x, H):
+    """[B, Hkv, N, d] -> [B, H, N, d]: query head h reads key/value head
+    h // (H / Hkv), i.e. each key/value head serves H / Hkv consecutive query
+    heads (grouped-query attention; Hkv = 1 is multi-query attention)."""
+    x = np.asarray(x, dtype=np.float64)
+    Hkv = x.shape[1]
+    if H % Hkv:
+        raise ValueError("H must be a multiple of the key/value heads")
+    return np.repeat(x, H // Hkv, axis=1)
+
+
+def varlen_attention(q, k, v, cu_q, cu_k, scale, causal=False):
+    """Packed batch: q [Tq, H, d], k and v [Tk, Hkv, d]; sequence b holds
+    query tokens cu_q[b] .. cu_q[b+1]-1 and keys cu_k[b] .. cu_k[b+1]-1.
+    Each sequence is attention on its own tokens with its query rows at the
+    end of its keys (end aligned, as ``attention``), heads grouped as
+    ``expand_kv_heads``.  Returns (o [Tq, H, dv], lse [Tq, H])."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    Tq, H, _ = q.shape
+    o = np.zeros((Tq, H, v.shape[-1]))
+    lse = np.full((Tq, H), NEG_INF)
+    for b in range(len(cu_q) - 1):
+        q0, q1, k0, k1 = int(cu_q[b]), int(cu_q[b + 1]), int(cu_k[b]), int(cu_k[b + 1])
+        if q1 == q0:
+            continue
+        qb = q[q0:q1].transpose(1, 0, 2)[None]
+        kb = expand_kv_heads(k[k0:k1].transpose(1, 0, 2)[None], H)
+        vb = expand_kv_heads(v[k0:k1].transpose(1, 0, 2)[None], H)
+        ob, lb = attention(qb, kb, vb, scale, causal=causal, end_aligned=True)
+        o[q0:q1] = ob[0].transpose(1, 0, 2)
+        lse[q0:q1] = lb[0].T
     return o, lse

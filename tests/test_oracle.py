@@ -630,3 +630,70 @@ def test_planted_mistakes_are_caught(mistake):
         raise AssertionError(mistake)
 
     assert _pin_suite(attn) != []
+
+
+# ---------------------------------------------------------------------------
+# Grouped key/value heads and packed variable-length batches
+# ---------------------------------------------------------------------------
+
+def test_grouped_heads_read_their_group():
+    """Value rows of key/value head g all equal g: every output row of query
+    head h is exactly h // (H / Hkv), and with equal K/V heads the result is
+    independent of the grouping."""
+    B, H, Hkv, N, d = 2, 8, 2, 11, 4
+    q = rand((B, H, N, d), 900)
+    k = rand((B, Hkv, N, d), 901)
+    v = np.broadcast_to(np.arange(Hkv, dtype=np.float64)[None, :, None, None], (B, Hkv, N, d))
+    o, _ = oracle.attention(q, oracle.expand_kv_heads(k, H), oracle.expand_kv_heads(v, H), 0.5)
+    for h in range(H):
+        assert np.allclose(o[:, h], h // (H // Hkv), atol=1e-14)
+    k1 = np.broadcast_to(k[:, :1], (B, Hkv, N, d))
+    v1 = rand((B, 1, N, d), 902)
+    a, _ = oracle.attention(q, oracle.expand_kv_heads(k1, H),
+                            oracle.expand_kv_heads(np.broadcast_to(v1, (B, Hkv, N, d)), H), 0.5)
+    b, _ = oracle.attention(q, oracle.expand_kv_heads(k1[:, :1], H), oracle.expand_kv_heads(v1, H), 0.5)
+    assert np.array_equal(a, b)
+    with pytest.raises(ValueError):
+        oracle.expand_kv_heads(k, 7)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_varlen_equals_padded_batch(causal):
+    """A packed batch with equal query and key lengths per sequence equals the
+    padded [B, H, N, d] problem with per-sequence lengths."""
+    H, Hkv, d = 4, 2, 6
+    lens = [5, 0, 1, 13, 7]
+    N = max(lens)
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    T = int(cu[-1])
+    q, k, v = rand((T, H, d), 910), rand((T, Hkv, d), 911), rand((T, Hkv, d), 912)
+    o, lse = oracle.varlen_attention(q, k, v, cu, cu, 0.4, causal)
+    B = len(lens)
+    qp = np.zeros((B, H, N, d)); kp = np.zeros((B, Hkv, N, d)); vp = np.zeros((B, Hkv, N, d))
+    for b, L in enumerate(lens):
+        qp[b, :, :L] = q[cu[b]:cu[b + 1]].transpose(1, 0, 2)
+        kp[b, :, :L] = k[cu[b]:cu[b + 1]].transpose(1, 0, 2)
+        vp[b, :, :L] = v[cu[b]:cu[b + 1]].transpose(1, 0, 2)
+    op, lp = oracle.attention(qp, oracle.expand_kv_heads(kp, H), oracle.expand_kv_heads(vp, H), 0.4,
+                              causal=causal, key_len=np.array(lens))
+    for b, L in enumerate(lens):
+        assert np.allclose(o[cu[b]:cu[b + 1]], op[b, :, :L].transpose(1, 0, 2), atol=1e-14)
+        assert np.allclose(lse[cu[b]:cu[b + 1]], lp[b, :, :L].T, atol=1e-14)
+
+
+def test_varlen_brute_force_with_cache():
+    """Query chunks shorter than their key sequences: brute force per
+    (sequence, head) with the end-aligned positions."""
+    H, Hkv, d = 2, 1, 3
+    lq, lk = [2, 3, 1], [5, 3, 4]
+    cq = np.concatenate([[0], np.cumsum(lq)])
+    ck = np.concatenate([[0], np.cumsum(lk)])
+    q, k, v = rand((cq[-1], H, d), 920), rand((ck[-1], Hkv, d), 921), rand((ck[-1], Hkv, d), 922)
+    for causal in (False, True):
+        o, lse = oracle.varlen_attention(q, k, v, cq, ck, 0.9, causal)
+        for b in range(3):
+            for h in range(H):
+                O, LSE = brute(q[cq[b]:cq[b + 1], h].tolist(), k[ck[b]:ck[b + 1], 0].tolist(),
+                               v[ck[b]:ck[b + 1], 0].tolist(), 0.9, causal, lk[b], end_aligned=True)
+                assert np.allclose(o[cq[b]:cq[b + 1], h], np.array(O), atol=1e-13)
+                assert np.allclose(lse[cq[b]:cq[b + 1], h], np.array(LSE), atol=1e-13)
