@@ -6,7 +6,9 @@
 With --workload decode_b8_h32_k16384_d128_bf16 a step is instead one
 fa_forward_split call (a decode step: one query row per sequence and head),
 and the roofline is HBM bandwidth.  With --workload bwd_b2_h16_n4096_d64_bf16
-a step is one fa_backward call (gradients of all heads).
+a step is one fa_backward call (gradients of all heads); with --workload
+varlen_b16_h32_hkv8_n8192_d128_bf16 one fa_forward_varlen call over a packed
+batch of 16 causal sequences with grouped key/value heads.
 
 A step is one fa_forward call over the whole workload (every batch, head and
 query row), with Q, K, V already resident in device memory.  Default
@@ -381,6 +383,89 @@ def bench_backward(args) -> int:
     return 0
 
 
+def bench_varlen(args) -> int:
+    """Packed variable-length causal batch with grouped key/value heads: one
+    fa_forward_varlen call over the whole batch.  Useful work 4*d flops per
+    visible pair, as for the square workloads."""
+    import numpy as np
+    import torch
+
+    import io_aware_exact_forward_amd as fa
+    import oracle
+    from io_aware_exact_forward_amd import workloads as W
+
+    wl = W.VARLEN_WORKLOADS[args.workload]
+    inp = W.varlen_inputs(wl)
+    lens = np.diff(inp.cu_q).astype(np.int64)
+    dev = torch.device("cuda:0")
+    conv = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+    q, k, v = conv(inp.q), conv(inp.k), conv(inp.v)
+    cq = torch.from_numpy(inp.cu_q).to(dev)
+    ck = torch.from_numpy(inp.cu_k).to(dev)
+    mx = int(lens.max())
+    out = torch.empty_like(q)
+    lse = torch.empty((q.shape[0], wl.H), dtype=torch.float32, device=dev)
+    flops = 4.0 * wl.d * wl.H * float(sum(L * (L + 1) // 2 for L in lens))
+
+    def step():
+        fa.forward_varlen(q, k, v, cq, ck, mx, mx, scale=wl.scale, causal=True, out=out, lse=lse)
+
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    t_wall = time.perf_counter()
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms = start.elapsed_time(end) / args.steps
+    tflops = flops / (ms * 1e-3) / 1e12
+    result = {
+        "metric": "attention fwd TFLOP/s (bf16, 1 GPU); packed variable-length batch",
+        "value": tflops, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": dict(wl.describe(), seq_lens=lens.tolist(), total_tokens=int(lens.sum()),
+                       useful_flops=flops, parallelism="single GPU"),
+        "roofline": {"bound": "mfma", "achieved": tflops, "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": tflops / PEAK_BF16_TFLOPS,
+                     "traffic": stored_traffic(wl.name), "kernel": "fa_fwd_bf16_kernel",
+                     "kernel_hash": kernel_hash()},
+        "wall_s_timed_region": t_wall,
+    }
+    if not args.no_cpu_baseline:
+        # the oracle on whole sequences, shortest first, within the time budget
+        qx, kx, vx = inp.exact("q"), inp.exact("k"), inp.exact("v")
+        t0, done, pairs = time.perf_counter(), 0, 0
+        for b in np.argsort(lens):
+            a0, a1 = int(inp.cu_q[b]), int(inp.cu_q[b + 1])
+            oracle.varlen_attention(qx[a0:a1], kx[a0:a1], vx[a0:a1], np.array([0, a1 - a0]),
+                                    np.array([0, a1 - a0]), wl.scale, True)
+            done += 1
+            pairs += (a1 - a0) * (a1 - a0 + 1) // 2
+            if time.perf_counter() - t0 > args.cpu_seconds:
+                break
+        dt = time.perf_counter() - t0
+        try:
+            from threadpoolctl import threadpool_info
+            threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        except Exception:
+            threads = len(os.sched_getaffinity(0))
+        result["cpu_baseline"] = {
+            "value": 4.0 * wl.d * wl.H * pairs / dt / 1e12, "unit": "TFLOP/s",
+            "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} of {wl.B} sequences (shortest first), all heads, fp64; {dt:.1f} s",
+            "seconds": dt,
+        }
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -391,7 +476,8 @@ def main() -> int:
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD,
                     help="a square workload name, decode_b8_h32_k16384_d128_bf16 (one query "
                          "row per sequence and head against its key cache, split over key ranges) "
-                         "or bwd_b2_h16_n4096_d64_bf16 (the backward pass)")
+                         "bwd_b2_h16_n4096_d64_bf16 (the backward pass) or "
+                         "varlen_b16_h32_hkv8_n8192_d128_bf16 (packed sequences, grouped heads)")
     ap.add_argument("--n", type=int, default=0,
                     help="backward workload only: another sequence length (512 .. 4096)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -436,6 +522,8 @@ def main() -> int:
         return bench_decode(args)
     if args.workload in W.BWD_WORKLOADS:
         return bench_backward(args)
+    if args.workload in W.VARLEN_WORKLOADS:
+        return bench_varlen(args)
     wl = W.workload(args.workload)
     inp = W.make_inputs(wl)
     dev = torch.device("cuda:0")

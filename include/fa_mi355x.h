@@ -136,7 +136,10 @@ int fa_naive_forward(const void* q, const void* k, const void* v, void* o, float
  * query rows against many keys (decode), or few (batch, head) pairs at long
  * Nk -- which "IO-aware exact attention" (section "Common errors") names as
  * needing a different schedule.
- *   q, o         [B, H, Nq, d] of `dtype`; k, v [B, H, Nk, d]; lse [B, H, Nq].
+ *   q, o         [B, H, Nq, d] of `dtype`; k, v [B, Hkv, Nk, d]; lse [B, H, Nq].
+ *   Hkv          key/value heads, >= 1, dividing H: query head h reads key/value
+ *                head h / (H / Hkv) (grouped-query attention; Hkv = H is plain
+ *                multi-head attention, Hkv = 1 multi-query attention).
  *   Positions    L_b = clamp(key_len_mask[b], 0, Nk), or Nk when key_len_mask
  *                is NULL: sequence b holds keys 0 .. L_b - 1 and its query
  *                rows are the last Nq positions of that sequence, row i at key
@@ -170,9 +173,39 @@ int fa_naive_forward(const void* q, const void* k, const void* v, void* o, float
  */
 size_t fa_split_workspace_bytes(int B, int H, int Nq, int Nk, int d, int num_splits);
 int fa_forward_split(const void* q, const void* k, const void* v, void* o, float* lse,
-                     int B, int H, int Nq, int Nk, int d, float scale, int causal,
+                     int B, int H, int Hkv, int Nq, int Nk, int d, float scale, int causal,
                      const int32_t* key_len_mask, int dtype, int num_splits,
                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Attention forward over a packed batch of variable-length sequences with
+ * grouped key/value heads ("IO-aware exact attention", section "Why
+ * implementations form a family": packing and grouped heads change the
+ * indexing, not the result).
+ *   q, o         [total_q, H, d] of `dtype`: sequence b owns query rows
+ *                cu_seqlens_q[b] .. cu_seqlens_q[b+1] - 1 (token-major, heads
+ *                interleaved); k, v [total_k, Hkv, d] likewise with cu_seqlens_k;
+ *                lse [total_q, H] fp32.
+ *   cu_seqlens_q, cu_seqlens_k  device int32 [B + 1], non-decreasing, starting
+ *                at 0 and ending at total_q / total_k.  The library cannot read
+ *                them on the host: offsets outside the tensors are the caller's
+ *                error (like any bad pointer).
+ *   max_seqlen_q, max_seqlen_k  at least every sequence's query / key count;
+ *                rows beyond max_seqlen_q are not computed.
+ *   Positions    each sequence's query rows are the last of its keys: row i of a
+ *                sequence with Lq queries and Lk keys sits at key position
+ *                i + Lk - Lq (with Lq = Lk, position i), as in fa_forward_split.
+ *   Mask         causal != 0 hides keys after the row's position; a row that
+ *                sees no key (Lk = 0, or position < 0) gets O = 0, LSE = -inf.
+ *   Hkv          key/value heads, dividing H, as in fa_forward_split.
+ *   dtype        FA_DTYPE_BF16 only; d = 64 or 128.
+ *   Sizes        one sequence's rows of q (and of k) at most 2^31 - 1 bytes.
+ * Enqueues one kernel on `stream`; allocates nothing.
+ */
+int fa_forward_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                      const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int B, int H,
+                      int Hkv, int total_q, int total_k, int max_seqlen_q, int max_seqlen_k,
+                      int d, float scale, int causal, int dtype, void* stream);
 
 /*
  * Attention backward by recomputation ("IO-aware exact attention", section
@@ -221,7 +254,7 @@ const char* fa_status_string(int status);
 /* ABI version of this header: (major << 16) | minor. */
 int fa_abi_version(void);
 
-#define FA_ABI_VERSION ((1 << 16) | 2)
+#define FA_ABI_VERSION ((1 << 16) | 3)
 
 #ifdef __cplusplus
 }

@@ -20,6 +20,7 @@ from ._lib import (  # noqa: F401
     fa_backward_workspace_bytes,
     fa_forward,
     fa_forward_split,
+    fa_forward_varlen,
     fa_naive_backward,
     fa_naive_forward,
     fa_naive_workspace_bytes,
@@ -31,6 +32,7 @@ from ._lib import (  # noqa: F401
 __all__ = [
     "forward", "forward_split", "backward", "naive_forward", "fa_forward", "fa_forward_split",
     "fa_backward", "fa_backward_workspace_bytes", "fa_naive_backward", "naive_backward",
+    "fa_forward_varlen", "forward_varlen",
     "fa_split_workspace_bytes", "fa_naive_forward", "fa_naive_workspace_bytes",
     "fa_status_string", "fa_abi_version", "FAError", "FA_DTYPE_BF16", "FA_DTYPE_F32",
 ]
@@ -103,17 +105,17 @@ def forward_split(q, k, v, *, scale=None, causal=False, key_len=None, num_splits
     (query row i at key position i + Nk - Nq), keys split into ranges that are
     merged by their log-sum-exp.  num_splits = 0 lets the library choose."""
     import torch
-    if q.dim() != 4 or k.dim() != 4 or k.shape != v.shape or q.shape[:2] != k.shape[:2] \
-            or q.shape[3] != k.shape[3]:
-        raise FAError(-2, f"q [B, H, Nq, d] and k, v [B, H, Nk, d] expected; got "
-                          f"{tuple(q.shape)}, {tuple(k.shape)}, {tuple(v.shape)}")
+    if q.dim() != 4 or k.dim() != 4 or k.shape != v.shape or q.shape[0] != k.shape[0] \
+            or q.shape[3] != k.shape[3] or k.shape[1] < 1 or q.shape[1] % k.shape[1]:
+        raise FAError(-2, f"q [B, H, Nq, d] and k, v [B, Hkv, Nk, d] (Hkv dividing H) expected; "
+                          f"got {tuple(q.shape)}, {tuple(k.shape)}, {tuple(v.shape)}")
     if not (q.dtype == k.dtype == v.dtype):
         raise FAError(-4, "q, k, v must share one dtype")
     for t in (q, k, v):
         if not t.is_cuda or not t.is_contiguous():
             raise FAError(-1, "q, k, v must be contiguous device tensors")
     B, H, Nq, d = q.shape
-    Nk = k.shape[2]
+    Hkv, Nk = k.shape[1], k.shape[2]
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     kl = 0
@@ -131,8 +133,8 @@ def forward_split(q, k, v, *, scale=None, causal=False, key_len=None, num_splits
     stream = torch.cuda.current_stream(q.device).cuda_stream
     ws, wsb = (0, 0) if workspace is None else (workspace.data_ptr(), workspace.numel())
     check(fa_forward_split(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-                           lse.data_ptr(), B, H, Nq, Nk, d, float(scale), int(bool(causal)), kl,
-                           _dtype_code(q), int(num_splits), ws, wsb, stream))
+                           lse.data_ptr(), B, H, Hkv, Nq, Nk, d, float(scale), int(bool(causal)),
+                           kl, _dtype_code(q), int(num_splits), ws, wsb, stream))
     return out, lse
 
 
@@ -179,3 +181,33 @@ def backward(q, k, v, o, lse, dout, *, scale=None, causal=False, key_len=None, w
              float(scale), int(bool(causal)), kl, dt, workspace.data_ptr(), workspace.numel(),
              stream))
     return dq, dk, dv
+
+
+def forward_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, *,
+                   scale=None, causal=False, out=None, lse=None):
+    """O, LSE = fa_forward_varlen(...): packed q [Tq, H, d], k, v [Tk, Hkv, d],
+    device int32 offsets [B + 1]; lse is [Tq, H]."""
+    import torch
+    if q.dim() != 3 or k.dim() != 3 or k.shape != v.shape or q.shape[2] != k.shape[2]:
+        raise FAError(-2, "q [Tq, H, d] and k, v [Tk, Hkv, d] expected")
+    for t in (q, k, v, cu_seqlens_q, cu_seqlens_k):
+        if not t.is_cuda or not t.is_contiguous():
+            raise FAError(-1, "all tensors must be contiguous device tensors")
+    if cu_seqlens_q.dtype != torch.int32 or cu_seqlens_k.dtype != torch.int32 or \
+            cu_seqlens_q.numel() != cu_seqlens_k.numel():
+        raise FAError(-2, "cu_seqlens_q and cu_seqlens_k must be int32 [B + 1]")
+    Tq, H, d = q.shape
+    Tk, Hkv = k.shape[0], k.shape[1]
+    B = cu_seqlens_q.numel() - 1
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((Tq, H), dtype=torch.float32, device=q.device)
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    check(fa_forward_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                            lse.data_ptr(), cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(), B, H,
+                            Hkv, Tq, Tk, int(max_seqlen_q), int(max_seqlen_k), d, float(scale),
+                            int(bool(causal)), _dtype_code(q), stream))
+    return out, lse

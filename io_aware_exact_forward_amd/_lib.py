@@ -36,9 +36,14 @@ _SIGNATURES = {
         ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int]),
     "fa_forward_split": (ctypes.c_int, [
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+        ctypes.c_float, ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+        ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "fa_forward_varlen": (ctypes.c_int, [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
         ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float,
-        ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
-        ctypes.c_size_t, ctypes.c_void_p]),
+        ctypes.c_int, ctypes.c_int, ctypes.c_void_p]),
     "fa_backward_workspace_bytes": (ctypes.c_size_t, [
         ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int]),
     "fa_backward": (ctypes.c_int, [
@@ -123,11 +128,19 @@ def fa_split_workspace_bytes(B, H, Nq, Nk, d, num_splits) -> int:
     return load().fa_split_workspace_bytes(B, H, Nq, Nk, d, num_splits)
 
 
-def fa_forward_split(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, key_len_mask, dtype,
+def fa_forward_split(q, k, v, o, lse, B, H, Hkv, Nq, Nk, d, scale, causal, key_len_mask, dtype,
                      num_splits, workspace, workspace_bytes, stream) -> int:
-    return load().fa_forward_split(q, k, v, o, lse, B, H, Nq, Nk, d, scale, int(causal),
-                                   key_len_mask or None, dtype, num_splits, workspace or None,
-                                   workspace_bytes, stream or None)
+    return load().fa_forward_split(q or None, k or None, v or None, o or None, lse or None, B, H,
+                                   Hkv, Nq, Nk, d, scale, int(causal), key_len_mask or None,
+                                   dtype, num_splits, workspace or None, workspace_bytes,
+                                   stream or None)
+
+
+def fa_forward_varlen(q, k, v, o, lse, cu_q, cu_k, B, H, Hkv, total_q, total_k, max_q, max_k, d,
+                      scale, causal, dtype, stream) -> int:
+    return load().fa_forward_varlen(q or None, k or None, v or None, o or None, lse or None,
+                                    cu_q or None, cu_k or None, B, H, Hkv, total_q, total_k,
+                                    max_q, max_k, d, scale, int(causal), dtype, stream or None)
 
 
 def fa_backward_workspace_bytes(B, H, N, d, dtype) -> int:

@@ -86,6 +86,9 @@ fa::FwdParams make_params(const void* q, const void* k, const void* v, void* o, 
   p.H = H;
   p.N = N;
   p.Nk = N;
+  p.Hkv = H;
+  p.cu_q = nullptr;
+  p.cu_k = nullptr;
   p.end_aligned = 0;
   p.n_qtiles = (N + fa::kQueryTile - 1) / fa::kQueryTile;
   p.splits = 1;
@@ -140,12 +143,13 @@ void plan_split(int B, int H, int Nq, int Nk, int num_splits, SplitShape* sp) {
   sp->split_keys = static_cast<int>(per * kSplitBlock);
 }
 
-int check_split_scalars(int B, int H, int Nq, int Nk, int d, float scale, int dtype,
+int check_split_scalars(int B, int H, int Hkv, int Nq, int Nk, int d, float scale, int dtype,
                         int num_splits, SplitShape* sp, bool* empty) {
   if (dtype != FA_DTYPE_BF16) return FA_ERR_DTYPE;
   if (d != 64 && d != 128) return FA_ERR_HEAD_DIM;
   if (B < 0 || H < 0 || Nq < 0 || Nk < 0 || num_splits < 0 || num_splits > kMaxSplits)
     return FA_ERR_SHAPE;
+  if (Hkv < 1 || (H > 0 && H % Hkv != 0)) return FA_ERR_SHAPE;
   if (!std::isfinite(scale)) return FA_ERR_SCALE;
   const double c = std::fabs(static_cast<double>(scale)) * 1.4426950408889634;
   if (!std::isfinite(static_cast<float>(c))) return FA_ERR_SCALE;
@@ -161,7 +165,7 @@ int check_split_scalars(int B, int H, int Nq, int Nk, int d, float scale, int dt
   if (qtiles * bh * sp->splits > INT_MAX) return FA_ERR_SHAPE;
   sp->bh = bh;
   sp->rows = bh * Nq;
-  sp->kv_elems = bh * Nk * d;
+  sp->kv_elems = int64_t(B) * Hkv * Nk * d;
   return FA_OK;
 }
 
@@ -279,19 +283,19 @@ extern "C" int fa_naive_forward(const void* q, const void* k, const void* v, voi
 extern "C" size_t fa_split_workspace_bytes(int B, int H, int Nq, int Nk, int d, int num_splits) {
   SplitShape sp;
   bool empty = false;
-  if (check_split_scalars(B, H, Nq, Nk, d, 1.f, FA_DTYPE_BF16, num_splits, &sp, &empty) != FA_OK ||
+  if (check_split_scalars(B, H, 1, Nq, Nk, d, 1.f, FA_DTYPE_BF16, num_splits, &sp, &empty) != FA_OK ||
       empty)
     return 0;
   return split_workspace(sp, d);
 }
 
 extern "C" int fa_forward_split(const void* q, const void* k, const void* v, void* o, float* lse,
-                                int B, int H, int Nq, int Nk, int d, float scale, int causal,
-                                const int32_t* key_len_mask, int dtype, int num_splits,
+                                int B, int H, int Hkv, int Nq, int Nk, int d, float scale,
+                                int causal, const int32_t* key_len_mask, int dtype, int num_splits,
                                 void* workspace, size_t workspace_bytes, void* stream) {
   SplitShape sp;
   bool empty = false;
-  int st = check_split_scalars(B, H, Nq, Nk, d, scale, dtype, num_splits, &sp, &empty);
+  int st = check_split_scalars(B, H, Hkv, Nq, Nk, d, scale, dtype, num_splits, &sp, &empty);
   if (st != FA_OK || empty) return st;
   // an empty cache (Nk = 0) is never read: k and v may then be NULL
   if (!q || !o || !lse || (Nk > 0 && (!k || !v))) return FA_ERR_NULL;
@@ -317,6 +321,7 @@ extern "C" int fa_forward_split(const void* q, const void* k, const void* v, voi
 
   fa::FwdParams p = make_params(q, k, v, o, lse, B, H, Nq, scale, key_len_mask, dtype);
   p.Nk = Nk;
+  p.Hkv = Hkv;
   p.end_aligned = 1;
   p.splits = sp.splits;
   p.split_keys = sp.split_keys;
@@ -492,6 +497,54 @@ extern "C" int fa_naive_backward(const void* q, const void* k, const void* v, co
   if (!gemm(NN, NN, d, N, N, scale, k, d, snd, dpm, N, snn, dq, d, snd)) return FA_ERR_HIP;
   if (!gemm(NN, TT, d, N, N, scale, q, d, snd, dpm, N, snn, dk, d, snd)) return FA_ERR_HIP;
   return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+extern "C" int fa_forward_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                                 const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int B,
+                                 int H, int Hkv, int total_q, int total_k, int max_seqlen_q,
+                                 int max_seqlen_k, int d, float scale, int causal, int dtype,
+                                 void* stream) {
+  if (dtype != FA_DTYPE_BF16) return FA_ERR_DTYPE;
+  if (d != 64 && d != 128) return FA_ERR_HEAD_DIM;
+  if (B < 0 || H < 0 || total_q < 0 || total_k < 0 || max_seqlen_q < 0 || max_seqlen_k < 0)
+    return FA_ERR_SHAPE;
+  if (Hkv < 1 || (H > 0 && H % Hkv != 0)) return FA_ERR_SHAPE;
+  if (!std::isfinite(scale)) return FA_ERR_SCALE;
+  const double c = std::fabs(static_cast<double>(scale)) * 1.4426950408889634;
+  if (!std::isfinite(static_cast<float>(c))) return FA_ERR_SCALE;
+  if (B == 0 || H == 0 || total_q == 0 || max_seqlen_q == 0) return FA_OK;
+  // offsets within one sequence are 32-bit in the kernel
+  if (int64_t(max_seqlen_q) * H * d * 2 > INT_MAX || int64_t(max_seqlen_k) * Hkv * d * 2 > INT_MAX)
+    return FA_ERR_SHAPE;
+  const int64_t qtiles = (int64_t(max_seqlen_q) + fa::kQueryTile - 1) / fa::kQueryTile;
+  if (int64_t(B) * H > INT_MAX || qtiles * B * H > INT_MAX) return FA_ERR_SHAPE;
+  if (!q || !o || !lse || !cu_seqlens_q || !cu_seqlens_k || (total_k > 0 && (!k || !v)))
+    return FA_ERR_NULL;
+  if (!is_aligned(q, 16) || !is_aligned(k, 16) || !is_aligned(v, 16) || !is_aligned(o, 16))
+    return FA_ERR_ALIGN;
+  if (!is_aligned(lse, 4) || !is_aligned(cu_seqlens_q, 4) || !is_aligned(cu_seqlens_k, 4))
+    return FA_ERR_ALIGN;
+  const int64_t nq = int64_t(total_q) * H * d * 2, nkv = int64_t(total_k) * Hkv * d * 2;
+  const int64_t nl = int64_t(total_q) * H * 4, ncu = (int64_t(B) + 1) * 4;
+  struct Region { const void* p; int64_t n; };
+  const Region written[] = {{o, nq}, {lse, nl}};
+  const Region read[] = {{q, nq}, {k, nkv}, {v, nkv}, {cu_seqlens_q, ncu}, {cu_seqlens_k, ncu}};
+  for (const Region& w : written)
+    for (const Region& r : read)
+      if (overlaps(w.p, w.n, r.p, r.n)) return FA_ERR_ALIAS;
+  if (overlaps(o, nq, lse, nl)) return FA_ERR_ALIAS;
+
+  fa::FwdParams p = make_params(q, k, v, o, lse, B, H, max_seqlen_q, scale, nullptr, dtype);
+  p.Nk = max_seqlen_k;
+  p.Hkv = Hkv;
+  p.cu_q = cu_seqlens_q;
+  p.cu_k = cu_seqlens_k;
+  p.end_aligned = 1;
+  p.split_keys = static_cast<int>(
+      std::min<int64_t>((int64_t(max_seqlen_k) + 127) / 128 * 128, INT_MAX - 127));
+  if (fa::launch_fwd_bf16(p, d, causal != 0, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return FA_ERR_HIP;
+  return FA_OK;
 }
 
 extern "C" const char* fa_status_string(int status) {

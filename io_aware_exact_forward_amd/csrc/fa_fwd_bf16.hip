@@ -104,8 +104,33 @@ void fa_fwd_bf16_kernel(FwdParams p) {
   int qt = x / BH;
   if (CAUSAL) qt = p.n_qtiles - 1 - qt;  // heaviest tiles first
   const int b = bh / p.H;
-  const int N = p.N;    // query rows
-  const int Nk = p.Nk;  // key rows
+  const int hq = bh - b * p.H;
+  const int hk = hq / (p.H / p.Hkv);  // the key/value head this query head reads
+  // Layout of this (batch, head): dense [B, H, N, d] / [B, Hkv, Nk, d], or a
+  // packed batch [T, H, d] / [T, Hkv, d] with sequence b at rows cu[b] ..
+  // cu[b+1]-1.  Row strides and bases in elements; all workgroup-uniform.
+  int N, Nk, q_ld, kv_ld, lse_ld;
+  int64_t base, kvbase, lse_base;
+  if (p.cu_q) {
+    const int s0 = p.cu_q[b], k0 = p.cu_k[b];
+    N = __builtin_amdgcn_readfirstlane(p.cu_q[b + 1] - s0);
+    Nk = __builtin_amdgcn_readfirstlane(p.cu_k[b + 1] - k0);
+    q_ld = p.H * D;
+    kv_ld = p.Hkv * D;
+    base = ((int64_t)__builtin_amdgcn_readfirstlane(s0) * p.H + hq) * D;
+    kvbase = ((int64_t)__builtin_amdgcn_readfirstlane(k0) * p.Hkv + hk) * D;
+    lse_base = (int64_t)__builtin_amdgcn_readfirstlane(s0) * p.H + hq;
+    lse_ld = p.H;
+  } else {
+    N = p.N;
+    Nk = p.Nk;
+    q_ld = D;
+    kv_ld = D;
+    base = (int64_t)bh * N * D;
+    kvbase = ((int64_t)b * p.Hkv + hk) * Nk * D;
+    lse_base = (int64_t)bh * N;
+    lse_ld = 1;
+  }
   const int q0 = qt * C::BQ;
   int kv_lim = Nk;
   if (p.key_len) {
@@ -130,8 +155,6 @@ void fa_fwd_bf16_kernel(FwdParams p) {
   const int kv_last = min(n_kv, kv_first + p.split_keys);
   const int ntiles = kv_last > kv_first ? (kv_last - kv_first + C::BK - 1) / C::BK : 0;
 
-  const int64_t base = (int64_t)bh * N * D;     // Q, O
-  const int64_t kvbase = (int64_t)bh * Nk * D;  // K, V
   const uint16_t* __restrict__ qg = (const uint16_t*)p.q + base;
 
   const int qw0 = q0 + 32 * wave;  // first query row of this wave
@@ -144,7 +167,7 @@ void fa_fwd_bf16_kernel(FwdParams p) {
 #pragma unroll
   for (int kk = 0; kk < D / 16; ++kk) {
     u32x4 w = {0u, 0u, 0u, 0u};
-    if (qrow < N) w = *(const u32x4*)(qg + (int64_t)qrow * D + 16 * kk + 8 * h);
+    if (qrow < N) w = *(const u32x4*)(qg + (int64_t)qrow * q_ld + 16 * kk + 8 * h);
     w ^= p.q_sign;
     qf[kk] = __builtin_bit_cast(bf16x8, w);
   }
@@ -152,7 +175,8 @@ void fa_fwd_bf16_kernel(FwdParams p) {
   // ---- K/V tile loads: HBM -> LDS, range-checked ---------------------------
   // Buffer range = the valid keys of this (batch, head): loads beyond it
   // return zeros, so padded keys contribute exact zeros to both products.
-  const uint32_t valid_bytes = (uint32_t)kv_lim * C::ROW_BYTES;
+  const uint32_t row_stride = (uint32_t)kv_ld * 2;  // bytes between key rows in memory
+  const uint32_t valid_bytes = (uint32_t)kv_lim * row_stride;
   const void* kbase = (const uint16_t*)p.k + kvbase;
   const void* vbase = (const uint16_t*)p.v + kvbase;
   // Per-lane source offsets within a tile (bytes): load i of this wave fills
@@ -162,15 +186,15 @@ void fa_fwd_bf16_kernel(FwdParams p) {
   for (int i = 0; i < C::LOADS; ++i) {
     const int pch = (WAVES * i + wave) * 64 + lane;  // physical chunk index in the tile
     const int row = pch / C::CPR, phys = pch % C::CPR;
-    koff[i] = row * C::ROW_BYTES + 16 * k_chunk<D>(row, phys);  // XOR is its own inverse
-    voff[i] = row * C::ROW_BYTES + 16 * v_chunk<D>(row, phys);
+    koff[i] = row * row_stride + 16 * k_chunk<D>(row, phys);  // XOR is its own inverse
+    voff[i] = row * row_stride + 16 * v_chunk<D>(row, phys);
   }
   // With nbytes = 0 every lane is out of range: the stage is filled with
   // zeros and no memory is read.
   auto load_tile_n = [&](int kv0, int stage, uint32_t nbytes) __attribute__((always_inline)) {
     uint8_t* ks = lds + stage * C::STAGE_BYTES;
     uint8_t* vs = ks + C::TILE_BYTES;
-    const uint32_t tile_off = __builtin_amdgcn_readfirstlane(kv0 * C::ROW_BYTES);
+    const uint32_t tile_off = __builtin_amdgcn_readfirstlane((uint32_t)kv0 * row_stride);
 #pragma unroll
     for (int i = 0; i < C::LOADS; ++i) {
       const int blk = (WAVES * i + wave) * 1024;
@@ -668,7 +692,7 @@ void fa_fwd_bf16_kernel(FwdParams p) {
       }
       if (h == 0) p.lse_part[prow] = lse_row;
     } else {
-      uint16_t* og = (uint16_t*)p.o + base + (int64_t)qrow * D;
+      uint16_t* og = (uint16_t*)p.o + base + (int64_t)qrow * q_ld;
 #pragma unroll
       for (int db = 0; db < C::ND; ++db) {
 #pragma unroll
@@ -681,7 +705,7 @@ void fa_fwd_bf16_kernel(FwdParams p) {
           *(u32x2*)(og + d0) = w;
         }
       }
-      if (h == 0) p.lse[(int64_t)bh * N + qrow] = lse_row;
+      if (h == 0) p.lse[lse_base + (int64_t)qrow * lse_ld] = lse_row;
     }
   }
 }

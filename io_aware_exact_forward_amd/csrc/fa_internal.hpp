@@ -15,8 +15,11 @@ struct FwdParams {
   void* o;                 // [B, H, N, d] (unused when o_part is set)
   float* lse;              // [B, H, N]    (unused when o_part is set)
   const int32_t* key_len;  // device [B] or nullptr
-  int B, H, N;             // N: query rows
-  int Nk;                  // key rows
+  int B, H, N;             // N: query rows (packed batches: the longest sequence)
+  int Hkv;                 // key/value heads; query head h reads head h / (H / Hkv)
+  int Nk;                  // key rows (dense layout)
+  const int32_t* cu_q;     // packed batch: device [B + 1] query row offsets, or nullptr
+  const int32_t* cu_k;     // packed batch: device [B + 1] key row offsets
   int end_aligned;         // 0: query row i sits at key position i; 1: at i + L_b - N
   int n_qtiles;            // ceil(N / query-tile rows)
   int splits;              // key ranges per (batch, head, query tile), >= 1

@@ -42,6 +42,11 @@ __all__ = [
     "Inputs",
     "grad_inputs",
     "BWD_WORKLOADS",
+    "PackedInputs",
+    "packed_inputs",
+    "VarlenWorkload",
+    "VARLEN_WORKLOADS",
+    "varlen_inputs",
 ]
 
 
@@ -188,13 +193,14 @@ def random_inputs(B, H, N, d, dtype, seed, *, q_mult=1.0, key_len=None):
     return Inputs(wl, q, k, v, kl, None)
 
 
-def cache_inputs(B, H, Nq, Nk, d, seed, *, q_mult=1.0, key_len=None):
+def cache_inputs(B, H, Nq, Nk, d, seed, *, q_mult=1.0, key_len=None, Hkv=None):
     """Query rows against a longer key cache (same recipe, bf16): q [B, H, Nq, d]
-    is drawn first, then k and v [B, H, Nk, d]."""
+    is drawn first, then k and v [B, Hkv, Nk, d] (Hkv = H unless given)."""
+    Hkv = H if Hkv is None else Hkv
     rng = np.random.default_rng(seed)
     q = rng.standard_normal((B, H, Nq, d), dtype=np.float32)
-    k = rng.standard_normal((B, H, Nk, d), dtype=np.float32)
-    v = rng.standard_normal((B, H, Nk, d), dtype=np.float32)
+    k = rng.standard_normal((B, Hkv, Nk, d), dtype=np.float32)
+    v = rng.standard_normal((B, Hkv, Nk, d), dtype=np.float32)
     if q_mult != 1.0:
         q *= np.float32(q_mult)
     kl = None if key_len is None else np.asarray(key_len, dtype=np.int32)
@@ -246,6 +252,72 @@ def decode_inputs(wl: DecodeWorkload, *, B=None, H=None, Nk=None, seed=None) -> 
     kl = rng.integers(1, Nk, size=B, endpoint=True, dtype=np.int64).astype(np.int32)
     sq = Workload(wl.name, B, H, Nk, d, "bf16", True, wl.scale, seed, ragged=True)
     return Inputs(sq, q, k, v, kl, None)
+
+
+@dataclasses.dataclass
+class PackedInputs:
+    """A packed batch: q [Tq, H, d], k and v [Tk, Hkv, d] as bf16 bits, and
+    the int32 row offsets [B + 1] of the sequences."""
+    q: np.ndarray
+    k: np.ndarray
+    v: np.ndarray
+    cu_q: np.ndarray
+    cu_k: np.ndarray
+
+    def exact(self, name: str) -> np.ndarray:
+        return bf16_decode(getattr(self, name), np.float64)
+
+
+def packed_inputs(lens_q, lens_k, H, Hkv, d, seed):
+    """Packed variable-length batch (same recipe): q, then k, then v, each
+    standard normal, rounded to bf16."""
+    cu_q = np.concatenate([[0], np.cumsum(lens_q)]).astype(np.int32)
+    cu_k = np.concatenate([[0], np.cumsum(lens_k)]).astype(np.int32)
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((int(cu_q[-1]), H, d), dtype=np.float32)
+    k = rng.standard_normal((int(cu_k[-1]), Hkv, d), dtype=np.float32)
+    v = rng.standard_normal((int(cu_k[-1]), Hkv, d), dtype=np.float32)
+    return PackedInputs(bf16_encode(q), bf16_encode(k), bf16_encode(v), cu_q, cu_k)
+
+
+@dataclasses.dataclass(frozen=True)
+class VarlenWorkload:
+    """A packed causal batch of B sequences whose lengths are drawn uniform on
+    [1, max_len] (query and key lengths equal), H query heads sharing Hkv
+    key/value heads."""
+    name: str
+    B: int
+    H: int
+    Hkv: int
+    max_len: int
+    d: int
+    seed: int
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+    def lengths(self) -> np.ndarray:
+        rng = np.random.default_rng(self.seed)
+        return rng.integers(1, self.max_len, size=self.B, endpoint=True, dtype=np.int64)
+
+    def describe(self) -> dict:
+        return {"workload": self.name, "B": self.B, "H": self.H, "Hkv": self.Hkv,
+                "max_len": self.max_len, "d": self.d, "dtype": "bf16", "causal": True,
+                "scale": self.scale, "lengths": "uniform on [1, max_len], packed"}
+
+
+VARLEN_WORKLOADS = {
+    # 16 packed causal sequences of up to 8192 tokens, 32 query heads on 8 key/value heads
+    "varlen_b16_h32_hkv8_n8192_d128_bf16": VarlenWorkload(
+        "varlen_b16_h32_hkv8_n8192_d128_bf16", 16, 32, 8, 8192, 128, 1008),
+}
+
+
+def varlen_inputs(wl: VarlenWorkload) -> PackedInputs:
+    """Lengths from the workload's seed, then the tensors from seed + 1."""
+    lens = wl.lengths()
+    return packed_inputs(lens, lens, wl.H, wl.Hkv, wl.d, wl.seed + 1)
 
 
 # The backward exercise of "IO-aware exact attention" (section "Measure

@@ -33,7 +33,8 @@ def declared_functions():
 def test_header_declares_expected_entry_points():
     assert declared_functions() == sorted(
         ["fa_forward", "fa_naive_workspace_bytes", "fa_naive_forward", "fa_split_workspace_bytes",
-         "fa_forward_split", "fa_backward_workspace_bytes", "fa_backward", "fa_naive_backward",
+         "fa_forward_split", "fa_forward_varlen", "fa_backward_workspace_bytes", "fa_backward",
+         "fa_naive_backward",
          "fa_status_string", "fa_abi_version"])
 
 
@@ -42,7 +43,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     for name in declared_functions():
         assert hasattr(lib, name), name
     assert set(_lib.exported_symbols()) == set(declared_functions())
-    assert fa.fa_abi_version() == (1 << 16) | 2
+    assert fa.fa_abi_version() == (1 << 16) | 3
 
 
 def test_status_strings():
@@ -137,9 +138,9 @@ def test_python_wrapper_rejects_host_tensors():
 
 # ---- split-KV entry point -------------------------------------------------------
 
-def split_call(q=Q, k=K, v=V, o=O, lse=L, B=1, H=2, Nq=64, Nk=1024, d=64, scale=0.125, causal=0,
-               kl=0, dtype=BF16, num_splits=4, ws=WS, wsb=1 << 30, stream=0):
-    return fa.fa_forward_split(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, kl, dtype,
+def split_call(q=Q, k=K, v=V, o=O, lse=L, B=1, H=2, Hkv=2, Nq=64, Nk=1024, d=64, scale=0.125,
+               causal=0, kl=0, dtype=BF16, num_splits=4, ws=WS, wsb=1 << 30, stream=0):
+    return fa.fa_forward_split(q, k, v, o, lse, B, H, Hkv, Nq, Nk, d, scale, causal, kl, dtype,
                                num_splits, ws, wsb, stream)
 
 
@@ -171,7 +172,7 @@ def test_split_bad_arguments():
     assert split_call(dtype=3) == DTYPE
     assert split_call(d=96) == HEAD_DIM
     for bad in (dict(B=-1), dict(H=-1), dict(Nq=-1), dict(Nk=-1), dict(num_splits=-1),
-                dict(num_splits=65537)):
+                dict(num_splits=65537), dict(Hkv=0), dict(Hkv=3), dict(H=6, Hkv=4)):
         assert split_call(**bad) == SHAPE, bad
     # one (batch, head) slice above 2^31 - 1 bytes
     assert split_call(Nq=1 << 24, d=128) == SHAPE
@@ -279,3 +280,36 @@ def test_naive_backward_bad_arguments():
     assert nb(wsb=100) == WORKSPACE
     assert nb(dv=K) == ALIAS
     assert nb(B=0, q=0, k=0, v=0, o=0, lse=0, do=0, dq=0, dk=0, dv=0, ws=0, wsb=0) == OK
+
+
+
+# ---- packed variable-length entry point -------------------------------------
+
+CUQ, CUK = A + 12 * (1 << 34), A + 13 * (1 << 34)
+
+
+def varlen_call(q=Q, k=K, v=V, o=O, lse=L, cuq=CUQ, cuk=CUK, B=3, H=4, Hkv=2, tq=100, tk=120,
+                mq=50, mk=60, d=64, scale=0.125, causal=1, dtype=BF16, stream=0):
+    return fa.fa_forward_varlen(q, k, v, o, lse, cuq, cuk, B, H, Hkv, tq, tk, mq, mk, d, scale,
+                                causal, dtype, stream)
+
+
+def test_varlen_bad_arguments():
+    assert varlen_call(dtype=F32) == DTYPE
+    assert varlen_call(d=32) == HEAD_DIM
+    for bad in (dict(B=-1), dict(tq=-1), dict(mk=-1), dict(Hkv=0), dict(Hkv=3),
+                dict(mq=1 << 24, d=128)):
+        assert varlen_call(**bad) == SHAPE, bad
+    assert varlen_call(scale=float("inf")) == SCALE
+    for field in ("q", "o", "lse", "cuq", "cuk", "k", "v"):
+        assert varlen_call(**{field: 0}) == NULL, field
+    for field, val in (("q", Q + 8), ("o", O + 4), ("lse", L + 2), ("cuq", CUQ + 2)):
+        assert varlen_call(**{field: val}) == ALIGN, field
+    assert varlen_call(o=Q) == ALIAS
+    assert varlen_call(lse=CUK) == ALIAS
+    assert varlen_call(o=L - 1024) == ALIAS
+
+
+def test_varlen_empty_is_a_no_op():
+    for kw in (dict(B=0), dict(H=0), dict(tq=0), dict(mq=0)):
+        assert varlen_call(q=0, k=0, v=0, o=0, lse=0, cuq=0, cuk=0, **kw) == OK

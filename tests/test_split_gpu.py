@@ -43,9 +43,11 @@ def run_split(inp, causal, scale, num_splits):
 def check(inp, causal, scale, o_gpu, lse_gpu, label, rows=None):
     """All rows (or rows [R] of every head) of the GPU result against the oracle."""
     tol = TOL["bf16"]
-    o_ref, lse_ref = oracle.attention(inp.exact("q"), inp.exact("k"), inp.exact("v"), scale,
-                                      causal=causal, key_len=inp.key_len, rows=rows,
-                                      end_aligned=True)
+    H = inp.q.shape[1]
+    kx = oracle.expand_kv_heads(inp.exact("k"), H)
+    vx = oracle.expand_kv_heads(inp.exact("v"), H)
+    o_ref, lse_ref = oracle.attention(inp.exact("q"), kx, vx, scale, causal=causal,
+                                      key_len=inp.key_len, rows=rows, end_aligned=True)
     if rows is not None:
         o_gpu, lse_gpu = o_gpu[:, :, rows], lse_gpu[:, :, rows]
     live = np.isfinite(lse_ref)
@@ -149,3 +151,22 @@ def test_decode_full_size_sampled_heads():
         sub = W.Inputs(inp.wl, inp.q[:, h:h + 1], inp.k[:, h:h + 1], inp.v[:, h:h + 1],
                        inp.key_len, None)
         check(sub, True, wl.scale, o[:, h:h + 1], lse[:, h:h + 1], f"decode head {h}")
+
+
+GQA_CASES = [
+    # (B, H, Hkv, Nq, Nk, d, key_len, seed)
+    (2, 8, 2, 1, 2000, 128, [2000, 333], 9801),     # grouped decode
+    (1, 6, 1, 130, 700, 64, None, 9802),            # multi-query, chunked prefill
+    (2, 4, 2, 300, 300, 128, None, 9803),           # square
+]
+
+
+@pytest.mark.parametrize("case", GQA_CASES, ids=lambda c: f"h{c[1]}kv{c[2]}q{c[3]}k{c[4]}d{c[5]}")
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("num_splits", [0, 1, 5])
+def test_split_grouped_heads(case, causal, num_splits):
+    B, H, Hkv, Nq, Nk, d, key_len, seed = case
+    inp = W.cache_inputs(B, H, Nq, Nk, d, seed, key_len=key_len, Hkv=Hkv)
+    scale = 1.0 / np.sqrt(d)
+    o, lse = run_split(inp, causal, scale, num_splits)
+    check(inp, causal, scale, o, lse, f"gqa {case} causal={causal} splits={num_splits}")
