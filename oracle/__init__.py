@@ -16,3 +16,4 @@ from .attention import (  # noqa: F401
     varlen_attention,
 )
 from .backward import attention_backward  # noqa: F401
+from .dropout import dropout_attention, dropout_keep, philox4x32_10  # noqa: F401
