@@ -72,13 +72,19 @@ def dropout_keep(b, h, H, N, Nk, p, seed, offset):
     return u >= threshold
 
 
-def dropout_attention(q, k, v, scale, p, seed, offset=0, causal=False, key_len=None):
+def dropout_attention(q, k, v, scale, p, seed, offset=0, causal=False, key_len=None,
+                      head_ids=None, H_all=None):
     """O = (P * Z / (1 - p)) V and the undropped LSE, square problems
-    ([B, H, N, d], positions and masks as ``attention``).  fp64."""
+    ([B, H, N, d], positions and masks as ``attention``).  fp64.
+
+    head_ids / H_all: q, k, v hold heads head_ids[0..H-1] of an H_all-head
+    problem (the mask depends on the head index); by default all heads."""
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
     B, H, N, _ = q.shape
+    ids = list(range(H)) if head_ids is None else [int(x) for x in head_ids]
+    H_all = H if H_all is None else int(H_all)
     o = np.zeros((B, H, N, v.shape[-1]))
     lse = np.full((B, H, N), NEG_INF)
     for b in range(B):
@@ -91,7 +97,7 @@ def dropout_attention(q, k, v, scale, p, seed, offset=0, causal=False, key_len=N
             w = np.where(vis, np.exp(s - m[:, None]), 0.0)
             ell = w.sum(axis=1)
             P = np.divide(w, ell[:, None], out=np.zeros_like(w), where=live[:, None])
-            Z = dropout_keep(b, h, H, N, N, p, seed, offset)
+            Z = dropout_keep(b, ids[h], H_all, N, N, p, seed, offset)
             o[b, h] = (P * Z) @ v[b, h] / (1.0 - p)
             with np.errstate(divide="ignore"):
                 lse[b, h] = np.where(live, m + np.log(np.where(live, ell, 1.0)), NEG_INF)

@@ -106,3 +106,12 @@ def test_planted_scale_mistake():
     outs = np.stack([oracle.dropout_attention(q, k, v, 0.5, 0.5, seed=3, offset=t)[0] * 0.5
                      for t in range(400)])  # 1/(1-p) dropped
     assert np.abs(outs.mean(axis=0) - o_ref).max() > 0.1
+
+
+def test_head_selection_matches_full_problem():
+    B, H, N, d = 2, 5, 16, 4
+    q, k, v = rand((B, H, N, d), 1040), rand((B, H, N, d), 1041), rand((B, H, N, d), 1042)
+    full, _ = oracle.dropout_attention(q, k, v, 0.5, 0.4, seed=8, offset=2, causal=True)
+    part, _ = oracle.dropout_attention(q[:, [3, 1]], k[:, [3, 1]], v[:, [3, 1]], 0.5, 0.4, seed=8,
+                                       offset=2, causal=True, head_ids=[3, 1], H_all=H)
+    assert np.array_equal(part, full[:, [3, 1]])
