@@ -480,6 +480,8 @@ def main() -> int:
                          "varlen_b16_h32_hkv8_n8192_d128_bf16 (packed sequences, grouped heads)")
     ap.add_argument("--n", type=int, default=0,
                     help="backward workload only: another sequence length (512 .. 4096)")
+    ap.add_argument("--dropout", type=float, default=0.0,
+                    help="square workloads: time fa_forward_dropout at this rate instead")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-naive", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -538,15 +540,22 @@ def main() -> int:
     compulsory = sum(3 * H * L * d * esz for L in lens) + B * H * N * d * esz + B * H * N * 4
 
     stream = torch.cuda.current_stream(dev)
+    if args.dropout > 0:
+        def fwd():
+            fa.forward_dropout(q, k, v, p_drop=args.dropout, seed=2024, offset=0, scale=wl.scale,
+                               causal=wl.causal, key_len=kl, out=out, lse=lse)
+    else:
+        def fwd():
+            fa.forward(q, k, v, scale=wl.scale, causal=wl.causal, key_len=kl, out=out, lse=lse)
     for _ in range(args.warmup):
-        fa.forward(q, k, v, scale=wl.scale, causal=wl.causal, key_len=kl, out=out, lse=lse)
+        fwd()
     torch.cuda.synchronize()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     t_wall = time.perf_counter()
     start.record(stream)
     for _ in range(args.steps):
-        fa.forward(q, k, v, scale=wl.scale, causal=wl.causal, key_len=kl, out=out, lse=lse)
+        fwd()
     end.record(stream)
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
@@ -568,21 +577,22 @@ def main() -> int:
         "dtype": wl.dtype,
         "data": "synthetic",
         "config": dict(wl.describe(), useful_flops=flops, compulsory_hbm_bytes=compulsory,
-                       parallelism="single GPU"),
+                       parallelism="single GPU",
+                       **({"dropout": args.dropout} if args.dropout > 0 else {})),
         "roofline": {
             "bound": "mfma",
             "achieved": tflops,
             "peak": peak,
             "unit": "TFLOP/s",
             "frac": tflops / peak,
-            "traffic": stored_traffic(wl.name),
+            "traffic": stored_traffic(wl.name) if args.dropout == 0 else None,
             "kernel": "fa_fwd_bf16_kernel" if wl.dtype == "bf16" else "fa_fwd_f32_kernel",
             "kernel_hash": kernel_hash(),
         },
         "wall_s_timed_region": t_wall,
     }
 
-    if not args.no_naive:
+    if not args.no_naive and args.dropout == 0:
         need = fa.fa_naive_workspace_bytes(B, H, N, fa.FA_DTYPE_BF16 if wl.dtype == "bf16" else fa.FA_DTYPE_F32)
         free = torch.cuda.mem_get_info(dev)[0]
         if need < 0.8 * free:
@@ -603,7 +613,7 @@ def main() -> int:
             del ws
             torch.cuda.empty_cache()
 
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.dropout == 0:
         o_host = out
         if wl.dtype == "bf16":
             o_np = W.bf16_decode(o_host.view(torch.int16).cpu().numpy().view(np.uint16))

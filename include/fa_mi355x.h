@@ -82,7 +82,7 @@ typedef enum {
   FA_ERR_HEAD_DIM = -3,    /* d not in {64, 128}                               */
   FA_ERR_DTYPE = -4,       /* dtype not an fa_dtype_t                          */
   FA_ERR_ALIGN = -5,       /* a pointer is not aligned as required             */
-  FA_ERR_SCALE = -6,       /* scale is NaN or infinite                         */
+  FA_ERR_SCALE = -6,       /* scale not finite, or dropout rate outside [0, 1) */
   FA_ERR_ALIAS = -7,       /* an output overlaps an input or the other output */
   FA_ERR_WORKSPACE = -8,   /* workspace NULL, misaligned or too small          */
   FA_ERR_HIP = -9          /* the HIP runtime reported an error at launch      */
@@ -248,13 +248,31 @@ int fa_naive_backward(const void* q, const void* k, const void* v, const void* o
                       int H, int N, int d, float scale, int causal, const int32_t* key_len_mask,
                       int dtype, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * fa_forward with dropout on the attention probabilities ("IO-aware exact
+ * attention", section "Why implementations form a family", names dropout
+ * as a variant): O = (P * Z / (1 - p_drop)) V, LSE of the undropped row.
+ * Z_ij (keep = 1) is decided by Philox4x32-10 (Salmon, Moraes, Dror, Shaw,
+ * SC 2011) with key (seed & 0xffffffff, seed >> 32) and counter
+ * (j / 4, i, b * H + h, offset): with u the counter's output word j % 4,
+ * Z_ij = 1 iff u >= floor(p_drop * 2^32).  The same (seed, offset) gives the
+ * same mask on every call; vary offset between steps.
+ *   p_drop       in [0, 1) (FA_ERR_SCALE otherwise).
+ *   dtype        FA_DTYPE_BF16 only.
+ * Other arguments and conventions are those of fa_forward.
+ */
+int fa_forward_dropout(const void* q, const void* k, const void* v, void* o, float* lse,
+                       int B, int H, int N, int d, float scale, int causal,
+                       const int32_t* key_len_mask, int dtype, float p_drop, uint64_t seed,
+                       uint32_t offset, void* stream);
+
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* fa_status_string(int status);
 
 /* ABI version of this header: (major << 16) | minor. */
 int fa_abi_version(void);
 
-#define FA_ABI_VERSION ((1 << 16) | 3)
+#define FA_ABI_VERSION ((1 << 16) | 4)
 
 #ifdef __cplusplus
 }

@@ -21,6 +21,7 @@ from ._lib import (  # noqa: F401
     fa_forward,
     fa_forward_split,
     fa_forward_varlen,
+    fa_forward_dropout,
     fa_naive_backward,
     fa_naive_forward,
     fa_naive_workspace_bytes,
@@ -32,7 +33,7 @@ from ._lib import (  # noqa: F401
 __all__ = [
     "forward", "forward_split", "backward", "naive_forward", "fa_forward", "fa_forward_split",
     "fa_backward", "fa_backward_workspace_bytes", "fa_naive_backward", "naive_backward",
-    "fa_forward_varlen", "forward_varlen",
+    "fa_forward_varlen", "forward_varlen", "fa_forward_dropout", "forward_dropout",
     "fa_split_workspace_bytes", "fa_naive_forward", "fa_naive_workspace_bytes",
     "fa_status_string", "fa_abi_version", "FAError", "FA_DTYPE_BF16", "FA_DTYPE_F32",
 ]
@@ -210,4 +211,33 @@ def forward_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen
                             lse.data_ptr(), cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(), B, H,
                             Hkv, Tq, Tk, int(max_seqlen_q), int(max_seqlen_k), d, float(scale),
                             int(bool(causal)), _dtype_code(q), stream))
+    return out, lse
+
+
+def forward_dropout(q, k, v, *, p_drop, seed, offset=0, scale=None, causal=False, key_len=None,
+                    out=None, lse=None):
+    """O, LSE = fa_forward_dropout(...): dropout with rate p_drop on the
+    probabilities, mask from Philox4x32-10 keyed by seed, counter word 3 = offset."""
+    import torch
+    if q.dim() != 4 or q.shape != k.shape or q.shape != v.shape:
+        raise FAError(-2, "q, k, v must share one [B, H, N, d] shape")
+    for t in (q, k, v):
+        if not t.is_cuda or not t.is_contiguous():
+            raise FAError(-1, "q, k, v must be contiguous device tensors")
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    kl = 0
+    if key_len is not None:
+        if key_len.dtype != torch.int32 or not key_len.is_cuda or key_len.numel() != B:
+            raise FAError(-1, "key_len must be a device int32 tensor of B elements")
+        kl = key_len.data_ptr()
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    check(fa_forward_dropout(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                             lse.data_ptr(), B, H, N, d, float(scale), int(bool(causal)), kl,
+                             _dtype_code(q), float(p_drop), int(seed), int(offset), stream))
     return out, lse

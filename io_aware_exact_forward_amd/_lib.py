@@ -56,6 +56,11 @@ _SIGNATURES = {
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
         ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float, ctypes.c_int,
         ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "fa_forward_dropout": (ctypes.c_int, [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float, ctypes.c_int,
+        ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_uint64, ctypes.c_uint32,
+        ctypes.c_void_p]),
     "fa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "fa_abi_version": (ctypes.c_int, []),
 }
@@ -159,6 +164,13 @@ def fa_naive_backward(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, d, scale, caus
     return load().fa_naive_backward(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, d, scale,
                                     int(causal), key_len_mask or None, dtype, workspace or None,
                                     workspace_bytes, stream or None)
+
+
+def fa_forward_dropout(q, k, v, o, lse, B, H, N, d, scale, causal, key_len_mask, dtype, p_drop,
+                       seed, offset, stream) -> int:
+    return load().fa_forward_dropout(q or None, k or None, v or None, o or None, lse or None, B, H,
+                                     N, d, scale, int(causal), key_len_mask or None, dtype,
+                                     p_drop, seed, offset, stream or None)
 
 
 def fa_status_string(status) -> str:

@@ -547,6 +547,31 @@ extern "C" int fa_forward_varlen(const void* q, const void* k, const void* v, vo
   return FA_OK;
 }
 
+extern "C" int fa_forward_dropout(const void* q, const void* k, const void* v, void* o,
+                                  float* lse, int B, int H, int N, int d, float scale, int causal,
+                                  const int32_t* key_len_mask, int dtype, float p_drop,
+                                  uint64_t seed, uint32_t offset, void* stream) {
+  if (dtype != FA_DTYPE_BF16) return FA_ERR_DTYPE;
+  if (!(p_drop >= 0.f && p_drop < 1.f)) return FA_ERR_SCALE;
+  Shape s;
+  bool empty = false;
+  int st = check_scalars(B, H, N, d, scale, dtype, &s, &empty);
+  if (st != FA_OK || empty) return st;
+  st = check_pointers(q, k, v, o, lse, key_len_mask, B, s);
+  if (st != FA_OK) return st;
+  fa::FwdParams p = make_params(q, k, v, o, lse, B, H, N, scale, key_len_mask, dtype);
+  p.drop = 1;
+  const double t = std::floor(static_cast<double>(p_drop) * 4294967296.0);
+  p.drop_threshold = static_cast<uint32_t>(std::min(t, 4294967295.0));
+  p.seed_lo = static_cast<uint32_t>(seed & 0xFFFFFFFFu);
+  p.seed_hi = static_cast<uint32_t>(seed >> 32);
+  p.drop_offset = offset;
+  p.keep_scale = static_cast<float>(1.0 / (1.0 - static_cast<double>(p_drop)));
+  if (fa::launch_fwd_bf16(p, d, causal != 0, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return FA_ERR_HIP;
+  return FA_OK;
+}
+
 extern "C" const char* fa_status_string(int status) {
   switch (status) {
     case FA_OK: return "ok";
@@ -555,7 +580,7 @@ extern "C" const char* fa_status_string(int status) {
     case FA_ERR_HEAD_DIM: return "head dimension must be 64 or 128";
     case FA_ERR_DTYPE: return "dtype not supported by this entry point";
     case FA_ERR_ALIGN: return "a pointer is misaligned (q, k, v, o: 16 bytes; lse, key_len: 4)";
-    case FA_ERR_SCALE: return "scale must be finite";
+    case FA_ERR_SCALE: return "scale must be finite (and a dropout rate in [0, 1))";
     case FA_ERR_ALIAS: return "an output overlaps an input or another output";
     case FA_ERR_WORKSPACE: return "workspace is NULL, misaligned or too small";
     case FA_ERR_HIP: return "the HIP runtime reported an error";

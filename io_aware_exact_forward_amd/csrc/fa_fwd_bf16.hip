@@ -79,9 +79,29 @@ struct Bf16Cfg {
   static_assert(LDS_BYTES <= 160 * 1024, "LDS capacity");
 };
 
-template <int D, bool CAUSAL, int WAVES, int NSTAGE, bool PINGPONG>
+// Philox4x32 with 10 rounds (Salmon, Moraes, Dror, Shaw, "Parallel random
+// numbers: as easy as 1, 2, 3", SC 2011): words 0 and 2 are multiplied by
+// the round constants, the high halves are mixed with words 1 and 3 and the
+// key, and the key advances by the Weyl increments between rounds.
+__device__ __forceinline__ u32x4 philox4x32_10(u32x4 c, uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r) {
+      k0 += 0x9E3779B9u;
+      k1 += 0xBB67AE85u;
+    }
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c[0];
+    const uint64_t p1 = (uint64_t)0xCD9E8D57u * c[2];
+    c = u32x4{(uint32_t)(p1 >> 32) ^ c[1] ^ k0, (uint32_t)p1, (uint32_t)(p0 >> 32) ^ c[3] ^ k1,
+              (uint32_t)p0};
+  }
+  return c;
+}
+
+template <int D, bool CAUSAL, int WAVES, int NSTAGE, bool PINGPONG, bool DROP = false>
 __global__ __launch_bounds__(64 * WAVES, (WAVES == 4 && NSTAGE == 2) ? 2 : 1)
 void fa_fwd_bf16_kernel(FwdParams p) {
+  static_assert(!DROP || !PINGPONG, "dropout runs in the lockstep schedule");
   using C = Bf16Cfg<D, WAVES, NSTAGE>;
   __shared__ __attribute__((aligned(1024))) uint8_t lds[C::LDS_BYTES];
 
@@ -406,6 +426,7 @@ void fa_fwd_bf16_kernel(FwdParams p) {
   auto pv = [&](const uint32_t vbase, const bf16x8 (&pf)[C::NB][2], auto chain_tag,
                 const uint32_t kbase) __attribute__((always_inline)) {
     constexpr bool chain_k = decltype(chain_tag)::value;
+    constexpr bool sum_weights = !DROP;  // with dropout the sum is taken before the mask
     static_for<VG>([&](auto gc) __attribute__((always_inline)) {
       constexpr int g = decltype(gc)::value;
       if constexpr (g + 1 < VG) {
@@ -432,17 +453,19 @@ void fa_fwd_bf16_kernel(FwdParams p) {
       // softmax step each would wait for a whole MFMA of the other wave
       // sharing the SIMD.  Group g sums 2*NB/NG of the weight vectors.
       constexpr int PER = 2 * C::NB / VG;
-      static_for<PER>([&](auto ic) __attribute__((always_inline)) {
-        constexpr int f = g * PER + decltype(ic)::value;
-        const bf16x8 w = pf[f / 2][f % 2];
-        static_for<4>([&](auto jc) __attribute__((always_inline)) {
-          constexpr int j = decltype(jc)::value;
-          lp_run = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{w[2 * j], w[2 * j + 1]}, ones, lp_run,
-                                                   false);
+      if constexpr (sum_weights) {
+        static_for<PER>([&](auto ic) __attribute__((always_inline)) {
+          constexpr int f = g * PER + decltype(ic)::value;
+          const bf16x8 w = pf[f / 2][f % 2];
+          static_for<4>([&](auto jc) __attribute__((always_inline)) {
+            constexpr int j = decltype(jc)::value;
+            lp_run = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{w[2 * j], w[2 * j + 1]}, ones,
+                                                     lp_run, false);
+          });
         });
-      });
-      // keeps the compiler from sinking the sum into the softmax step
-      asm volatile("" : "+v"(lp_run));
+        // keeps the compiler from sinking the sum into the softmax step
+        asm volatile("" : "+v"(lp_run));
+      }
     });
   };
 
@@ -502,6 +525,46 @@ void fa_fwd_bf16_kernel(FwdParams p) {
     });
   };
 
+  // Dropout on the probabilities: the weight sum that normalises O is taken
+  // over the undropped bf16 weights first, then each weight whose draw is
+  // below the threshold is zeroed (the 1 / (1 - p) scale is applied to O at
+  // the end).  The draw of query row i and key j is word j % 4 of Philox
+  // on the counter (j / 4, i, b * H + h, offset); a lane's 16 keys of a
+  // 32-key block are four aligned groups of four, one Philox call each.
+  auto dropout = [&](const int kv0, bf16x8 (&pf)[C::NB][2]) __attribute__((always_inline)) {
+    static_for<2 * C::NB>([&](auto fc) __attribute__((always_inline)) {
+      constexpr int f = decltype(fc)::value;
+      const bf16x8 w = pf[f / 2][f % 2];
+      static_for<4>([&](auto jc) __attribute__((always_inline)) {
+        constexpr int j = decltype(jc)::value;
+        lp_run = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{w[2 * j], w[2 * j + 1]}, ones, lp_run,
+                                                 false);
+      });
+    });
+#pragma unroll
+    for (int bb = 0; bb < C::NB; ++bb) {
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        u32x4 w = __builtin_bit_cast(u32x4, pf[bb][half]);
+#pragma unroll
+        for (int q2 = 0; q2 < 2; ++q2) {
+          // registers 8*half + 4*q2 .. +3: keys kv0 + 32bb + 16half + 8q2 + 4h + 0..3
+          const uint32_t key0 = (uint32_t)(kv0 + 32 * bb + 16 * half + 8 * q2 + 4 * h);
+          const u32x4 u = philox4x32_10(u32x4{key0 >> 2, (uint32_t)qrow, (uint32_t)bh,
+                                              p.drop_offset},
+                                        p.seed_lo, p.seed_hi);
+#pragma unroll
+          for (int t2 = 0; t2 < 2; ++t2) {
+            const uint32_t lo = u[2 * t2] >= p.drop_threshold ? 0x0000FFFFu : 0u;
+            const uint32_t hi = u[2 * t2 + 1] >= p.drop_threshold ? 0xFFFF0000u : 0u;
+            w[2 * q2 + t2] &= lo | hi;
+          }
+        }
+        pf[bb][half] = __builtin_bit_cast(bf16x8, w);
+      }
+    }
+  };
+
   f32x16 s[C::NB];
   bf16x8 pf[C::NB][2];
   const uint32_t lds0 = lds_addr(lds);
@@ -535,6 +598,7 @@ void fa_fwd_bf16_kernel(FwdParams p) {
       k_issue(G0, kbase, kr[0]);
       compute_s(kbase, s, std::integral_constant<int, 1>{});
       softmax(kv0, s, pf, [] {});
+      if constexpr (DROP) dropout(kv0, pf);
       v_issue(G0, kbase + C::TILE_BYTES, vr[0]);
       pv(kbase + C::TILE_BYTES, pf, std::false_type{}, 0u);
     };
@@ -672,7 +736,7 @@ void fa_fwd_bf16_kernel(FwdParams p) {
   const float l_tot = halves_sum(l_run);
   const float lp_tot = halves_sum(lp_run);
   const bool valid = qpos < kv_lim && lp_tot > 0.f;
-  const float inv = valid ? 1.f / lp_tot : 0.f;
+  const float inv = valid ? (DROP ? p.keep_scale : 1.f) / lp_tot : 0.f;
   const float lse_row = valid ? (m_ref + __log2f(l_tot)) * kLn2 : kNegInf;
   if (qrow < N) {
     if (p.o_part) {
@@ -710,12 +774,12 @@ void fa_fwd_bf16_kernel(FwdParams p) {
   }
 }
 
-template <int D, bool CAUSAL, int WAVES, int NSTAGE, bool PINGPONG>
+template <int D, bool CAUSAL, int WAVES, int NSTAGE, bool PINGPONG, bool DROP = false>
 hipError_t launch_cfg(FwdParams p, hipStream_t stream) {
   using C = Bf16Cfg<D, WAVES, NSTAGE>;
   p.n_qtiles = (p.N + C::BQ - 1) / C::BQ;
   const dim3 grid((unsigned)((int64_t)p.n_qtiles * p.B * p.H * p.splits));
-  hipLaunchKernelGGL((fa_fwd_bf16_kernel<D, CAUSAL, WAVES, NSTAGE, PINGPONG>), grid,
+  hipLaunchKernelGGL((fa_fwd_bf16_kernel<D, CAUSAL, WAVES, NSTAGE, PINGPONG, DROP>), grid,
                      dim3(64 * WAVES), 0, stream, p);
   return hipGetLastError();
 }
@@ -726,6 +790,7 @@ hipError_t launch_d(const FwdParams& p, hipStream_t stream) {
   // the query tiles are full and there are enough workgroups to fill the
   // chip twice over; 128-row tiles (4 waves, two workgroups per CU, lockstep
   // schedule, which skips rows past the end) otherwise.
+  if (p.drop) return launch_cfg<D, CAUSAL, 4, 2, false, true>(p, stream);
   const int64_t big_tiles = (int64_t)p.B * p.H * ((p.N + 255) / 256) * p.splits;
   if (p.N >= 256 && big_tiles >= 512)
     return launch_cfg<D, CAUSAL, 8, kPingPongStages, true>(p, stream);

@@ -26,6 +26,10 @@ struct FwdParams {
   int split_keys;          // keys per range, a multiple of 128
   float* o_part;           // [splits, B, H, N, d] fp32 partial outputs, or nullptr
   float* lse_part;         // [splits, B, H, N] their log-sum-exp
+  int drop;                // dropout on the probabilities (lockstep schedule)
+  uint32_t drop_threshold; // a weight is dropped when its draw is below this
+  uint32_t seed_lo, seed_hi, drop_offset;  // Philox key and counter word 3
+  float keep_scale;        // 1 / (1 - p)
   float c;                 // |scale| * log2(e): scores enter exp2 in log2 units
   uint32_t q_sign;         // sign bits xor-ed into Q when scale < 0 (0 otherwise)
 };

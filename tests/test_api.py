@@ -33,7 +33,8 @@ def declared_functions():
 def test_header_declares_expected_entry_points():
     assert declared_functions() == sorted(
         ["fa_forward", "fa_naive_workspace_bytes", "fa_naive_forward", "fa_split_workspace_bytes",
-         "fa_forward_split", "fa_forward_varlen", "fa_backward_workspace_bytes", "fa_backward",
+         "fa_forward_split", "fa_forward_varlen", "fa_forward_dropout",
+         "fa_backward_workspace_bytes", "fa_backward",
          "fa_naive_backward",
          "fa_status_string", "fa_abi_version"])
 
@@ -43,7 +44,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     for name in declared_functions():
         assert hasattr(lib, name), name
     assert set(_lib.exported_symbols()) == set(declared_functions())
-    assert fa.fa_abi_version() == (1 << 16) | 3
+    assert fa.fa_abi_version() == (1 << 16) | 4
 
 
 def test_status_strings():
@@ -313,3 +314,22 @@ def test_varlen_bad_arguments():
 def test_varlen_empty_is_a_no_op():
     for kw in (dict(B=0), dict(H=0), dict(tq=0), dict(mq=0)):
         assert varlen_call(q=0, k=0, v=0, o=0, lse=0, cuq=0, cuk=0, **kw) == OK
+
+
+
+def test_dropout_bad_arguments():
+    def dc(**kw):
+        a = dict(q=Q, k=K, v=V, o=O, lse=L, B=1, H=2, N=64, d=64, scale=0.125, causal=0, kl=0,
+                 dtype=BF16, p=0.1, seed=1, offset=0)
+        a.update(kw)
+        return fa.fa_forward_dropout(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"],
+                                     a["N"], a["d"], a["scale"], a["causal"], a["kl"], a["dtype"],
+                                     a["p"], a["seed"], a["offset"], 0)
+    assert dc(dtype=F32) == DTYPE
+    for bad in (-0.1, 1.0, 1.5, float("nan")):
+        assert dc(p=bad) == SCALE, bad
+    assert dc(d=96) == HEAD_DIM
+    assert dc(o=0) == NULL
+    assert dc(o=Q) == ALIAS
+    assert dc(B=0, q=0, k=0, v=0, o=0, lse=0) == OK
+    assert dc(seed=2 ** 64 - 1, o=0) == NULL   # the full 64-bit seed range passes marshalling
