@@ -55,7 +55,9 @@ square problem (causal and padded) and by decode rows against scipy's
 softmax over the visible keys.  Grouped key/value heads are pinned by a
 closed form (value rows that name their head) and varlen batches by the
 padded problem with per-sequence lengths and by brute force with a key
-cache.  No function here is parity unpinned.
+cache.  The additive mask (bias) is pinned by zero and row-constant biases,
+-inf entries reproducing the causal mask, a closed form with log weights and
+brute force.  No function here is parity unpinned.
 """
 from __future__ import annotations
 
@@ -99,7 +101,7 @@ def visible_mask(rows: np.ndarray, N: int, L: int, causal: bool, pos_off: int = 
 
 
 def attention(q, k, v, scale, causal=False, key_len=None, rows=None, chunk_rows=256,
-              end_aligned=False):
+              end_aligned=False, bias=None):
     """Plain definition: O = softmax(scale * Q K^T + M) V, and per-row LSE.
 
     [P1 "Problem setting"] defines O = softmax(Q K^T / sqrt(d)) V; [P3 "Move
@@ -114,6 +116,10 @@ def attention(q, k, v, scale, causal=False, key_len=None, rows=None, chunk_rows=
     last dim).  Query row i sits at key position i, or with end_aligned at
     i + L_b - Nq, where no row is padding (see the module notes).
     rows: None (all rows), or int array [R], [H, R] or [B, H, R] of query rows.
+    bias: None, or the additive mask M of [P3 "Move less data"] as an array
+    broadcastable to [B, H, Nq, Nk], added to the scaled scores before the
+    causal and length masks; -inf entries hide a pair, and a row whose every
+    score is -inf gets O = 0, LSE = -inf.
     Returns (o [B, H, R, dv], lse [B, H, R]) with R = Nq when rows is None.
     """
     q = np.asarray(q, dtype=np.float64)
@@ -132,6 +138,8 @@ def attention(q, k, v, scale, causal=False, key_len=None, rows=None, chunk_rows=
             r = r[None, :, :]
         rows_bh = np.broadcast_to(r, (B, H, r.shape[-1]))
     R = rows_bh.shape[-1]
+    if bias is not None:
+        bias = np.broadcast_to(np.asarray(bias, dtype=np.float64), (B, H, Nq, N))
     o = np.zeros((B, H, R, dv), dtype=np.float64)
     lse = np.full((B, H, R), NEG_INF, dtype=np.float64)
     for b in range(B):
@@ -143,6 +151,9 @@ def attention(q, k, v, scale, causal=False, key_len=None, rows=None, chunk_rows=
                 # S = scale * Q K^T for whole rows (all N keys).
                 s = scale * (q[b, h, rr, :] @ k[b, h].T)
                 vis = visible_mask(rr, N, L, causal, pos_off)
+                if bias is not None:
+                    s = s + bias[b, h, rr, :]
+                    vis = vis & (s > NEG_INF)  # an additive -inf hides the pair
                 live = vis.any(axis=1)
                 # Additive mask: -inf where not visible.
                 s = np.where(vis, s, NEG_INF)

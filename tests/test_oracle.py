@@ -697,3 +697,61 @@ def test_varlen_brute_force_with_cache():
                                v[ck[b]:ck[b + 1], 0].tolist(), 0.9, causal, lk[b], end_aligned=True)
                 assert np.allclose(o[cq[b]:cq[b + 1], h], np.array(O), atol=1e-13)
                 assert np.allclose(lse[cq[b]:cq[b + 1], h], np.array(LSE), atol=1e-13)
+
+
+# ---------------------------------------------------------------------------
+# Additive mask (bias)
+# ---------------------------------------------------------------------------
+
+def test_bias_zero_and_row_constant():
+    B, H, N, d = 2, 2, 19, 5
+    q, k, v = rand((B, H, N, d), 950), rand((B, H, N, d), 951), rand((B, H, N, d), 952)
+    o0, l0 = oracle.attention(q, k, v, 0.5, causal=True)
+    o1, l1 = oracle.attention(q, k, v, 0.5, causal=True, bias=np.zeros((N, N)))
+    assert np.array_equal(o0, o1) and np.array_equal(l0, l1)
+    # a constant per row shifts the LSE and leaves O unchanged
+    c = rand((B, H, N, 1), 953)
+    o2, l2 = oracle.attention(q, k, v, 0.5, causal=True, bias=np.broadcast_to(c, (B, H, N, N)))
+    assert np.allclose(o2, o0, atol=1e-13) and np.allclose(l2, l0 + c[..., 0], atol=1e-13)
+
+
+def test_bias_minus_inf_is_a_mask():
+    """-inf above the diagonal reproduces the causal mask; a row of -inf gets 0 / -inf."""
+    B, H, N, d = 1, 2, 13, 3
+    q, k, v = rand((B, H, N, d), 960), rand((B, H, N, d), 961), rand((B, H, N, d), 962)
+    tri = np.where(np.arange(N)[None, :] <= np.arange(N)[:, None], 0.0, -np.inf)
+    oc, lc = oracle.attention(q, k, v, 0.7, causal=True)
+    ob, lb = oracle.attention(q, k, v, 0.7, bias=tri)
+    assert np.allclose(oc, ob, atol=1e-14) and np.allclose(lc, lb, atol=1e-14)
+    m = np.zeros((N, N))
+    m[4] = -np.inf
+    o, l = oracle.attention(q, k, v, 0.7, bias=m)
+    assert np.all(o[:, :, 4] == 0) and np.all(l[:, :, 4] == -np.inf)
+
+
+def test_bias_log_weights_closed_form():
+    """q = 0 and bias log w_j: O_i = sum_j w_j v_j / sum_j w_j, LSE = log sum w."""
+    B, H, N, d = 1, 1, 9, 4
+    q = np.zeros((B, H, N, d))
+    k, v = rand((B, H, N, d), 970), rand((B, H, N, d), 971)
+    w = np.random.default_rng(972).uniform(0.1, 3.0, size=(N, N))
+    o, l = oracle.attention(q, k, v, 1.0, bias=np.log(w))
+    assert np.allclose(o[0, 0], (w @ v[0, 0]) / w.sum(axis=1)[:, None], atol=1e-14)
+    assert np.allclose(l[0, 0], np.log(w.sum(axis=1)), atol=1e-14)
+
+
+def test_bias_brute_force():
+    N, d = 6, 3
+    q, k, v = rand((1, 1, N, d), 980), rand((1, 1, N, d), 981), rand((1, 1, N, d), 982)
+    m = rand((N, N), 983)
+    m[2, 3] = -np.inf
+    for causal in (False, True):
+        o, l = oracle.attention(q, k, v, 0.6, causal=causal, bias=m)
+        for i in range(N):
+            keys = [j for j in range(N) if (not causal or j <= i) and m[i, j] > -np.inf]
+            e = {j: math.exp(0.6 * math.fsum(q[0, 0, i, c] * k[0, 0, j, c] for c in range(d)) + m[i, j])
+                 for j in keys}
+            den = math.fsum(e.values())
+            ref = [math.fsum(e[j] * v[0, 0, j, c] for j in keys) / den for c in range(d)]
+            assert np.allclose(o[0, 0, i], ref, atol=1e-13)
+            assert abs(l[0, 0, i] - math.log(den)) < 1e-13
