@@ -480,6 +480,9 @@ def main() -> int:
                          "varlen_b16_h32_hkv8_n8192_d128_bf16 (packed sequences, grouped heads)")
     ap.add_argument("--n", type=int, default=0,
                     help="backward workload only: another sequence length (512 .. 4096)")
+    ap.add_argument("--bias", action="store_true",
+                    help="square workloads: time fa_forward_bias with a random fp32 [N, N] "
+                         "additive mask shared by all batches and heads")
     ap.add_argument("--dropout", type=float, default=0.0,
                     help="square workloads: time fa_forward_dropout at this rate instead")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -540,7 +543,14 @@ def main() -> int:
     compulsory = sum(3 * H * L * d * esz for L in lens) + B * H * N * d * esz + B * H * N * 4
 
     stream = torch.cuda.current_stream(dev)
-    if args.dropout > 0:
+    if args.bias:
+        bias_t = torch.randn((1, 1, N, (N + 3) // 4 * 4), device=dev, dtype=torch.float32,
+                             generator=torch.Generator(device=dev).manual_seed(7))
+
+        def fwd():
+            fa.forward_bias(q, k, v, bias_t, scale=wl.scale, causal=wl.causal, key_len=kl,
+                            out=out, lse=lse)
+    elif args.dropout > 0:
         def fwd():
             fa.forward_dropout(q, k, v, p_drop=args.dropout, seed=2024, offset=0, scale=wl.scale,
                                causal=wl.causal, key_len=kl, out=out, lse=lse)
@@ -578,21 +588,22 @@ def main() -> int:
         "data": "synthetic",
         "config": dict(wl.describe(), useful_flops=flops, compulsory_hbm_bytes=compulsory,
                        parallelism="single GPU",
-                       **({"dropout": args.dropout} if args.dropout > 0 else {})),
+                       **({"dropout": args.dropout} if args.dropout > 0 else {}),
+                       **({"bias": "fp32 [N, N] shared"} if args.bias else {})),
         "roofline": {
             "bound": "mfma",
             "achieved": tflops,
             "peak": peak,
             "unit": "TFLOP/s",
             "frac": tflops / peak,
-            "traffic": stored_traffic(wl.name) if args.dropout == 0 else None,
+            "traffic": stored_traffic(wl.name) if args.dropout == 0 and not args.bias else None,
             "kernel": "fa_fwd_bf16_kernel" if wl.dtype == "bf16" else "fa_fwd_f32_kernel",
             "kernel_hash": kernel_hash(),
         },
         "wall_s_timed_region": t_wall,
     }
 
-    if not args.no_naive and args.dropout == 0:
+    if not args.no_naive and args.dropout == 0 and not args.bias:
         need = fa.fa_naive_workspace_bytes(B, H, N, fa.FA_DTYPE_BF16 if wl.dtype == "bf16" else fa.FA_DTYPE_F32)
         free = torch.cuda.mem_get_info(dev)[0]
         if need < 0.8 * free:
@@ -613,7 +624,7 @@ def main() -> int:
             del ws
             torch.cuda.empty_cache()
 
-    if not args.no_cpu_baseline and args.dropout == 0:
+    if not args.no_cpu_baseline and args.dropout == 0 and not args.bias:
         o_host = out
         if wl.dtype == "bf16":
             o_np = W.bf16_decode(o_host.view(torch.int16).cpu().numpy().view(np.uint16))

@@ -266,13 +266,34 @@ int fa_forward_dropout(const void* q, const void* k, const void* v, void* o, flo
                        const int32_t* key_len_mask, int dtype, float p_drop, uint64_t seed,
                        uint32_t offset, void* stream);
 
+/*
+ * fa_forward with a general additive mask M ("FlashAttention" glossary,
+ * section "Move less data": O = softmax(Q K^T / sqrt(d) + M) V):
+ * s_ij = scale * q_i . k_j + M_bhij, then the causal and length masks of
+ * fa_forward.  M may hold -inf (the pair is hidden); a row whose every score
+ * is -inf gets O = 0, LSE = -inf.
+ *   bias         device fp32, element (b, h, i, j) at
+ *                bias[b * bias_stride_b + h * bias_stride_h + i * bias_ld + j];
+ *                a stride of 0 broadcasts over batch or heads.  16-byte aligned;
+ *                bias_ld >= N; bias_ld and both strides multiples of 4 (pad the
+ *                rows); FA_ERR_SHAPE otherwise.
+ *   dtype        FA_DTYPE_BF16 only.
+ * Reading M costs 4 * N * N bytes per (batch, head) it does not broadcast
+ * over, on top of the IO-aware traffic.  Other arguments and conventions
+ * are those of fa_forward.
+ */
+int fa_forward_bias(const void* q, const void* k, const void* v, void* o, float* lse,
+                    const float* bias, int B, int H, int N, int d, float scale, int causal,
+                    const int32_t* key_len_mask, int dtype, int64_t bias_stride_b,
+                    int64_t bias_stride_h, int64_t bias_ld, void* stream);
+
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* fa_status_string(int status);
 
 /* ABI version of this header: (major << 16) | minor. */
 int fa_abi_version(void);
 
-#define FA_ABI_VERSION ((1 << 16) | 4)
+#define FA_ABI_VERSION ((1 << 16) | 5)
 
 #ifdef __cplusplus
 }

@@ -22,6 +22,7 @@ from ._lib import (  # noqa: F401
     fa_forward_split,
     fa_forward_varlen,
     fa_forward_dropout,
+    fa_forward_bias,
     fa_naive_backward,
     fa_naive_forward,
     fa_naive_workspace_bytes,
@@ -34,6 +35,7 @@ __all__ = [
     "forward", "forward_split", "backward", "naive_forward", "fa_forward", "fa_forward_split",
     "fa_backward", "fa_backward_workspace_bytes", "fa_naive_backward", "naive_backward",
     "fa_forward_varlen", "forward_varlen", "fa_forward_dropout", "forward_dropout",
+    "fa_forward_bias", "forward_bias",
     "fa_split_workspace_bytes", "fa_naive_forward", "fa_naive_workspace_bytes",
     "fa_status_string", "fa_abi_version", "FAError", "FA_DTYPE_BF16", "FA_DTYPE_F32",
 ]
@@ -240,4 +242,40 @@ def forward_dropout(q, k, v, *, p_drop, seed, offset=0, scale=None, causal=False
     check(fa_forward_dropout(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                              lse.data_ptr(), B, H, N, d, float(scale), int(bool(causal)), kl,
                              _dtype_code(q), float(p_drop), int(seed), int(offset), stream))
+    return out, lse
+
+
+def forward_bias(q, k, v, bias, *, scale=None, causal=False, key_len=None, out=None, lse=None):
+    """O, LSE = fa_forward_bias(...): bias is a device float32 tensor whose last
+    two dims are [N, ld >= N] (ld a multiple of 4), with batch and head dims of
+    size B or 1 and H or 1 (size 1 broadcasts: stride 0)."""
+    import torch
+    if q.dim() != 4 or q.shape != k.shape or q.shape != v.shape:
+        raise FAError(-2, "q, k, v must share one [B, H, N, d] shape")
+    for t in (q, k, v):
+        if not t.is_cuda or not t.is_contiguous():
+            raise FAError(-1, "q, k, v must be contiguous device tensors")
+    B, H, N, d = q.shape
+    if bias.dtype != torch.float32 or not bias.is_cuda or bias.dim() != 4 or \
+            bias.shape[2] != N or bias.shape[0] not in (1, B) or bias.shape[1] not in (1, H) or \
+            bias.stride(3) != 1:
+        raise FAError(-2, "bias must be a device float32 [B|1, H|1, N, ld] tensor, unit column stride")
+    sb = bias.stride(0) if bias.shape[0] == B and B > 1 else 0
+    sh = bias.stride(1) if bias.shape[1] == H and H > 1 else 0
+    ld = bias.stride(2)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    kl = 0
+    if key_len is not None:
+        if key_len.dtype != torch.int32 or not key_len.is_cuda or key_len.numel() != B:
+            raise FAError(-1, "key_len must be a device int32 tensor of B elements")
+        kl = key_len.data_ptr()
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    check(fa_forward_bias(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                          bias.data_ptr(), B, H, N, d, float(scale), int(bool(causal)), kl,
+                          _dtype_code(q), sb, sh, ld, stream))
     return out, lse

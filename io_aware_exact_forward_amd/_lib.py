@@ -61,6 +61,11 @@ _SIGNATURES = {
         ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float, ctypes.c_int,
         ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_uint64, ctypes.c_uint32,
         ctypes.c_void_p]),
+    "fa_forward_bias": (ctypes.c_int, [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float,
+        ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
+        ctypes.c_int64, ctypes.c_void_p]),
     "fa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "fa_abi_version": (ctypes.c_int, []),
 }
@@ -171,6 +176,13 @@ def fa_forward_dropout(q, k, v, o, lse, B, H, N, d, scale, causal, key_len_mask,
     return load().fa_forward_dropout(q or None, k or None, v or None, o or None, lse or None, B, H,
                                      N, d, scale, int(causal), key_len_mask or None, dtype,
                                      p_drop, seed, offset, stream or None)
+
+
+def fa_forward_bias(q, k, v, o, lse, bias, B, H, N, d, scale, causal, key_len_mask, dtype, sb,
+                    sh, ld, stream) -> int:
+    return load().fa_forward_bias(q or None, k or None, v or None, o or None, lse or None,
+                                  bias or None, B, H, N, d, scale, int(causal),
+                                  key_len_mask or None, dtype, sb, sh, ld, stream or None)
 
 
 def fa_status_string(status) -> str:

@@ -572,6 +572,41 @@ extern "C" int fa_forward_dropout(const void* q, const void* k, const void* v, v
   return FA_OK;
 }
 
+extern "C" int fa_forward_bias(const void* q, const void* k, const void* v, void* o, float* lse,
+                               const float* bias, int B, int H, int N, int d, float scale,
+                               int causal, const int32_t* key_len_mask, int dtype,
+                               int64_t bias_stride_b, int64_t bias_stride_h, int64_t bias_ld,
+                               void* stream) {
+  if (dtype != FA_DTYPE_BF16) return FA_ERR_DTYPE;
+  Shape s;
+  bool empty = false;
+  int st = check_scalars(B, H, N, d, scale, dtype, &s, &empty);
+  if (st != FA_OK || empty) return st;
+  if (bias_stride_b < 0 || bias_stride_h < 0 || bias_ld < N || bias_ld % 4 != 0 ||
+      bias_stride_b % 4 != 0 || bias_stride_h % 4 != 0)
+    return FA_ERR_SHAPE;
+  // extent of the bias in elements (the largest offset read, plus one)
+  const double ext_d = double(B - 1) * double(bias_stride_b) + double(H - 1) * double(bias_stride_h) +
+                       double(N - 1) * double(bias_ld) + double(N);
+  if (ext_d > double(int64_t(1) << 60)) return FA_ERR_SHAPE;
+  const int64_t ext = int64_t(B - 1) * bias_stride_b + int64_t(H - 1) * bias_stride_h +
+                      int64_t(N - 1) * bias_ld + N;
+  st = check_pointers(q, k, v, o, lse, key_len_mask, B, s);
+  if (st != FA_OK) return st;
+  if (!bias) return FA_ERR_NULL;
+  if (!is_aligned(bias, 16)) return FA_ERR_ALIGN;
+  if (overlaps(o, s.elems * s.esz, bias, ext * 4) || overlaps(lse, s.rows * 4, bias, ext * 4))
+    return FA_ERR_ALIAS;
+  fa::FwdParams p = make_params(q, k, v, o, lse, B, H, N, scale, key_len_mask, dtype);
+  p.bias = bias;
+  p.bias_sb = bias_stride_b;
+  p.bias_sh = bias_stride_h;
+  p.bias_ld = bias_ld;
+  if (fa::launch_fwd_bf16(p, d, causal != 0, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return FA_ERR_HIP;
+  return FA_OK;
+}
+
 extern "C" const char* fa_status_string(int status) {
   switch (status) {
     case FA_OK: return "ok";

@@ -98,10 +98,14 @@ __device__ __forceinline__ u32x4 philox4x32_10(u32x4 c, uint32_t k0, uint32_t k1
   return c;
 }
 
-template <int D, bool CAUSAL, int WAVES, int NSTAGE, bool PINGPONG, bool DROP = false>
-__global__ __launch_bounds__(64 * WAVES, (WAVES == 4 && NSTAGE == 2) ? 2 : 1)
+template <int D, bool CAUSAL, int WAVES, int NSTAGE, bool PINGPONG, bool DROP = false,
+          bool BIAS = false>
+// Two lockstep workgroups per CU (256 registers per lane), except with an
+// additive mask at d = 64, whose extra registers do not fit: one workgroup.
+__global__ __launch_bounds__(64 * WAVES,
+                             (WAVES == 4 && NSTAGE == 2 && !(BIAS && D == 64)) ? 2 : 1)
 void fa_fwd_bf16_kernel(FwdParams p) {
-  static_assert(!DROP || !PINGPONG, "dropout runs in the lockstep schedule");
+  static_assert(!(DROP || BIAS) || !PINGPONG, "dropout and bias run in the lockstep schedule");
   using C = Bf16Cfg<D, WAVES, NSTAGE>;
   __shared__ __attribute__((aligned(1024))) uint8_t lds[C::LDS_BYTES];
 
@@ -235,7 +239,9 @@ void fa_fwd_bf16_kernel(FwdParams p) {
   float m_ref = kNegInf;  // reference maximum of scale*log2(e)*s
   float l_run = 0.f;      // this lane's part of the fp32 denominator
   float lp_run = 0.f;     // the same over the bf16-rounded probabilities
-  const float c = p.c;
+  // With an additive mask the scores are taken to log2 units (and the mask
+  // added) before the softmax step, which then works with a unit scale.
+  const float c = BIAS ? 1.f : p.c;
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
   // Waves whose rows see no key of the tile at kv0 skip it (wave-uniform).
@@ -347,10 +353,52 @@ void fa_fwd_bf16_kernel(FwdParams p) {
   // the exponentials.  The reference therefore moves only when some weight
   // would exceed the bound, and the row maximum costs nothing on the
   // common path.
+  // Additive mask (fp32, row-major with row stride bias_ld): the lane's row,
+  // keys kv0 + 32*bb + 8*q4 + 4*h + 0..3 as one 16-byte load per (bb, q4).
+  // With two 32-key blocks per tile the loads are issued before the first
+  // product of the tile; with four (d = 64) the registers are not there, and
+  // each block's values are loaded just before they are added.
+  constexpr bool kBiasAhead = C::NB <= 2;
+  f32x4 bias_r[BIAS && kBiasAhead ? C::NB : 1][4];
+  const float* bias_row = BIAS && qrow < N
+                              ? p.bias + (int64_t)b * p.bias_sb + (int64_t)hq * p.bias_sh +
+                                    (int64_t)qrow * p.bias_ld
+                              : nullptr;
+  auto bias_load = [&](const int kv0, const int bb, f32x4 (&dst)[4]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int key0 = kv0 + 32 * bb + 8 * q4 + 4 * h;
+      f32x4 x = {0.f, 0.f, 0.f, 0.f};
+      if (bias_row && key0 < kv_lim) x = *(const f32x4*)(bias_row + key0);
+      dst[q4] = x;
+    }
+  };
+  auto bias_issue = [&](const int kv0) __attribute__((always_inline)) {
+    if constexpr (BIAS && kBiasAhead) {
+#pragma unroll
+      for (int bb = 0; bb < C::NB; ++bb) bias_load(kv0, bb, bias_r[bb]);
+    }
+  };
+
   auto softmax = [&](const int kv0, f32x16 (&s)[C::NB], bf16x8 (&pf)[C::NB][2], auto&& mid)
       __attribute__((always_inline)) {
     // Element masks only where the tile crosses the diagonal or the
     // sequence end (wave-uniform test).
+    if constexpr (BIAS) {
+#pragma unroll
+      for (int bb = 0; bb < C::NB; ++bb) {
+        f32x4 x[4];
+        if constexpr (kBiasAhead) {
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) x[q4] = bias_r[bb][q4];
+        } else {
+          bias_load(kv0, bb, x);
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          s[bb][r] = __builtin_fmaf(s[bb][r], p.c, x[r >> 2][r & 3] * kLog2e);
+      }
+    }
     const bool masked = (CAUSAL && kv0 + C::BK - 1 > qwpos) || (kv0 + C::BK > kv_lim);
     if (masked) {
 #pragma unroll
@@ -596,6 +644,7 @@ void fa_fwd_bf16_kernel(FwdParams p) {
       uint32_t kbase = lds0 + S * C::STAGE_BYTES;
       asm volatile("" : "+s"(kbase));  // see the ping-pong schedule
       k_issue(G0, kbase, kr[0]);
+      if constexpr (BIAS) bias_issue(kv0);
       compute_s(kbase, s, std::integral_constant<int, 1>{});
       softmax(kv0, s, pf, [] {});
       if constexpr (DROP) dropout(kv0, pf);
@@ -774,12 +823,13 @@ void fa_fwd_bf16_kernel(FwdParams p) {
   }
 }
 
-template <int D, bool CAUSAL, int WAVES, int NSTAGE, bool PINGPONG, bool DROP = false>
+template <int D, bool CAUSAL, int WAVES, int NSTAGE, bool PINGPONG, bool DROP = false,
+          bool BIAS = false>
 hipError_t launch_cfg(FwdParams p, hipStream_t stream) {
   using C = Bf16Cfg<D, WAVES, NSTAGE>;
   p.n_qtiles = (p.N + C::BQ - 1) / C::BQ;
   const dim3 grid((unsigned)((int64_t)p.n_qtiles * p.B * p.H * p.splits));
-  hipLaunchKernelGGL((fa_fwd_bf16_kernel<D, CAUSAL, WAVES, NSTAGE, PINGPONG, DROP>), grid,
+  hipLaunchKernelGGL((fa_fwd_bf16_kernel<D, CAUSAL, WAVES, NSTAGE, PINGPONG, DROP, BIAS>), grid,
                      dim3(64 * WAVES), 0, stream, p);
   return hipGetLastError();
 }
@@ -791,6 +841,7 @@ hipError_t launch_d(const FwdParams& p, hipStream_t stream) {
   // chip twice over; 128-row tiles (4 waves, two workgroups per CU, lockstep
   // schedule, which skips rows past the end) otherwise.
   if (p.drop) return launch_cfg<D, CAUSAL, 4, 2, false, true>(p, stream);
+  if (p.bias) return launch_cfg<D, CAUSAL, 4, 2, false, false, true>(p, stream);
   const int64_t big_tiles = (int64_t)p.B * p.H * ((p.N + 255) / 256) * p.splits;
   if (p.N >= 256 && big_tiles >= 512)
     return launch_cfg<D, CAUSAL, 8, kPingPongStages, true>(p, stream);

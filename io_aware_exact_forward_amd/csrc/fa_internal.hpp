@@ -26,6 +26,8 @@ struct FwdParams {
   int split_keys;          // keys per range, a multiple of 128
   float* o_part;           // [splits, B, H, N, d] fp32 partial outputs, or nullptr
   float* lse_part;         // [splits, B, H, N] their log-sum-exp
+  const float* bias;       // additive mask, fp32, or nullptr (lockstep schedule)
+  int64_t bias_sb, bias_sh, bias_ld;  // its batch, head and row strides (elements)
   int drop;                // dropout on the probabilities (lockstep schedule)
   uint32_t drop_threshold; // a weight is dropped when its draw is below this
   uint32_t seed_lo, seed_hi, drop_offset;  // Philox key and counter word 3

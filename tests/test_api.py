@@ -33,7 +33,7 @@ def declared_functions():
 def test_header_declares_expected_entry_points():
     assert declared_functions() == sorted(
         ["fa_forward", "fa_naive_workspace_bytes", "fa_naive_forward", "fa_split_workspace_bytes",
-         "fa_forward_split", "fa_forward_varlen", "fa_forward_dropout",
+         "fa_forward_split", "fa_forward_varlen", "fa_forward_dropout", "fa_forward_bias",
          "fa_backward_workspace_bytes", "fa_backward",
          "fa_naive_backward",
          "fa_status_string", "fa_abi_version"])
@@ -44,7 +44,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     for name in declared_functions():
         assert hasattr(lib, name), name
     assert set(_lib.exported_symbols()) == set(declared_functions())
-    assert fa.fa_abi_version() == (1 << 16) | 4
+    assert fa.fa_abi_version() == (1 << 16) | 5
 
 
 def test_status_strings():
@@ -333,3 +333,25 @@ def test_dropout_bad_arguments():
     assert dc(o=Q) == ALIAS
     assert dc(B=0, q=0, k=0, v=0, o=0, lse=0) == OK
     assert dc(seed=2 ** 64 - 1, o=0) == NULL   # the full 64-bit seed range passes marshalling
+
+
+
+BI = A + 20 * (1 << 34)
+
+
+def test_bias_bad_arguments():
+    def bc(**kw):
+        a = dict(q=Q, k=K, v=V, o=O, lse=L, bias=BI, B=2, H=2, N=64, d=64, scale=0.125, causal=0,
+                 kl=0, dtype=BF16, sb=2 * 64 * 64, sh=64 * 64, ld=64)
+        a.update(kw)
+        return fa.fa_forward_bias(a["q"], a["k"], a["v"], a["o"], a["lse"], a["bias"], a["B"],
+                                  a["H"], a["N"], a["d"], a["scale"], a["causal"], a["kl"],
+                                  a["dtype"], a["sb"], a["sh"], a["ld"], 0)
+    assert bc(dtype=F32) == DTYPE
+    for bad in (dict(ld=60), dict(ld=66), dict(sb=-4), dict(sh=2), dict(sb=6)):
+        assert bc(**bad) == SHAPE, bad
+    assert bc(bias=0) == NULL
+    assert bc(bias=BI + 4) == ALIGN
+    assert bc(o=BI) == ALIAS
+    assert bc(lse=BI + 2 * 64 * 64 * 4) == ALIAS
+    assert bc(B=0, q=0, k=0, v=0, o=0, lse=0, bias=0) == OK
