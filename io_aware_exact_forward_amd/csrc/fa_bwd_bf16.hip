@@ -203,21 +203,32 @@ __global__ __launch_bounds__(256, 2) void fa_bwd_dq_kernel(BwdParams p) {
         dp[bb] = mfma_32x32x16_bf16(lds_b128(vt, toff_p<D>(kr, 2 * kk + h)), dof[kk], dp[bb]);
       }
     }
-    // P^T and dS^T: lane = query row, register r of block bb = key 32bb + acc_row(r, h)
+    // P^T and dS^T: lane = query row, register r of block bb = key 32bb + acc_row(r, h).
+    // Element masks only where the tile crosses the diagonal or a length
+    // (wave-uniform test).
     bf16x8 dsb[NB][2];
+    const bool full = (!CAUSAL || kv0 + BK - 1 <= qw0) && kv0 + BK <= L && qw0 + 31 < L;
+    auto grads = [&](auto masked_tag) __attribute__((always_inline)) {
+      constexpr bool masked = decltype(masked_tag)::value;
 #pragma unroll
-    for (int bb = 0; bb < NB; ++bb) {
-      float ds[16];
+      for (int bb = 0; bb < NB; ++bb) {
+        float ds[16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = kv0 + 32 * bb + acc_row(r, h);
-        const bool vis = row_ok && key < L && (!CAUSAL || key <= row);
-        const float pr = vis ? fast_exp2(__builtin_fmaf(s[bb][r], p.c2, -lse2)) : 0.f;
-        ds[r] = pr * (dp[bb][r] - dval);
+        for (int r = 0; r < 16; ++r) {
+          float pr = fast_exp2(__builtin_fmaf(s[bb][r], p.c2, -lse2));
+          if constexpr (masked) {
+            const int key = kv0 + 32 * bb + acc_row(r, h);
+            const bool vis = row_ok && key < L && (!CAUSAL || key <= row);
+            pr = vis ? pr : 0.f;
+          }
+          ds[r] = pr * (dp[bb][r] - dval);
+        }
+        dsb[bb][0] = pack8(ds);
+        dsb[bb][1] = pack8(ds + 8);
       }
-      dsb[bb][0] = pack8(ds);
-      dsb[bb][1] = pack8(ds + 8);
-    }
+    };
+    if (full) grads(std::false_type{});
+    else grads(std::true_type{});
     // dQ^T += K^T dS^T
 #pragma unroll
     for (int db = 0; db < C::ND; ++db)
@@ -367,20 +378,31 @@ __global__ __launch_bounds__(256, 2) void fa_bwd_dkdv_kernel(BwdParams p) {
       }
       // lane = key, register r = row 32qb + acc_row(r, h)
       float pr[16], ds[16];
+      auto probs = [&](auto masked_tag) __attribute__((always_inline)) {
+        constexpr bool masked = decltype(masked_tag)::value;
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int r0 = 32 * qb + 8 * q4 + 4 * h;  // four consecutive rows
-        const f32x4 l4 = *(const f32x4*)(lse2 + r0);
-        const f32x4 d4 = *(const f32x4*)(dd + r0);
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int r0 = 32 * qb + 8 * q4 + 4 * h;  // four consecutive rows
+          const f32x4 l4 = *(const f32x4*)(lse2 + r0);
+          const f32x4 d4 = *(const f32x4*)(dd + r0);
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const int r = 4 * q4 + t;
-          const int qrow = q0 + r0 + t;
-          const bool vis = key_ok && qrow < L && (!CAUSAL || key <= qrow);
-          pr[r] = vis ? fast_exp2(__builtin_fmaf(s[r], p.c2, -l4[t])) : 0.f;
-          ds[r] = pr[r] * (dp[r] - d4[t]);
+          for (int t = 0; t < 4; ++t) {
+            const int r = 4 * q4 + t;
+            float e = fast_exp2(__builtin_fmaf(s[r], p.c2, -l4[t]));
+            if constexpr (masked) {
+              const int qrow = q0 + r0 + t;
+              const bool vis = key_ok && qrow < L && (!CAUSAL || key <= qrow);
+              e = vis ? e : 0.f;
+            }
+            pr[r] = e;
+            ds[r] = e * (dp[r] - d4[t]);
+          }
         }
-      }
+      };
+      // masks only where the block crosses the diagonal or a length (wave-uniform)
+      const int qb0 = q0 + 32 * qb;
+      if ((!CAUSAL || kw0 + 31 <= qb0) && qb0 + 31 < L && kw0 + 31 < L) probs(std::false_type{});
+      else probs(std::true_type{});
       pb[qb][0] = pack8(pr);
       pb[qb][1] = pack8(pr + 8);
       dsb[qb][0] = pack8(ds);

@@ -317,7 +317,9 @@ void fa_fwd_bf16_kernel(FwdParams p) {
   // taken in the second product's step).
   auto exp_pack = [&](f32x16 (&s)[C::NB], bf16x8 (&pf)[C::NB][2], const float neg_m)
       __attribute__((always_inline)) {
-    float part[4] = {0.f, 0.f, 0.f, 0.f};
+    // -0 is the identity of fp32 addition (0 is not, for -0 operands), so the
+    // compiler drops the first addition of each chain
+    float part[4] = {-0.f, -0.f, -0.f, -0.f};
 #pragma unroll
     for (int bb = 0; bb < C::NB; ++bb) {
 #pragma unroll
