@@ -119,13 +119,22 @@ void fa_fwd_bf16_kernel(FwdParams p) {
 
   // ---- tile assignment ----------------------------------------------------
   // Workgroup = (key range, (batch, head), query tile); consecutive ids
-  // take consecutive key ranges, then cycle over (batch, head).
+  // take consecutive key ranges, then cycle over a chunk of at most 32
+  // (batch, head) pairs, then over the query tiles, then over the chunks.
+  // Within a chunk all the query tiles of a head run close together, so its
+  // K/V rows are reused from L2; with 32 pairs per chunk every head's tiles
+  // land on one XCD (workgroups are dealt round-robin to the 8 XCDs).
   const int BH = p.B * p.H;
   int x = blockIdx.x;
   const int split = x % p.splits;
   x /= p.splits;
-  const int bh = x % BH;
-  int qt = x / BH;
+  constexpr int kChunk = 32;
+  const int chunk_wgs = kChunk * p.n_qtiles;
+  const int chunk = x / chunk_wgs;
+  const int in_chunk = x - chunk * chunk_wgs;
+  const int chunk_heads = min(kChunk, BH - chunk * kChunk);
+  const int bh = chunk * kChunk + in_chunk % chunk_heads;
+  int qt = in_chunk / chunk_heads;
   if (CAUSAL) qt = p.n_qtiles - 1 - qt;  // heaviest tiles first
   const int b = bh / p.H;
   const int hq = bh - b * p.H;
