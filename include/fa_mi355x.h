@@ -218,7 +218,7 @@ int fa_forward_varlen(const void* q, const void* k, const void* v, void* o, floa
  *                written by fa_forward with the same scale, causal and key_len_mask.
  *   Masks        those of fa_forward; padding rows and keys at or beyond L_b get
  *                zero gradients (their dO and lse entries are not read).
- *   dtype        FA_DTYPE_BF16 only; d = 64 only (FA_ERR_HEAD_DIM otherwise).
+ *   dtype        FA_DTYPE_BF16 only; d = 64 or 128 (FA_ERR_HEAD_DIM otherwise).
  *   workspace    device memory, 256-byte aligned, of at least
  *                fa_backward_workspace_bytes(B, H, N, d, dtype) bytes (fp32 D,
  *                [B, H, N]); it and dq, dk, dv overlap no input and no other output.

@@ -347,7 +347,7 @@ extern "C" int fa_forward_split(const void* q, const void* k, const void* v, voi
 extern "C" size_t fa_backward_workspace_bytes(int B, int H, int N, int d, int dtype) {
   Shape s;
   bool empty = false;
-  if (dtype != FA_DTYPE_BF16 || d != 64) return 0;
+  if (dtype != FA_DTYPE_BF16 || (d != 64 && d != 128)) return 0;
   if (check_scalars(B, H, N, d, 1.f, dtype, &s, &empty) != FA_OK || empty) return 0;
   return round256(size_t(s.rows) * sizeof(float));
 }
@@ -358,7 +358,7 @@ extern "C" int fa_backward(const void* q, const void* k, const void* v, const vo
                            const int32_t* key_len_mask, int dtype, void* workspace,
                            size_t workspace_bytes, void* stream) {
   if (dtype != FA_DTYPE_BF16) return FA_ERR_DTYPE;
-  if (d != 64) return FA_ERR_HEAD_DIM;
+  if (d != 64 && d != 128) return FA_ERR_HEAD_DIM;
   Shape s;
   bool empty = false;
   int st = check_scalars(B, H, N, d, scale, dtype, &s, &empty);

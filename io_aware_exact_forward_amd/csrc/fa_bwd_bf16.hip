@@ -101,8 +101,13 @@ __device__ __forceinline__ int seq_len(const BwdParams& p, int b) {
 // ---------------------------------------------------------------------------
 // dQ (and D): one workgroup per 128 query rows of one (batch, head)
 // ---------------------------------------------------------------------------
+// Workgroups per CU: two at d = 64; at d = 128 the accumulators of one
+// workgroup take the registers of two.
+template <int D>
+constexpr int kBwdOccupancy = D == 64 ? 2 : 1;
+
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 2) void fa_bwd_dq_kernel(BwdParams p) {
+__global__ __launch_bounds__(256, kBwdOccupancy<D>) void fa_bwd_dq_kernel(BwdParams p) {
   using C = BwdCfg<D>;
   constexpr int BQ = 128, BK = 64, NB = BK / 32;
   constexpr int TILE = BK * C::ROW_BYTES;
@@ -272,9 +277,10 @@ __global__ __launch_bounds__(256, 2) void fa_bwd_dq_kernel(BwdParams p) {
 // dK, dV: one workgroup per 128 keys of one (batch, head)
 // ---------------------------------------------------------------------------
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 2) void fa_bwd_dkdv_kernel(BwdParams p) {
+__global__ __launch_bounds__(256, kBwdOccupancy<D>) void fa_bwd_dkdv_kernel(BwdParams p) {
   using C = BwdCfg<D>;
-  constexpr int BKW = 128, BQ = 64, NQB = BQ / 32;
+  // 64-row query tiles at d = 64, 32-row tiles at d = 128 (registers)
+  constexpr int BKW = 128, BQ = D == 64 ? 64 : 32, NQB = BQ / 32;
   constexpr int TILE = BQ * C::ROW_BYTES;
   constexpr int LPT = BQ * C::CPR / 256;
   // [stage][Q tile | dO tile | LSE2 (BQ floats) | D (BQ floats)]
@@ -468,6 +474,7 @@ hipError_t launch_bwd(const BwdParams& p, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_bwd_bf16(const BwdParams& p, int d, bool causal, hipStream_t stream) {
+  if (d == 128) return causal ? launch_bwd<128, true>(p, stream) : launch_bwd<128, false>(p, stream);
   if (d != 64) return hipErrorInvalidValue;
   return causal ? launch_bwd<64, true>(p, stream) : launch_bwd<64, false>(p, stream);
 }

@@ -235,13 +235,15 @@ def test_backward_workspace_size():
     assert fa.fa_backward_workspace_bytes(2, 16, 4096, 64, BF16) == 2 * 16 * 4096 * 4
     assert fa.fa_backward_workspace_bytes(1, 1, 3, 64, BF16) == 256
     assert fa.fa_backward_workspace_bytes(1, 1, 3, 64, F32) == 0
-    assert fa.fa_backward_workspace_bytes(1, 1, 3, 128, BF16) == 0
+    assert fa.fa_backward_workspace_bytes(1, 1, 3, 128, BF16) == 256
+    assert fa.fa_backward_workspace_bytes(1, 1, 3, 96, BF16) == 0
     assert fa.fa_backward_workspace_bytes(0, 1, 3, 64, BF16) == 0
 
 
 def test_backward_bad_arguments():
     assert bwd_call(dtype=F32) == DTYPE
-    assert bwd_call(d=128) == HEAD_DIM
+    assert bwd_call(d=96) == HEAD_DIM
+    assert bwd_call(d=32) == HEAD_DIM
     assert bwd_call(N=-1) == SHAPE
     assert bwd_call(scale=float("nan")) == SCALE
     for field in ("q", "k", "v", "o", "lse", "do", "dq", "dk", "dv"):

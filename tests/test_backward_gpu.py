@@ -167,3 +167,28 @@ def test_stored_state_backward_against_oracle():
                 assert err.max() <= 6e-2 * np.abs(r).max(), (name, stats[name])
                 assert err.mean() <= 3e-2 * np.abs(r).mean(), (name, stats[name])
             say("stored-state", B, H, N, causal, stats)
+
+
+D128_CASES = [
+    # (B, H, N, key_len, seed)
+    (1, 2, 300, None, 9801),
+    (2, 2, 513, [513, 130], 9802),
+    (1, 1, 33, None, 9803),
+]
+
+
+@pytest.mark.parametrize("case", D128_CASES, ids=lambda c: f"b{c[0]}h{c[1]}n{c[2]}")
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_d128_against_oracle(case, causal):
+    B, H, N, key_len, seed = case
+    scale = 1.0 / np.sqrt(128)
+    inp, do = W.grad_inputs(B, H, N, 128, seed, key_len=key_len)
+    got = run(inp, do, causal, scale)
+    check(inp, do, causal, scale, got, f"d128 {case} causal={causal}")
+
+
+def test_backward_d128_mid_size():
+    """32 heads at N = 2048, d = 128, causal: every element of two heads."""
+    inp, do = W.grad_inputs(1, 32, 2048, 128, 9804)
+    got = run(inp, do, True, 1 / np.sqrt(128))
+    check(inp, do, True, 1 / np.sqrt(128), got, "d128 h32 n2048", heads=[0, 31])
