@@ -232,6 +232,56 @@ int fa_backward(const void* q, const void* k, const void* v, const void* o, cons
                 void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Backward of fa_forward_split's result (grouped key/value heads, query rows
+ * at the end of each sequence's keys), by the recomputation of fa_backward
+ * ("IO-aware exact attention", section "Backward recomputation"; grouped
+ * heads are among the variants of section "Why implementations form a
+ * family").
+ *   q, o, dout, dq  [B, H, Nq, d]; k, v, dk, dv [B, Hkv, Nk, d]; lse [B, H, Nq]
+ *                fp32 as written by fa_forward_split with the same scale,
+ *                causal and key_len_mask.  H % Hkv == 0; query head h reads
+ *                key/value head h / (H / Hkv), and dk, dv of a key/value head
+ *                are the sums over the H / Hkv query heads that read it.
+ *   Positions    as fa_forward_split: row i of sequence b at key position
+ *                i + L_b - Nq, L_b = clamp(key_len_mask[b], 0, Nk) (Nk without
+ *                a mask).  Keys at or beyond L_b, and rows that see no key,
+ *                get zero gradients.
+ *   workspace    256-byte aligned, fa_backward_workspace_bytes(B, H, Nq, d,
+ *                dtype) bytes (fp32 D in the layout of lse); may be NULL when
+ *                B * H * Nq == 0.
+ *   Empty cases  Nq == 0 or H == 0 writes dk = dv = 0; Nk == 0 writes dq = 0
+ *                (k, v, dk, dv may then be NULL).
+ * bf16 only, d = 64 or 128.  Validation, alignment, aliasing and error
+ * conventions are those of fa_backward.
+ */
+int fa_backward_gqa(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                    const void* dout, void* dq, void* dk, void* dv, int B, int H, int Hkv, int Nq,
+                    int Nk, int d, float scale, int causal, const int32_t* key_len_mask, int dtype,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Backward of fa_forward_varlen's result: packed batches, grouped heads.
+ *   q, o, dout, dq  [total_q, H, d]; k, v, dk, dv [total_k, Hkv, d]; lse
+ *                [total_q, H] fp32 as written by fa_forward_varlen with the
+ *                same arguments; cu_seqlens_q / cu_seqlens_k as there (device
+ *                [B + 1], non-decreasing from 0 to the totals, each length at
+ *                most max_seqlen_q / max_seqlen_k: not checked on the host).
+ *   Positions    row i of sequence b at key position i + Lk_b - Lq_b.
+ *   workspace    256-byte aligned, fa_backward_workspace_bytes(1, H, total_q,
+ *                d, dtype) bytes (fp32 D in the layout of lse); may be NULL
+ *                when H * total_q == 0.
+ *   Empty cases  a sequence without queries gets dk = dv = 0 for its keys; one
+ *                without keys gets dq = 0.
+ * bf16 only, d = 64 or 128.  Other conventions as fa_backward.
+ */
+int fa_backward_varlen(const void* q, const void* k, const void* v, const void* o,
+                       const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                       const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int B, int H,
+                       int Hkv, int total_q, int total_k, int max_seqlen_q, int max_seqlen_k,
+                       int d, float scale, int causal, int dtype, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
+/*
  * Stored-state backward: the same gradients as fa_backward, computed the
  * conventional way with the N x N matrices in HBM (S and then P in the first
  * half of the workspace, dP and then dS in the second), by five rocBLAS
@@ -293,7 +343,7 @@ const char* fa_status_string(int status);
 /* ABI version of this header: (major << 16) | minor. */
 int fa_abi_version(void);
 
-#define FA_ABI_VERSION ((1 << 16) | 5)
+#define FA_ABI_VERSION ((1 << 16) | 6)
 
 #ifdef __cplusplus
 }

@@ -17,6 +17,8 @@ from ._lib import (  # noqa: F401
     check,
     fa_abi_version,
     fa_backward,
+    fa_backward_gqa,
+    fa_backward_varlen,
     fa_backward_workspace_bytes,
     fa_forward,
     fa_forward_split,
@@ -35,7 +37,8 @@ __all__ = [
     "forward", "forward_split", "backward", "naive_forward", "fa_forward", "fa_forward_split",
     "fa_backward", "fa_backward_workspace_bytes", "fa_naive_backward", "naive_backward",
     "fa_forward_varlen", "forward_varlen", "fa_forward_dropout", "forward_dropout",
-    "fa_forward_bias", "forward_bias",
+    "fa_forward_bias", "forward_bias", "fa_backward_gqa", "backward_gqa", "fa_backward_varlen",
+    "backward_varlen",
     "fa_split_workspace_bytes", "fa_naive_forward", "fa_naive_workspace_bytes",
     "fa_status_string", "fa_abi_version", "FAError", "FA_DTYPE_BF16", "FA_DTYPE_F32",
 ]
@@ -183,6 +186,90 @@ def backward(q, k, v, o, lse, dout, *, scale=None, causal=False, key_len=None, w
              dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d,
              float(scale), int(bool(causal)), kl, dt, workspace.data_ptr(), workspace.numel(),
              stream))
+    return dq, dk, dv
+
+
+def backward_gqa(q, k, v, o, lse, dout, *, scale=None, causal=False, key_len=None,
+                 workspace=None, dq=None, dk=None, dv=None):
+    """dQ, dK, dV = fa_backward_gqa(...): gradients for the result (o, lse) of
+    forward_split on q [B, H, Nq, d], k, v [B, Hkv, Nk, d] (rows at the end of
+    the keys); dk, dv sum over the query heads that share a key/value head."""
+    import torch
+    if q.dim() != 4 or k.dim() != 4 or k.shape != v.shape or q.shape[0] != k.shape[0] \
+            or q.shape[3] != k.shape[3] or k.shape[1] < 1 or q.shape[1] % k.shape[1]:
+        raise FAError(-2, "q [B, H, Nq, d] and k, v [B, Hkv, Nk, d] (Hkv dividing H) expected")
+    for t in (o, dout):
+        if t.shape != q.shape or t.dtype != q.dtype:
+            raise FAError(-2, "o and dout must have the shape and dtype of q")
+    for t in (q, k, v, o, dout):
+        if t.dtype != q.dtype or not t.is_cuda or not t.is_contiguous():
+            raise FAError(-1, "q, k, v, o, dout must be contiguous device tensors of one dtype")
+    B, H, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    if lse.shape != (B, H, Nq) or lse.dtype != torch.float32 or not lse.is_cuda:
+        raise FAError(-2, "lse must be a device float32 tensor [B, H, Nq]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    kl = 0
+    if key_len is not None:
+        if key_len.dtype != torch.int32 or not key_len.is_cuda or key_len.numel() != B:
+            raise FAError(-1, "key_len must be a device int32 tensor of B elements")
+        kl = key_len.data_ptr()
+    dt = _dtype_code(q)
+    if workspace is None:
+        need = fa_backward_workspace_bytes(B, H, Nq, d, dt)
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    check(fa_backward_gqa(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                          dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, Hkv,
+                          Nq, Nk, d, float(scale), int(bool(causal)), kl, dt,
+                          workspace.data_ptr(), workspace.numel(), stream))
+    return dq, dk, dv
+
+
+def backward_varlen(q, k, v, o, lse, dout, cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
+                    max_seqlen_k, *, scale=None, causal=False, workspace=None, dq=None, dk=None,
+                    dv=None):
+    """dQ, dK, dV = fa_backward_varlen(...): gradients for the result (o, lse)
+    of forward_varlen on the same packed batch (q, o, dout [Tq, H, d]; k, v
+    [Tk, Hkv, d]; lse [Tq, H])."""
+    import torch
+    if q.dim() != 3 or k.dim() != 3 or k.shape != v.shape or q.shape[2] != k.shape[2] \
+            or k.shape[1] < 1 or q.shape[1] % k.shape[1]:
+        raise FAError(-2, "q [Tq, H, d] and k, v [Tk, Hkv, d] (Hkv dividing H) expected")
+    for t in (o, dout):
+        if t.shape != q.shape or t.dtype != q.dtype:
+            raise FAError(-2, "o and dout must have the shape and dtype of q")
+    for t in (q, k, v, o, dout, cu_seqlens_q, cu_seqlens_k):
+        if not t.is_cuda or not t.is_contiguous():
+            raise FAError(-1, "all tensors must be contiguous device tensors")
+    if cu_seqlens_q.dtype != torch.int32 or cu_seqlens_k.dtype != torch.int32 or \
+            cu_seqlens_q.numel() != cu_seqlens_k.numel():
+        raise FAError(-2, "cu_seqlens_q and cu_seqlens_k must be int32 [B + 1]")
+    Tq, H, d = q.shape
+    Tk, Hkv = k.shape[0], k.shape[1]
+    if lse.shape != (Tq, H) or lse.dtype != torch.float32 or not lse.is_cuda:
+        raise FAError(-2, "lse must be a device float32 tensor [Tq, H]")
+    B = cu_seqlens_q.numel() - 1
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dt = _dtype_code(q)
+    if workspace is None:
+        need = fa_backward_workspace_bytes(1, H, Tq, d, dt)
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    check(fa_backward_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                             lse.data_ptr(), dout.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                             dv.data_ptr(), cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(), B,
+                             H, Hkv, Tq, Tk, int(max_seqlen_q), int(max_seqlen_k), d,
+                             float(scale), int(bool(causal)), dt, workspace.data_ptr(),
+                             workspace.numel(), stream))
     return dq, dk, dv
 
 

@@ -51,6 +51,18 @@ _SIGNATURES = {
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
         ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float, ctypes.c_int,
         ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "fa_backward_gqa": (ctypes.c_int, [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+        ctypes.c_float, ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
+        ctypes.c_size_t, ctypes.c_void_p]),
+    "fa_backward_varlen": (ctypes.c_int, [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+        ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float,
+        ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
     "fa_naive_backward": (ctypes.c_int, [
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
@@ -162,6 +174,24 @@ def fa_backward(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, d, scale, causal, ke
     return load().fa_backward(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, d, scale, int(causal),
                               key_len_mask or None, dtype, workspace or None, workspace_bytes,
                               stream or None)
+
+
+def fa_backward_gqa(q, k, v, o, lse, dout, dq, dk, dv, B, H, Hkv, Nq, Nk, d, scale, causal,
+                    key_len_mask, dtype, workspace, workspace_bytes, stream) -> int:
+    return load().fa_backward_gqa(q or None, k or None, v or None, o or None, lse or None,
+                                  dout or None, dq or None, dk or None, dv or None, B, H, Hkv,
+                                  Nq, Nk, d, scale, int(causal), key_len_mask or None, dtype,
+                                  workspace or None, workspace_bytes, stream or None)
+
+
+def fa_backward_varlen(q, k, v, o, lse, dout, dq, dk, dv, cu_q, cu_k, B, H, Hkv, total_q,
+                       total_k, max_q, max_k, d, scale, causal, dtype, workspace,
+                       workspace_bytes, stream) -> int:
+    return load().fa_backward_varlen(q or None, k or None, v or None, o or None, lse or None,
+                                     dout or None, dq or None, dk or None, dv or None,
+                                     cu_q or None, cu_k or None, B, H, Hkv, total_q, total_k,
+                                     max_q, max_k, d, scale, int(causal), dtype,
+                                     workspace or None, workspace_bytes, stream or None)
 
 
 def fa_naive_backward(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, d, scale, causal,

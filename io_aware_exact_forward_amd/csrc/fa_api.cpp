@@ -406,10 +406,159 @@ extern "C" int fa_backward(const void* q, const void* k, const void* v, const vo
   p.B = B;
   p.H = H;
   p.N = N;
+  p.Hkv = H;
+  p.Nk = N;
   p.n_qtiles = (N + 127) / 128;
   p.n_ktiles = (N + 127) / 128;
   p.scale = scale;
   p.c2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
+  if (fa::launch_bwd_bf16(p, d, causal != 0, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return FA_ERR_HIP;
+  return FA_OK;
+}
+
+namespace {
+
+// Pointer, alignment, workspace and aliasing checks shared by the grouped and
+// packed backward entry points.  nq: bytes of q, o, dout and dq; nkv: bytes
+// of k, v, dk and dv; nl: bytes of lse and of the D workspace; extra: other
+// read-only arrays (lengths, sequence offsets).
+struct Region {
+  const void* p;
+  int64_t n;
+};
+
+int check_backward_buffers(const void* q, const void* k, const void* v, const void* o,
+                           const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                           int64_t nq, int64_t nkv, int64_t nl, const Region* extra, int n_extra,
+                           void* workspace, size_t workspace_bytes) {
+  if (nq > 0 && (!q || !o || !dout || !dq || !lse)) return FA_ERR_NULL;
+  if (nkv > 0 && (!k || !v || !dk || !dv)) return FA_ERR_NULL;
+  for (int i = 0; i < n_extra; ++i)
+    if (extra[i].n > 0 && !extra[i].p) return FA_ERR_NULL;
+  const void* tensors[] = {q, k, v, o, dout, dq, dk, dv};
+  for (const void* x : tensors)
+    if (!is_aligned(x, 16)) return FA_ERR_ALIGN;
+  if (!is_aligned(lse, 4)) return FA_ERR_ALIGN;
+  for (int i = 0; i < n_extra; ++i)
+    if (!is_aligned(extra[i].p, 4)) return FA_ERR_ALIGN;
+  const size_t need = round256(static_cast<size_t>(nl));
+  if (need > 0 && (!workspace || workspace_bytes < need || !is_aligned(workspace, 256)))
+    return FA_ERR_WORKSPACE;
+  const int64_t nw = static_cast<int64_t>(need);
+  // the outputs (and the workspace) overlap no input and no other output
+  const Region written[] = {{dq, nq}, {dk, nkv}, {dv, nkv}, {workspace, nw}};
+  const Region read[] = {{q, nq}, {k, nkv}, {v, nkv}, {o, nq}, {dout, nq}, {lse, nl}};
+  for (int i = 0; i < 4; ++i) {
+    for (const Region& r : read)
+      if (overlaps(written[i].p, written[i].n, r.p, r.n)) return FA_ERR_ALIAS;
+    for (int e = 0; e < n_extra; ++e)
+      if (overlaps(written[i].p, written[i].n, extra[e].p, extra[e].n)) return FA_ERR_ALIAS;
+    for (int j = i + 1; j < 4; ++j)
+      if (overlaps(written[i].p, written[i].n, written[j].p, written[j].n)) return FA_ERR_ALIAS;
+  }
+  return FA_OK;
+}
+
+fa::BwdParams backward_params(const void* q, const void* k, const void* v, const void* o,
+                              const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                              void* workspace, int B, int H, int Hkv, float scale) {
+  fa::BwdParams p{};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.dout = dout;
+  p.lse = lse;
+  p.dq = dq;
+  p.dk = dk;
+  p.dv = dv;
+  p.dvec = static_cast<float*>(workspace);
+  p.B = B;
+  p.H = H;
+  p.Hkv = Hkv;
+  p.scale = scale;
+  p.c2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
+  return p;
+}
+
+int backward_scalars(int H, int Hkv, int d, float scale, int dtype) {
+  if (dtype != FA_DTYPE_BF16) return FA_ERR_DTYPE;
+  if (d != 64 && d != 128) return FA_ERR_HEAD_DIM;
+  if (H < 0 || Hkv < 1 || (H > 0 && H % Hkv != 0)) return FA_ERR_SHAPE;
+  if (!std::isfinite(scale)) return FA_ERR_SCALE;
+  const double c = std::fabs(static_cast<double>(scale)) * 1.4426950408889634;
+  if (!std::isfinite(static_cast<float>(c))) return FA_ERR_SCALE;
+  return FA_OK;
+}
+
+}  // namespace
+
+extern "C" int fa_backward_gqa(const void* q, const void* k, const void* v, const void* o,
+                               const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                               int B, int H, int Hkv, int Nq, int Nk, int d, float scale,
+                               int causal, const int32_t* key_len_mask, int dtype,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  int st = backward_scalars(H, Hkv, d, scale, dtype);
+  if (st != FA_OK) return st;
+  if (B < 0 || Nq < 0 || Nk < 0) return FA_ERR_SHAPE;
+  if (B == 0) return FA_OK;
+  // offsets within one (batch, head) slice are 32-bit; grids fit an int
+  if (int64_t(Nq) * d * 2 > INT_MAX || int64_t(Nk) * d * 2 > INT_MAX) return FA_ERR_SHAPE;
+  const int64_t qtiles = (int64_t(Nq) + 127) / 128, ktiles = (int64_t(Nk) + 127) / 128;
+  if (int64_t(B) * H * qtiles > INT_MAX || int64_t(B) * Hkv * ktiles > INT_MAX)
+    return FA_ERR_SHAPE;
+  const int64_t nq = int64_t(B) * H * Nq * d * 2, nkv = int64_t(B) * Hkv * Nk * d * 2;
+  const int64_t nl = int64_t(B) * H * Nq * 4;
+  const Region extra[] = {{key_len_mask, key_len_mask ? int64_t(B) * 4 : 0}};
+  st = check_backward_buffers(q, k, v, o, lse, dout, dq, dk, dv, nq, nkv, nl, extra, 1, workspace,
+                              workspace_bytes);
+  if (st != FA_OK) return st;
+  fa::BwdParams p = backward_params(q, k, v, o, lse, dout, dq, dk, dv, workspace, B, H, Hkv, scale);
+  p.N = Nq;
+  p.Nk = Nk;
+  p.key_len = key_len_mask;
+  p.end_aligned = 1;
+  p.n_qtiles = static_cast<int>(qtiles);
+  p.n_ktiles = static_cast<int>(ktiles);
+  if (fa::launch_bwd_bf16(p, d, causal != 0, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return FA_ERR_HIP;
+  return FA_OK;
+}
+
+extern "C" int fa_backward_varlen(const void* q, const void* k, const void* v, const void* o,
+                                  const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                                  const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int B,
+                                  int H, int Hkv, int total_q, int total_k, int max_seqlen_q,
+                                  int max_seqlen_k, int d, float scale, int causal, int dtype,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+  int st = backward_scalars(H, Hkv, d, scale, dtype);
+  if (st != FA_OK) return st;
+  if (B < 0 || total_q < 0 || total_k < 0 || max_seqlen_q < 0 || max_seqlen_k < 0)
+    return FA_ERR_SHAPE;
+  if (B == 0) return FA_OK;
+  // offsets within one sequence are 32-bit in the kernels; grids fit an int
+  if (int64_t(max_seqlen_q) * H * d * 2 > INT_MAX || int64_t(max_seqlen_k) * Hkv * d * 2 > INT_MAX)
+    return FA_ERR_SHAPE;
+  const int64_t qtiles = (int64_t(max_seqlen_q) + 127) / 128;
+  const int64_t ktiles = (int64_t(max_seqlen_k) + 127) / 128;
+  if (int64_t(B) * H * qtiles > INT_MAX || int64_t(B) * Hkv * ktiles > INT_MAX)
+    return FA_ERR_SHAPE;
+  const int64_t nq = int64_t(total_q) * H * d * 2, nkv = int64_t(total_k) * Hkv * d * 2;
+  const int64_t nl = int64_t(total_q) * H * 4, ncu = (int64_t(B) + 1) * 4;
+  const Region extra[] = {{cu_seqlens_q, ncu}, {cu_seqlens_k, ncu}};
+  st = check_backward_buffers(q, k, v, o, lse, dout, dq, dk, dv, nq, nkv, nl, extra, 2, workspace,
+                              workspace_bytes);
+  if (st != FA_OK) return st;
+  fa::BwdParams p = backward_params(q, k, v, o, lse, dout, dq, dk, dv, workspace, B, H, Hkv, scale);
+  p.N = max_seqlen_q;
+  p.Nk = max_seqlen_k;
+  p.cu_q = cu_seqlens_q;
+  p.cu_k = cu_seqlens_k;
+  p.end_aligned = 1;
+  // with no query rows (or no key rows) in the batch only the other kernel runs
+  p.n_qtiles = total_q > 0 ? static_cast<int>(qtiles) : 0;
+  p.n_ktiles = total_k > 0 ? static_cast<int>(ktiles) : 0;
   if (fa::launch_bwd_bf16(p, d, causal != 0, static_cast<hipStream_t>(stream)) != hipSuccess)
     return FA_ERR_HIP;
   return FA_OK;

@@ -89,13 +89,58 @@ __device__ __forceinline__ float dot8(u32x4 a, u32x4 b) {
   return s;
 }
 
-__device__ __forceinline__ int seq_len(const BwdParams& p, int b) {
-  int L = p.N;
+// Layout of one (batch, query head) and the key/value head it reads: dense
+// [B, H, Nq, d] / [B, Hkv, Nk, d], or a packed batch [T, H, d] / [T, Hkv, d]
+// with sequence b at rows cu[b] .. cu[b+1]-1.  LSE and D share one layout
+// ([B, H, Nq] dense, [T, H] packed).  Query row i sits at key position
+// i + off (off = 0, or L_b - Nq with the rows at the end of the keys);
+// keys j < kv_lim are valid.  Strides and bases in elements, all
+// workgroup-uniform; a lane's offset from its base is below 2^31 elements
+// (the host bounds a slice or packed sequence to 2^31 bytes), so offsets
+// are 32-bit and the loads take the scalar-base form.
+struct BwdLayout {
+  int Nq, Nk, kv_lim, off;
+  int q_ld, kv_ld, lse_ld;         // row strides
+  int64_t q_hs, lse_hs;            // head strides (Q/O/dO/dQ, LSE/D)
+  int64_t base, kvbase, lse_base;  // of query head hq and key/value head hk
+};
+
+template <int D>
+__device__ __forceinline__ BwdLayout bwd_layout(const BwdParams& p, int b, int hq, int hk) {
+  BwdLayout l;
+  if (p.cu_q) {
+    const int s0 = __builtin_amdgcn_readfirstlane(p.cu_q[b]);
+    const int k0 = __builtin_amdgcn_readfirstlane(p.cu_k[b]);
+    l.Nq = __builtin_amdgcn_readfirstlane(p.cu_q[b + 1]) - s0;
+    l.Nk = __builtin_amdgcn_readfirstlane(p.cu_k[b + 1]) - k0;
+    l.q_ld = p.H * D;
+    l.kv_ld = p.Hkv * D;
+    l.lse_ld = p.H;
+    l.q_hs = D;
+    l.lse_hs = 1;
+    l.base = ((int64_t)s0 * p.H + hq) * D;
+    l.kvbase = ((int64_t)k0 * p.Hkv + hk) * D;
+    l.lse_base = (int64_t)s0 * p.H + hq;
+  } else {
+    l.Nq = p.N;
+    l.Nk = p.Nk;
+    l.q_ld = D;
+    l.kv_ld = D;
+    l.lse_ld = 1;
+    l.q_hs = (int64_t)p.N * D;
+    l.lse_hs = p.N;
+    l.base = ((int64_t)b * p.H + hq) * p.N * D;
+    l.kvbase = ((int64_t)b * p.Hkv + hk) * p.Nk * D;
+    l.lse_base = ((int64_t)b * p.H + hq) * p.N;
+  }
+  int lim = l.Nk;
   if (p.key_len) {
     const int x = p.key_len[b];
-    L = x < 0 ? 0 : (x > p.N ? p.N : x);
+    lim = x < 0 ? 0 : (x > l.Nk ? l.Nk : x);
   }
-  return __builtin_amdgcn_readfirstlane(L);
+  l.kv_lim = __builtin_amdgcn_readfirstlane(lim);
+  l.off = p.end_aligned ? l.kv_lim - l.Nq : 0;
+  return l;
 }
 
 // ---------------------------------------------------------------------------
@@ -122,24 +167,29 @@ __global__ __launch_bounds__(256, kBwdOccupancy<D>) void fa_bwd_dq_kernel(BwdPar
   int qt = blockIdx.x / BH;
   if (CAUSAL) qt = p.n_qtiles - 1 - qt;  // heaviest tiles first
   const int b = bh / p.H;
-  const int N = p.N;
-  const int L = seq_len(p, b);
+  const int hq = bh - b * p.H;
+  const BwdLayout lay = bwd_layout<D>(p, b, hq, hq / (p.H / p.Hkv));
+  const int Nq = lay.Nq, kv_lim = lay.kv_lim, off = lay.off;
   const int q0 = qt * BQ;
-  int n_kv = L;
-  if (CAUSAL) n_kv = min(n_kv, q0 + BQ);
-  if (q0 >= L) n_kv = 0;
+  // keys this query tile sees: below the length and, if causal, at or
+  // before the position of its last row
+  int n_kv = kv_lim;
+  if (CAUSAL) n_kv = min(n_kv, max(0, q0 + BQ + off));
+  if (q0 >= Nq || q0 + off >= kv_lim) n_kv = 0;
   const int ntiles = (n_kv + BK - 1) / BK;
 
-  const int64_t base = (int64_t)bh * N * D;
-  const uint16_t* qg = (const uint16_t*)p.q + base;
-  const uint16_t* kg = (const uint16_t*)p.k + base;
-  const uint16_t* vg = (const uint16_t*)p.v + base;
-  const uint16_t* og = (const uint16_t*)p.o + base;
-  const uint16_t* dog = (const uint16_t*)p.dout + base;
+  const uint16_t* qg = (const uint16_t*)p.q + lay.base;
+  const uint16_t* kg = (const uint16_t*)p.k + lay.kvbase;
+  const uint16_t* vg = (const uint16_t*)p.v + lay.kvbase;
+  const uint16_t* og = (const uint16_t*)p.o + lay.base;
+  const uint16_t* dog = (const uint16_t*)p.dout + lay.base;
+  const int q_ld = lay.q_ld, kv_ld = lay.kv_ld;
 
   const int qw0 = q0 + 32 * wave;
   const int row = qw0 + l32;
-  const bool row_ok = row < L;
+  const int pos = row + off;  // key position of this lane's row
+  // a row that sees at least one key
+  const bool row_ok = row < Nq && pos < kv_lim && (CAUSAL ? pos >= 0 : kv_lim > 0);
 
   // Q and dO of this lane's row (half of the head dim, B-operand layout),
   // and D = dO . O over the whole row.
@@ -149,37 +199,38 @@ __global__ __launch_bounds__(256, kBwdOccupancy<D>) void fa_bwd_dq_kernel(BwdPar
   for (int kk = 0; kk < C::KD; ++kk) {
     u32x4 wq = {0u, 0u, 0u, 0u}, wd = {0u, 0u, 0u, 0u}, wo = {0u, 0u, 0u, 0u};
     if (row_ok) {
-      const int64_t off = (int64_t)row * D + 16 * kk + 8 * h;
-      wq = *(const u32x4*)(qg + off);
-      wd = *(const u32x4*)(dog + off);
-      wo = *(const u32x4*)(og + off);
+      const uint32_t ro = (uint32_t)row * q_ld + 16 * kk + 8 * h;
+      wq = *(const u32x4*)(qg + ro);
+      wd = *(const u32x4*)(dog + ro);
+      wo = *(const u32x4*)(og + ro);
     }
     qf[kk] = __builtin_bit_cast(bf16x8, wq);
     dof[kk] = __builtin_bit_cast(bf16x8, wd);
     dsum += dot8(wd, wo);
   }
   const float dval = halves_sum(dsum);
-  const float lse2 = row_ok ? p.lse[(int64_t)bh * N + row] * kLog2e : 0.f;
-  if (h == 0 && row < N) p.dvec[(int64_t)bh * N + row] = row_ok ? dval : 0.f;
+  const uint32_t lse_at = (uint32_t)row * lay.lse_ld;
+  const float lse2 = row_ok ? p.lse[lay.lse_base + lse_at] * kLog2e : 0.f;
+  if (h == 0 && row < Nq) (p.dvec + lay.lse_base)[lse_at] = row_ok ? dval : 0.f;
 
   f32x16 dq[C::ND];
 #pragma unroll
   for (int i = 0; i < C::ND; ++i) dq[i] = f32x16{};
 
   // K tile: read plainly (S^T) and transposed (dQ^T); V tile: plainly (dP^T).
+  // Chunk i of a thread is row tid/CPR + i*256/CPR of the tile, at a byte
+  // offset from the tile's first row that is the same for every tile; keys
+  // at or beyond the length lie outside the buffer range and read as zeros.
   u32x4 kst[LPT], vst[LPT];
+  const uint32_t kv_off0 = ((uint32_t)(tid / C::CPR) * kv_ld + 8 * (tid % C::CPR)) * 2;
+  const uint32_t kv_step = (256 / C::CPR) * (uint32_t)kv_ld * 2;
   auto load_regs = [&](int kv0) __attribute__((always_inline)) {
+    const uint32_t nb = (uint32_t)max(0, kv_lim - kv0) * kv_ld * 2;
+    const int64_t at = (int64_t)kv0 * kv_ld;
 #pragma unroll
     for (int i = 0; i < LPT; ++i) {
-      const int c = tid + 256 * i, r = c / C::CPR, lc = c % C::CPR;
-      const int key = kv0 + r;
-      u32x4 a = {0u, 0u, 0u, 0u}, v = {0u, 0u, 0u, 0u};
-      if (key < L) {
-        a = *(const u32x4*)(kg + (int64_t)key * D + 8 * lc);
-        v = *(const u32x4*)(vg + (int64_t)key * D + 8 * lc);
-      }
-      kst[i] = a;
-      vst[i] = v;
+      kst[i] = load_ranged_16(kg + at, nb, kv_off0 + i * kv_step);
+      vst[i] = load_ranged_16(vg + at, nb, kv_off0 + i * kv_step);
     }
   };
   auto store_lds = [&](int st) __attribute__((always_inline)) {
@@ -193,7 +244,7 @@ __global__ __launch_bounds__(256, kBwdOccupancy<D>) void fa_bwd_dq_kernel(BwdPar
 
   auto compute = [&](int st, int kv0) __attribute__((always_inline)) {
     // keys all after the wave's last row, or the wave's rows all padding
-    if ((CAUSAL && kv0 > qw0 + 31) || qw0 >= L) return;
+    if ((CAUSAL && kv0 > qw0 + off + 31) || qw0 + off >= kv_lim || qw0 >= Nq) return;
     const uint8_t* kt = lds[st];
     const uint8_t* vt = lds[st] + TILE;
     f32x16 s[NB], dp[NB];
@@ -212,7 +263,8 @@ __global__ __launch_bounds__(256, kBwdOccupancy<D>) void fa_bwd_dq_kernel(BwdPar
     // Element masks only where the tile crosses the diagonal or a length
     // (wave-uniform test).
     bf16x8 dsb[NB][2];
-    const bool full = (!CAUSAL || kv0 + BK - 1 <= qw0) && kv0 + BK <= L && qw0 + 31 < L;
+    const bool full = (!CAUSAL || kv0 + BK - 1 <= qw0 + off) && kv0 + BK <= kv_lim &&
+                      qw0 + 31 < Nq && qw0 + 31 + off < kv_lim;
     auto grads = [&](auto masked_tag) __attribute__((always_inline)) {
       constexpr bool masked = decltype(masked_tag)::value;
 #pragma unroll
@@ -223,7 +275,7 @@ __global__ __launch_bounds__(256, kBwdOccupancy<D>) void fa_bwd_dq_kernel(BwdPar
           float pr = fast_exp2(__builtin_fmaf(s[bb][r], p.c2, -lse2));
           if constexpr (masked) {
             const int key = kv0 + 32 * bb + acc_row(r, h);
-            const bool vis = row_ok && key < L && (!CAUSAL || key <= row);
+            const bool vis = row_ok && key < kv_lim && (!CAUSAL || key <= pos);
             pr = vis ? pr : 0.f;
           }
           ds[r] = pr * (dp[bb][r] - dval);
@@ -258,8 +310,8 @@ __global__ __launch_bounds__(256, kBwdOccupancy<D>) void fa_bwd_dq_kernel(BwdPar
   }
 
   // dQ = scale * (dQ^T)^T: lane = row, register r of slice db = dim 32db + acc_row(r, h)
-  if (row < N) {
-    uint16_t* dqg = (uint16_t*)p.dq + base + (int64_t)row * D;
+  if (row < Nq) {
+    uint16_t* dqg = (uint16_t*)p.dq + lay.base + (uint32_t)row * q_ld;
 #pragma unroll
     for (int db = 0; db < C::ND; ++db)
 #pragma unroll
@@ -274,7 +326,9 @@ __global__ __launch_bounds__(256, kBwdOccupancy<D>) void fa_bwd_dq_kernel(BwdPar
 }
 
 // ---------------------------------------------------------------------------
-// dK, dV: one workgroup per 128 keys of one (batch, head)
+// dK, dV: one workgroup per 128 keys of one (batch, key/value head); it
+// streams the query tiles of every query head that reads this key/value
+// head (H / Hkv of them), so the sum over the group needs no atomics
 // ---------------------------------------------------------------------------
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256, kBwdOccupancy<D>) void fa_bwd_dkdv_kernel(BwdParams p) {
@@ -290,33 +344,31 @@ __global__ __launch_bounds__(256, kBwdOccupancy<D>) void fa_bwd_dkdv_kernel(BwdP
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, l32 = lane & 31, h = lane >> 5;
-  const int BH = p.B * p.H;
-  const int bh = blockIdx.x % BH;
-  const int kt_idx = blockIdx.x / BH;  // causal: lower key tiles see more rows: heaviest first
-  const int b = bh / p.H;
-  const int N = p.N;
-  const int L = seq_len(p, b);
+  const int BHK = p.B * p.Hkv;
+  const int bhk = blockIdx.x % BHK;
+  const int kt_idx = blockIdx.x / BHK;  // causal: lower key tiles see more rows: heaviest first
+  const int b = bhk / p.Hkv;
+  const int hk = bhk - b * p.Hkv;
+  const int G = p.H / p.Hkv;  // query heads hk*G .. hk*G+G-1 read this head
+  const BwdLayout lay = bwd_layout<D>(p, b, hk * G, hk);
+  const int kv_lim = lay.kv_lim, off = lay.off;
   const int k0 = kt_idx * BKW;
   const int kw0 = k0 + 32 * wave;
   const int key = kw0 + l32;
-  const bool key_ok = key < L;
+  const bool key_ok = key < kv_lim;
 
-  const int64_t base = (int64_t)bh * N * D;
-  const uint16_t* qg = (const uint16_t*)p.q + base;
-  const uint16_t* kg = (const uint16_t*)p.k + base;
-  const uint16_t* vg = (const uint16_t*)p.v + base;
-  const uint16_t* dog = (const uint16_t*)p.dout + base;
-  const float* lseg = p.lse + (int64_t)bh * N;
-  const float* dvg = p.dvec + (int64_t)bh * N;
+  const uint16_t* kg = (const uint16_t*)p.k + lay.kvbase;
+  const uint16_t* vg = (const uint16_t*)p.v + lay.kvbase;
+  const int q_ld = lay.q_ld, kv_ld = lay.kv_ld;
 
   bf16x8 kf[C::KD], vf[C::KD];
 #pragma unroll
   for (int kk = 0; kk < C::KD; ++kk) {
     u32x4 a = {0u, 0u, 0u, 0u}, v = {0u, 0u, 0u, 0u};
     if (key_ok) {
-      const int64_t off = (int64_t)key * D + 16 * kk + 8 * h;
-      a = *(const u32x4*)(kg + off);
-      v = *(const u32x4*)(vg + off);
+      const uint32_t ko = (uint32_t)key * kv_ld + 16 * kk + 8 * h;
+      a = *(const u32x4*)(kg + ko);
+      v = *(const u32x4*)(vg + ko);
     }
     kf[kk] = __builtin_bit_cast(bf16x8, a);
     vf[kk] = __builtin_bit_cast(bf16x8, v);
@@ -329,30 +381,44 @@ __global__ __launch_bounds__(256, kBwdOccupancy<D>) void fa_bwd_dkdv_kernel(BwdP
     dv[i] = f32x16{};
   }
 
-  // Query tiles that see any key of this workgroup: rows >= k0 if causal,
-  // below the sequence length.
-  const int qfirst = (k0 < L) ? (CAUSAL ? (k0 / BQ) : 0) : 0;
-  const int qend = (k0 < L) ? (L + BQ - 1) / BQ : 0;
+  // Rows whose position is below the key length (the others are padding
+  // or see no key), and the query tiles that see any key of this
+  // workgroup: rows at positions >= k0 if causal.  Tile t of the loop is
+  // query tile qfirst + t % nt of query head hk*G + t / nt.
+  const int qlim = max(0, min(lay.Nq, kv_lim - off));
+  const int qfirst = CAUSAL ? max(0, k0 - off) / BQ : 0;
+  const int qend = k0 < kv_lim ? (qlim + BQ - 1) / BQ : 0;
+  const int nt = max(0, qend - qfirst);
+  const int total = G * nt;
 
+  // Q and dO tiles: chunk i of a thread at a fixed byte offset from the
+  // tile's first row; rows at or beyond qlim read as zeros (buffer range).
   u32x4 qst[LPT], dst[LPT];
   float aux = 0.f;  // LSE2 (threads 0..BQ-1) or D (threads BQ..2BQ-1) of one row
-  auto load_regs = [&](int q0) __attribute__((always_inline)) {
+  const uint32_t q_off0 = ((uint32_t)(tid / C::CPR) * q_ld + 8 * (tid % C::CPR)) * 2;
+  const uint32_t q_step = (256 / C::CPR) * (uint32_t)q_ld * 2;
+  auto load_regs = [&](int g, int q0) __attribute__((always_inline)) {
+    const int64_t hb = lay.base + g * lay.q_hs + (int64_t)q0 * q_ld;
+    const uint32_t nb = (uint32_t)max(0, qlim - q0) * q_ld * 2;
 #pragma unroll
     for (int i = 0; i < LPT; ++i) {
-      const int c = tid + 256 * i, r = c / C::CPR, lc = c % C::CPR;
-      const int qr = q0 + r;
-      u32x4 a = {0u, 0u, 0u, 0u}, d = {0u, 0u, 0u, 0u};
-      if (qr < L) {
-        a = *(const u32x4*)(qg + (int64_t)qr * D + 8 * lc);
-        d = *(const u32x4*)(dog + (int64_t)qr * D + 8 * lc);
-      }
-      qst[i] = a;
-      dst[i] = d;
+      qst[i] = load_ranged_16((const uint16_t*)p.q + hb, nb, q_off0 + i * q_step);
+      dst[i] = load_ranged_16((const uint16_t*)p.dout + hb, nb, q_off0 + i * q_step);
     }
     if (tid < 2 * BQ) {
       const int qr = q0 + (tid % BQ);
       aux = 0.f;
-      if (qr < L) aux = tid < BQ ? lseg[qr] * kLog2e : dvg[qr];
+      if (qr < qlim) {
+        const int64_t hb = lay.lse_base + g * lay.lse_hs;
+        const uint32_t at = (uint32_t)qr * lay.lse_ld;
+        if (tid < BQ) {
+          // a causal row before the first key has LSE -inf and sees no key
+          const float l = (p.lse + hb)[at];
+          aux = l == kNegInf ? 0.f : l * kLog2e;
+        } else {
+          aux = (p.dvec + hb)[at];
+        }
+      }
     }
   };
   auto store_lds = [&](int st) __attribute__((always_inline)) {
@@ -367,7 +433,7 @@ __global__ __launch_bounds__(256, kBwdOccupancy<D>) void fa_bwd_dkdv_kernel(BwdP
 
   auto compute = [&](int st, int q0) __attribute__((always_inline)) {
     // rows all before the wave's first key, or the wave's keys all padding
-    if ((CAUSAL && q0 + BQ - 1 < kw0) || kw0 >= L) return;
+    if ((CAUSAL && q0 + BQ - 1 + off < kw0) || kw0 >= kv_lim) return;
     const uint8_t* qt = lds[st];
     const uint8_t* dt = lds[st] + TILE;
     const float* lse2 = (const float*)(lds[st] + 2 * TILE);
@@ -397,7 +463,7 @@ __global__ __launch_bounds__(256, kBwdOccupancy<D>) void fa_bwd_dkdv_kernel(BwdP
             float e = fast_exp2(__builtin_fmaf(s[r], p.c2, -l4[t]));
             if constexpr (masked) {
               const int qrow = q0 + r0 + t;
-              const bool vis = key_ok && qrow < L && (!CAUSAL || key <= qrow);
+              const bool vis = key_ok && qrow < qlim && (!CAUSAL || key <= qrow + off);
               e = vis ? e : 0.f;
             }
             pr[r] = e;
@@ -407,7 +473,8 @@ __global__ __launch_bounds__(256, kBwdOccupancy<D>) void fa_bwd_dkdv_kernel(BwdP
       };
       // masks only where the block crosses the diagonal or a length (wave-uniform)
       const int qb0 = q0 + 32 * qb;
-      if ((!CAUSAL || kw0 + 31 <= qb0) && qb0 + 31 < L && kw0 + 31 < L) probs(std::false_type{});
+      if ((!CAUSAL || kw0 + 31 <= qb0 + off) && qb0 + 31 < qlim && kw0 + 31 < kv_lim)
+        probs(std::false_type{});
       else probs(std::true_type{});
       pb[qb][0] = pack8(pr);
       pb[qb][1] = pack8(pr + 8);
@@ -426,23 +493,29 @@ __global__ __launch_bounds__(256, kBwdOccupancy<D>) void fa_bwd_dkdv_kernel(BwdP
         }
   };
 
-  if (qend > qfirst) {
-    load_regs(qfirst * BQ);
+  if (total > 0) {
+    load_regs(0, qfirst * BQ);
     store_lds(0);
     __syncthreads();
-    for (int t = qfirst; t < qend; ++t) {
-      const bool more = t + 1 < qend;
-      if (more) load_regs((t + 1) * BQ);
-      compute((t - qfirst) & 1, t * BQ);
-      if (more) store_lds((t + 1 - qfirst) & 1);
+    int g = 0, qi = qfirst;  // head and query tile of step t
+    for (int t = 0; t < total; ++t) {
+      const bool more = t + 1 < total;
+      const int q0 = qi * BQ;
+      if (++qi == qend) {
+        qi = qfirst;
+        ++g;
+      }
+      if (more) load_regs(g, qi * BQ);
+      compute(t & 1, q0);
+      if (more) store_lds((t + 1) & 1);
       __syncthreads();
     }
   }
 
   // dK = scale * (dK^T)^T, dV = (dV^T)^T: lane = key, register r of slice db = dim
-  if (key < N) {
-    uint16_t* dkg = (uint16_t*)p.dk + base + (int64_t)key * D;
-    uint16_t* dvg2 = (uint16_t*)p.dv + base + (int64_t)key * D;
+  if (key < lay.Nk) {
+    uint16_t* dkg = (uint16_t*)p.dk + lay.kvbase + (uint32_t)key * kv_ld;
+    uint16_t* dvg2 = (uint16_t*)p.dv + lay.kvbase + (uint32_t)key * kv_ld;
 #pragma unroll
     for (int db = 0; db < C::ND; ++db)
 #pragma unroll
@@ -461,14 +534,20 @@ __global__ __launch_bounds__(256, kBwdOccupancy<D>) void fa_bwd_dkdv_kernel(BwdP
 
 template <int D, bool CAUSAL>
 hipError_t launch_bwd(const BwdParams& p, hipStream_t stream) {
-  const int BH = p.B * p.H;
-  hipLaunchKernelGGL((fa_bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)((int64_t)p.n_qtiles * BH)),
-                     dim3(256), 0, stream, p);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)((int64_t)p.n_ktiles * BH)),
-                     dim3(256), 0, stream, p);
-  return hipGetLastError();
+  const int64_t dq_wgs = (int64_t)p.n_qtiles * p.B * p.H;
+  const int64_t dkdv_wgs = (int64_t)p.n_ktiles * p.B * p.Hkv;
+  if (dq_wgs > 0) {
+    hipLaunchKernelGGL((fa_bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)dq_wgs), dim3(256), 0,
+                       stream, p);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (dkdv_wgs > 0) {
+    hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)dkdv_wgs), dim3(256), 0,
+                       stream, p);
+    return hipGetLastError();
+  }
+  return hipSuccess;
 }
 
 }  // namespace

@@ -80,6 +80,17 @@ __device__ __forceinline__ void load_lds_16(const void* base, uint32_t nbytes, v
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)lds_base, 16, offset, 0, 0, 0);
 }
 
+// 16 bytes per lane from the raw buffer [base, base + nbytes) into registers
+// (buffer_load_dwordx4): a lane whose offset lies past nbytes reads zeros,
+// so a tile's rows beyond a length need no branch.  nbytes and offsets are
+// multiples of 16, so an access is wholly inside or wholly outside.
+__device__ __forceinline__ u32x4 load_ranged_16(const void* base, uint32_t nbytes,
+                                                uint32_t offset) {
+  const __amdgpu_buffer_rsrc_t rsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)nbytes, 0x00020000);
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, offset, 0, 0));
+}
+
 // Transpose read of 4 bf16 (ds_read_b64_tr_b16).  Within each group of 16
 // lanes, lane r supplies an 8-byte address; lane i receives element i % 4 of
 // the chunks addressed by lanes i/4, i/4 + 4, i/4 + 8 and i/4 + 12, in that

@@ -58,20 +58,24 @@ struct NaiveSoftmaxParams {
 
 // Everything the two backward kernels need.
 struct BwdParams {
-  const void* q;           // [B, H, N, d] bf16
-  const void* k;
+  const void* q;           // [B, H, N, d] bf16 (packed: [T, H, d])
+  const void* k;           // [B, Hkv, Nk, d] (packed: [Tk, Hkv, d])
   const void* v;
-  const void* o;           // forward output
-  const void* dout;        // upstream gradient dO
-  const float* lse;        // [B, H, N] forward log-sum-exp (natural log)
-  void* dq;                // [B, H, N, d] bf16 outputs
+  const void* o;           // forward output, layout of q
+  const void* dout;        // upstream gradient dO, layout of q
+  const float* lse;        // [B, H, N] forward log-sum-exp (natural log); packed [T, H]
+  void* dq;                // bf16 outputs in the layouts of q, k, v
   void* dk;
   void* dv;
-  float* dvec;             // [B, H, N] workspace: D_i = dO_i . O_i
-  const int32_t* key_len;  // device [B] or nullptr
-  int B, H, N;
-  int n_qtiles;            // ceil(N / 128): workgroups per (b, h) of the dQ kernel
-  int n_ktiles;            // ceil(N / 128): workgroups per (b, h) of the dK/dV kernel
+  float* dvec;             // workspace in the layout of lse: D_i = dO_i . O_i
+  const int32_t* key_len;  // device [B] or nullptr (dense only)
+  int B, H, N;             // N: query rows per sequence (dense)
+  int Hkv, Nk;             // key/value heads (H % Hkv == 0); keys per sequence (dense)
+  const int32_t* cu_q;     // packed batch: sequence b at rows cu_q[b] .. cu_q[b+1]-1, else nullptr
+  const int32_t* cu_k;
+  int end_aligned;         // query row i at key position i + L_b - N_b (else i)
+  int n_qtiles;            // ceil(max N / 128): workgroups per (b, h) of the dQ kernel
+  int n_ktiles;            // ceil(max Nk / 128): workgroups per (b, hkv) of the dK/dV kernel
   float scale;             // signed
   float c2;                // scale * log2(e), signed
 };

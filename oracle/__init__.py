@@ -15,5 +15,10 @@ from .attention import (  # noqa: F401
     expand_kv_heads,
     varlen_attention,
 )
-from .backward import attention_backward  # noqa: F401
+from .backward import (  # noqa: F401
+    attention_backward,
+    grouped_attention_backward,
+    kv_head_of,
+    varlen_attention_backward,
+)
 from .dropout import dropout_attention, dropout_keep, philox4x32_10  # noqa: F401

@@ -34,7 +34,7 @@ def test_header_declares_expected_entry_points():
     assert declared_functions() == sorted(
         ["fa_forward", "fa_naive_workspace_bytes", "fa_naive_forward", "fa_split_workspace_bytes",
          "fa_forward_split", "fa_forward_varlen", "fa_forward_dropout", "fa_forward_bias",
-         "fa_backward_workspace_bytes", "fa_backward",
+         "fa_backward_workspace_bytes", "fa_backward", "fa_backward_gqa", "fa_backward_varlen",
          "fa_naive_backward",
          "fa_status_string", "fa_abi_version"])
 
@@ -44,7 +44,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     for name in declared_functions():
         assert hasattr(lib, name), name
     assert set(_lib.exported_symbols()) == set(declared_functions())
-    assert fa.fa_abi_version() == (1 << 16) | 5
+    assert fa.fa_abi_version() == (1 << 16) | 6
 
 
 def test_status_strings():
@@ -264,6 +264,66 @@ def test_backward_empty_is_a_no_op():
     for B, H, N in ((0, 2, 64), (1, 0, 64), (1, 2, 0)):
         assert bwd_call(q=0, k=0, v=0, o=0, lse=0, do=0, dq=0, dk=0, dv=0, ws=0, wsb=0,
                         B=B, H=H, N=N) == OK
+
+
+def gqa_call(q=Q, k=K, v=V, o=OO, lse=L, do=DO, dq=DQ, dk=DK, dv=DV, B=2, H=8, Hkv=2, Nq=64,
+             Nk=100, d=64, scale=0.125, causal=1, kl=0, dtype=BF16, ws=WS, wsb=1 << 20, stream=0):
+    return fa.fa_backward_gqa(q, k, v, o, lse, do, dq, dk, dv, B, H, Hkv, Nq, Nk, d, scale, causal,
+                              kl, dtype, ws, wsb, stream)
+
+
+def test_backward_gqa_bad_arguments():
+    assert gqa_call(dtype=F32) == DTYPE
+    assert gqa_call(d=96) == HEAD_DIM
+    for bad in (dict(B=-1), dict(Nq=-1), dict(Nk=-1), dict(H=-2), dict(Hkv=0), dict(Hkv=3),
+                dict(Nq=1 << 24, d=128)):
+        assert gqa_call(**bad) == SHAPE, bad
+    assert gqa_call(scale=float("nan")) == SCALE
+    for field in ("q", "k", "v", "o", "lse", "do", "dq", "dk", "dv"):
+        assert gqa_call(**{field: 0}) == NULL, field
+    for field, val in (("q", Q + 8), ("dv", DV + 8), ("lse", L + 2), ("kl", KL + 2)):
+        assert gqa_call(**{field: val}) == ALIGN, field
+    assert gqa_call(ws=0) == WORKSPACE
+    assert gqa_call(wsb=2 * 8 * 64 * 4 - 4) == WORKSPACE
+    assert gqa_call(ws=WS + 64) == WORKSPACE
+    assert gqa_call(dq=OO) == ALIAS
+    assert gqa_call(dk=DV - 1024) == ALIAS          # dk runs into dv
+    assert gqa_call(ws=L) == ALIAS
+    assert gqa_call(dv=KL - 64, kl=KL) == ALIAS      # dv runs into the lengths
+
+
+def test_backward_gqa_batch_zero_is_a_no_op():
+    assert gqa_call(q=0, k=0, v=0, o=0, lse=0, do=0, dq=0, dk=0, dv=0, ws=0, wsb=0, B=0) == OK
+
+
+def bvl_call(q=Q, k=K, v=V, o=OO, lse=L, do=DO, dq=DQ, dk=DK, dv=DV, cuq=A + 12 * (1 << 34),
+             cuk=A + 13 * (1 << 34), B=3, H=4, Hkv=2, tq=100, tk=120, mq=50, mk=60, d=64,
+             scale=0.125, causal=1, dtype=BF16, ws=WS, wsb=1 << 20, stream=0):
+    return fa.fa_backward_varlen(q, k, v, o, lse, do, dq, dk, dv, cuq, cuk, B, H, Hkv, tq, tk, mq,
+                                 mk, d, scale, causal, dtype, ws, wsb, stream)
+
+
+def test_backward_varlen_bad_arguments():
+    assert bvl_call(dtype=F32) == DTYPE
+    assert bvl_call(d=32) == HEAD_DIM
+    for bad in (dict(B=-1), dict(tq=-1), dict(tk=-1), dict(mq=-1), dict(Hkv=0), dict(Hkv=3),
+                dict(mk=1 << 24, d=128)):
+        assert bvl_call(**bad) == SHAPE, bad
+    assert bvl_call(scale=float("inf")) == SCALE
+    for field in ("q", "k", "o", "lse", "do", "dq", "dk", "cuq", "cuk"):
+        assert bvl_call(**{field: 0}) == NULL, field
+    for field, val in (("q", Q + 8), ("dq", DQ + 4), ("lse", L + 2), ("cuk", A + 13 * (1 << 34) + 2)):
+        assert bvl_call(**{field: val}) == ALIGN, field
+    assert bvl_call(ws=0) == WORKSPACE
+    assert bvl_call(wsb=100 * 4 * 4 - 4) == WORKSPACE
+    assert bvl_call(dq=Q) == ALIAS
+    assert bvl_call(ws=A + 12 * (1 << 34)) == ALIAS   # workspace over the offsets
+    assert bvl_call(dv=DK + 64) == ALIAS
+
+
+def test_backward_varlen_batch_zero_is_a_no_op():
+    assert bvl_call(q=0, k=0, v=0, o=0, lse=0, do=0, dq=0, dk=0, dv=0, cuq=0, cuk=0, ws=0, wsb=0,
+                    B=0) == OK
 
 
 def test_naive_backward_bad_arguments():

@@ -193,3 +193,120 @@ def test_pins_pass_on_oracle():
                                      "dv_from_dp", "d_from_wrong_axis"])
 def test_planted_mistakes_are_caught(mistake):
     assert _pins_fail(_mistaken_backward(mistake))
+
+
+# ---------------------------------------------------------------------------
+# Grouped key/value heads, end-aligned rows, packed batches
+# ---------------------------------------------------------------------------
+
+def _fd(params, loss_fn, eps=1e-6):
+    """Central differences of loss_fn() with respect to every entry of the
+    arrays in params (changed in place and restored)."""
+    grads = []
+    for x in params:
+        g = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            old = x[idx]
+            x[idx] = old + eps
+            lp = loss_fn()
+            x[idx] = old - eps
+            lm = loss_fn()
+            x[idx] = old
+            g[idx] = (lp - lm) / (2 * eps)
+        grads.append(g)
+    return grads
+
+
+def grouped_loss(q, k, v, do, scale, causal, key_len, end_aligned):
+    H = q.shape[1]
+    o, _ = oracle.attention(q, oracle.expand_kv_heads(k, H), oracle.expand_kv_heads(v, H), scale,
+                            causal=causal, key_len=key_len, end_aligned=end_aligned)
+    return float((do * o).sum())
+
+
+GROUPED_SHAPES = [
+    # (B, H, Hkv, Nq, Nk, key_len)
+    (1, 4, 2, 3, 5, None),      # fewer rows than keys: positions 2..4
+    (2, 4, 1, 4, 3, [3, 1]),    # more rows than keys: causal rows before key 0 see nothing
+    (1, 2, 2, 4, 4, [2]),       # ungrouped, a length below Nk
+    (1, 3, 1, 2, 4, [0]),       # no key at all
+]
+
+
+@pytest.mark.parametrize("shape", GROUPED_SHAPES, ids=lambda s: f"h{s[1]}kv{s[2]}q{s[3]}k{s[4]}")
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("end_aligned", [True, False])
+def test_grouped_finite_differences(shape, causal, end_aligned):
+    B, H, Hkv, Nq, Nk, kl = shape
+    key_len = None if kl is None else np.array(kl)
+    q, do = (rand((B, H, Nq, 2), s) for s in (851, 852))
+    k, v = (rand((B, Hkv, Nk, 2), s) for s in (853, 854))
+    dq, dk, dv, _ = oracle.grouped_attention_backward(q, k, v, do, 0.9, causal=causal,
+                                                      key_len=key_len, end_aligned=end_aligned)
+    fq, fk, fv = _fd((q, k, v), lambda: grouped_loss(q, k, v, do, 0.9, causal, key_len, end_aligned))
+    for a, b, name in ((dq, fq, "dq"), (dk, fk, "dk"), (dv, fv, "dv")):
+        assert np.allclose(a, b, atol=1e-8, rtol=0), (name, np.abs(a - b).max())
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_grouped_reduces_to_square(causal):
+    """Hkv = H, Nq = Nk and rows at their own positions: the pinned square
+    backward."""
+    B, H, N, d = 2, 3, 11, 4
+    q, k, v, do = (rand((B, H, N, d), s, 1.5) for s in (861, 862, 863, 864))
+    key_len = np.array([11, 6])
+    want = oracle.attention_backward(q, k, v, do, 0.6, causal=causal, key_len=key_len)
+    got = oracle.grouped_attention_backward(q, k, v, do, 0.6, causal=causal, key_len=key_len,
+                                            end_aligned=False)
+    for a, b in zip(got, want):
+        assert np.allclose(a, b, atol=1e-13)
+
+
+def test_grouped_wrong_head_mapping_is_caught(monkeypatch):
+    """Planted: query head h reading key/value head h % Hkv (interleaved)
+    instead of h // (H / Hkv) fails the finite-difference pin."""
+    B, H, Hkv, Nq, Nk = 1, 4, 2, 3, 4
+    q, do = (rand((B, H, Nq, 2), s) for s in (871, 872))
+    k, v = (rand((B, Hkv, Nk, 2), s) for s in (873, 874))
+    fq, fk, fv = _fd((q, k, v), lambda: grouped_loss(q, k, v, do, 0.9, True, None, True))
+    monkeypatch.setattr("oracle.backward.kv_head_of", lambda h, H, Hkv: h % Hkv)
+    dq, dk, dv, _ = oracle.grouped_attention_backward(q, k, v, do, 0.9, causal=True)
+    assert not (np.allclose(dk, fk, atol=1e-7) and np.allclose(dv, fv, atol=1e-7)
+                and np.allclose(dq, fq, atol=1e-7))
+
+
+def test_grouped_rows_not_end_aligned_is_caught():
+    """Planted: rows taken at their own positions when the forward puts them
+    at the end of the keys fails the finite-difference pin."""
+    B, H, Hkv, Nq, Nk = 1, 2, 1, 3, 6
+    q, do = (rand((B, H, Nq, 2), s) for s in (881, 882))
+    k, v = (rand((B, Hkv, Nk, 2), s) for s in (883, 884))
+    fq, fk, fv = _fd((q, k, v), lambda: grouped_loss(q, k, v, do, 0.9, True, None, True))
+    dq, dk, dv, _ = oracle.grouped_attention_backward(q, k, v, do, 0.9, causal=True,
+                                                      end_aligned=False)
+    assert not np.allclose(dk, fk, atol=1e-7)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_varlen_finite_differences(causal):
+    """Packed batch with an empty query range, more rows than keys and a
+    sequence without keys, through the packed forward oracle."""
+    cu_q = np.array([0, 2, 2, 6, 7])
+    cu_k = np.array([0, 3, 5, 7, 7])
+    H, Hkv, d = 2, 1, 2
+    q, do = (rand((cu_q[-1], H, d), s) for s in (891, 892))
+    k, v = (rand((cu_k[-1], Hkv, d), s) for s in (893, 894))
+
+    def loss_fn():
+        o, _ = oracle.varlen_attention(q, k, v, cu_q, cu_k, 0.8, causal=causal)
+        return float((do * o).sum())
+
+    dq, dk, dv, dvec = oracle.varlen_attention_backward(q, k, v, do, cu_q, cu_k, 0.8, causal=causal)
+    fq, fk, fv = _fd((q, k, v), loss_fn)
+    for a, b, name in ((dq, fq, "dq"), (dk, fk, "dk"), (dv, fv, "dv")):
+        assert np.allclose(a, b, atol=1e-8, rtol=0), (name, np.abs(a - b).max())
+    # keys of the sequence without queries, and rows of the one without keys
+    assert np.all(dk[3:5] == 0) and np.all(dv[3:5] == 0) and np.all(dq[6:7] == 0)
+    # D_i = dO_i . O_i
+    o, _ = oracle.varlen_attention(q, k, v, cu_q, cu_k, 0.8, causal=causal)
+    assert np.allclose(dvec, (do * o).sum(axis=-1), atol=1e-12)
