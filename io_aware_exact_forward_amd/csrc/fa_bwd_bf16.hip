@@ -151,6 +151,30 @@ __device__ __forceinline__ BwdLayout bwd_layout(const BwdParams& p, int b, int h
 template <int D>
 constexpr int kBwdOccupancy = D == 64 ? 2 : 1;
 
+// Grid order of both kernels: (batch, head) pairs in chunks of 32, every tile
+// of a chunk before the next chunk, one tile of each pair of the chunk per
+// round of 32 workgroups, heaviest tiles first.  The hardware deals
+// workgroup x to XCD x % 8 and, within it, to one of four shader engines by
+// (x / 8) % 4.  Pair q + 8t (mod the chunk's pairs) takes slot q of round t,
+// so a pair stays on one XCD (the rows its workgroups stream, K/V or Q/dO,
+// are shared through that XCD's L2) while its tiles rotate over the four
+// engines: pairs of unequal work (sequences of different lengths) then load
+// every engine alike, and no engine fills up while the in-order dispatcher
+// waits on it with the others idle.
+struct GridPos {
+  int pair, tile;
+};
+__device__ __forceinline__ GridPos grid_pos(int x, int pairs, int tiles) {
+  constexpr int kChunk = 32;
+  const int chunk_wgs = kChunk * tiles;
+  const int chunk = x / chunk_wgs;
+  const int in_chunk = x - chunk * chunk_wgs;
+  const int chunk_pairs = min(kChunk, pairs - chunk * kChunk);
+  const int tile = in_chunk / chunk_pairs;
+  const int slot = in_chunk - tile * chunk_pairs;
+  return {chunk * kChunk + (int)(((unsigned)slot + 8u * (unsigned)tile) % (unsigned)chunk_pairs), tile};
+}
+
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256, kBwdOccupancy<D>) void fa_bwd_dq_kernel(BwdParams p) {
   using C = BwdCfg<D>;
@@ -162,10 +186,9 @@ __global__ __launch_bounds__(256, kBwdOccupancy<D>) void fa_bwd_dq_kernel(BwdPar
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, l32 = lane & 31, h = lane >> 5;
-  const int BH = p.B * p.H;
-  const int bh = blockIdx.x % BH;
-  int qt = blockIdx.x / BH;
-  if (CAUSAL) qt = p.n_qtiles - 1 - qt;  // heaviest tiles first
+  const GridPos gp = grid_pos(blockIdx.x, p.B * p.H, p.n_qtiles);
+  const int bh = gp.pair;
+  const int qt = CAUSAL ? p.n_qtiles - 1 - gp.tile : gp.tile;  // heaviest tiles first
   const int b = bh / p.H;
   const int hq = bh - b * p.H;
   const BwdLayout lay = bwd_layout<D>(p, b, hq, hq / (p.H / p.Hkv));
@@ -333,8 +356,9 @@ __global__ __launch_bounds__(256, kBwdOccupancy<D>) void fa_bwd_dq_kernel(BwdPar
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256, kBwdOccupancy<D>) void fa_bwd_dkdv_kernel(BwdParams p) {
   using C = BwdCfg<D>;
-  // 64-row query tiles at d = 64, 32-row tiles at d = 128 (registers)
-  constexpr int BKW = 128, BQ = D == 64 ? 64 : 32, NQB = BQ / 32;
+  // 64-row query tiles (at d = 128 the workgroup then holds 490 of the 512
+  // registers a lane has at one workgroup per CU)
+  constexpr int BKW = 128, BQ = 64, NQB = BQ / 32;
   constexpr int TILE = BQ * C::ROW_BYTES;
   constexpr int LPT = BQ * C::CPR / 256;
   // [stage][Q tile | dO tile | LSE2 (BQ floats) | D (BQ floats)]
@@ -344,9 +368,10 @@ __global__ __launch_bounds__(256, kBwdOccupancy<D>) void fa_bwd_dkdv_kernel(BwdP
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, l32 = lane & 31, h = lane >> 5;
-  const int BHK = p.B * p.Hkv;
-  const int bhk = blockIdx.x % BHK;
-  const int kt_idx = blockIdx.x / BHK;  // causal: lower key tiles see more rows: heaviest first
+  // causal: lower key tiles see more rows, so ascending is heaviest first
+  const GridPos gp = grid_pos(blockIdx.x, p.B * p.Hkv, p.n_ktiles);
+  const int bhk = gp.pair;
+  const int kt_idx = gp.tile;
   const int b = bhk / p.Hkv;
   const int hk = bhk - b * p.Hkv;
   const int G = p.H / p.Hkv;  // query heads hk*G .. hk*G+G-1 read this head
@@ -384,7 +409,10 @@ __global__ __launch_bounds__(256, kBwdOccupancy<D>) void fa_bwd_dkdv_kernel(BwdP
   // Rows whose position is below the key length (the others are padding
   // or see no key), and the query tiles that see any key of this
   // workgroup: rows at positions >= k0 if causal.  Tile t of the loop is
-  // query tile qfirst + t % nt of query head hk*G + t / nt.
+  // query tile qend - 1 - t % nt of query head hk*G + t / nt: every key tile
+  // of a sequence shares its last query tile, so the workgroups of one
+  // (batch, head) pair that run together start on the same rows and stream
+  // them in step (from L2) until each reaches its own first tile.
   const int qlim = max(0, min(lay.Nq, kv_lim - off));
   const int qfirst = CAUSAL ? max(0, k0 - off) / BQ : 0;
   const int qend = k0 < kv_lim ? (qlim + BQ - 1) / BQ : 0;
@@ -494,15 +522,15 @@ __global__ __launch_bounds__(256, kBwdOccupancy<D>) void fa_bwd_dkdv_kernel(BwdP
   };
 
   if (total > 0) {
-    load_regs(0, qfirst * BQ);
+    load_regs(0, (qend - 1) * BQ);
     store_lds(0);
     __syncthreads();
-    int g = 0, qi = qfirst;  // head and query tile of step t
+    int g = 0, qi = qend - 1;  // head and query tile of step t
     for (int t = 0; t < total; ++t) {
       const bool more = t + 1 < total;
       const int q0 = qi * BQ;
-      if (++qi == qend) {
-        qi = qfirst;
+      if (--qi < qfirst) {
+        qi = qend - 1;
         ++g;
       }
       if (more) load_regs(g, qi * BQ);
