@@ -386,7 +386,9 @@ def bench_backward(args) -> int:
 def bench_varlen(args) -> int:
     """Packed variable-length causal batch with grouped key/value heads: one
     fa_forward_varlen call over the whole batch.  Useful work 4*d flops per
-    visible pair, as for the square workloads."""
+    visible pair, as for the square workloads.  With --backward: one
+    fa_backward_varlen call (dQ, dK, dV of the same batch from its O and
+    LSE), useful work 10*d flops per visible pair."""
     import numpy as np
     import torch
 
@@ -405,10 +407,26 @@ def bench_varlen(args) -> int:
     mx = int(lens.max())
     out = torch.empty_like(q)
     lse = torch.empty((q.shape[0], wl.H), dtype=torch.float32, device=dev)
-    flops = 4.0 * wl.d * wl.H * float(sum(L * (L + 1) // 2 for L in lens))
+    pairs_all = float(sum(L * (L + 1) // 2 for L in lens))
+    flops = (10.0 if args.backward else 4.0) * wl.d * wl.H * pairs_all
 
-    def step():
+    if args.backward:
+        # upstream gradient: standard normal, bf16, drawn after the inputs
+        rng = np.random.default_rng(wl.seed + 50)
+        dout = conv(W.bf16_encode(rng.standard_normal(inp.q.shape, dtype=np.float32)))
         fa.forward_varlen(q, k, v, cq, ck, mx, mx, scale=wl.scale, causal=True, out=out, lse=lse)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        ws = torch.empty(max(fa.fa_backward_workspace_bytes(1, wl.H, q.shape[0], wl.d,
+                                                            fa.FA_DTYPE_BF16), 1),
+                         dtype=torch.uint8, device=dev)
+
+        def step():
+            fa.backward_varlen(q, k, v, out, lse, dout, cq, ck, mx, mx, scale=wl.scale,
+                               causal=True, workspace=ws, dq=dq, dk=dk, dv=dv)
+    else:
+        def step():
+            fa.forward_varlen(q, k, v, cq, ck, mx, mx, scale=wl.scale, causal=True, out=out,
+                              lse=lse)
 
     stream = torch.cuda.current_stream(dev)
     for _ in range(args.warmup):
@@ -425,27 +443,39 @@ def bench_varlen(args) -> int:
     t_wall = time.perf_counter() - t_wall
     ms = start.elapsed_time(end) / args.steps
     tflops = flops / (ms * 1e-3) / 1e12
+    kind = "backward" if args.backward else "forward"
     result = {
-        "metric": "attention fwd TFLOP/s (bf16, 1 GPU); packed variable-length batch",
+        "metric": ("attention bwd TFLOP/s (bf16, 1 GPU; useful 10*d flops per visible pair); "
+                   "packed variable-length batch" if args.backward else
+                   "attention fwd TFLOP/s (bf16, 1 GPU); packed variable-length batch"),
         "value": tflops, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": dict(wl.describe(), seq_lens=lens.tolist(), total_tokens=int(lens.sum()),
-                       useful_flops=flops, parallelism="single GPU"),
+                       useful_flops=flops, parallelism="single GPU", **{"pass": kind}),
         "roofline": {"bound": "mfma", "achieved": tflops, "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": tflops / PEAK_BF16_TFLOPS,
-                     "traffic": stored_traffic(wl.name), "kernel": "fa_fwd_bf16_kernel",
-                     "kernel_hash": kernel_hash()},
+                     "traffic": stored_traffic(wl.name + (":backward" if args.backward else ""),
+                                               kind),
+                     "kernel": ("fa_bwd_dq_kernel + fa_bwd_dkdv_kernel" if args.backward
+                                else "fa_fwd_bf16_kernel"),
+                     "kernel_hash": kernel_hash(kind)},
         "wall_s_timed_region": t_wall,
     }
     if not args.no_cpu_baseline:
         # the oracle on whole sequences, shortest first, within the time budget
         qx, kx, vx = inp.exact("q"), inp.exact("k"), inp.exact("v")
         t0, done, pairs = time.perf_counter(), 0, 0
+        dox = W.bf16_decode(dout.view(torch.int16).cpu().numpy().view(np.uint16), np.float64) \
+            if args.backward else None
         for b in np.argsort(lens):
             a0, a1 = int(inp.cu_q[b]), int(inp.cu_q[b + 1])
-            oracle.varlen_attention(qx[a0:a1], kx[a0:a1], vx[a0:a1], np.array([0, a1 - a0]),
-                                    np.array([0, a1 - a0]), wl.scale, True)
+            cu1 = np.array([0, a1 - a0])
+            if args.backward:
+                oracle.varlen_attention_backward(qx[a0:a1], kx[a0:a1], vx[a0:a1], dox[a0:a1],
+                                                 cu1, cu1, wl.scale, True)
+            else:
+                oracle.varlen_attention(qx[a0:a1], kx[a0:a1], vx[a0:a1], cu1, cu1, wl.scale, True)
             done += 1
             pairs += (a1 - a0) * (a1 - a0 + 1) // 2
             if time.perf_counter() - t0 > args.cpu_seconds:
@@ -457,7 +487,7 @@ def bench_varlen(args) -> int:
         except Exception:
             threads = len(os.sched_getaffinity(0))
         result["cpu_baseline"] = {
-            "value": 4.0 * wl.d * wl.H * pairs / dt / 1e12, "unit": "TFLOP/s",
+            "value": flops / pairs_all * pairs / dt / 1e12, "unit": "TFLOP/s",
             "cores": int(threads), "kind": "oracle",
             "sample": f"{done} of {wl.B} sequences (shortest first), all heads, fp64; {dt:.1f} s",
             "seconds": dt,
@@ -483,6 +513,8 @@ def main() -> int:
     ap.add_argument("--bias", action="store_true",
                     help="square workloads: time fa_forward_bias with a random fp32 [N, N] "
                          "additive mask shared by all batches and heads")
+    ap.add_argument("--backward", action="store_true",
+                    help="packed workload: time fa_backward_varlen on the batch instead")
     ap.add_argument("--dropout", type=float, default=0.0,
                     help="square workloads: time fa_forward_dropout at this rate instead")
     ap.add_argument("--no-cpu-baseline", action="store_true")
