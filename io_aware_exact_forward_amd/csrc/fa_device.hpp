@@ -80,6 +80,25 @@ __device__ __forceinline__ void load_lds_16(const void* base, uint32_t nbytes, v
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)lds_base, 16, offset, 0, 0, 0);
 }
 
+// Philox4x32 with 10 rounds (Salmon, Moraes, Dror, Shaw, "Parallel random
+// numbers: as easy as 1, 2, 3", SC 2011): words 0 and 2 are multiplied by
+// the round constants, the high halves are mixed with words 1 and 3 and the
+// key, and the key advances by the Weyl increments between rounds.
+__device__ __forceinline__ u32x4 philox4x32_10(u32x4 c, uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r) {
+      k0 += 0x9E3779B9u;
+      k1 += 0xBB67AE85u;
+    }
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c[0];
+    const uint64_t p1 = (uint64_t)0xCD9E8D57u * c[2];
+    c = u32x4{(uint32_t)(p1 >> 32) ^ c[1] ^ k0, (uint32_t)p1, (uint32_t)(p0 >> 32) ^ c[3] ^ k1,
+              (uint32_t)p0};
+  }
+  return c;
+}
+
 // 16 bytes per lane from the raw buffer [base, base + nbytes) into registers
 // (buffer_load_dwordx4): a lane whose offset lies past nbytes reads zeros,
 // so a tile's rows beyond a length need no branch.  nbytes and offsets are

@@ -21,4 +21,9 @@ from .backward import (  # noqa: F401
     kv_head_of,
     varlen_attention_backward,
 )
-from .dropout import dropout_attention, dropout_keep, philox4x32_10  # noqa: F401
+from .dropout import (  # noqa: F401
+    dropout_attention,
+    dropout_attention_backward,
+    dropout_keep,
+    philox4x32_10,
+)

@@ -17,6 +17,15 @@ fixing its random numbers.  The reading taken here:
   * Z_ij = 1 iff u_ij >= floor(p * 2^32), so the keep probability is
     1 - floor(p * 2^32) / 2^32.
 
+The gradient (dropout_attention_backward) treats the mask Z as a constant of
+the step (the same seed and offset regenerate it): with P the undropped
+softmax and dO the upstream gradient of the loss sum(dO * O),
+
+    dV = (P * Z)^T dO / (1 - p)
+    dP = Z * (dO V^T) / (1 - p)
+    D_i = sum_j P_ij dP_ij        (equals dO_i . O_i with the dropped O)
+    dS = P * (dP - D),  dQ = scale * dS K,  dK = scale * dS^T Q.
+
 Pins (tests/test_oracle_dropout.py): the generator against the published
 known-answer vectors of Philox4x32-10 (tests/golden/philox4x32_10_kat.json);
 p = 0 equals attention(); the kept fraction within a binomial bound; the
@@ -30,7 +39,7 @@ import numpy as np
 
 from .attention import NEG_INF, _clamped_length, visible_mask
 
-__all__ = ["philox4x32_10", "dropout_keep", "dropout_attention"]
+__all__ = ["philox4x32_10", "dropout_keep", "dropout_attention", "dropout_attention_backward"]
 
 _M0, _M1 = 0xD2511F53, 0xCD9E8D57  # round multipliers
 _W0, _W1 = 0x9E3779B9, 0xBB67AE85  # key schedule (Weyl) increments
@@ -102,3 +111,35 @@ def dropout_attention(q, k, v, scale, p, seed, offset=0, causal=False, key_len=N
             with np.errstate(divide="ignore"):
                 lse[b, h] = np.where(live, m + np.log(np.where(live, ell, 1.0)), NEG_INF)
     return o, lse
+
+
+def dropout_attention_backward(q, k, v, do, scale, p, seed, offset=0, causal=False, key_len=None):
+    """Gradients (dq, dk, dv, D) of sum(do * O) for O = dropout_attention(q, k,
+    v, scale, p, seed, offset, causal, key_len): square problems [B, H, N, d],
+    masks and positions as ``attention``; the keep mask of every head from
+    ``dropout_keep``.  fp64, materialised per (batch, head)."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    B, H, N, _ = q.shape
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    dvec = np.zeros((B, H, N))
+    for b in range(B):
+        L = _clamped_length(key_len, b, N)
+        vis = visible_mask(np.arange(N), N, L, causal)
+        live = vis.any(axis=1)
+        for h in range(H):
+            s = np.where(vis, scale * (q[b, h] @ k[b, h].T), NEG_INF)
+            m = np.where(live, s.max(axis=1, initial=NEG_INF), 0.0)
+            w = np.where(vis, np.exp(s - m[:, None]), 0.0)
+            ell = w.sum(axis=1)
+            P = np.divide(w, ell[:, None], out=np.zeros_like(w), where=live[:, None])
+            Z = dropout_keep(b, h, H, N, N, p, seed, offset)
+            dv[b, h] = (P * Z).T @ do[b, h] / (1.0 - p)
+            dP = Z * (do[b, h] @ v[b, h].T) / (1.0 - p)
+            dvec[b, h] = (P * dP).sum(axis=1)
+            dS = P * (dP - dvec[b, h][:, None])
+            dq[b, h] = scale * (dS @ k[b, h])
+            dk[b, h] = scale * (dS.T @ q[b, h])
+    return dq, dk, dv, dvec

@@ -115,3 +115,79 @@ def test_head_selection_matches_full_problem():
     part, _ = oracle.dropout_attention(q[:, [3, 1]], k[:, [3, 1]], v[:, [3, 1]], 0.5, 0.4, seed=8,
                                        offset=2, causal=True, head_ids=[3, 1], H_all=H)
     assert np.array_equal(part, full[:, [3, 1]])
+
+
+# ---------------------------------------------------------------------------
+# The gradient with dropout
+# ---------------------------------------------------------------------------
+
+def _fd_dropout(q, k, v, do, scale, p, seed, offset, causal, key_len, eps=1e-6):
+    def loss():
+        o, _ = oracle.dropout_attention(q, k, v, scale, p, seed, offset, causal=causal,
+                                        key_len=key_len)
+        return float((do * o).sum())
+    grads = []
+    for x in (q, k, v):
+        g = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            old = x[idx]
+            x[idx] = old + eps
+            lp = loss()
+            x[idx] = old - eps
+            lm = loss()
+            x[idx] = old
+            g[idx] = (lp - lm) / (2 * eps)
+        grads.append(g)
+    return grads
+
+
+@pytest.mark.parametrize("causal,L", [(False, 7), (True, 7), (True, 4), (False, 0)])
+def test_dropout_gradient_finite_differences(causal, L):
+    B, H, N, d = 1, 2, 7, 3
+    q, k, v, do = (rand((B, H, N, d), s) for s in (951, 952, 953, 954))
+    key_len = np.array([L])
+    dq, dk, dv, _ = oracle.dropout_attention_backward(q, k, v, do, 0.8, 0.3, 77, 5, causal=causal,
+                                                      key_len=key_len)
+    fq, fk, fv = _fd_dropout(q, k, v, do, 0.8, 0.3, 77, 5, causal, key_len)
+    for a, b, name in ((dq, fq, "dq"), (dk, fk, "dk"), (dv, fv, "dv")):
+        assert np.allclose(a, b, atol=1e-8, rtol=0), (name, np.abs(a - b).max())
+
+
+def test_dropout_gradient_zero_rate_is_plain_gradient():
+    B, H, N, d = 2, 2, 9, 4
+    q, k, v, do = (rand((B, H, N, d), s) for s in (961, 962, 963, 964))
+    key_len = np.array([9, 5])
+    for causal in (False, True):
+        got = oracle.dropout_attention_backward(q, k, v, do, 0.5, 0.0, 3, 0, causal=causal,
+                                                key_len=key_len)
+        want = oracle.attention_backward(q, k, v, do, 0.5, causal=causal, key_len=key_len)
+        for a, b in zip(got, want):
+            assert np.allclose(a, b, atol=1e-13)
+
+
+def test_dropout_gradient_d_is_do_dot_o():
+    B, H, N, d = 1, 3, 11, 4
+    q, k, v, do = (rand((B, H, N, d), s) for s in (971, 972, 973, 974))
+    _, _, _, dvec = oracle.dropout_attention_backward(q, k, v, do, 0.6, 0.25, 9, 2, causal=True)
+    o, _ = oracle.dropout_attention(q, k, v, 0.6, 0.25, 9, 2, causal=True)
+    assert np.allclose(dvec, (do * o).sum(axis=-1), atol=1e-12)
+
+
+def test_dropout_gradient_planted_mistakes():
+    """Plausible mistakes fail the finite-difference pin: the mask or the
+    1/(1-p) factor left out of dP (the value gradient alone is still right)."""
+    B, H, N, d = 1, 1, 6, 3
+    q, k, v, do = (rand((B, H, N, d), s) for s in (981, 982, 983, 984))
+    fq, fk, fv = _fd_dropout(q, k, v, do, 0.8, 0.3, 11, 0, False, None)
+    # dP without the mask: the undropped gradient scaled by 1/(1-p)
+    wrong_q = oracle.attention_backward(q, k, v, do / 0.7, 0.8)[0]
+    assert not np.allclose(wrong_q, fq, atol=1e-6)
+    # dP masked but not rescaled: reproduce by scaling dO for dP only
+    Z = D.dropout_keep(0, 0, 1, N, N, 0.3, 11, 0)
+    s = 0.8 * q[0, 0] @ k[0, 0].T
+    P = np.exp(s - s.max(axis=1, keepdims=True)); P /= P.sum(axis=1, keepdims=True)
+    dP = Z * (do[0, 0] @ v[0, 0].T)
+    dS = P * (dP - (P * dP).sum(axis=1, keepdims=True))
+    assert not np.allclose(0.8 * dS @ k[0, 0], fq[0, 0], atol=1e-6)
+    got = oracle.dropout_attention_backward(q, k, v, do, 0.8, 0.3, 11, 0)
+    assert np.allclose(got[0], fq, atol=1e-8)
