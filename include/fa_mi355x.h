@@ -232,6 +232,24 @@ int fa_backward(const void* q, const void* k, const void* v, const void* o, cons
                 void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Backward of fa_forward_dropout's result: the gradients of sum(dO * O) for
+ * O = (P * Z / (1 - p)) V with the keep mask Z of the forward ("IO-aware
+ * exact attention", section "Why implementations form a family", names
+ * dropout among the variants), regenerated from the same Philox4x32-10
+ * stream (seed, offset; counter (j/4, i, b*H + h, offset), draw = word j % 4,
+ * kept iff draw >= floor(p * 2^32)), never stored:
+ *   dV = (P*Z)^T dO / (1-p),  dS = P * (Z * dO V^T / (1-p) - D),  D_i = dO_i . O_i.
+ * Arguments as fa_backward plus p_drop, seed and offset, which must be those
+ * of the fa_forward_dropout call that produced o and lse; p_drop outside
+ * [0, 1) returns FA_ERR_SCALE.  bf16, d = 64 or 128.
+ */
+int fa_backward_dropout(const void* q, const void* k, const void* v, const void* o,
+                        const float* lse, const void* dout, void* dq, void* dk, void* dv, int B,
+                        int H, int N, int d, float scale, int causal,
+                        const int32_t* key_len_mask, int dtype, float p_drop, uint64_t seed,
+                        uint32_t offset, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Backward of fa_forward_split's result (grouped key/value heads, query rows
  * at the end of each sequence's keys), by the recomputation of fa_backward
  * ("IO-aware exact attention", section "Backward recomputation"; grouped
@@ -343,7 +361,7 @@ const char* fa_status_string(int status);
 /* ABI version of this header: (major << 16) | minor. */
 int fa_abi_version(void);
 
-#define FA_ABI_VERSION ((1 << 16) | 6)
+#define FA_ABI_VERSION ((1 << 16) | 7)
 
 #ifdef __cplusplus
 }

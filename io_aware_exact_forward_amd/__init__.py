@@ -17,6 +17,7 @@ from ._lib import (  # noqa: F401
     check,
     fa_abi_version,
     fa_backward,
+    fa_backward_dropout,
     fa_backward_gqa,
     fa_backward_varlen,
     fa_backward_workspace_bytes,
@@ -38,7 +39,7 @@ __all__ = [
     "fa_backward", "fa_backward_workspace_bytes", "fa_naive_backward", "naive_backward",
     "fa_forward_varlen", "forward_varlen", "fa_forward_dropout", "forward_dropout",
     "fa_forward_bias", "forward_bias", "fa_backward_gqa", "backward_gqa", "fa_backward_varlen",
-    "backward_varlen",
+    "backward_varlen", "fa_backward_dropout", "backward_dropout",
     "fa_split_workspace_bytes", "fa_naive_forward", "fa_naive_workspace_bytes",
     "fa_status_string", "fa_abi_version", "FAError", "FA_DTYPE_BF16", "FA_DTYPE_F32",
 ]
@@ -152,8 +153,16 @@ def naive_backward(q, k, v, o, lse, dout, *, scale=None, causal=False, key_len=N
                     workspace=workspace, dq=dq, dk=dk, dv=dv, _naive=True)
 
 
+def backward_dropout(q, k, v, o, lse, dout, *, p_drop, seed, offset=0, scale=None, causal=False,
+                     key_len=None, workspace=None, dq=None, dk=None, dv=None):
+    """dQ, dK, dV = fa_backward_dropout(...): gradients for the result (o, lse)
+    of forward_dropout with the same p_drop, seed, offset and masks."""
+    return backward(q, k, v, o, lse, dout, scale=scale, causal=causal, key_len=key_len,
+                    workspace=workspace, dq=dq, dk=dk, dv=dv, _drop=(p_drop, seed, offset))
+
+
 def backward(q, k, v, o, lse, dout, *, scale=None, causal=False, key_len=None, workspace=None,
-             dq=None, dk=None, dv=None, _naive=False):
+             dq=None, dk=None, dv=None, _naive=False, _drop=None):
     """dQ, dK, dV = fa_backward(...): gradients of sum(dout * O) for the forward
     result (o, lse) of the same q, k, v, scale, causal and key_len."""
     import torch
@@ -181,11 +190,15 @@ def backward(q, k, v, o, lse, dout, *, scale=None, causal=False, key_len=None, w
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
     stream = torch.cuda.current_stream(q.device).cuda_stream
-    fn = fa_naive_backward if _naive else fa_backward
-    check(fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
-             dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d,
-             float(scale), int(bool(causal)), kl, dt, workspace.data_ptr(), workspace.numel(),
-             stream))
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+            dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d,
+            float(scale), int(bool(causal)), kl, dt)
+    tail = (workspace.data_ptr(), workspace.numel(), stream)
+    if _drop is not None:
+        check(fa_backward_dropout(*args, float(_drop[0]), int(_drop[1]), int(_drop[2]), *tail))
+    else:
+        fn = fa_naive_backward if _naive else fa_backward
+        check(fn(*args, *tail))
     return dq, dk, dv
 
 

@@ -352,12 +352,22 @@ extern "C" size_t fa_backward_workspace_bytes(int B, int H, int N, int d, int dt
   return round256(size_t(s.rows) * sizeof(float));
 }
 
-extern "C" int fa_backward(const void* q, const void* k, const void* v, const void* o,
-                           const float* lse, const void* dout, void* dq, void* dk, void* dv,
-                           int B, int H, int N, int d, float scale, int causal,
-                           const int32_t* key_len_mask, int dtype, void* workspace,
-                           size_t workspace_bytes, void* stream) {
+namespace {
+
+// Dropout of the forward whose gradients are taken (fa_forward_dropout's
+// arguments); nullptr for none.
+struct DropArgs {
+  float p;
+  uint64_t seed;
+  uint32_t offset;
+};
+
+int backward_dense(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                   const void* dout, void* dq, void* dk, void* dv, int B, int H, int N, int d,
+                   float scale, int causal, const int32_t* key_len_mask, int dtype,
+                   void* workspace, size_t workspace_bytes, void* stream, const DropArgs* drop) {
   if (dtype != FA_DTYPE_BF16) return FA_ERR_DTYPE;
+  if (drop && !(drop->p >= 0.f && drop->p < 1.f)) return FA_ERR_SCALE;
   if (d != 64 && d != 128) return FA_ERR_HEAD_DIM;
   Shape s;
   bool empty = false;
@@ -412,9 +422,41 @@ extern "C" int fa_backward(const void* q, const void* k, const void* v, const vo
   p.n_ktiles = (N + 127) / 128;
   p.scale = scale;
   p.c2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
+  if (drop) {
+    // the forward's stream and threshold (fa_forward_dropout)
+    p.drop = 1;
+    const double t = std::floor(static_cast<double>(drop->p) * 4294967296.0);
+    p.drop_threshold = static_cast<uint32_t>(std::min(t, 4294967295.0));
+    p.seed_lo = static_cast<uint32_t>(drop->seed & 0xFFFFFFFFu);
+    p.seed_hi = static_cast<uint32_t>(drop->seed >> 32);
+    p.drop_offset = drop->offset;
+    p.keep_scale = static_cast<float>(1.0 / (1.0 - static_cast<double>(drop->p)));
+  }
   if (fa::launch_bwd_bf16(p, d, causal != 0, static_cast<hipStream_t>(stream)) != hipSuccess)
     return FA_ERR_HIP;
   return FA_OK;
+}
+
+}  // namespace
+
+extern "C" int fa_backward(const void* q, const void* k, const void* v, const void* o,
+                           const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                           int B, int H, int N, int d, float scale, int causal,
+                           const int32_t* key_len_mask, int dtype, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  return backward_dense(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, d, scale, causal,
+                        key_len_mask, dtype, workspace, workspace_bytes, stream, nullptr);
+}
+
+extern "C" int fa_backward_dropout(const void* q, const void* k, const void* v, const void* o,
+                                   const float* lse, const void* dout, void* dq, void* dk,
+                                   void* dv, int B, int H, int N, int d, float scale, int causal,
+                                   const int32_t* key_len_mask, int dtype, float p_drop,
+                                   uint64_t seed, uint32_t offset, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+  const DropArgs drop{p_drop, seed, offset};
+  return backward_dense(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, d, scale, causal,
+                        key_len_mask, dtype, workspace, workspace_bytes, stream, &drop);
 }
 
 namespace {

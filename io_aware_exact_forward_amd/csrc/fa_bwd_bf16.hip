@@ -24,6 +24,10 @@
 // (ds_read_b64_tr_b16), with the contraction index permuted to match the
 // register layout of P and dS, exactly as the forward reads V^T.
 //
+// With dropout (the forward's keep mask Z, kept weights scaled by 1/(1-p))
+// the gradients are dV = (P*Z)^T dO / (1-p) and dS = P * (Z*dP/(1-p) - D);
+// both kernels regenerate Z from the forward's Philox4x32-10 stream.
+//
 // Tiles go global -> registers -> LDS (two stages, one workgroup barrier
 // per tile).  Rows and keys at or beyond a sequence's length are loaded as
 // zeros and masked, so they contribute nothing, and their gradients are 0.
@@ -175,7 +179,23 @@ __device__ __forceinline__ GridPos grid_pos(int x, int pairs, int tiles) {
   return {chunk * kChunk + (int)(((unsigned)slot + 8u * (unsigned)tile) % (unsigned)chunk_pairs), tile};
 }
 
-template <int D, bool CAUSAL>
+// Value of lane l ^ K within each group of four lanes (DPP quad permute).
+template <int K>
+__device__ __forceinline__ uint32_t quad_xor(uint32_t x) {
+  constexpr int ctrl = (0 ^ K) | ((1 ^ K) << 2) | ((2 ^ K) << 4) | ((3 ^ K) << 6);
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, ctrl, 0xF, 0xF, false);
+}
+
+// The forward's dropout draws for query row `row` and the four keys
+// 4*(key0/4) .. +3 of head bh: bit t set iff key 4*(key0/4) + t is kept.
+__device__ __forceinline__ uint32_t keep_nibble(const BwdParams& p, uint32_t key0, uint32_t row,
+                                                uint32_t bh) {
+  const u32x4 w = philox4x32_10(u32x4{key0 >> 2, row, bh, p.drop_offset}, p.seed_lo, p.seed_hi);
+  return (uint32_t)(w[0] >= p.drop_threshold) | ((uint32_t)(w[1] >= p.drop_threshold) << 1) |
+         ((uint32_t)(w[2] >= p.drop_threshold) << 2) | ((uint32_t)(w[3] >= p.drop_threshold) << 3);
+}
+
+template <int D, bool CAUSAL, bool DROP>
 __global__ __launch_bounds__(256, kBwdOccupancy<D>) void fa_bwd_dq_kernel(BwdParams p) {
   using C = BwdCfg<D>;
   constexpr int BQ = 128, BK = 64, NB = BK / 32;
@@ -294,14 +314,25 @@ __global__ __launch_bounds__(256, kBwdOccupancy<D>) void fa_bwd_dq_kernel(BwdPar
       for (int bb = 0; bb < NB; ++bb) {
         float ds[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float pr = fast_exp2(__builtin_fmaf(s[bb][r], p.c2, -lse2));
-          if constexpr (masked) {
-            const int key = kv0 + 32 * bb + acc_row(r, h);
-            const bool vis = row_ok && key < kv_lim && (!CAUSAL || key <= pos);
-            pr = vis ? pr : 0.f;
+        for (int q4 = 0; q4 < 4; ++q4) {
+          // registers 4*q4 .. +3: keys kv0 + 32bb + 8q4 + 4h + 0..3 of this lane's row
+          uint32_t keep = 0xFu;
+          if constexpr (DROP)
+            keep = keep_nibble(p, (uint32_t)(kv0 + 32 * bb + 8 * q4 + 4 * h), (uint32_t)row,
+                               (uint32_t)bh);
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const int r = 4 * q4 + t;
+            float pr = fast_exp2(__builtin_fmaf(s[bb][r], p.c2, -lse2));
+            if constexpr (masked) {
+              const int key = kv0 + 32 * bb + acc_row(r, h);
+              const bool vis = row_ok && key < kv_lim && (!CAUSAL || key <= pos);
+              pr = vis ? pr : 0.f;
+            }
+            float g = dp[bb][r];
+            if constexpr (DROP) g = (keep >> t) & 1u ? g * p.keep_scale : 0.f;
+            ds[r] = pr * (g - dval);
           }
-          ds[r] = pr * (dp[bb][r] - dval);
         }
         dsb[bb][0] = pack8(ds);
         dsb[bb][1] = pack8(ds + 8);
@@ -353,8 +384,13 @@ __global__ __launch_bounds__(256, kBwdOccupancy<D>) void fa_bwd_dq_kernel(BwdPar
 // streams the query tiles of every query head that reads this key/value
 // head (H / Hkv of them), so the sum over the group needs no atomics
 // ---------------------------------------------------------------------------
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256, kBwdOccupancy<D>) void fa_bwd_dkdv_kernel(BwdParams p) {
+// The dK/dV kernel with dropout holds its draws as well: one workgroup per CU
+// (twice the registers) at d = 64 too.
+template <int D, bool DROP>
+constexpr int kDkdvOccupancy = DROP ? 1 : kBwdOccupancy<D>;
+
+template <int D, bool CAUSAL, bool DROP>
+__global__ __launch_bounds__(256, (kDkdvOccupancy<D, DROP>)) void fa_bwd_dkdv_kernel(BwdParams p) {
   using C = BwdCfg<D>;
   // 64-row query tiles (at d = 128 the workgroup then holds 490 of the 512
   // registers a lane has at one workgroup per CU)
@@ -375,6 +411,7 @@ __global__ __launch_bounds__(256, kBwdOccupancy<D>) void fa_bwd_dkdv_kernel(BwdP
   const int b = bhk / p.Hkv;
   const int hk = bhk - b * p.Hkv;
   const int G = p.H / p.Hkv;  // query heads hk*G .. hk*G+G-1 read this head
+  const int bh_drop = b * p.H + hk * G;  // dropout stream (dense, G == 1)
   const BwdLayout lay = bwd_layout<D>(p, b, hk * G, hk);
   const int kv_lim = lay.kv_lim, off = lay.off;
   const int k0 = kt_idx * BKW;
@@ -485,6 +522,18 @@ __global__ __launch_bounds__(256, kBwdOccupancy<D>) void fa_bwd_dkdv_kernel(BwdP
           const int r0 = 32 * qb + 8 * q4 + 4 * h;  // four consecutive rows
           const f32x4 l4 = *(const f32x4*)(lse2 + r0);
           const f32x4 d4 = *(const f32x4*)(dd + r0);
+          // Dropout: the four lanes of a quad hold keys 4m .. 4m+3, one draw
+          // group of each row.  Lane u draws for row r0 + u; bit 4t + u of
+          // `keep` is then the mask of this lane's key in row r0 + t.
+          uint32_t keep = 0xFFFFu;
+          if constexpr (DROP) {
+            const uint32_t u = (uint32_t)(l32 & 3);
+            const uint32_t nib =
+                keep_nibble(p, (uint32_t)key, (uint32_t)(q0 + r0) + u, (uint32_t)bh_drop);
+            keep = (nib << (4 * u)) | (quad_xor<1>(nib) << (4 * (u ^ 1))) |
+                   (quad_xor<2>(nib) << (4 * (u ^ 2))) | (quad_xor<3>(nib) << (4 * (u ^ 3)));
+            keep >>= u;
+          }
 #pragma unroll
           for (int t = 0; t < 4; ++t) {
             const int r = 4 * q4 + t;
@@ -494,8 +543,14 @@ __global__ __launch_bounds__(256, kBwdOccupancy<D>) void fa_bwd_dkdv_kernel(BwdP
               const bool vis = key_ok && qrow < qlim && (!CAUSAL || key <= qrow + off);
               e = vis ? e : 0.f;
             }
-            pr[r] = e;
-            ds[r] = e * (dp[r] - d4[t]);
+            if constexpr (DROP) {
+              const bool kept = (keep >> (4 * t)) & 1u;
+              pr[r] = kept ? e * p.keep_scale : 0.f;
+              ds[r] = e * ((kept ? dp[r] * p.keep_scale : 0.f) - d4[t]);
+            } else {
+              pr[r] = e;
+              ds[r] = e * (dp[r] - d4[t]);
+            }
           }
         }
       };
@@ -560,18 +615,18 @@ __global__ __launch_bounds__(256, kBwdOccupancy<D>) void fa_bwd_dkdv_kernel(BwdP
   }
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool DROP>
 hipError_t launch_bwd(const BwdParams& p, hipStream_t stream) {
   const int64_t dq_wgs = (int64_t)p.n_qtiles * p.B * p.H;
   const int64_t dkdv_wgs = (int64_t)p.n_ktiles * p.B * p.Hkv;
   if (dq_wgs > 0) {
-    hipLaunchKernelGGL((fa_bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)dq_wgs), dim3(256), 0,
+    hipLaunchKernelGGL((fa_bwd_dq_kernel<D, CAUSAL, DROP>), dim3((unsigned)dq_wgs), dim3(256), 0,
                        stream, p);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (dkdv_wgs > 0) {
-    hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)dkdv_wgs), dim3(256), 0,
+    hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, CAUSAL, DROP>), dim3((unsigned)dkdv_wgs), dim3(256), 0,
                        stream, p);
     return hipGetLastError();
   }
@@ -580,10 +635,16 @@ hipError_t launch_bwd(const BwdParams& p, hipStream_t stream) {
 
 }  // namespace
 
-hipError_t launch_bwd_bf16(const BwdParams& p, int d, bool causal, hipStream_t stream) {
-  if (d == 128) return causal ? launch_bwd<128, true>(p, stream) : launch_bwd<128, false>(p, stream);
+template <bool DROP>
+hipError_t launch_bwd_d(const BwdParams& p, int d, bool causal, hipStream_t stream) {
+  if (d == 128)
+    return causal ? launch_bwd<128, true, DROP>(p, stream) : launch_bwd<128, false, DROP>(p, stream);
   if (d != 64) return hipErrorInvalidValue;
-  return causal ? launch_bwd<64, true>(p, stream) : launch_bwd<64, false>(p, stream);
+  return causal ? launch_bwd<64, true, DROP>(p, stream) : launch_bwd<64, false, DROP>(p, stream);
+}
+
+hipError_t launch_bwd_bf16(const BwdParams& p, int d, bool causal, hipStream_t stream) {
+  return p.drop ? launch_bwd_d<true>(p, d, causal, stream) : launch_bwd_d<false>(p, d, causal, stream);
 }
 
 }  // namespace fa

@@ -78,6 +78,12 @@ struct BwdParams {
   int n_ktiles;            // ceil(max Nk / 128): workgroups per (b, hkv) of the dK/dV kernel
   float scale;             // signed
   float c2;                // scale * log2(e), signed
+  // dropout of the forward (dense, Hkv == H): keep mask regenerated from the
+  // same Philox4x32-10 stream, dP masked and scaled by keep_scale
+  int drop;
+  uint32_t drop_threshold;  // keep iff draw >= threshold (floor(p * 2^32))
+  uint32_t seed_lo, seed_hi, drop_offset;
+  float keep_scale;         // 1 / (1 - p)
 };
 
 // Row passes of the stored-state (materialised) backward.

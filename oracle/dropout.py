@@ -113,16 +113,24 @@ def dropout_attention(q, k, v, scale, p, seed, offset=0, causal=False, key_len=N
     return o, lse
 
 
-def dropout_attention_backward(q, k, v, do, scale, p, seed, offset=0, causal=False, key_len=None):
+def dropout_attention_backward(q, k, v, do, scale, p, seed, offset=0, causal=False, key_len=None,
+                               head_ids=None, H_all=None, batch_ids=None):
     """Gradients (dq, dk, dv, D) of sum(do * O) for O = dropout_attention(q, k,
     v, scale, p, seed, offset, causal, key_len): square problems [B, H, N, d],
     masks and positions as ``attention``; the keep mask of every head from
-    ``dropout_keep``.  fp64, materialised per (batch, head)."""
+    ``dropout_keep``.  fp64, materialised per (batch, head).
+
+    head_ids / H_all / batch_ids: q, k, v hold heads head_ids of batch
+    entries batch_ids of an H_all-head problem (the mask depends on both
+    indices); by default all of them.  key_len is indexed like q's batch."""
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
     do = np.asarray(do, dtype=np.float64)
     B, H, N, _ = q.shape
+    hids = list(range(H)) if head_ids is None else [int(x) for x in head_ids]
+    bids = list(range(B)) if batch_ids is None else [int(x) for x in batch_ids]
+    H_all = H if H_all is None else int(H_all)
     dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
     dvec = np.zeros((B, H, N))
     for b in range(B):
@@ -135,7 +143,7 @@ def dropout_attention_backward(q, k, v, do, scale, p, seed, offset=0, causal=Fal
             w = np.where(vis, np.exp(s - m[:, None]), 0.0)
             ell = w.sum(axis=1)
             P = np.divide(w, ell[:, None], out=np.zeros_like(w), where=live[:, None])
-            Z = dropout_keep(b, h, H, N, N, p, seed, offset)
+            Z = dropout_keep(bids[b], hids[h], H_all, N, N, p, seed, offset)
             dv[b, h] = (P * Z).T @ do[b, h] / (1.0 - p)
             dP = Z * (do[b, h] @ v[b, h].T) / (1.0 - p)
             dvec[b, h] = (P * dP).sum(axis=1)

@@ -35,6 +35,7 @@ def test_header_declares_expected_entry_points():
         ["fa_forward", "fa_naive_workspace_bytes", "fa_naive_forward", "fa_split_workspace_bytes",
          "fa_forward_split", "fa_forward_varlen", "fa_forward_dropout", "fa_forward_bias",
          "fa_backward_workspace_bytes", "fa_backward", "fa_backward_gqa", "fa_backward_varlen",
+         "fa_backward_dropout",
          "fa_naive_backward",
          "fa_status_string", "fa_abi_version"])
 
@@ -44,7 +45,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     for name in declared_functions():
         assert hasattr(lib, name), name
     assert set(_lib.exported_symbols()) == set(declared_functions())
-    assert fa.fa_abi_version() == (1 << 16) | 6
+    assert fa.fa_abi_version() == (1 << 16) | 7
 
 
 def test_status_strings():
@@ -264,6 +265,27 @@ def test_backward_empty_is_a_no_op():
     for B, H, N in ((0, 2, 64), (1, 0, 64), (1, 2, 0)):
         assert bwd_call(q=0, k=0, v=0, o=0, lse=0, do=0, dq=0, dk=0, dv=0, ws=0, wsb=0,
                         B=B, H=H, N=N) == OK
+
+
+def test_backward_dropout_bad_arguments():
+    def bd(**kw):
+        a = dict(q=Q, k=K, v=V, o=OO, lse=L, do=DO, dq=DQ, dk=DK, dv=DV, B=1, H=2, N=64, d=64,
+                 scale=0.125, causal=0, kl=0, dtype=BF16, p=0.1, seed=5, offset=0, ws=WS,
+                 wsb=1 << 20)
+        a.update(kw)
+        return fa.fa_backward_dropout(a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"], a["dq"],
+                                      a["dk"], a["dv"], a["B"], a["H"], a["N"], a["d"],
+                                      a["scale"], a["causal"], a["kl"], a["dtype"], a["p"],
+                                      a["seed"], a["offset"], a["ws"], a["wsb"], 0)
+    assert bd(dtype=F32) == DTYPE
+    for bad in (-0.1, 1.0, 1.5, float("nan")):
+        assert bd(p=bad) == SCALE, bad
+    assert bd(d=96) == HEAD_DIM
+    assert bd(dq=0) == NULL
+    assert bd(dk=DK + 8) == ALIGN
+    assert bd(ws=0) == WORKSPACE
+    assert bd(dv=Q) == ALIAS
+    assert bd(B=0, q=0, k=0, v=0, o=0, lse=0, do=0, dq=0, dk=0, dv=0, ws=0, wsb=0) == OK
 
 
 def gqa_call(q=Q, k=K, v=V, o=OO, lse=L, do=DO, dq=DQ, dk=DK, dv=DV, B=2, H=8, Hkv=2, Nq=64,

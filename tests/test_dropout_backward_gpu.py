@@ -1,0 +1,132 @@
+"""GPU parity of the backward with dropout (fa_backward_dropout) against
+oracle.dropout_attention_backward, every element of dQ, dK and dV.
+
+Each case runs the HIP forward with dropout (fa_forward_dropout) for O and
+LSE, then the HIP backward with the same rate, seed and offset.  Both sides
+draw the keep mask from Philox4x32-10 with the same key and counters and
+decide it by integer comparison, so the masks agree exactly; the dK/dV
+kernel, whose lanes hold keys rather than rows, exchanges the draws inside
+groups of four lanes, which the cases with several key tiles and ragged
+lengths exercise.
+
+Tolerance: the backward's (tests/test_backward_gpu.py: per gradient tensor,
+max error <= 2e-2 * max |ref|, mean error <= 1.5e-2 * mean |ref|).  Kept
+terms are amplified by 1 / (1 - p), and so are their rounding errors, so the
+errors stay in proportion to the gradients' own scale.  Keys past a length
+and padding rows get exactly zero gradients.  Rate 0 reproduces
+fa_backward.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from io_aware_exact_forward_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+TOL_MAX, TOL_MEAN = 2e-2, 1.5e-2
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def dev(a):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to("cuda:0")
+
+
+def host(t):
+    import torch
+    return W.bf16_decode(t.view(torch.int16).cpu().numpy().view(np.uint16), np.float64)
+
+
+def run(inp, do_bits, causal, scale, p, seed, offset):
+    import torch
+    import io_aware_exact_forward_amd as fa
+    q, k, v, do = dev(inp.q), dev(inp.k), dev(inp.v), dev(do_bits)
+    kl = None if inp.key_len is None else torch.from_numpy(inp.key_len).to("cuda:0")
+    o, lse = fa.forward_dropout(q, k, v, p_drop=p, seed=seed, offset=offset, scale=scale,
+                                causal=causal, key_len=kl)
+    dq, dk, dv = fa.backward_dropout(q, k, v, o, lse, do, p_drop=p, seed=seed, offset=offset,
+                                     scale=scale, causal=causal, key_len=kl)
+    torch.cuda.synchronize()
+    return host(dq), host(dk), host(dv)
+
+
+def check(inp, do_bits, causal, scale, p, seed, offset, got, label):
+    ref = oracle.dropout_attention_backward(inp.exact("q"), inp.exact("k"), inp.exact("v"),
+                                            W.bf16_decode(do_bits, np.float64), scale, p, seed,
+                                            offset, causal=causal, key_len=inp.key_len)[:3]
+    stats = {"label": label}
+    for name, g, r in zip(("dq", "dk", "dv"), got, ref):
+        assert np.all(np.isfinite(g)), f"{label} {name}: non-finite"
+        err = np.abs(g - r)
+        smax, smean = float(np.abs(r).max()), float(np.abs(r).mean())
+        stats[name] = (float(err.max()) / max(smax, 1e-30), float(err.mean()) / max(smean, 1e-30))
+        if smax > 0:
+            assert err.max() <= TOL_MAX * smax, f"{label} {name}: max err {err.max():.3g} vs {smax:.3g}"
+            assert err.mean() <= TOL_MEAN * smean, f"{label} {name}: mean {err.mean():.3g} vs {smean:.3g}"
+        else:
+            assert np.all(g == 0), f"{label} {name}: expected zeros"
+    if inp.key_len is not None:
+        N = inp.exact("q").shape[2]
+        for b, L in enumerate(np.clip(inp.key_len, 0, N)):
+            for g in got:
+                assert np.all(g[b, :, L:] == 0.0), f"{label}: nonzero gradient past the length"
+    say(stats)
+
+
+CASES = [
+    # (B, H, N, d, key_len, p, seed, offset, data seed)
+    (1, 2, 300, 64, None, 0.1, 1234, 0, 9801),
+    (1, 2, 300, 128, None, 0.5, 99, 7, 9802),
+    (2, 2, 513, 128, [513, 200], 0.2, 2 ** 63 + 5, 3, 9803),
+    (2, 1, 129, 64, [129, 63], 0.9, 42, 1, 9804),
+    (1, 2, 64, 128, None, 0.3, 7, 2, 9805),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: f"n{c[2]}d{c[3]}p{c[5]}")
+@pytest.mark.parametrize("causal", [False, True])
+def test_dropout_backward_against_oracle(case, causal):
+    B, H, N, d, key_len, p, seed, offset, ds = case
+    say("case", case, "causal", causal)
+    inp, do = W.grad_inputs(B, H, N, d, ds, key_len=key_len)
+    got = run(inp, do, causal, 1 / np.sqrt(d), p, seed, offset)
+    check(inp, do, causal, 1 / np.sqrt(d), p, seed, offset, got, f"{case} causal={causal}")
+
+
+def test_dropout_backward_rate_zero_is_plain_backward():
+    import torch
+    import io_aware_exact_forward_amd as fa
+    inp, do_bits = W.grad_inputs(1, 2, 333, 128, 9810)
+    q, k, v, do = dev(inp.q), dev(inp.k), dev(inp.v), dev(do_bits)
+    for causal in (False, True):
+        o, lse = fa.forward(q, k, v, causal=causal)
+        a = fa.backward(q, k, v, o, lse, do, causal=causal)
+        b = fa.backward_dropout(q, k, v, o, lse, do, p_drop=0.0, seed=3, causal=causal)
+        torch.cuda.synchronize()
+        for x, y in zip(a, b):
+            assert torch.equal(x, y)
+
+
+def test_dropout_backward_full_size_heads():
+    """The pages' backward workload (batch 2, 16 heads, N 4096, d 64) at rate
+    0.1, causal: every element of two heads (each with its own mask stream)."""
+    wl = W.BWD_WORKLOADS["bwd_b2_h16_n4096_d64_bf16"]
+    inp, do = W.grad_inputs(wl.B, wl.H, wl.N, wl.d, wl.seed)
+    say("full size", wl.name)
+    got = run(inp, do, True, wl.scale, 0.1, 2024, 1)
+    dox = W.bf16_decode(do, np.float64)
+    for b, h in ((0, 0), (1, 15)):
+        sl = lambda x: x[b:b + 1, h:h + 1]
+        ref = oracle.dropout_attention_backward(
+            sl(inp.exact("q")), sl(inp.exact("k")), sl(inp.exact("v")), sl(dox), wl.scale, 0.1,
+            2024, 1, causal=True, head_ids=[h], H_all=wl.H, batch_ids=[b])[:3]
+        for name, g, r in zip(("dq", "dk", "dv"), got, ref):
+            g, r = g[b, h], r[0, 0]
+            err = np.abs(g - r)
+            assert err.max() <= TOL_MAX * np.abs(r).max(), (b, h, name, err.max())
+            assert err.mean() <= TOL_MEAN * np.abs(r).mean(), (b, h, name, err.mean())
+        say({"head": (b, h), "ok": True})

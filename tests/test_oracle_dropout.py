@@ -191,3 +191,15 @@ def test_dropout_gradient_planted_mistakes():
     assert not np.allclose(0.8 * dS @ k[0, 0], fq[0, 0], atol=1e-6)
     got = oracle.dropout_attention_backward(q, k, v, do, 0.8, 0.3, 11, 0)
     assert np.allclose(got[0], fq, atol=1e-8)
+
+
+def test_dropout_gradient_head_selection_matches_full_problem():
+    B, H, N, d = 2, 3, 8, 3
+    q, k, v, do = (rand((B, H, N, d), s) for s in (991, 992, 993, 994))
+    full = oracle.dropout_attention_backward(q, k, v, do, 0.7, 0.4, 21, 3, causal=True)
+    for b, h in ((1, 2), (0, 1)):
+        sl = lambda x: x[b:b + 1, h:h + 1]
+        part = oracle.dropout_attention_backward(sl(q), sl(k), sl(v), sl(do), 0.7, 0.4, 21, 3,
+                                                 causal=True, head_ids=[h], H_all=H, batch_ids=[b])
+        for a, c in zip(part, full):
+            assert np.allclose(a[0, 0], c[b, h], atol=1e-14)
