@@ -33,9 +33,15 @@ is the sum of the per-query-head gradients (grouped_attention_backward); a
 packed batch is a set of independent sequences (varlen_attention_backward).
 Rows sit at the positions of the forward oracle's end-aligned reading.
 
+An additive mask M ("IO-aware exact attention", section "Move less data":
+softmax(Q K^T / sqrt(d) + M)) is a constant of the loss: it enters S and so P,
+and the chain rule above is unchanged (attention_backward(..., bias=M)).
+
 Pins (tests/test_oracle_backward.py): central finite differences of
 sum(dO * O) through the forward oracle on tiny inputs, for every mask, for
-grouped heads with end-aligned rows and for packed batches;
+grouped heads with end-aligned rows, for packed batches and with an additive
+mask (hidden pairs and a wholly hidden row); a per-row constant mask changes
+nothing;
 torch.autograd in float64 through an independently written forward; closed
 forms for uniform scores; invariants (keys' gradients sum to zero, a
 constant added to every value row changes no gradient, the query gradient
@@ -52,13 +58,16 @@ __all__ = ["attention_backward", "grouped_attention_backward", "varlen_attention
            "kv_head_of"]
 
 
-def attention_backward(q, k, v, do, scale, causal=False, key_len=None):
+def attention_backward(q, k, v, do, scale, causal=False, key_len=None, bias=None):
     """Gradients (dq, dk, dv) of sum(do * O) for O = attention(q, k, v, ...).
 
     q, k, v, do: float64 arrays [B, H, N, d] (square: Nq = Nk = N); the
     positions and masks are those of ``attention`` (query row i at key
-    position i, keys j < L_b, padding rows i >= L_b).  Returns three arrays
-    shaped like q, k and v, and D [B, H, N] (D_i = sum_j P_ij dP_ij).
+    position i, keys j < L_b, padding rows i >= L_b).  bias: None, or the
+    additive mask M of ``attention`` (broadcastable to [B, H, N, N]), a
+    constant of the loss: S = scale * Q K^T + M, and -inf entries hide their
+    pair.  Returns three arrays shaped like q, k and v, and D [B, H, N]
+    (D_i = sum_j P_ij dP_ij).
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -69,13 +78,20 @@ def attention_backward(q, k, v, do, scale, causal=False, key_len=None):
     dk = np.zeros_like(k)
     dv = np.zeros_like(v)
     dvec = np.zeros((B, H, N))
+    if bias is not None:
+        bias = np.broadcast_to(np.asarray(bias, dtype=np.float64), (B, H, N, N))
     for b in range(B):
         L = _clamped_length(key_len, b, N)
-        vis = visible_mask(np.arange(N), N, L, causal)
-        live = vis.any(axis=1)
+        vis0 = visible_mask(np.arange(N), N, L, causal)
         for h in range(H):
             # P: the masked softmax of the scaled scores, materialised.
-            s = np.where(vis, scale * (q[b, h] @ k[b, h].T), NEG_INF)
+            s = scale * (q[b, h] @ k[b, h].T)
+            vis = vis0
+            if bias is not None:
+                s = s + bias[b, h]
+                vis = vis0 & (s > NEG_INF)
+            live = vis.any(axis=1)
+            s = np.where(vis, s, NEG_INF)
             m = np.where(live, s.max(axis=1, initial=NEG_INF), 0.0)
             w = np.where(vis, np.exp(s - m[:, None]), 0.0)
             ell = w.sum(axis=1)

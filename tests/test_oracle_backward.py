@@ -310,3 +310,51 @@ def test_varlen_finite_differences(causal):
     # D_i = dO_i . O_i
     o, _ = oracle.varlen_attention(q, k, v, cu_q, cu_k, 0.8, causal=causal)
     assert np.allclose(dvec, (do * o).sum(axis=-1), atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# Additive mask M (a constant of the loss)
+# ---------------------------------------------------------------------------
+
+def bias_loss(q, k, v, do, scale, causal, key_len, bias):
+    o, _ = oracle.attention(q, k, v, scale, causal=causal, key_len=key_len, bias=bias)
+    return float((do * o).sum())
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_bias_finite_differences(causal):
+    B, H, N, d = 1, 2, 6, 3
+    q, k, v, do = (rand((B, H, N, d), s) for s in (1101, 1102, 1103, 1104))
+    bias = rand((1, H, N, N), 1105, 1.5)
+    bias[0, 1, 2, :] = -np.inf            # a row hidden entirely by the mask
+    bias[0, 0, 3, [0, 4]] = -np.inf       # two hidden pairs
+    key_len = np.array([5])
+    dq, dk, dv, _ = oracle.attention_backward(q, k, v, do, 0.7, causal=causal, key_len=key_len,
+                                              bias=bias)
+    fq, fk, fv = _fd((q, k, v), lambda: bias_loss(q, k, v, do, 0.7, causal, key_len, bias))
+    for a, b, name in ((dq, fq, "dq"), (dk, fk, "dk"), (dv, fv, "dv")):
+        assert np.allclose(a, b, atol=1e-8, rtol=0), (name, np.abs(a - b).max())
+    assert np.all(dq[0, 1, 2] == 0)       # the hidden row has no gradient
+
+
+def test_bias_invariants():
+    B, H, N, d = 2, 2, 9, 4
+    q, k, v, do = (rand((B, H, N, d), s) for s in (1111, 1112, 1113, 1114))
+    plain = oracle.attention_backward(q, k, v, do, 0.5, causal=True)
+    zero = oracle.attention_backward(q, k, v, do, 0.5, causal=True, bias=np.zeros((N, N)))
+    # a constant per query row shifts every score of the row: nothing changes
+    row_const = oracle.attention_backward(q, k, v, do, 0.5, causal=True,
+                                          bias=rand((B, H, N, 1), 1115, 3.0))
+    for a, b, c in zip(plain, zero, row_const):
+        assert np.allclose(a, b, atol=1e-14) and np.allclose(a, c, atol=1e-12)
+
+
+def test_bias_planted_mistake_is_caught():
+    """Planted: the mask multiplying the weights instead of adding to the
+    scores fails the finite-difference pin."""
+    B, H, N, d = 1, 1, 5, 3
+    q, k, v, do = (rand((B, H, N, d), s) for s in (1121, 1122, 1123, 1124))
+    bias = rand((N, N), 1125)
+    fq, fk, fv = _fd((q, k, v), lambda: bias_loss(q, k, v, do, 0.8, False, None, bias))
+    wrong = oracle.attention_backward(q, k, v, do, 0.8, bias=np.log(np.abs(bias)))
+    assert not np.allclose(wrong[0], fq, atol=1e-6)
