@@ -250,6 +250,22 @@ int fa_backward_dropout(const void* q, const void* k, const void* v, const void*
                         uint32_t offset, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Backward of fa_forward_bias's result: the gradients dQ, dK, dV of
+ * sum(dO * O) for O = softmax(scale * Q K^T + M) V with the masks of
+ * fa_forward, by the recomputation of fa_backward with P rebuilt from the
+ * masked scores ("IO-aware exact attention", sections "Move less data" and
+ * "Backward recomputation").  M is a constant: no gradient is formed for it.
+ * Arguments as fa_backward, plus the mask of the fa_forward_bias call that
+ * produced o and lse (bias, bias_stride_b, bias_stride_h, bias_ld, with the
+ * layout and checks described there).  bf16, d = 64 or 128.
+ */
+int fa_backward_bias(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                     const void* dout, void* dq, void* dk, void* dv, const float* bias, int B,
+                     int H, int N, int d, float scale, int causal, const int32_t* key_len_mask,
+                     int dtype, int64_t bias_stride_b, int64_t bias_stride_h, int64_t bias_ld,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Backward of fa_forward_split's result (grouped key/value heads, query rows
  * at the end of each sequence's keys), by the recomputation of fa_backward
  * ("IO-aware exact attention", section "Backward recomputation"; grouped
@@ -344,7 +360,9 @@ int fa_forward_dropout(const void* q, const void* k, const void* v, void* o, flo
  *                bias[b * bias_stride_b + h * bias_stride_h + i * bias_ld + j];
  *                a stride of 0 broadcasts over batch or heads.  16-byte aligned;
  *                bias_ld >= N; bias_ld and both strides multiples of 4 (pad the
- *                rows); FA_ERR_SHAPE otherwise.
+ *                rows); FA_ERR_SHAPE otherwise.  Rows are read in 16-byte
+ *                groups, so each row's elements up to the next multiple of 4
+ *                at or above N must be readable (they lie within bias_ld).
  *   dtype        FA_DTYPE_BF16 only.
  * Reading M costs 4 * N * N bytes per (batch, head) it does not broadcast
  * over, on top of the IO-aware traffic.  Other arguments and conventions
@@ -361,7 +379,7 @@ const char* fa_status_string(int status);
 /* ABI version of this header: (major << 16) | minor. */
 int fa_abi_version(void);
 
-#define FA_ABI_VERSION ((1 << 16) | 7)
+#define FA_ABI_VERSION ((1 << 16) | 8)
 
 #ifdef __cplusplus
 }

@@ -17,6 +17,7 @@ from ._lib import (  # noqa: F401
     check,
     fa_abi_version,
     fa_backward,
+    fa_backward_bias,
     fa_backward_dropout,
     fa_backward_gqa,
     fa_backward_varlen,
@@ -40,6 +41,7 @@ __all__ = [
     "fa_forward_varlen", "forward_varlen", "fa_forward_dropout", "forward_dropout",
     "fa_forward_bias", "forward_bias", "fa_backward_gqa", "backward_gqa", "fa_backward_varlen",
     "backward_varlen", "fa_backward_dropout", "backward_dropout",
+    "fa_backward_bias", "backward_bias",
     "fa_split_workspace_bytes", "fa_naive_forward", "fa_naive_workspace_bytes",
     "fa_status_string", "fa_abi_version", "FAError", "FA_DTYPE_BF16", "FA_DTYPE_F32",
 ]
@@ -161,8 +163,17 @@ def backward_dropout(q, k, v, o, lse, dout, *, p_drop, seed, offset=0, scale=Non
                     workspace=workspace, dq=dq, dk=dk, dv=dv, _drop=(p_drop, seed, offset))
 
 
+def backward_bias(q, k, v, o, lse, dout, bias, *, scale=None, causal=False, key_len=None,
+                  workspace=None, dq=None, dk=None, dv=None):
+    """dQ, dK, dV = fa_backward_bias(...): gradients for the result (o, lse) of
+    forward_bias with the same mask (a device float32 tensor broadcastable to
+    [B, H, N, N] as for forward_bias)."""
+    return backward(q, k, v, o, lse, dout, scale=scale, causal=causal, key_len=key_len,
+                    workspace=workspace, dq=dq, dk=dk, dv=dv, _bias=bias)
+
+
 def backward(q, k, v, o, lse, dout, *, scale=None, causal=False, key_len=None, workspace=None,
-             dq=None, dk=None, dv=None, _naive=False, _drop=None):
+             dq=None, dk=None, dv=None, _naive=False, _drop=None, _bias=None):
     """dQ, dK, dV = fa_backward(...): gradients of sum(dout * O) for the forward
     result (o, lse) of the same q, k, v, scale, causal and key_len."""
     import torch
@@ -196,6 +207,9 @@ def backward(q, k, v, o, lse, dout, *, scale=None, causal=False, key_len=None, w
     tail = (workspace.data_ptr(), workspace.numel(), stream)
     if _drop is not None:
         check(fa_backward_dropout(*args, float(_drop[0]), int(_drop[1]), int(_drop[2]), *tail))
+    elif _bias is not None:
+        ptr, sb, sh, ld = _bias_layout(_bias, B, H, N)
+        check(fa_backward_bias(*args[:9], ptr, *args[9:], sb, sh, ld, *tail))
     else:
         fn = fa_naive_backward if _naive else fa_backward
         check(fn(*args, *tail))
@@ -345,6 +359,20 @@ def forward_dropout(q, k, v, *, p_drop, seed, offset=0, scale=None, causal=False
     return out, lse
 
 
+def _bias_layout(bias, B, H, N):
+    """(pointer, batch stride, head stride, row stride) of a mask tensor whose
+    last two dims are [N, ld >= N] and whose batch and head dims have size B
+    or 1 and H or 1 (size 1 broadcasts: stride 0)."""
+    import torch
+    if bias.dtype != torch.float32 or not bias.is_cuda or bias.dim() != 4 or \
+            bias.shape[2] != N or bias.shape[0] not in (1, B) or bias.shape[1] not in (1, H) or \
+            bias.stride(3) != 1:
+        raise FAError(-2, "bias must be a device float32 [B|1, H|1, N, ld] tensor, unit column stride")
+    sb = bias.stride(0) if bias.shape[0] == B and B > 1 else 0
+    sh = bias.stride(1) if bias.shape[1] == H and H > 1 else 0
+    return bias.data_ptr(), sb, sh, bias.stride(2)
+
+
 def forward_bias(q, k, v, bias, *, scale=None, causal=False, key_len=None, out=None, lse=None):
     """O, LSE = fa_forward_bias(...): bias is a device float32 tensor whose last
     two dims are [N, ld >= N] (ld a multiple of 4), with batch and head dims of
@@ -356,13 +384,7 @@ def forward_bias(q, k, v, bias, *, scale=None, causal=False, key_len=None, out=N
         if not t.is_cuda or not t.is_contiguous():
             raise FAError(-1, "q, k, v must be contiguous device tensors")
     B, H, N, d = q.shape
-    if bias.dtype != torch.float32 or not bias.is_cuda or bias.dim() != 4 or \
-            bias.shape[2] != N or bias.shape[0] not in (1, B) or bias.shape[1] not in (1, H) or \
-            bias.stride(3) != 1:
-        raise FAError(-2, "bias must be a device float32 [B|1, H|1, N, ld] tensor, unit column stride")
-    sb = bias.stride(0) if bias.shape[0] == B and B > 1 else 0
-    sh = bias.stride(1) if bias.shape[1] == H and H > 1 else 0
-    ld = bias.stride(2)
+    ptr, sb, sh, ld = _bias_layout(bias, B, H, N)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     kl = 0
@@ -376,6 +398,6 @@ def forward_bias(q, k, v, bias, *, scale=None, causal=False, key_len=None, out=N
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     stream = torch.cuda.current_stream(q.device).cuda_stream
     check(fa_forward_bias(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
-                          bias.data_ptr(), B, H, N, d, float(scale), int(bool(causal)), kl,
+                          ptr, B, H, N, d, float(scale), int(bool(causal)), kl,
                           _dtype_code(q), sb, sh, ld, stream))
     return out, lse

@@ -57,6 +57,12 @@ _SIGNATURES = {
         ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float, ctypes.c_int,
         ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_uint64, ctypes.c_uint32,
         ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "fa_backward_bias": (ctypes.c_int, [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float, ctypes.c_int,
+        ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+        ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
     "fa_backward_gqa": (ctypes.c_int, [
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
@@ -190,6 +196,16 @@ def fa_backward_dropout(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, d, scale, ca
                                       d, scale, int(causal), key_len_mask or None, dtype,
                                       float(p_drop), int(seed), int(offset), workspace or None,
                                       workspace_bytes, stream or None)
+
+
+def fa_backward_bias(q, k, v, o, lse, dout, dq, dk, dv, bias, B, H, N, d, scale, causal,
+                     key_len_mask, dtype, bias_sb, bias_sh, bias_ld, workspace, workspace_bytes,
+                     stream) -> int:
+    return load().fa_backward_bias(q or None, k or None, v or None, o or None, lse or None,
+                                   dout or None, dq or None, dk or None, dv or None, bias or None,
+                                   B, H, N, d, scale, int(causal), key_len_mask or None, dtype,
+                                   bias_sb, bias_sh, bias_ld, workspace or None, workspace_bytes,
+                                   stream or None)
 
 
 def fa_backward_gqa(q, k, v, o, lse, dout, dq, dk, dv, B, H, Hkv, Nq, Nk, d, scale, causal,

@@ -362,10 +362,30 @@ struct DropArgs {
   uint32_t offset;
 };
 
+// Additive mask of the forward whose gradients are taken (fa_forward_bias's
+// arguments); nullptr for none.
+struct BiasArgs {
+  const float* bias;
+  int64_t sb, sh, ld;
+};
+
+// Validates a mask of fa_forward_bias's form for a [B, H, N, N] problem and
+// returns its extent in elements (rows read up to the next multiple of 4,
+// inside bias_ld), or -1 for a bad shape.
+int64_t bias_extent(int B, int H, int N, int64_t sb, int64_t sh, int64_t ld) {
+  if (sb < 0 || sh < 0 || ld < N || ld % 4 != 0 || sb % 4 != 0 || sh % 4 != 0) return -1;
+  const int64_t row = (int64_t(N) + 3) / 4 * 4;
+  const double ext_d = double(B - 1) * double(sb) + double(H - 1) * double(sh) +
+                       double(N - 1) * double(ld) + double(row);
+  if (ext_d > double(int64_t(1) << 60)) return -1;
+  return int64_t(B - 1) * sb + int64_t(H - 1) * sh + int64_t(N - 1) * ld + row;
+}
+
 int backward_dense(const void* q, const void* k, const void* v, const void* o, const float* lse,
                    const void* dout, void* dq, void* dk, void* dv, int B, int H, int N, int d,
                    float scale, int causal, const int32_t* key_len_mask, int dtype,
-                   void* workspace, size_t workspace_bytes, void* stream, const DropArgs* drop) {
+                   void* workspace, size_t workspace_bytes, void* stream, const DropArgs* drop,
+                   const BiasArgs* mask = nullptr) {
   if (dtype != FA_DTYPE_BF16) return FA_ERR_DTYPE;
   if (drop && !(drop->p >= 0.f && drop->p < 1.f)) return FA_ERR_SCALE;
   if (d != 64 && d != 128) return FA_ERR_HEAD_DIM;
@@ -400,6 +420,14 @@ int backward_dense(const void* q, const void* k, const void* v, const void* o, c
     for (int j = i + 1; j < 4; ++j)
       if (overlaps(written[i].p, written[i].n, written[j].p, written[j].n)) return FA_ERR_ALIAS;
   }
+  if (mask) {
+    const int64_t ext = bias_extent(B, H, N, mask->sb, mask->sh, mask->ld);
+    if (ext < 0) return FA_ERR_SHAPE;
+    if (!mask->bias) return FA_ERR_NULL;
+    if (!is_aligned(mask->bias, 16)) return FA_ERR_ALIGN;
+    for (int i = 0; i < 4; ++i)
+      if (overlaps(written[i].p, written[i].n, mask->bias, ext * 4)) return FA_ERR_ALIAS;
+  }
 
   fa::BwdParams p{};
   p.q = q;
@@ -432,6 +460,12 @@ int backward_dense(const void* q, const void* k, const void* v, const void* o, c
     p.drop_offset = drop->offset;
     p.keep_scale = static_cast<float>(1.0 / (1.0 - static_cast<double>(drop->p)));
   }
+  if (mask) {
+    p.bias = mask->bias;
+    p.bias_sb = mask->sb;
+    p.bias_sh = mask->sh;
+    p.bias_ld = mask->ld;
+  }
   if (fa::launch_bwd_bf16(p, d, causal != 0, static_cast<hipStream_t>(stream)) != hipSuccess)
     return FA_ERR_HIP;
   return FA_OK;
@@ -457,6 +491,17 @@ extern "C" int fa_backward_dropout(const void* q, const void* k, const void* v, 
   const DropArgs drop{p_drop, seed, offset};
   return backward_dense(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, d, scale, causal,
                         key_len_mask, dtype, workspace, workspace_bytes, stream, &drop);
+}
+
+extern "C" int fa_backward_bias(const void* q, const void* k, const void* v, const void* o,
+                                const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                                const float* bias, int B, int H, int N, int d, float scale,
+                                int causal, const int32_t* key_len_mask, int dtype,
+                                int64_t bias_stride_b, int64_t bias_stride_h, int64_t bias_ld,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  const BiasArgs mask{bias, bias_stride_b, bias_stride_h, bias_ld};
+  return backward_dense(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, d, scale, causal,
+                        key_len_mask, dtype, workspace, workspace_bytes, stream, nullptr, &mask);
 }
 
 namespace {
@@ -773,15 +818,9 @@ extern "C" int fa_forward_bias(const void* q, const void* k, const void* v, void
   bool empty = false;
   int st = check_scalars(B, H, N, d, scale, dtype, &s, &empty);
   if (st != FA_OK || empty) return st;
-  if (bias_stride_b < 0 || bias_stride_h < 0 || bias_ld < N || bias_ld % 4 != 0 ||
-      bias_stride_b % 4 != 0 || bias_stride_h % 4 != 0)
-    return FA_ERR_SHAPE;
   // extent of the bias in elements (the largest offset read, plus one)
-  const double ext_d = double(B - 1) * double(bias_stride_b) + double(H - 1) * double(bias_stride_h) +
-                       double(N - 1) * double(bias_ld) + double(N);
-  if (ext_d > double(int64_t(1) << 60)) return FA_ERR_SHAPE;
-  const int64_t ext = int64_t(B - 1) * bias_stride_b + int64_t(H - 1) * bias_stride_h +
-                      int64_t(N - 1) * bias_ld + N;
+  const int64_t ext = bias_extent(B, H, N, bias_stride_b, bias_stride_h, bias_ld);
+  if (ext < 0) return FA_ERR_SHAPE;
   st = check_pointers(q, k, v, o, lse, key_len_mask, B, s);
   if (st != FA_OK) return st;
   if (!bias) return FA_ERR_NULL;

@@ -26,7 +26,10 @@
 //
 // With dropout (the forward's keep mask Z, kept weights scaled by 1/(1-p))
 // the gradients are dV = (P*Z)^T dO / (1-p) and dS = P * (Z*dP/(1-p) - D);
-// both kernels regenerate Z from the forward's Philox4x32-10 stream.
+// both kernels regenerate Z from the forward's Philox4x32-10 stream.  With an
+// additive mask M the scores are scale * q . k + M and P is rebuilt from
+// them; the rest is unchanged.  Kernel variants: VAR 0 plain, 1 dropout,
+// 2 additive mask.
 //
 // Tiles go global -> registers -> LDS (two stages, one workgroup barrier
 // per tile).  Rows and keys at or beyond a sequence's length are loaded as
@@ -195,8 +198,9 @@ __device__ __forceinline__ uint32_t keep_nibble(const BwdParams& p, uint32_t key
          ((uint32_t)(w[2] >= p.drop_threshold) << 2) | ((uint32_t)(w[3] >= p.drop_threshold) << 3);
 }
 
-template <int D, bool CAUSAL, bool DROP>
+template <int D, bool CAUSAL, int VAR>
 __global__ __launch_bounds__(256, kBwdOccupancy<D>) void fa_bwd_dq_kernel(BwdParams p) {
+  constexpr bool DROP = VAR == 1, BIAS = VAR == 2;
   using C = BwdCfg<D>;
   constexpr int BQ = 128, BK = 64, NB = BK / 32;
   constexpr int TILE = BK * C::ROW_BYTES;
@@ -253,7 +257,16 @@ __global__ __launch_bounds__(256, kBwdOccupancy<D>) void fa_bwd_dq_kernel(BwdPar
   }
   const float dval = halves_sum(dsum);
   const uint32_t lse_at = (uint32_t)row * lay.lse_ld;
-  const float lse2 = row_ok ? p.lse[lay.lse_base + lse_at] * kLog2e : 0.f;
+  float lse2 = row_ok ? p.lse[lay.lse_base + lse_at] * kLog2e : 0.f;
+  // a row the additive mask hides entirely has LSE -inf (and mask -inf on
+  // every key, so its weights are exactly 0 with lse2 = 0)
+  if (BIAS && lse2 == kNegInf) lse2 = 0.f;
+  // additive mask of this lane's row (clamped to a row of the slice; the
+  // values of rows and keys outside the sequence are masked out)
+  const float* bias_row = nullptr;
+  if constexpr (BIAS)
+    bias_row = p.bias + (int64_t)b * p.bias_sb + (int64_t)hq * p.bias_sh +
+               (int64_t)min(row, Nq - 1) * p.bias_ld;
   if (h == 0 && row < Nq) (p.dvec + lay.lse_base)[lse_at] = row_ok ? dval : 0.f;
 
   f32x16 dq[C::ND];
@@ -320,10 +333,16 @@ __global__ __launch_bounds__(256, kBwdOccupancy<D>) void fa_bwd_dq_kernel(BwdPar
           if constexpr (DROP)
             keep = keep_nibble(p, (uint32_t)(kv0 + 32 * bb + 8 * q4 + 4 * h), (uint32_t)row,
                                (uint32_t)bh);
+          // mask values of the four keys (a 16-byte group inside the padded row)
+          f32x4 m4 = {0.f, 0.f, 0.f, 0.f};
+          if constexpr (BIAS)
+            m4 = *(const f32x4*)(bias_row + min(kv0 + 32 * bb + 8 * q4 + 4 * h,
+                                                (kv_lim - 1) & ~3));
 #pragma unroll
           for (int t = 0; t < 4; ++t) {
             const int r = 4 * q4 + t;
-            float pr = fast_exp2(__builtin_fmaf(s[bb][r], p.c2, -lse2));
+            const float shift = BIAS ? m4[t] * kLog2e - lse2 : -lse2;
+            float pr = fast_exp2(__builtin_fmaf(s[bb][r], p.c2, shift));
             if constexpr (masked) {
               const int key = kv0 + 32 * bb + acc_row(r, h);
               const bool vis = row_ok && key < kv_lim && (!CAUSAL || key <= pos);
@@ -384,13 +403,14 @@ __global__ __launch_bounds__(256, kBwdOccupancy<D>) void fa_bwd_dq_kernel(BwdPar
 // streams the query tiles of every query head that reads this key/value
 // head (H / Hkv of them), so the sum over the group needs no atomics
 // ---------------------------------------------------------------------------
-// The dK/dV kernel with dropout holds its draws as well: one workgroup per CU
-// (twice the registers) at d = 64 too.
-template <int D, bool DROP>
-constexpr int kDkdvOccupancy = DROP ? 1 : kBwdOccupancy<D>;
+// The dK/dV kernel with dropout or a mask holds its draws or mask values as
+// well: one workgroup per CU (twice the registers) at d = 64 too.
+template <int D, int VAR>
+constexpr int kDkdvOccupancy = VAR != 0 ? 1 : kBwdOccupancy<D>;
 
-template <int D, bool CAUSAL, bool DROP>
-__global__ __launch_bounds__(256, (kDkdvOccupancy<D, DROP>)) void fa_bwd_dkdv_kernel(BwdParams p) {
+template <int D, bool CAUSAL, int VAR>
+__global__ __launch_bounds__(256, (kDkdvOccupancy<D, VAR>)) void fa_bwd_dkdv_kernel(BwdParams p) {
+  constexpr bool DROP = VAR == 1, BIAS = VAR == 2;
   using C = BwdCfg<D>;
   // 64-row query tiles (at d = 128 the workgroup then holds 490 of the 512
   // registers a lane has at one workgroup per CU)
@@ -418,6 +438,12 @@ __global__ __launch_bounds__(256, (kDkdvOccupancy<D, DROP>)) void fa_bwd_dkdv_ke
   const int kw0 = k0 + 32 * wave;
   const int key = kw0 + l32;
   const bool key_ok = key < kv_lim;
+  // additive mask column of this lane's key (clamped into the slice; values
+  // of rows and keys outside the sequence are masked out)
+  const float* bias_col = nullptr;
+  if constexpr (BIAS)
+    bias_col = p.bias + (int64_t)b * p.bias_sb + (int64_t)(hk * G) * p.bias_sh +
+               min(kw0 + l32, max(kv_lim - 1, 0));
 
   const uint16_t* kg = (const uint16_t*)p.k + lay.kvbase;
   const uint16_t* vg = (const uint16_t*)p.v + lay.kvbase;
@@ -537,7 +563,10 @@ __global__ __launch_bounds__(256, (kDkdvOccupancy<D, DROP>)) void fa_bwd_dkdv_ke
 #pragma unroll
           for (int t = 0; t < 4; ++t) {
             const int r = 4 * q4 + t;
-            float e = fast_exp2(__builtin_fmaf(s[r], p.c2, -l4[t]));
+            float shift = -l4[t];
+            if constexpr (BIAS)
+              shift += bias_col[(int64_t)min(q0 + r0 + t, max(qlim - 1, 0)) * p.bias_ld] * kLog2e;
+            float e = fast_exp2(__builtin_fmaf(s[r], p.c2, shift));
             if constexpr (masked) {
               const int qrow = q0 + r0 + t;
               const bool vis = key_ok && qrow < qlim && (!CAUSAL || key <= qrow + off);
@@ -615,18 +644,18 @@ __global__ __launch_bounds__(256, (kDkdvOccupancy<D, DROP>)) void fa_bwd_dkdv_ke
   }
 }
 
-template <int D, bool CAUSAL, bool DROP>
+template <int D, bool CAUSAL, int VAR>
 hipError_t launch_bwd(const BwdParams& p, hipStream_t stream) {
   const int64_t dq_wgs = (int64_t)p.n_qtiles * p.B * p.H;
   const int64_t dkdv_wgs = (int64_t)p.n_ktiles * p.B * p.Hkv;
   if (dq_wgs > 0) {
-    hipLaunchKernelGGL((fa_bwd_dq_kernel<D, CAUSAL, DROP>), dim3((unsigned)dq_wgs), dim3(256), 0,
+    hipLaunchKernelGGL((fa_bwd_dq_kernel<D, CAUSAL, VAR>), dim3((unsigned)dq_wgs), dim3(256), 0,
                        stream, p);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (dkdv_wgs > 0) {
-    hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, CAUSAL, DROP>), dim3((unsigned)dkdv_wgs), dim3(256), 0,
+    hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, CAUSAL, VAR>), dim3((unsigned)dkdv_wgs), dim3(256), 0,
                        stream, p);
     return hipGetLastError();
   }
@@ -635,16 +664,18 @@ hipError_t launch_bwd(const BwdParams& p, hipStream_t stream) {
 
 }  // namespace
 
-template <bool DROP>
+template <int VAR>
 hipError_t launch_bwd_d(const BwdParams& p, int d, bool causal, hipStream_t stream) {
   if (d == 128)
-    return causal ? launch_bwd<128, true, DROP>(p, stream) : launch_bwd<128, false, DROP>(p, stream);
+    return causal ? launch_bwd<128, true, VAR>(p, stream) : launch_bwd<128, false, VAR>(p, stream);
   if (d != 64) return hipErrorInvalidValue;
-  return causal ? launch_bwd<64, true, DROP>(p, stream) : launch_bwd<64, false, DROP>(p, stream);
+  return causal ? launch_bwd<64, true, VAR>(p, stream) : launch_bwd<64, false, VAR>(p, stream);
 }
 
 hipError_t launch_bwd_bf16(const BwdParams& p, int d, bool causal, hipStream_t stream) {
-  return p.drop ? launch_bwd_d<true>(p, d, causal, stream) : launch_bwd_d<false>(p, d, causal, stream);
+  if (p.drop) return launch_bwd_d<1>(p, d, causal, stream);
+  if (p.bias) return launch_bwd_d<2>(p, d, causal, stream);
+  return launch_bwd_d<0>(p, d, causal, stream);
 }
 
 }  // namespace fa

@@ -84,6 +84,10 @@ struct BwdParams {
   uint32_t drop_threshold;  // keep iff draw >= threshold (floor(p * 2^32))
   uint32_t seed_lo, seed_hi, drop_offset;
   float keep_scale;         // 1 / (1 - p)
+  // additive mask of the forward (dense, Hkv == H): fp32, element (b, h, i, j)
+  // at bias[b * bias_sb + h * bias_sh + i * bias_ld + j], or nullptr
+  const float* bias;
+  int64_t bias_sb, bias_sh, bias_ld;
 };
 
 // Row passes of the stored-state (materialised) backward.

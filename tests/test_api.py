@@ -35,7 +35,7 @@ def test_header_declares_expected_entry_points():
         ["fa_forward", "fa_naive_workspace_bytes", "fa_naive_forward", "fa_split_workspace_bytes",
          "fa_forward_split", "fa_forward_varlen", "fa_forward_dropout", "fa_forward_bias",
          "fa_backward_workspace_bytes", "fa_backward", "fa_backward_gqa", "fa_backward_varlen",
-         "fa_backward_dropout",
+         "fa_backward_dropout", "fa_backward_bias",
          "fa_naive_backward",
          "fa_status_string", "fa_abi_version"])
 
@@ -45,7 +45,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     for name in declared_functions():
         assert hasattr(lib, name), name
     assert set(_lib.exported_symbols()) == set(declared_functions())
-    assert fa.fa_abi_version() == (1 << 16) | 7
+    assert fa.fa_abi_version() == (1 << 16) | 8
 
 
 def test_status_strings():
@@ -286,6 +286,30 @@ def test_backward_dropout_bad_arguments():
     assert bd(ws=0) == WORKSPACE
     assert bd(dv=Q) == ALIAS
     assert bd(B=0, q=0, k=0, v=0, o=0, lse=0, do=0, dq=0, dk=0, dv=0, ws=0, wsb=0) == OK
+
+
+def test_backward_bias_bad_arguments():
+    BI = A + 14 * (1 << 34)
+
+    def bb(**kw):
+        a = dict(q=Q, k=K, v=V, o=OO, lse=L, do=DO, dq=DQ, dk=DK, dv=DV, bias=BI, B=2, H=2, N=64,
+                 d=64, scale=0.125, causal=0, kl=0, dtype=BF16, sb=2 * 64 * 64, sh=64 * 64, ld=64,
+                 ws=WS, wsb=1 << 20)
+        a.update(kw)
+        return fa.fa_backward_bias(a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"], a["dq"],
+                                   a["dk"], a["dv"], a["bias"], a["B"], a["H"], a["N"], a["d"],
+                                   a["scale"], a["causal"], a["kl"], a["dtype"], a["sb"], a["sh"],
+                                   a["ld"], a["ws"], a["wsb"], 0)
+    assert bb(dtype=F32) == DTYPE
+    assert bb(d=96) == HEAD_DIM
+    for bad in (dict(ld=60), dict(ld=66), dict(sb=-4), dict(sh=6)):
+        assert bb(**bad) == SHAPE, bad
+    assert bb(bias=0) == NULL
+    assert bb(bias=BI + 8) == ALIGN
+    assert bb(dq=BI + 1024) == ALIAS           # an output over the mask
+    assert bb(ws=BI) == ALIAS
+    assert bb(ws=0) == WORKSPACE
+    assert bb(B=0, q=0, k=0, v=0, o=0, lse=0, do=0, dq=0, dk=0, dv=0, bias=0, ws=0, wsb=0) == OK
 
 
 def gqa_call(q=Q, k=K, v=V, o=OO, lse=L, do=DO, dq=DQ, dk=DK, dv=DV, B=2, H=8, Hkv=2, Nq=64,
