@@ -259,7 +259,20 @@ def bench_backward(args) -> int:
     dev = torch.device("cuda:0")
     q, k, v, _ = to_device(inp, dev)
     dout = torch.from_numpy(np.ascontiguousarray(do_bits).view(np.int16)).view(torch.bfloat16).to(dev)
-    o, lse = fa.forward(q, k, v, scale=wl.scale, causal=wl.causal)
+    drop = args.dropout
+    seed, offset = 2024, 1
+    bias_t = None
+    if args.bias:
+        # an fp32 [N, N] additive mask shared by every batch entry and head
+        bias_t = torch.randn((1, 1, N, (N + 3) // 4 * 4), device=dev, dtype=torch.float32,
+                             generator=torch.Generator(device=dev).manual_seed(7))
+        o, lse = fa.forward_bias(q, k, v, bias_t, scale=wl.scale, causal=wl.causal)
+    elif drop > 0:
+        # the forward with dropout, then its gradient with the same stream
+        o, lse = fa.forward_dropout(q, k, v, p_drop=drop, seed=seed, offset=offset,
+                                    scale=wl.scale, causal=wl.causal)
+    else:
+        o, lse = fa.forward(q, k, v, scale=wl.scale, causal=wl.causal)
     ws = torch.empty(fa.fa_backward_workspace_bytes(B, H, N, d, fa.FA_DTYPE_BF16), dtype=torch.uint8,
                      device=dev)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
@@ -267,8 +280,16 @@ def bench_backward(args) -> int:
     flops = 10.0 * d * pairs
 
     def step():
-        fa.backward(q, k, v, o, lse, dout, scale=wl.scale, causal=wl.causal, workspace=ws,
-                    dq=dq, dk=dk, dv=dv)
+        if bias_t is not None:
+            fa.backward_bias(q, k, v, o, lse, dout, bias_t, scale=wl.scale, causal=wl.causal,
+                             workspace=ws, dq=dq, dk=dk, dv=dv)
+        elif drop > 0:
+            fa.backward_dropout(q, k, v, o, lse, dout, p_drop=drop, seed=seed, offset=offset,
+                                scale=wl.scale, causal=wl.causal, workspace=ws, dq=dq, dk=dk,
+                                dv=dv)
+        else:
+            fa.backward(q, k, v, o, lse, dout, scale=wl.scale, causal=wl.causal, workspace=ws,
+                        dq=dq, dk=dk, dv=dv)
 
     stream = torch.cuda.current_stream(dev)
     for _ in range(args.warmup):
@@ -286,7 +307,9 @@ def bench_backward(args) -> int:
     ms = start.elapsed_time(end) / args.steps
     tflops = flops / (ms * 1e-3) / 1e12
     result = {
-        "metric": "attention bwd TFLOP/s (bf16, 1 GPU; useful 10*d flops per visible pair)",
+        "metric": "attention bwd TFLOP/s (bf16, 1 GPU; useful 10*d flops per visible pair)"
+                  + (f"; dropout p={drop}" if drop > 0 else "")
+                  + ("; additive mask fp32 [N, N]" if bias_t is not None else ""),
         "value": tflops,
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -306,7 +329,8 @@ def bench_backward(args) -> int:
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": tflops / PEAK_BF16_TFLOPS,
-            "traffic": stored_traffic(wl.name, "backward") if N == wl.N else None,
+            "traffic": (stored_traffic(wl.name, "backward")
+                        if N == wl.N and drop == 0 and bias_t is None else None),
             "kernel": "fa_bwd_dq_kernel + fa_bwd_dkdv_kernel (one call; both inside the events)",
             "kernel_hash": kernel_hash("backward"),
         },
@@ -315,7 +339,7 @@ def bench_backward(args) -> int:
     # Stored-state comparison (the N x N matrices in HBM): latency and peak
     # allocated memory of both paths, each measured from the same resident
     # inputs and outputs.
-    if not args.no_naive:
+    if not args.no_naive and drop == 0 and bias_t is None:
         def peak_of(fn, ws_bytes):
             torch.cuda.synchronize()
             torch.cuda.reset_peak_memory_stats(dev)
@@ -355,12 +379,21 @@ def bench_backward(args) -> int:
     if not args.no_cpu_baseline:
         qx, kx, vx = inp.exact("q"), inp.exact("k"), inp.exact("v")
         dox = W.bf16_decode(do_bits, np.float64)
+        bias_np = None if bias_t is None else bias_t[0, 0, :, :N].double().cpu().numpy()
         t0, done = time.perf_counter(), 0
         for b in range(B):
             for h in range(H):
-                oracle.attention_backward(qx[b:b + 1, h:h + 1], kx[b:b + 1, h:h + 1],
-                                          vx[b:b + 1, h:h + 1], dox[b:b + 1, h:h + 1], wl.scale,
-                                          causal=wl.causal)
+                sl = lambda x: x[b:b + 1, h:h + 1]
+                if bias_t is not None:
+                    oracle.attention_backward(sl(qx), sl(kx), sl(vx), sl(dox), wl.scale,
+                                              causal=wl.causal, bias=bias_np)
+                elif drop > 0:
+                    oracle.dropout_attention_backward(sl(qx), sl(kx), sl(vx), sl(dox), wl.scale,
+                                                      drop, seed, offset, causal=wl.causal,
+                                                      head_ids=[h], H_all=H, batch_ids=[b])
+                else:
+                    oracle.attention_backward(sl(qx), sl(kx), sl(vx), sl(dox), wl.scale,
+                                              causal=wl.causal)
                 done += 1
                 if time.perf_counter() - t0 > args.cpu_seconds:
                     break
@@ -512,11 +545,13 @@ def main() -> int:
                     help="backward workload only: another sequence length (512 .. 4096)")
     ap.add_argument("--bias", action="store_true",
                     help="square workloads: time fa_forward_bias with a random fp32 [N, N] "
-                         "additive mask shared by all batches and heads")
+                         "additive mask shared by all batches and heads; the backward "
+                         "workload: fa_backward_bias of such a forward")
     ap.add_argument("--backward", action="store_true",
                     help="packed workload: time fa_backward_varlen on the batch instead")
     ap.add_argument("--dropout", type=float, default=0.0,
-                    help="square workloads: time fa_forward_dropout at this rate instead")
+                    help="square workloads: time fa_forward_dropout at this rate instead; the "
+                         "backward workload: fa_backward_dropout of such a forward")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-naive", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
