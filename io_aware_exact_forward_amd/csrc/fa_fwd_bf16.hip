@@ -81,13 +81,14 @@ struct Bf16Cfg {
 
 
 template <int D, bool CAUSAL, int WAVES, int NSTAGE, bool PINGPONG, bool DROP = false,
-          bool BIAS = false>
+          bool BIAS = false, bool PERSIST = false>
 // Two lockstep workgroups per CU (256 registers per lane), except with an
 // additive mask at d = 64, whose extra registers do not fit: one workgroup.
 __global__ __launch_bounds__(64 * WAVES,
                              (WAVES == 4 && NSTAGE == 2 && !(BIAS && D == 64)) ? 2 : 1)
 void fa_fwd_bf16_kernel(FwdParams p) {
   static_assert(!(DROP || BIAS) || !PINGPONG, "dropout and bias run in the lockstep schedule");
+  static_assert(!PERSIST || PINGPONG, "the persistent form is the ping-pong schedule's");
   using C = Bf16Cfg<D, WAVES, NSTAGE>;
   __shared__ __attribute__((aligned(1024))) uint8_t lds[C::LDS_BYTES];
 
@@ -107,20 +108,38 @@ void fa_fwd_bf16_kernel(FwdParams p) {
   // K/V rows are reused from L2; with 32 pairs per chunk every head's tiles
   // land on one XCD (workgroups are dealt round-robin to the 8 XCDs).
   const int BH = p.B * p.H;
-  int x = blockIdx.x;
-  const int split = x % p.splits;
-  x /= p.splits;
-  constexpr int kChunk = 32;
-  const int chunk_wgs = kChunk * p.n_qtiles;
-  const int chunk = x / chunk_wgs;
-  const int in_chunk = x - chunk * chunk_wgs;
-  const int chunk_heads = min(kChunk, BH - chunk * kChunk);
-  const int bh = chunk * kChunk + in_chunk % chunk_heads;
-  int qt = in_chunk / chunk_heads;
-  if (CAUSAL) qt = p.n_qtiles - 1 - qt;  // heaviest tiles first
-  const int b = bh / p.H;
-  const int hq = bh - b * p.H;
-  const int hk = hq / (p.H / p.Hkv);  // the key/value head this query head reads
+  // Persistent form (dense layout, one key range): workgroup w takes the
+  // units w, w + G, w + 2G, ... (G workgroups, p.persist units each); unit
+  // u is the query tiles n_qtiles - 1 - j and j of (batch, head) u % BH,
+  // j = u / BH, in that order.  The two tiles of a unit see n_qtiles + 1
+  // query tiles' worth of keys together under the causal mask, so every
+  // workgroup gets the same work; with G a multiple of 8 and BH a multiple
+  // of 8, all the units of a (batch, head) run on the XCD of its workgroups.
+  auto item_of = [&](const int i, int& ibh, int& iqt) __attribute__((always_inline)) {
+    const int u = (int)blockIdx.x + (i >> 1) * (int)gridDim.x;
+    ibh = u % BH;
+    const int j = u / BH;
+    iqt = (i & 1) ? j : p.n_qtiles - 1 - j;
+  };
+  int split = 0, bh, qt;
+  if constexpr (PERSIST) {
+    item_of(0, bh, qt);
+  } else {
+    int x = blockIdx.x;
+    split = x % p.splits;
+    x /= p.splits;
+    constexpr int kChunk = 32;
+    const int chunk_wgs = kChunk * p.n_qtiles;
+    const int chunk = x / chunk_wgs;
+    const int in_chunk = x - chunk * chunk_wgs;
+    const int chunk_heads = min(kChunk, BH - chunk * kChunk);
+    bh = chunk * kChunk + in_chunk % chunk_heads;
+    qt = in_chunk / chunk_heads;
+    if (CAUSAL) qt = p.n_qtiles - 1 - qt;  // heaviest tiles first
+  }
+  int b = bh / p.H;
+  int hq = bh - b * p.H;
+  int hk = hq / (p.H / p.Hkv);  // the key/value head this query head reads
   // Layout of this (batch, head): dense [B, H, N, d] / [B, Hkv, Nk, d], or a
   // packed batch [T, H, d] / [T, Hkv, d] with sequence b at rows cu[b] ..
   // cu[b+1]-1.  Row strides and bases in elements; all workgroup-uniform.
@@ -146,7 +165,7 @@ void fa_fwd_bf16_kernel(FwdParams p) {
     lse_base = (int64_t)bh * N;
     lse_ld = 1;
   }
-  const int q0 = qt * C::BQ;
+  int q0 = qt * C::BQ;
   int kv_lim = Nk;
   if (p.key_len) {
     const int L = p.key_len[b];
@@ -168,23 +187,26 @@ void fa_fwd_bf16_kernel(FwdParams p) {
   // sequence end and the diagonal need element masks.
   const int kv_first = split * p.split_keys;
   const int kv_last = min(n_kv, kv_first + p.split_keys);
-  const int ntiles = kv_last > kv_first ? (kv_last - kv_first + C::BK - 1) / C::BK : 0;
+  int ntiles = kv_last > kv_first ? (kv_last - kv_first + C::BK - 1) / C::BK : 0;
 
   const uint16_t* __restrict__ qg = (const uint16_t*)p.q + base;
 
-  const int qw0 = q0 + 32 * wave;  // first query row of this wave
-  const int qrow = qw0 + l32;      // the query row this lane owns
-  const int qwpos = qw0 + off;     // key position of the wave's first row
-  const int qpos = qrow + off;     // key position of this lane's row
+  int qw0 = q0 + 32 * wave;  // first query row of this wave
+  int qrow = qw0 + l32;      // the query row this lane owns
+  int qwpos = qw0 + off;     // key position of the wave's first row
+  int qpos = qrow + off;     // key position of this lane's row
 
   // ---- Q fragments (B operand of S^T = K Q^T) -----------------------------
+  // (the persistent form loads them at the start of each query tile)
   bf16x8 qf[D / 16];
+  if constexpr (!PERSIST) {
 #pragma unroll
-  for (int kk = 0; kk < D / 16; ++kk) {
-    u32x4 w = {0u, 0u, 0u, 0u};
-    if (qrow < N) w = *(const u32x4*)(qg + (int64_t)qrow * q_ld + 16 * kk + 8 * h);
-    w ^= p.q_sign;
-    qf[kk] = __builtin_bit_cast(bf16x8, w);
+    for (int kk = 0; kk < D / 16; ++kk) {
+      u32x4 w = {0u, 0u, 0u, 0u};
+      if (qrow < N) w = *(const u32x4*)(qg + (int64_t)qrow * q_ld + 16 * kk + 8 * h);
+      w ^= p.q_sign;
+      qf[kk] = __builtin_bit_cast(bf16x8, w);
+    }
   }
 
   // ---- K/V tile loads: HBM -> LDS, range-checked ---------------------------
@@ -692,8 +714,17 @@ void fa_fwd_bf16_kernel(FwdParams p) {
     static_assert(WAVES == 8 && NSTAGE >= 4, "ping-pong needs 8 waves and 4 or more stages");
     constexpr int LA = NSTAGE - 2;  // tiles loaded ahead of the one being multiplied
     const int grp = wave >> 2;
+    // Persistent form: the tiles of all this workgroup's query tiles form one
+    // stream through the ring; sbase is the stream position of the current
+    // query tile's first key tile.
+    int sbase = 0;
     auto stage_of = [&](const int t) __attribute__((always_inline)) {
-      return (uint32_t)(NSTAGE == 4 ? (t & 3) : t % NSTAGE);
+      if constexpr (PERSIST) {
+        static_assert(NSTAGE == 4, "stream positions map to stages by their low bits");
+        return (uint32_t)((sbase + t) & 3);
+      } else {
+        return (uint32_t)(NSTAGE == 4 ? (t & 3) : t % NSTAGE);
+      }
     };
     auto k_stage = [&](const int t) __attribute__((always_inline)) {
       return lds0 + stage_of(t) * C::STAGE_BYTES;
@@ -707,10 +738,61 @@ void fa_fwd_bf16_kernel(FwdParams p) {
       const uint32_t nb = u < ntiles ? valid_bytes : 0u;
       load_tile_n(kv_first + u * C::BK, stage_of(u), __builtin_amdgcn_readfirstlane(nb));
     };
-    auto issue_loads = [&](const int t) __attribute__((always_inline)) { load_ahead(t + LA); };
+    // Persistent form: a cursor over the stream.  Each call loads the next
+    // stream position (the next key tile of the query tile the cursor is in,
+    // else the first of the next query tile; past the last one a zero fill),
+    // so the loads that run ahead of a query tile's last products bring in
+    // the first tiles of the next one.
+    const int n_items = PERSIST ? 2 * p.persist : 1;
+    auto item_ntiles = [&](const int iqt) __attribute__((always_inline)) {
+      const int nk = CAUSAL ? min(Nk, iqt * C::BQ + C::BQ) : Nk;
+      return (nk + C::BK - 1) / C::BK;
+    };
+    auto item_kv = [&](const int ibh) __attribute__((always_inline)) {
+      const int ib = ibh / p.H, ihq = ibh - ib * p.H;
+      return ((int64_t)ib * p.Hkv + ihq / (p.H / p.Hkv)) * Nk * D;
+    };
+    int l_item = 0, l_tile = 0, l_nt = ntiles, l_pos = 0;
+    int64_t l_kv = kvbase;
+    auto load_next = [&]() __attribute__((always_inline)) {
+      const bool live = l_item < n_items;
+      uint8_t* ks = lds + (l_pos & 3) * C::STAGE_BYTES;
+      uint8_t* vs = ks + C::TILE_BYTES;
+      const uint32_t nb = __builtin_amdgcn_readfirstlane(live ? valid_bytes : 0u);
+      const uint32_t tile_off =
+          __builtin_amdgcn_readfirstlane((uint32_t)(l_tile * C::BK) * row_stride);
+      const void* kb = (const uint16_t*)p.k + l_kv;
+      const void* vb = (const uint16_t*)p.v + l_kv;
 #pragma unroll
-    for (int u = 0; u < LA; ++u) load_ahead(u);
-    vmem_wait<(LA - 1) * C::LOADS_PER_TILE>();  // tile 0
+      for (int i = 0; i < C::LOADS; ++i) {
+        const int blk = (WAVES * i + wave) * 1024;
+        load_lds_16(kb, nb, ks + blk, koff[i] + tile_off);
+        load_lds_16(vb, nb, vs + blk, voff[i] + tile_off);
+      }
+      ++l_pos;
+      if (live && ++l_tile == l_nt) {
+        ++l_item;
+        l_tile = 0;
+        if (l_item < n_items) {
+          int ibh, iqt;
+          item_of(l_item, ibh, iqt);
+          l_nt = item_ntiles(iqt);
+          l_kv = item_kv(ibh);
+        }
+      }
+    };
+    auto issue_loads = [&](const int t) __attribute__((always_inline)) {
+      if constexpr (PERSIST) load_next();
+      else load_ahead(t + LA);
+    };
+    if constexpr (PERSIST) {
+      load_next();
+      load_next();
+    } else {
+#pragma unroll
+      for (int u = 0; u < LA; ++u) load_ahead(u);
+      vmem_wait<(LA - 1) * C::LOADS_PER_TILE>();  // tile 0
+    }
     // Softmax phase t.  The V fragments of tile t are read at its end, where
     // this wave's SIMD has LDS bandwidth to spare, so the MFMA phase that
     // multiplies them reads only K.  (Issued after the exponentials, when
@@ -765,8 +847,106 @@ void fa_fwd_bf16_kernel(FwdParams p) {
       issue_loads(ntiles);
       pv_pre(pf, K0, K0, [](auto) {});
     };
-    if (grp == 0) run(std::integral_constant<int, 0>{});
-    else run(std::integral_constant<int, 1>{});
+    // Persistent form.  Query tile X's own loop is the one above, with these
+    // differences.  Its first key tiles were loaded by the previous query
+    // tile's last phases (the loads that would otherwise be zero fills);
+    // its Q rows are loaded at its start (buffer loads into the Q fragments;
+    // rows past N read zeros), and the epilogue of X runs right after its
+    // last product, then the state is reset.  Stage reuse across the
+    // boundary is the same as within a query tile: the last phase of X and
+    // the first phase of X + 1 together are one phase of the stream.
+    //
+    // Before barrier 0 only key tile 0 must have landed.  The loads issued
+    // after it are its successors in the stream (tile 1, and for X > 0
+    // tile 2) and the Q rows; loads complete in issue order, so while tile
+    // 0 is in flight all of those are too, and waiting until no more than
+    // their number are outstanding waits for tile 0 and nothing later
+    // (stores in between only make the wait stricter).
+    auto epilogue_dense = [&](const int ebh, const int eq0) __attribute__((always_inline)) {
+      const float l_tot = halves_sum(l_run);
+      const float lp_tot = halves_sum(lp_run);
+      const int row = eq0 + 32 * wave + l32;
+      const bool valid = row < N && lp_tot > 0.f;
+      const float inv = valid ? 1.f / lp_tot : 0.f;
+      const float lse_row = valid ? (m_ref + __log2f(l_tot)) * kLn2 : kNegInf;
+      if (row < N) {
+        uint16_t* og = (uint16_t*)p.o + ((int64_t)ebh * N + row) * D;
+#pragma unroll
+        for (int db = 0; db < C::ND; ++db) {
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int d0 = 32 * db + 8 * g + 4 * h;
+            float y[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) y[e] = valid ? o_acc[db][4 * g + e] * inv : 0.f;
+            u32x2 w = {pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
+            *(u32x2*)(og + d0) = w;
+          }
+        }
+        if (h == 0) p.lse[(int64_t)ebh * N + row] = lse_row;
+      }
+#pragma unroll
+      for (int i = 0; i < C::ND; ++i) o_acc[i] = f32x16{};
+      m_ref = kNegInf;
+      l_run = 0.f;
+      lp_run = 0.f;
+    };
+    auto run_p = [&](auto grp_tag) __attribute__((always_inline)) {
+      constexpr bool first = decltype(grp_tag)::value == 0;
+      for (int it = 0;; ++it) {
+        {
+          const void* qn = (const uint16_t*)p.q + (int64_t)bh * N * D;
+          const uint32_t qoff = (uint32_t)(qrow * C::ROW_BYTES + 16 * h);
+#pragma unroll
+          for (int kk = 0; kk < D / 16; ++kk)
+            qf[kk] = __builtin_bit_cast(bf16x8, load_ranged_16(qn, (uint32_t)N * C::ROW_BYTES,
+                                                               qoff + 32 * kk));
+        }
+        constexpr int QL = D / 16;  // Q loads per wave
+        if (it == 0) vmem_wait<C::LOADS_PER_TILE + QL>();  // tile 0 (tile 1, Q in flight)
+        else vmem_wait<2 * C::LOADS_PER_TILE + QL>();      // tile 0 (tiles 1, 2, Q in flight)
+        barrier_no_fence();  // barrier 0
+        __builtin_amdgcn_s_setprio(1);
+        if (it == 0) load_next();
+        k_issue(G0, k_stage(0), kr[0]);
+        compute_s(k_stage(0), s, PRE1);
+        for (int t = 1; t < ntiles; ++t) {
+          if constexpr (first) softmax_phase(t - 1);
+          vmem_wait<(LA - 1) * C::LOADS_PER_TILE>();  // this wave's loads of tile t
+          barrier_no_fence();              // barrier t
+          if constexpr (!first) softmax_phase(t - 1);
+          mfma_phase(t);
+        }
+        if constexpr (first) softmax_phase(ntiles - 1);
+        barrier_no_fence();  // barrier ntiles
+        if constexpr (!first) softmax_phase(ntiles - 1);
+        __builtin_amdgcn_s_setprio(1);
+        issue_loads(ntiles);
+        pv_pre(pf, K0, K0, [](auto) {});
+        if (it + 1 >= n_items) break;
+        epilogue_dense(bh, q0);
+        int nbh, nqt;
+        item_of(it + 1, nbh, nqt);
+        sbase += ntiles;
+        bh = nbh;
+        q0 = nqt * C::BQ;
+        ntiles = item_ntiles(nqt);
+        qw0 = q0 + 32 * wave;
+        qrow = qw0 + l32;
+        qwpos = qw0;
+        qpos = qrow;
+      }
+    };
+    if constexpr (PERSIST) {
+      if (grp == 0) run_p(std::integral_constant<int, 0>{});
+      else run_p(std::integral_constant<int, 1>{});
+      // the last query tile's epilogue below writes through these
+      base = (int64_t)bh * N * D;
+      lse_base = (int64_t)bh * N;
+    } else {
+      if (grp == 0) run(std::integral_constant<int, 0>{});
+      else run(std::integral_constant<int, 1>{});
+    }
     __builtin_amdgcn_s_setprio(0);
     // No load into LDS may still be in flight when the workgroup ends.
     vmem_wait<0>();
@@ -817,14 +997,48 @@ void fa_fwd_bf16_kernel(FwdParams p) {
 }
 
 template <int D, bool CAUSAL, int WAVES, int NSTAGE, bool PINGPONG, bool DROP = false,
-          bool BIAS = false>
+          bool BIAS = false, bool PERSIST = false>
 hipError_t launch_cfg(FwdParams p, hipStream_t stream) {
   using C = Bf16Cfg<D, WAVES, NSTAGE>;
   p.n_qtiles = (p.N + C::BQ - 1) / C::BQ;
-  const dim3 grid((unsigned)((int64_t)p.n_qtiles * p.B * p.H * p.splits));
-  hipLaunchKernelGGL((fa_fwd_bf16_kernel<D, CAUSAL, WAVES, NSTAGE, PINGPONG, DROP, BIAS>), grid,
-                     dim3(64 * WAVES), 0, stream, p);
+  const int64_t items = (int64_t)p.n_qtiles * p.B * p.H * p.splits;
+  // persistent: items / 2 units, p.persist per workgroup
+  const dim3 grid((unsigned)(PERSIST ? items / 2 / p.persist : items));
+  hipLaunchKernelGGL((fa_fwd_bf16_kernel<D, CAUSAL, WAVES, NSTAGE, PINGPONG, DROP, BIAS, PERSIST>),
+                     grid, dim3(64 * WAVES), 0, stream, p);
   return hipGetLastError();
+}
+
+// Compute units of the current device (cached per device; 0 if unknown).
+int device_cus() {
+  static int cache[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  int n = __atomic_load_n(&cache[dev], __ATOMIC_RELAXED);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    __atomic_store_n(&cache[dev], n, __ATOMIC_RELAXED);
+  }
+  return n;
+}
+
+// Units (pairs of 256-row query tiles) per workgroup of the persistent
+// launch, or 0 where it does not apply: it needs the dense layout with as
+// many keys as queries and no per-sequence lengths (so every row sits at its
+// own key position and every query tile sees at least two key tiles), one
+// key range, a non-negative scale, and a number of units that the compute
+// units divide exactly (the static assignment is then balanced; otherwise
+// the hardware dispatcher's dynamic order balances better).
+int persist_units(const FwdParams& p) {
+  if (p.key_len || p.cu_q || p.splits != 1 || p.Nk != p.N || p.q_sign || p.o_part || p.drop ||
+      p.bias || p.N < 256)
+    return 0;
+  const int64_t nq = (p.N + 255) / 256;
+  if (nq % 2) return 0;
+  const int64_t units = (int64_t)p.B * p.H * nq / 2;
+  const int cus = device_cus();
+  if (cus <= 0 || cus % 8 || units % cus) return 0;
+  return (int)(units / cus);
 }
 
 template <int D, bool CAUSAL>
@@ -836,8 +1050,15 @@ hipError_t launch_d(const FwdParams& p, hipStream_t stream) {
   if (p.drop) return launch_cfg<D, CAUSAL, 4, 2, false, true>(p, stream);
   if (p.bias) return launch_cfg<D, CAUSAL, 4, 2, false, false, true>(p, stream);
   const int64_t big_tiles = (int64_t)p.B * p.H * ((p.N + 255) / 256) * p.splits;
-  if (p.N >= 256 && big_tiles >= 512)
+  if (p.N >= 256 && big_tiles >= 512) {
+    const int units = persist_units(p);
+    if (units > 0) {
+      FwdParams pp = p;
+      pp.persist = units;
+      return launch_cfg<D, CAUSAL, 8, kPingPongStages, true, false, false, true>(pp, stream);
+    }
     return launch_cfg<D, CAUSAL, 8, kPingPongStages, true>(p, stream);
+  }
   return launch_cfg<D, CAUSAL, 4, 2, false>(p, stream);
 }
 

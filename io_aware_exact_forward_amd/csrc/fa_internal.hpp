@@ -32,6 +32,7 @@ struct FwdParams {
   uint32_t drop_threshold; // a weight is dropped when its draw is below this
   uint32_t seed_lo, seed_hi, drop_offset;  // Philox key and counter word 3
   float keep_scale;        // 1 / (1 - p)
+  int persist;             // > 0: persistent launch, this many units (query-tile pairs) per workgroup
   float c;                 // |scale| * log2(e): scores enter exp2 in log2 units
   uint32_t q_sign;         // sign bits xor-ed into Q when scale < 0 (0 otherwise)
 };
