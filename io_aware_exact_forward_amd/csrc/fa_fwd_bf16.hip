@@ -252,6 +252,7 @@ void fa_fwd_bf16_kernel(FwdParams p) {
   float m_ref = kNegInf;  // reference maximum of scale*log2(e)*s
   float l_run = 0.f;      // this lane's part of the fp32 denominator
   float lp_run = 0.f;     // the same over the bf16-rounded probabilities
+  float lp_run2 = 0.f;    // its second chain in the ping-pong schedule (o uses the sum)
   // With an additive mask the scores are taken to log2 units (and the mask
   // added) before the softmax step, which then works with a unit scale.
   const float c = BIAS ? 1.f : p.c;
@@ -447,6 +448,7 @@ void fa_fwd_bf16_kernel(FwdParams p) {
       m_ref = m_new;
       l_run *= alpha;
       lp_run *= alpha;
+      lp_run2 *= alpha;
 #pragma unroll
       for (int i = 0; i < C::ND; ++i) o_acc[i] *= alpha;
       lt = exp_pack(s, pf, (m_ref == kNegInf) ? 0.f : -m_ref);
@@ -554,23 +556,25 @@ void fa_fwd_bf16_kernel(FwdParams p) {
       __attribute__((always_inline)) {
     constexpr int KPRE = decltype(kpre_tag)::value;
     constexpr int KPER = decltype(kper_tag)::value;
-    // lp_run, the sum of the bf16 weights the product multiplies, so that
-    // a / lp_run is an exact convex combination of V rows under those
-    // weights (a dominant key is then reproduced without the 2^-9 error
-    // of its rounded weight).  The dot products run on the matrix pipe:
-    // here, back to back ahead of this wave's own MFMAs (interleaved with
-    // them, each one costs the pipe a turnaround; in the softmax step each
-    // would wait for a whole MFMA of the other wave sharing the SIMD).
+    // lp_run + lp_run2, the sum of the bf16 weights the product multiplies,
+    // so that a / (lp_run + lp_run2) is an exact convex combination of V
+    // rows under those weights (a dominant key is then reproduced without
+    // the 2^-9 error of its rounded weight).  The dot products run on the
+    // matrix pipe: here, back to back ahead of this wave's own MFMAs
+    // (interleaved with them, each one costs the pipe a turnaround; in the
+    // softmax step each would wait for a whole MFMA of the other wave
+    // sharing the SIMD), in two independent chains (one chain waits out
+    // each product's latency: 1 % slower on the whole kernel).
     static_for<2 * C::NB>([&](auto fc) __attribute__((always_inline)) {
       constexpr int f = decltype(fc)::value;
       const bf16x8 w = pf[f / 2][f % 2];
       static_for<4>([&](auto jc) __attribute__((always_inline)) {
         constexpr int j = decltype(jc)::value;
-        lp_run = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{w[2 * j], w[2 * j + 1]}, ones, lp_run,
-                                                 false);
+        float& acc = j % 2 == 0 ? lp_run : lp_run2;
+        acc = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{w[2 * j], w[2 * j + 1]}, ones, acc, false);
       });
     });
-    asm volatile("" : "+v"(lp_run));  // keeps the sum here
+    asm volatile("" : "+v"(lp_run), "+v"(lp_run2));  // keeps the sums here
     __builtin_amdgcn_sched_barrier(0);
     static_for<VG>([&](auto gc) __attribute__((always_inline)) {
       constexpr int g = decltype(gc)::value;
@@ -864,7 +868,7 @@ void fa_fwd_bf16_kernel(FwdParams p) {
     // (stores in between only make the wait stricter).
     auto epilogue_dense = [&](const int ebh, const int eq0) __attribute__((always_inline)) {
       const float l_tot = halves_sum(l_run);
-      const float lp_tot = halves_sum(lp_run);
+      const float lp_tot = halves_sum(lp_run + lp_run2);
       const int row = eq0 + 32 * wave + l32;
       const bool valid = row < N && lp_tot > 0.f;
       const float inv = valid ? 1.f / lp_tot : 0.f;
@@ -890,6 +894,7 @@ void fa_fwd_bf16_kernel(FwdParams p) {
       m_ref = kNegInf;
       l_run = 0.f;
       lp_run = 0.f;
+      lp_run2 = 0.f;
     };
     auto run_p = [&](auto grp_tag) __attribute__((always_inline)) {
       constexpr bool first = decltype(grp_tag)::value == 0;
@@ -956,7 +961,7 @@ void fa_fwd_bf16_kernel(FwdParams p) {
   // Rows at or beyond the key length are padding (o = 0, LSE = -inf); so is
   // a row that saw no key in this workgroup's range.
   const float l_tot = halves_sum(l_run);
-  const float lp_tot = halves_sum(lp_run);
+  const float lp_tot = halves_sum(lp_run + lp_run2);
   const bool valid = qpos < kv_lim && lp_tot > 0.f;
   const float inv = valid ? (DROP ? p.keep_scale : 1.f) / lp_tot : 0.f;
   const float lse_row = valid ? (m_ref + __log2f(l_tot)) * kLn2 : kNegInf;
