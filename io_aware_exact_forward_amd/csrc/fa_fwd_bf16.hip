@@ -417,14 +417,18 @@ void fa_fwd_bf16_kernel(FwdParams p) {
     }
     const bool masked = (CAUSAL && kv0 + C::BK - 1 > qwpos) || (kv0 + C::BK > kv_lim);
     if (masked) {
+      // Key kv0 + 32 bb + acc_row(r, h) is visible iff it is below the
+      // length and (causal) at or before the row's position, i.e. iff the
+      // compile-time offset 32 bb + acc_row(r, 0) is at most one per-lane
+      // bound: one compare and one select per score.
+      int bound = kv_lim - 1 - kv0;
+      if (CAUSAL) bound = min(bound, qpos - kv0);
+      bound -= 4 * h;
 #pragma unroll
       for (int bb = 0; bb < C::NB; ++bb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kv0 + 32 * bb + acc_row(r, h);
-          const bool vis = key < kv_lim && (!CAUSAL || key <= qpos);
-          s[bb][r] = vis ? s[bb][r] : kNegInf;
-        }
+        for (int r = 0; r < 16; ++r)
+          s[bb][r] = 32 * bb + acc_row(r, 0) <= bound ? s[bb][r] : kNegInf;
     }
     mid();
     bool slow = __any(m_ref == kNegInf);
