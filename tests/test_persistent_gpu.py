@@ -1,7 +1,7 @@
 """GPU parity of the persistent form of the 256-row forward kernel.
 
 The library runs one workgroup per compute unit over a balanced list of
-query-tile pairs when the problem allows it (dense layout, Nk == N, no
+query tiles when the problem allows it (dense layout, Nk == N, no
 per-sequence lengths, one key range, and B*H*ceil(N/256)/2 a multiple of the
 compute-unit count).  Passing key lengths that are all N changes nothing in
 the result but takes the one-tile-per-workgroup launch of the same kernel, so
@@ -50,7 +50,9 @@ def sampled_rows(N, H, seed):
 
 @pytest.mark.parametrize("d,causal,N", [(128, True, 4096), (128, False, 4096),
                                         (64, True, 4096), (64, False, 2048),
-                                        (128, True, 4000)])
+                                        (128, True, 4000), (64, True, 4000),
+                                        (128, True, 8192), (128, False, 8192),
+                                        (64, True, 8192)])
 def test_persistent_matches_per_tile_launch(d, causal, N):
     import torch
     import io_aware_exact_forward_amd as fa
