@@ -45,7 +45,7 @@ DEFAULT_WORKLOAD = "h32_n8192_d128_causal_bf16"
 HEADERS = ["fa_bf16_tiles.hpp", "fa_device.hpp", "fa_internal.hpp"]
 KERNEL_SOURCES = {
     "forward": ["fa_fwd_bf16.hip", "fa_fwd_f32.hip"] + HEADERS,
-    "split": ["fa_fwd_bf16.hip", "fa_merge.hip"] + HEADERS,
+    "split": ["fa_fwd_bf16.hip", "fa_merge.hip", "fa_decode.hip"] + HEADERS,
     "backward": ["fa_bwd_bf16.hip"] + HEADERS,
 }
 

@@ -22,8 +22,8 @@ LIBDIR = os.path.join(PKG, "lib")
 LIBNAME = "libfa_mi355x.so"
 ARCH = "gfx950"
 
-SOURCES = ["fa_api.cpp", "fa_fwd_bf16.hip", "fa_fwd_f32.hip", "fa_merge.hip", "fa_bwd_bf16.hip",
-           "naive_softmax.hip", "naive_backward.hip"]
+SOURCES = ["fa_api.cpp", "fa_fwd_bf16.hip", "fa_fwd_f32.hip", "fa_merge.hip", "fa_decode.hip",
+           "fa_bwd_bf16.hip", "naive_softmax.hip", "naive_backward.hip"]
 
 # Packed fp32 VALU forms are kept out of the generated code; the compiler
 # would otherwise pair independent fp32 operations into them.

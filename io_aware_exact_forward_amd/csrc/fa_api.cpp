@@ -330,7 +330,11 @@ extern "C" int fa_forward_split(const void* q, const void* k, const void* v, voi
     p.o_part = static_cast<float*>(workspace);
     p.lse_part = reinterpret_cast<float*>(static_cast<char*>(workspace) + split_part_bytes(sp, d));
   }
-  if (fa::launch_fwd_bf16(p, d, causal != 0, hs) != hipSuccess) return FA_ERR_HIP;
+  // one query row: the row sees every key below its sequence's length
+  // whether or not the mask is causal
+  const hipError_t e = Nq == 1 ? fa::launch_decode_bf16(p, d, hs)
+                               : fa::launch_fwd_bf16(p, d, causal != 0, hs);
+  if (e != hipSuccess) return FA_ERR_HIP;
   if (sp.splits > 1) {
     fa::MergeParams mp{};
     mp.o_part = p.o_part;

@@ -64,6 +64,13 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+// x from another lane of the same row of 16, by a DPP control (quad_perm,
+// row mirrors): all rows and banks enabled, every lane has a source.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+  const int v = __builtin_bit_cast(int, x);
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(v, CTRL, 0xF, 0xF, false));
+}
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;

@@ -106,6 +106,8 @@ constexpr int kQueryTile = 128;
 
 hipError_t launch_fwd_bf16(const FwdParams& p, int d, bool causal, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdParams& p, int d, bool causal, hipStream_t stream);
+// One query row per (batch, head) (Nq = 1, rows at the end of the keys), bf16.
+hipError_t launch_decode_bf16(const FwdParams& p, int d, hipStream_t stream);
 hipError_t launch_naive_softmax(const NaiveSoftmaxParams& p, bool bf16, hipStream_t stream);
 hipError_t launch_merge(const MergeParams& p, int d, bool bf16, hipStream_t stream);
 hipError_t launch_bwd_bf16(const BwdParams& p, int d, bool causal, hipStream_t stream);
