@@ -203,7 +203,7 @@ def bench_decode(args) -> int:
             "unit": "GB/s",
             "frac": gbs / PEAK_HBM_GBS,
             "traffic": stored_traffic(wl.name, "split"),
-            "kernel": "fa_fwd_bf16_kernel + merge_kernel (one call; both inside the events)",
+            "kernel": "fa_decode_kernel + merge_kernel (one call; both inside the events)",
             "kernel_hash": kernel_hash("split"),
         },
         "wall_s_timed_region": t_wall,

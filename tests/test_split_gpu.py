@@ -170,3 +170,28 @@ def test_split_grouped_heads(case, causal, num_splits):
     scale = 1.0 / np.sqrt(d)
     o, lse = run_split(inp, causal, scale, num_splits)
     check(inp, causal, scale, o, lse, f"gqa {case} causal={causal} splits={num_splits}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("num_splits", [0, 3])
+def test_decode_negative_scale_and_nan_padding(d, num_splits):
+    """One query row per (sequence, head) with a negative scale (the sign is
+    folded into q) and NaN in the K/V rows past a sequence's length, which
+    must never be read: the result equals the oracle on the clean inputs."""
+    import torch
+    import io_aware_exact_forward_amd as fa
+    B, H, Nk = 2, 3, 700
+    inp = W.cache_inputs(B, H, 1, Nk, d, 9131 + d, key_len=[700, 333])
+    q, k, v = dev(inp.q), dev(inp.k), dev(inp.v)
+    nan = torch.tensor(0x7FC0, dtype=torch.int16).view(torch.bfloat16)
+    k[1, :, 333:] = nan
+    v[1, :, 333:] = nan
+    kl = torch.from_numpy(inp.key_len).to("cuda:0")
+    scale = -0.1
+    say("case", f"decode d={d} splits={num_splits} scale={scale}")
+    o, lse = fa.forward_split(q, k, v, scale=scale, causal=True, key_len=kl,
+                              num_splits=num_splits)
+    torch.cuda.synchronize()
+    og = W.bf16_decode(o.view(torch.int16).cpu().numpy().view(np.uint16), np.float64)
+    check(inp, True, scale, og, lse.cpu().numpy().astype(np.float64),
+          f"decode d={d} splits={num_splits} negative scale, NaN padding")
