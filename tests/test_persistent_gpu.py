@@ -48,15 +48,15 @@ def sampled_rows(N, H, seed):
     return np.array([x[:R] for x in out], dtype=np.int64)
 
 
-@pytest.mark.parametrize("d,causal,N", [(128, True, 4096), (128, False, 4096),
-                                        (64, True, 4096), (64, False, 2048),
-                                        (128, True, 4000), (64, True, 4000),
-                                        (128, True, 8192), (128, False, 8192),
-                                        (64, True, 8192)])
-def test_persistent_matches_per_tile_launch(d, causal, N):
+@pytest.mark.parametrize("B,d,causal,N", [(1, 128, True, 4096), (1, 128, False, 4096),
+                                          (1, 64, True, 4096), (1, 64, False, 2048),
+                                          (1, 128, True, 4000), (1, 64, True, 4000),
+                                          (1, 128, True, 8192), (1, 128, False, 8192),
+                                          (1, 64, True, 8192),
+                                          (2, 128, True, 4096), (2, 64, False, 4096)])
+def test_persistent_matches_per_tile_launch(B, d, causal, N):
     import torch
     import io_aware_exact_forward_amd as fa
-    B = 1
     H = heads_for_persistence(B, N)
     inp = W.random_inputs(B, H, N, d, "bf16", seed=400 + d + N + causal, key_len=None)
     scale = 1.0 / math.sqrt(d)
@@ -74,20 +74,21 @@ def test_persistent_matches_per_tile_launch(d, causal, N):
     say(st)
 
 
-def test_persistent_grouped_heads():
+@pytest.mark.parametrize("B,causal", [(1, True), (2, False)])
+def test_persistent_grouped_heads(B, causal):
     """Grouped K/V heads through the split entry point with one key range."""
     import torch
     import io_aware_exact_forward_amd as fa
-    B, N, d, G = 1, 4096, 128, 4
+    N, d, G = 4096, 128, 4
     H = heads_for_persistence(B, N)
     inp = W.random_inputs(B, H, N, d, "bf16", seed=431, key_len=None)
-    say("case", f"grouped B={B} H={H} Hkv={H // G} N={N} d={d}")
+    say("case", f"grouped B={B} H={H} Hkv={H // G} N={N} d={d} causal={causal}")
     q, k, v, _ = to_device(inp)
     k, v = k[:, ::G].contiguous(), v[:, ::G].contiguous()
     scale = 1.0 / math.sqrt(d)
-    o1, l1 = fa.forward_split(q, k, v, scale=scale, causal=True, num_splits=1)
+    o1, l1 = fa.forward_split(q, k, v, scale=scale, causal=causal, num_splits=1)
     kl = torch.full((B,), N, dtype=torch.int32, device=q.device)
-    o2, l2 = fa.forward_split(q, k, v, scale=scale, causal=True, num_splits=1, key_len=kl)
+    o2, l2 = fa.forward_split(q, k, v, scale=scale, causal=causal, num_splits=1, key_len=kl)
     torch.cuda.synchronize()
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
     assert torch.equal(l1.view(torch.int32), l2.view(torch.int32))
@@ -95,7 +96,7 @@ def test_persistent_grouped_heads():
     kx = np.repeat(inp.exact("k")[:, ::G], G, axis=1)
     vx = np.repeat(inp.exact("v")[:, ::G], G, axis=1)
     rows = sampled_rows(N, H, 6)
-    o_ref, l_ref = oracle.attention(inp.exact("q"), kx, vx, scale, causal=True, rows=rows)
+    o_ref, l_ref = oracle.attention(inp.exact("q"), kx, vx, scale, causal=causal, rows=rows)
     og = from_device(o1)
     lg = l1.cpu().numpy().astype(np.float64)
     og = np.stack([og[:, h, rows[h]] for h in range(H)], axis=1)
