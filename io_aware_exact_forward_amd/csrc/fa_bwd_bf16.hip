@@ -321,6 +321,11 @@ __global__ __launch_bounds__(256, kBwdOccupancy<D>) void fa_bwd_dq_kernel(BwdPar
     bf16x8 dsb[NB][2];
     const bool full = (!CAUSAL || kv0 + BK - 1 <= qw0 + off) && kv0 + BK <= kv_lim &&
                       qw0 + 31 < Nq && qw0 + 31 + off < kv_lim;
+    // Key kv0 + 32 bb + acc_row(r, h) is visible to this lane's row iff
+    // its compile-time offset 32 bb + acc_row(r, 0) is at most one per-lane
+    // bound (below the length, at or before the row's position if causal;
+    // nothing for a row outside the sequence).
+    const int kbound = row_ok ? (CAUSAL ? min(kv_lim - 1, pos) : kv_lim - 1) - kv0 - 4 * h : -1;
     auto grads = [&](auto masked_tag) __attribute__((always_inline)) {
       constexpr bool masked = decltype(masked_tag)::value;
 #pragma unroll
@@ -343,11 +348,7 @@ __global__ __launch_bounds__(256, kBwdOccupancy<D>) void fa_bwd_dq_kernel(BwdPar
             const int r = 4 * q4 + t;
             const float shift = BIAS ? m4[t] * kLog2e - lse2 : -lse2;
             float pr = fast_exp2(__builtin_fmaf(s[bb][r], p.c2, shift));
-            if constexpr (masked) {
-              const int key = kv0 + 32 * bb + acc_row(r, h);
-              const bool vis = row_ok && key < kv_lim && (!CAUSAL || key <= pos);
-              pr = vis ? pr : 0.f;
-            }
+            if constexpr (masked) pr = 32 * bb + acc_row(r, 0) <= kbound ? pr : 0.f;
             float g = dp[bb][r];
             if constexpr (DROP) g = (keep >> t) & 1u ? g * p.keep_scale : 0.f;
             ds[r] = pr * (g - dval);
@@ -541,6 +542,12 @@ __global__ __launch_bounds__(256, (kDkdvOccupancy<D, VAR>)) void fa_bwd_dkdv_ker
       }
       // lane = key, register r = row 32qb + acc_row(r, h)
       float pr[16], ds[16];
+      // Row q0 + 32 qb + 4 h + c sees this lane's key iff c lies in
+      // [rlo, rhi]: below the query count (nothing for a key outside the
+      // sequence) and, if causal, at or after the key's position.
+      const int rbase = q0 + 32 * qb + 4 * h;
+      const int rhi = key_ok ? qlim - 1 - rbase : -1;
+      const int rlo = key - off - rbase;
       auto probs = [&](auto masked_tag) __attribute__((always_inline)) {
         constexpr bool masked = decltype(masked_tag)::value;
 #pragma unroll
@@ -568,8 +575,8 @@ __global__ __launch_bounds__(256, (kDkdvOccupancy<D, VAR>)) void fa_bwd_dkdv_ker
               shift += bias_col[(int64_t)min(q0 + r0 + t, max(qlim - 1, 0)) * p.bias_ld] * kLog2e;
             float e = fast_exp2(__builtin_fmaf(s[r], p.c2, shift));
             if constexpr (masked) {
-              const int qrow = q0 + r0 + t;
-              const bool vis = key_ok && qrow < qlim && (!CAUSAL || key <= qrow + off);
+              const int c = 8 * (r >> 2) + (r & 3);  // row q0 + 32 qb + 4 h + c
+              const bool vis = CAUSAL ? (c <= rhi && c >= rlo) : c <= rhi;
               e = vis ? e : 0.f;
             }
             if constexpr (DROP) {
