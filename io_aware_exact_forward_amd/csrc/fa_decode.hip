@@ -31,8 +31,8 @@ constexpr int kDecodeWaves = 4;
 
 template <int D>
 __global__ __launch_bounds__(64 * kDecodeWaves) void fa_decode_kernel(FwdParams p) {
-  constexpr int LPR = D / 8;   // lanes per V row (16 bytes each)
-  constexpr int G = 64 / LPR;  // key groups per wave in the value step
+  constexpr int LPR = D / 8;   // lanes per K or V row (16 bytes each)
+  constexpr int G = 64 / LPR;  // key groups per wave
   constexpr int IT = 64 / G;   // keys per group and chunk
   static_assert(LPR == 8 || LPR == 16, "d = 64 or 128");
   __shared__ float m_lds[kDecodeWaves], l_lds[kDecodeWaves];
@@ -57,12 +57,11 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void fa_decode_kernel(FwdParams 
   const int k0 = split * p.split_keys;
   const int k1 = min(L, k0 + p.split_keys);
 
-
   const uint32_t row_bytes = D * 2;
   const void* kbase = (const uint16_t*)p.k + ((int64_t)b * p.Hkv + hk) * p.Nk * D;
   const void* vbase = (const uint16_t*)p.v + ((int64_t)b * p.Hkv + hk) * p.Nk * D;
   const uint32_t valid_bytes = (uint32_t)L * row_bytes;
-  const int g = lane / LPR, t = lane % LPR;  // value step: key group, 16-byte column
+  const int g = lane / LPR, t = lane % LPR;  // key group, 16-byte column
 
   float m_run = kNegInf;  // running maximum of c * s (log2 units), wave-uniform
   float l_g = 0.f;        // denominator over group g's keys (the same in its LPR lanes)
