@@ -1059,7 +1059,12 @@ hipError_t launch_d(const FwdParams& p, hipStream_t stream) {
   if (p.drop) return launch_cfg<D, CAUSAL, 4, 2, false, true>(p, stream);
   if (p.bias) return launch_cfg<D, CAUSAL, 4, 2, false, false, true>(p, stream);
   const int64_t big_tiles = (int64_t)p.B * p.H * ((p.N + 255) / 256) * p.splits;
-  if (p.N >= 256 && big_tiles >= 512) {
+  // At d = 64 with per-sequence key lengths the lockstep schedule is the
+  // faster one: the ping-pong computes masked tiles and padding rows in
+  // full, and at d = 64 their softmax work dominates (8 x 16 x 4096 with
+  // ragged lengths: 327 -> 295 us); at d = 128 it is not.
+  const bool ragged64 = D == 64 && p.key_len;
+  if (p.N >= 256 && big_tiles >= 512 && !ragged64) {
     const int units = persist_units(p);
     if (units > 0) {
       FwdParams pp = p;

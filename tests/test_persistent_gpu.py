@@ -3,10 +3,11 @@
 The library runs one workgroup per compute unit over a balanced list of
 query tiles when the problem allows it (dense layout, Nk == N, no
 per-sequence lengths, one key range, and B*H*ceil(N/256)/2 a multiple of the
-compute-unit count).  Passing key lengths that are all N changes nothing in
-the result but takes the one-tile-per-workgroup launch of the same kernel, so
-both launches must agree bit for bit on every element; sampled rows are also
-compared with the fp64 oracle.
+compute-unit count, non-negative scale).  A negative scale is applied by
+flipping the sign bits of Q, which is exact, and takes the one-tile-per-
+workgroup launch of the same kernel: forward(q, scale=-s) and forward(-q,
+scale=s) compute the same values, so the two launches must agree bit for bit
+on every element.  Sampled rows are also compared with the fp64 oracle.
 """
 import math
 
@@ -62,14 +63,13 @@ def test_persistent_matches_per_tile_launch(B, d, causal, N):
     scale = 1.0 / math.sqrt(d)
     say("case", f"B={B} H={H} N={N} d={d} causal={causal}")
     q, k, v, _ = to_device(inp)
-    o1, l1 = fa.forward(q, k, v, scale=scale, causal=causal)
-    kl = torch.full((B,), N, dtype=torch.int32, device=q.device)
-    o2, l2 = fa.forward(q, k, v, scale=scale, causal=causal, key_len=kl)
+    o1, l1 = fa.forward(q, k, v, scale=-scale, causal=causal)   # one tile per workgroup
+    o2, l2 = fa.forward(-q, k, v, scale=scale, causal=causal)   # persistent
     torch.cuda.synchronize()
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)), "O differs between launches"
     assert torch.equal(l1.view(torch.int32), l2.view(torch.int32)), "LSE differs between launches"
     rows = sampled_rows(N, H, 5)
-    st = compare(inp, from_device(o1), l1.cpu().numpy().astype(np.float64), causal, scale,
+    st = compare(inp, from_device(o2), l2.cpu().numpy().astype(np.float64), causal, -scale,
                  rows=rows, label=f"persistent d={d} causal={causal} N={N}")
     say(st)
 
