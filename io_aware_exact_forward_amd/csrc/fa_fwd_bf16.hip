@@ -338,11 +338,21 @@ void fa_fwd_bf16_kernel(FwdParams p) {
     for (int bb = 0; bb < C::NB; ++bb) {
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
+        // a group's eight FMAs, then its eight exponentials, then its sums
+        // and packing (the compiler would pair each FMA with its
+        // exponential; the blocked order measured 0.2-0.7 % faster)
         float e[8];
 #pragma unroll
         for (int t8 = 0; t8 < 8; ++t8)
+          e[t8] = __builtin_fmaf(s[bb][8 * half + t8], c, neg_m);
+        asm volatile("" : "+v"(e[0]), "+v"(e[1]), "+v"(e[2]), "+v"(e[3]), "+v"(e[4]), "+v"(e[5]),
+                     "+v"(e[6]), "+v"(e[7]));
+#pragma unroll
+        for (int t8 = 0; t8 < 8; ++t8)
           // masked scores are -inf and c > 0, so they give exactly 0
-          e[t8] = fast_exp2(__builtin_fmaf(s[bb][8 * half + t8], c, neg_m));
+          e[t8] = fast_exp2(e[t8]);
+        asm volatile("" : "+v"(e[0]), "+v"(e[1]), "+v"(e[2]), "+v"(e[3]), "+v"(e[4]), "+v"(e[5]),
+                     "+v"(e[6]), "+v"(e[7]));
         bf16x2 pr[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
