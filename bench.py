@@ -73,6 +73,112 @@ def stored_traffic(workload: str, kind: str = "forward"):
     return ent.get("hbm_bytes_per_launch")
 
 
+def stored_clock_cycles(workload: str, kind: str = "forward"):
+    """GRBM_GUI_ACTIVE cycles per XCD per launch from the committed counter
+    summary, if taken on the current kernel source; else None.  The count is
+    the same for every launch of a kernel (it is the work, not the time), so
+    dividing it by a launch's duration gives the engine clock of that run."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            ent = json.load(f).get(workload)
+    except (OSError, ValueError):
+        return None
+    if not ent or ent.get("kernel_hash") != kernel_hash(kind):
+        return None
+    return ent.get("grbm_gui_active_per_xcd_per_launch")
+
+
+def clock_record(workload: str, kind: str, ms: float, peak: float):
+    """Engine clock of the timed steps and the dense peak at that clock."""
+    cyc = stored_clock_cycles(workload, kind)
+    if not cyc:
+        return None
+    ghz = cyc / (ms * 1e-3) / 1e9
+    return {"engine_ghz": ghz, "peak_at_clock": peak * ghz / 2.4,
+            "source": "GRBM_GUI_ACTIVE cycles per XCD per launch (profiles/traffic.json) / "
+                      "event-timed launch duration"}
+
+
+def timed_steps(step, args, stream):
+    """Settle, then args.warmup untimed steps, then args.steps timed steps
+    between two events on the launch stream.
+
+    Settle: from idle, the power controller first lowers the engine clock
+    under this load and then brings it back (launches 5-25 of the 32-head
+    N = 8192 forward run up to 30 % slower than the steady state; the
+    engine cycles per launch stay the same).  The bench measures the steady
+    state: it runs the step until two consecutive blocks of 10 launches
+    agree within 1 % (at least 60 launches, at most 2 s), timing each launch,
+    and reports what launches 6-25 took, i.e. what 20 steps after 5 warm-ups
+    from idle would have measured."""
+    import torch
+    ev = []
+    t0 = time.perf_counter()
+    n, prev = 0, None
+    while True:
+        blk = [torch.cuda.Event(enable_timing=True) for _ in range(11)]
+        blk[0].record(stream)
+        for i in range(10):
+            step()
+            blk[i + 1].record(stream)
+        blk[-1].synchronize()
+        d = [blk[i].elapsed_time(blk[i + 1]) for i in range(10)]
+        ev += d
+        n += 10
+        mean = sum(d) / 10
+        if (n >= 60 and prev is not None and abs(mean - prev) <= 0.01 * prev) or \
+                time.perf_counter() - t0 > 2.0 or n >= 2000:
+            break
+        prev = mean
+    settle = {"launches": n, "seconds": time.perf_counter() - t0,
+              "first_launches_ms": [round(x, 4) for x in ev[:30]],
+              "launches_6_to_25_ms_per_step": (sum(ev[5:25]) / 20 if n >= 25 else None),
+              "last_block_ms_per_step": mean}
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    t_wall = time.perf_counter()
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    return start.elapsed_time(end) / args.steps, t_wall, settle
+
+
+def kv_byte_model(wl, lens, esz):
+    """HBM bytes of one forward if no key/value tile were shared between
+    query tiles through L2: each query tile reads its rows of Q once and every
+    key/value tile it sees (whole tiles, as the kernel loads them), and O and
+    the LSE are written once.  The query/key tile sizes mirror the launch
+    choice of the library (256 rows for large problems, 128 otherwise; 64 keys
+    at d = 128, 128 at d = 64).  Beside the compulsory bytes (every tile read
+    once) and the counters, it bounds how much L2 reuse the schedule gets."""
+    B, H, N, d = wl.B, wl.H, wl.N, wl.d
+    big = N >= 256 and B * H * ((N + 255) // 256) >= 512 and not (d == 64 and wl.ragged)
+    bq = 256 if big and wl.dtype == "bf16" else 128
+    bk = 64 if d == 128 else 128
+    if wl.dtype != "bf16":
+        bq, bk = 128, 64
+    row = d * esz
+    kv_tiles = 0
+    q_rows = 0
+    for L in lens:
+        for q0 in range(0, N, bq):
+            if q0 >= L:
+                continue
+            seen = min(L, q0 + bq) if wl.causal else L
+            kv_tiles += (seen + bk - 1) // bk
+            q_rows += min(bq, L - q0)
+    no_reuse = H * (q_rows * row + kv_tiles * 2 * bk * row) + B * H * N * (row + 4)
+    return {"query_tile_rows": bq, "key_tile_rows": bk, "kv_tile_loads": H * kv_tiles,
+            "no_l2_reuse_bytes": no_reuse}
+
+
 def to_device(inp, dev):
     import numpy as np
     import torch
@@ -166,19 +272,7 @@ def bench_decode(args) -> int:
                          workspace=ws, out=out, lse=lse)
 
     stream = torch.cuda.current_stream(dev)
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    t_wall = time.perf_counter()
-    start.record(stream)
-    for _ in range(args.steps):
-        step()
-    end.record(stream)
-    torch.cuda.synchronize()
-    t_wall = time.perf_counter() - t_wall
-    ms = start.elapsed_time(end) / args.steps
+    ms, t_wall, settle = timed_steps(step, args, stream)
     gbs = algo_bytes / (ms * 1e-3) / 1e9
     result = {
         "metric": "attention fwd TFLOP/s (bf16, 1 GPU); decode step, HBM-bound",
@@ -207,6 +301,7 @@ def bench_decode(args) -> int:
             "kernel_hash": kernel_hash("split"),
         },
         "wall_s_timed_region": t_wall,
+        "settle": settle,
     }
     if not args.no_cpu_baseline:
         # the oracle on whole (sequence, head) rows, as many as fit the time budget
@@ -292,19 +387,7 @@ def bench_backward(args) -> int:
                         dq=dq, dk=dk, dv=dv)
 
     stream = torch.cuda.current_stream(dev)
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    t_wall = time.perf_counter()
-    start.record(stream)
-    for _ in range(args.steps):
-        step()
-    end.record(stream)
-    torch.cuda.synchronize()
-    t_wall = time.perf_counter() - t_wall
-    ms = start.elapsed_time(end) / args.steps
+    ms, t_wall, settle = timed_steps(step, args, stream)
     tflops = flops / (ms * 1e-3) / 1e12
     result = {
         "metric": "attention bwd TFLOP/s (bf16, 1 GPU; useful 10*d flops per visible pair)"
@@ -335,6 +418,7 @@ def bench_backward(args) -> int:
             "kernel_hash": kernel_hash("backward"),
         },
         "wall_s_timed_region": t_wall,
+        "settle": settle,
     }
     # Stored-state comparison (the N x N matrices in HBM): latency and peak
     # allocated memory of both paths, each measured from the same resident
@@ -462,19 +546,7 @@ def bench_varlen(args) -> int:
                               lse=lse)
 
     stream = torch.cuda.current_stream(dev)
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    t_wall = time.perf_counter()
-    start.record(stream)
-    for _ in range(args.steps):
-        step()
-    end.record(stream)
-    torch.cuda.synchronize()
-    t_wall = time.perf_counter() - t_wall
-    ms = start.elapsed_time(end) / args.steps
+    ms, t_wall, settle = timed_steps(step, args, stream)
     tflops = flops / (ms * 1e-3) / 1e12
     kind = "backward" if args.backward else "forward"
     result = {
@@ -494,6 +566,7 @@ def bench_varlen(args) -> int:
                                 else "fa_fwd_bf16_kernel"),
                      "kernel_hash": kernel_hash(kind)},
         "wall_s_timed_region": t_wall,
+        "settle": settle,
     }
     if not args.no_cpu_baseline:
         # the oracle on whole sequences, shortest first, within the time budget
@@ -533,9 +606,9 @@ def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    # the engine clock ramps up over the first ~0.1-0.3 s of sustained work:
-    # the default warm-up covers that so the timed steps see steady state
-    ap.add_argument("--warmup", type=int, default=300)
+    # after the settle (timed_steps) the warm-up steps only need to cover the
+    # first launches' one-time costs
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD,
                     help="a square workload name, decode_b8_h32_k16384_d128_bf16 (one query "
                          "row per sequence and head against its key cache, split over key ranges) "
@@ -624,19 +697,7 @@ def main() -> int:
     else:
         def fwd():
             fa.forward(q, k, v, scale=wl.scale, causal=wl.causal, key_len=kl, out=out, lse=lse)
-    for _ in range(args.warmup):
-        fwd()
-    torch.cuda.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    t_wall = time.perf_counter()
-    start.record(stream)
-    for _ in range(args.steps):
-        fwd()
-    end.record(stream)
-    torch.cuda.synchronize()
-    t_wall = time.perf_counter() - t_wall
-    ms = start.elapsed_time(end) / args.steps
+    ms, t_wall, settle = timed_steps(fwd, args, stream)
     tflops = flops / (ms * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_F32_TFLOPS
 
@@ -668,7 +729,20 @@ def main() -> int:
             "kernel_hash": kernel_hash(),
         },
         "wall_s_timed_region": t_wall,
+        "settle": settle,
     }
+    clk = clock_record(wl.name, "forward", ms, peak) if args.dropout == 0 and not args.bias \
+        else None
+    if clk:
+        result["roofline"]["peak_at_measured_clock"] = clk["peak_at_clock"]
+        result["roofline"]["frac_at_measured_clock"] = tflops / clk["peak_at_clock"]
+        result["clock"] = clk
+
+    if args.dropout == 0 and not args.bias:
+        model = kv_byte_model(wl, lens, esz)
+        tr = result["roofline"]["traffic"]
+        result["byte_model"] = dict(model, compulsory_bytes=compulsory, counter_bytes=tr,
+                                    counters_over_compulsory=(tr / compulsory if tr else None))
 
     if not args.no_naive and args.dropout == 0 and not args.bias:
         need = fa.fa_naive_workspace_bytes(B, H, N, fa.FA_DTYPE_BF16 if wl.dtype == "bf16" else fa.FA_DTYPE_F32)
@@ -690,6 +764,29 @@ def main() -> int:
                                         "workspace_bytes": need, "speedup_of_fused": nms / ms}
             del ws
             torch.cuda.empty_cache()
+
+            # allocation peak of one call above the resident inputs, each path
+            # allocating what it needs (O and LSE; the naive path also S and P)
+            def peak_of(fn):
+                torch.cuda.synchronize()
+                torch.cuda.empty_cache()
+                torch.cuda.reset_peak_memory_stats(dev)
+                base = torch.cuda.memory_allocated(dev)
+                r = fn()
+                torch.cuda.synchronize()
+                peak = torch.cuda.max_memory_allocated(dev) - base
+                del r
+                torch.cuda.empty_cache()
+                return peak
+            fused_peak = peak_of(lambda: fa.forward(q, k, v, scale=wl.scale, causal=wl.causal,
+                                                    key_len=kl))
+            naive_peak = peak_of(lambda: fa.naive_forward(q, k, v, scale=wl.scale,
+                                                          causal=wl.causal, key_len=kl))
+            result["peak_memory"] = {
+                "fused_extra_peak_bytes": fused_peak, "naive_extra_peak_bytes": naive_peak,
+                "naive_over_fused": naive_peak / fused_peak if fused_peak else None,
+                "note": "allocation peak of one call above the resident Q, K, V (torch "
+                        "allocator): O and LSE for both, plus S and P for the naive path"}
 
     if not args.no_cpu_baseline and args.dropout == 0 and not args.bias:
         o_host = out

@@ -237,7 +237,8 @@ int fa_backward(const void* q, const void* k, const void* v, const void* o, cons
  * exact attention", section "Why implementations form a family", names
  * dropout among the variants), regenerated from the same Philox4x32-10
  * stream (seed, offset; counter (j/4, i, b*H + h, offset), draw = word j % 4,
- * kept iff draw >= floor(p * 2^32)), never stored:
+ * kept iff draw >= floor(p_drop * 2^32), formed exactly from the double
+ * p_drop), never stored:
  *   dV = (P*Z)^T dO / (1-p),  dS = P * (Z * dO V^T / (1-p) - D),  D_i = dO_i . O_i.
  * Arguments as fa_backward plus p_drop, seed and offset, which must be those
  * of the fa_forward_dropout call that produced o and lse; p_drop outside
@@ -246,7 +247,7 @@ int fa_backward(const void* q, const void* k, const void* v, const void* o, cons
 int fa_backward_dropout(const void* q, const void* k, const void* v, const void* o,
                         const float* lse, const void* dout, void* dq, void* dk, void* dv, int B,
                         int H, int N, int d, float scale, int causal,
-                        const int32_t* key_len_mask, int dtype, float p_drop, uint64_t seed,
+                        const int32_t* key_len_mask, int dtype, double p_drop, uint64_t seed,
                         uint32_t offset, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
@@ -339,15 +340,18 @@ int fa_naive_backward(const void* q, const void* k, const void* v, const void* o
  * Z_ij (keep = 1) is decided by Philox4x32-10 (Salmon, Moraes, Dror, Shaw,
  * SC 2011) with key (seed & 0xffffffff, seed >> 32) and counter
  * (j / 4, i, b * H + h, offset): with u the counter's output word j % 4,
- * Z_ij = 1 iff u >= floor(p_drop * 2^32).  The same (seed, offset) gives the
- * same mask on every call; vary offset between steps.
+ * Z_ij = 1 iff u >= floor(p_drop * 2^32).  The threshold is formed from the
+ * double p_drop exactly (p_drop * 2^32 is exact in binary64), so the rate a
+ * caller passes is the rate applied, with no rounding to a narrower type.
+ * The same (seed, offset) gives the same mask on every call; vary offset
+ * between steps.
  *   p_drop       in [0, 1) (FA_ERR_SCALE otherwise).
  *   dtype        FA_DTYPE_BF16 only.
  * Other arguments and conventions are those of fa_forward.
  */
 int fa_forward_dropout(const void* q, const void* k, const void* v, void* o, float* lse,
                        int B, int H, int N, int d, float scale, int causal,
-                       const int32_t* key_len_mask, int dtype, float p_drop, uint64_t seed,
+                       const int32_t* key_len_mask, int dtype, double p_drop, uint64_t seed,
                        uint32_t offset, void* stream);
 
 /*
@@ -379,7 +383,7 @@ const char* fa_status_string(int status);
 /* ABI version of this header: (major << 16) | minor. */
 int fa_abi_version(void);
 
-#define FA_ABI_VERSION ((1 << 16) | 8)
+#define FA_ABI_VERSION ((1 << 16) | 9)
 
 #ifdef __cplusplus
 }

@@ -56,6 +56,36 @@ def _dtype_code(t):
     raise FAError(-4, f"unsupported dtype {t.dtype}")
 
 
+def _output(t, shape, dtype, device, name):
+    """A caller-supplied output (validated: its shape, dtype and device, and
+    contiguous, since the C ABI cannot see buffer sizes), or a new tensor."""
+    import torch
+    if t is None:
+        return torch.empty(tuple(shape), dtype=dtype, device=device)
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype:
+        raise FAError(-2, f"{name} must be {dtype} {tuple(shape)}; got {t.dtype} {tuple(t.shape)}")
+    if not t.is_cuda or t.device != device or not t.is_contiguous():
+        raise FAError(-1, f"{name} must be a contiguous tensor on {device}")
+    return t
+
+
+def _workspace(ws, need, device):
+    """(pointer, bytes) of a workspace: a new one of `need` bytes, or the
+    caller's (a contiguous tensor on the device; its size in bytes)."""
+    import torch
+    if ws is None:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+    elif not ws.is_cuda or ws.device != device or not ws.is_contiguous():
+        raise FAError(-1, f"workspace must be a contiguous tensor on {device}")
+    return ws, ws.data_ptr(), ws.numel() * ws.element_size()
+
+
+def _same_device(device, *ts):
+    for t in ts:
+        if t is not None and t.device != device:
+            raise FAError(-1, f"all tensors must be on {device}")
+
+
 def _prepare(q, k, v, scale, key_len):
     import torch
     if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
@@ -66,6 +96,7 @@ def _prepare(q, k, v, scale, key_len):
     for t in (q, k, v):
         if not t.is_cuda or not t.is_contiguous():
             raise FAError(-1, "q, k, v must be contiguous device tensors")
+    _same_device(q.device, k, v, key_len)
     B, H, N, d = q.shape
     if scale is None:
         scale = 1.0 / math.sqrt(d)
@@ -73,7 +104,9 @@ def _prepare(q, k, v, scale, key_len):
     if key_len is not None:
         if key_len.dtype != torch.int32 or not key_len.is_cuda or key_len.numel() != B:
             raise FAError(-1, "key_len must be a device int32 tensor of B elements")
-        kl = key_len.contiguous().data_ptr()
+        if not key_len.is_contiguous():
+            raise FAError(-1, "key_len must be contiguous")
+        kl = key_len.data_ptr()
     return B, H, N, d, float(scale), kl
 
 
@@ -81,10 +114,8 @@ def forward(q, k, v, *, scale=None, causal=False, key_len=None, out=None, lse=No
     """O, LSE = fa_forward(...) on torch's current stream of q's device."""
     import torch
     B, H, N, d, scale, kl = _prepare(q, k, v, scale, key_len)
-    if out is None:
-        out = torch.empty_like(q)
-    if lse is None:
-        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    out = _output(out, q.shape, q.dtype, q.device, "out")
+    lse = _output(lse, (B, H, N), torch.float32, q.device, "lse")
     stream = torch.cuda.current_stream(q.device).cuda_stream
     check(fa_forward(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
                      B, H, N, d, scale, int(bool(causal)), kl, _dtype_code(q), stream))
@@ -97,14 +128,13 @@ def naive_forward(q, k, v, *, scale=None, causal=False, key_len=None, workspace=
     B, H, N, d, scale, kl = _prepare(q, k, v, scale, key_len)
     dt = _dtype_code(q)
     need = fa_naive_workspace_bytes(B, H, N, dt)
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    workspace, ws, wsb = _workspace(workspace, need, q.device)
     out = torch.empty_like(q)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     stream = torch.cuda.current_stream(q.device).cuda_stream
     check(fa_naive_forward(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                            lse.data_ptr(), B, H, N, d, scale, int(bool(causal)), kl, dt,
-                           workspace.data_ptr(), workspace.numel(), stream))
+                           ws, wsb, stream))
     return out, lse
 
 
@@ -123,24 +153,24 @@ def forward_split(q, k, v, *, scale=None, causal=False, key_len=None, num_splits
     for t in (q, k, v):
         if not t.is_cuda or not t.is_contiguous():
             raise FAError(-1, "q, k, v must be contiguous device tensors")
+    _same_device(q.device, k, v, key_len)
     B, H, Nq, d = q.shape
     Hkv, Nk = k.shape[1], k.shape[2]
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     kl = 0
     if key_len is not None:
-        if key_len.dtype != torch.int32 or not key_len.is_cuda or key_len.numel() != B:
-            raise FAError(-1, "key_len must be a device int32 tensor of B elements")
-        kl = key_len.contiguous().data_ptr()
+        if key_len.dtype != torch.int32 or not key_len.is_cuda or key_len.numel() != B or \
+                not key_len.is_contiguous():
+            raise FAError(-1, "key_len must be a contiguous device int32 tensor of B elements")
+        kl = key_len.data_ptr()
     need = fa_split_workspace_bytes(B, H, Nq, Nk, d, num_splits)
-    if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    if out is None:
-        out = torch.empty_like(q)
-    if lse is None:
-        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    ws, wsb = 0, 0
+    if workspace is not None or need > 0:
+        workspace, ws, wsb = _workspace(workspace, need, q.device)
+    out = _output(out, q.shape, q.dtype, q.device, "out")
+    lse = _output(lse, (B, H, Nq), torch.float32, q.device, "lse")
     stream = torch.cuda.current_stream(q.device).cuda_stream
-    ws, wsb = (0, 0) if workspace is None else (workspace.data_ptr(), workspace.numel())
     check(fa_forward_split(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                            lse.data_ptr(), B, H, Hkv, Nq, Nk, d, float(scale), int(bool(causal)),
                            kl, _dtype_code(q), int(num_splits), ws, wsb, stream))
@@ -183,8 +213,10 @@ def backward(q, k, v, o, lse, dout, *, scale=None, causal=False, key_len=None, w
         if not t.is_cuda or not t.is_contiguous():
             raise FAError(-1, "q, k, v, o, dout must be contiguous device tensors")
     B, H, N, d = q.shape
-    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_cuda:
-        raise FAError(-2, "lse must be a device float32 tensor [B, H, N]")
+    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_cuda or \
+            not lse.is_contiguous():
+        raise FAError(-2, "lse must be a contiguous device float32 tensor [B, H, N]")
+    _same_device(q.device, k, v, o, lse, dout, key_len)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     kl = 0
@@ -193,21 +225,21 @@ def backward(q, k, v, o, lse, dout, *, scale=None, causal=False, key_len=None, w
             raise FAError(-1, "key_len must be a device int32 tensor of B elements")
         kl = key_len.data_ptr()
     dt = _dtype_code(q)
-    if workspace is None:
-        need = (fa_naive_workspace_bytes(B, H, N, dt) if _naive
-                else fa_backward_workspace_bytes(B, H, N, d, dt))
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
-    dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(k) if dk is None else dk
-    dv = torch.empty_like(v) if dv is None else dv
+    need = (fa_naive_workspace_bytes(B, H, N, dt) if _naive
+            else fa_backward_workspace_bytes(B, H, N, d, dt))
+    workspace, ws, wsb = _workspace(workspace, need, q.device)
+    dq = _output(dq, q.shape, q.dtype, q.device, "dq")
+    dk = _output(dk, k.shape, k.dtype, q.device, "dk")
+    dv = _output(dv, v.shape, v.dtype, q.device, "dv")
     stream = torch.cuda.current_stream(q.device).cuda_stream
     args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
             dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d,
             float(scale), int(bool(causal)), kl, dt)
-    tail = (workspace.data_ptr(), workspace.numel(), stream)
+    tail = (ws, wsb, stream)
     if _drop is not None:
         check(fa_backward_dropout(*args, float(_drop[0]), int(_drop[1]), int(_drop[2]), *tail))
     elif _bias is not None:
+        _same_device(q.device, _bias)
         ptr, sb, sh, ld = _bias_layout(_bias, B, H, N)
         check(fa_backward_bias(*args[:9], ptr, *args[9:], sb, sh, ld, *tail))
     else:
@@ -233,27 +265,28 @@ def backward_gqa(q, k, v, o, lse, dout, *, scale=None, causal=False, key_len=Non
             raise FAError(-1, "q, k, v, o, dout must be contiguous device tensors of one dtype")
     B, H, Nq, d = q.shape
     Hkv, Nk = k.shape[1], k.shape[2]
-    if lse.shape != (B, H, Nq) or lse.dtype != torch.float32 or not lse.is_cuda:
-        raise FAError(-2, "lse must be a device float32 tensor [B, H, Nq]")
+    if lse.shape != (B, H, Nq) or lse.dtype != torch.float32 or not lse.is_cuda or \
+            not lse.is_contiguous():
+        raise FAError(-2, "lse must be a contiguous device float32 tensor [B, H, Nq]")
+    _same_device(q.device, k, v, o, lse, dout, key_len)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     kl = 0
     if key_len is not None:
-        if key_len.dtype != torch.int32 or not key_len.is_cuda or key_len.numel() != B:
-            raise FAError(-1, "key_len must be a device int32 tensor of B elements")
+        if key_len.dtype != torch.int32 or not key_len.is_cuda or key_len.numel() != B or \
+                not key_len.is_contiguous():
+            raise FAError(-1, "key_len must be a contiguous device int32 tensor of B elements")
         kl = key_len.data_ptr()
     dt = _dtype_code(q)
-    if workspace is None:
-        need = fa_backward_workspace_bytes(B, H, Nq, d, dt)
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
-    dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(k) if dk is None else dk
-    dv = torch.empty_like(v) if dv is None else dv
+    workspace, ws, wsb = _workspace(workspace, fa_backward_workspace_bytes(B, H, Nq, d, dt),
+                                    q.device)
+    dq = _output(dq, q.shape, q.dtype, q.device, "dq")
+    dk = _output(dk, k.shape, k.dtype, q.device, "dk")
+    dv = _output(dv, v.shape, v.dtype, q.device, "dv")
     stream = torch.cuda.current_stream(q.device).cuda_stream
     check(fa_backward_gqa(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                           dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, Hkv,
-                          Nq, Nk, d, float(scale), int(bool(causal)), kl, dt,
-                          workspace.data_ptr(), workspace.numel(), stream))
+                          Nq, Nk, d, float(scale), int(bool(causal)), kl, dt, ws, wsb, stream))
     return dq, dk, dv
 
 
@@ -278,25 +311,25 @@ def backward_varlen(q, k, v, o, lse, dout, cu_seqlens_q, cu_seqlens_k, max_seqle
         raise FAError(-2, "cu_seqlens_q and cu_seqlens_k must be int32 [B + 1]")
     Tq, H, d = q.shape
     Tk, Hkv = k.shape[0], k.shape[1]
-    if lse.shape != (Tq, H) or lse.dtype != torch.float32 or not lse.is_cuda:
-        raise FAError(-2, "lse must be a device float32 tensor [Tq, H]")
+    if lse.shape != (Tq, H) or lse.dtype != torch.float32 or not lse.is_cuda or \
+            not lse.is_contiguous():
+        raise FAError(-2, "lse must be a contiguous device float32 tensor [Tq, H]")
+    _same_device(q.device, k, v, o, lse, dout, cu_seqlens_q, cu_seqlens_k)
     B = cu_seqlens_q.numel() - 1
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     dt = _dtype_code(q)
-    if workspace is None:
-        need = fa_backward_workspace_bytes(1, H, Tq, d, dt)
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
-    dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(k) if dk is None else dk
-    dv = torch.empty_like(v) if dv is None else dv
+    workspace, ws, wsb = _workspace(workspace, fa_backward_workspace_bytes(1, H, Tq, d, dt),
+                                    q.device)
+    dq = _output(dq, q.shape, q.dtype, q.device, "dq")
+    dk = _output(dk, k.shape, k.dtype, q.device, "dk")
+    dv = _output(dv, v.shape, v.dtype, q.device, "dv")
     stream = torch.cuda.current_stream(q.device).cuda_stream
     check(fa_backward_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
                              lse.data_ptr(), dout.data_ptr(), dq.data_ptr(), dk.data_ptr(),
                              dv.data_ptr(), cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(), B,
                              H, Hkv, Tq, Tk, int(max_seqlen_q), int(max_seqlen_k), d,
-                             float(scale), int(bool(causal)), dt, workspace.data_ptr(),
-                             workspace.numel(), stream))
+                             float(scale), int(bool(causal)), dt, ws, wsb, stream))
     return dq, dk, dv
 
 
@@ -316,12 +349,11 @@ def forward_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen
     Tq, H, d = q.shape
     Tk, Hkv = k.shape[0], k.shape[1]
     B = cu_seqlens_q.numel() - 1
+    _same_device(q.device, k, v, cu_seqlens_q, cu_seqlens_k)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    if out is None:
-        out = torch.empty_like(q)
-    if lse is None:
-        lse = torch.empty((Tq, H), dtype=torch.float32, device=q.device)
+    out = _output(out, q.shape, q.dtype, q.device, "out")
+    lse = _output(lse, (Tq, H), torch.float32, q.device, "lse")
     stream = torch.cuda.current_stream(q.device).cuda_stream
     check(fa_forward_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                             lse.data_ptr(), cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(), B, H,
@@ -341,17 +373,17 @@ def forward_dropout(q, k, v, *, p_drop, seed, offset=0, scale=None, causal=False
         if not t.is_cuda or not t.is_contiguous():
             raise FAError(-1, "q, k, v must be contiguous device tensors")
     B, H, N, d = q.shape
+    _same_device(q.device, k, v, key_len)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     kl = 0
     if key_len is not None:
-        if key_len.dtype != torch.int32 or not key_len.is_cuda or key_len.numel() != B:
-            raise FAError(-1, "key_len must be a device int32 tensor of B elements")
+        if key_len.dtype != torch.int32 or not key_len.is_cuda or key_len.numel() != B or \
+                not key_len.is_contiguous():
+            raise FAError(-1, "key_len must be a contiguous device int32 tensor of B elements")
         kl = key_len.data_ptr()
-    if out is None:
-        out = torch.empty_like(q)
-    if lse is None:
-        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    out = _output(out, q.shape, q.dtype, q.device, "out")
+    lse = _output(lse, (B, H, N), torch.float32, q.device, "lse")
     stream = torch.cuda.current_stream(q.device).cuda_stream
     check(fa_forward_dropout(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                              lse.data_ptr(), B, H, N, d, float(scale), int(bool(causal)), kl,
@@ -384,18 +416,18 @@ def forward_bias(q, k, v, bias, *, scale=None, causal=False, key_len=None, out=N
         if not t.is_cuda or not t.is_contiguous():
             raise FAError(-1, "q, k, v must be contiguous device tensors")
     B, H, N, d = q.shape
+    _same_device(q.device, k, v, bias, key_len)
     ptr, sb, sh, ld = _bias_layout(bias, B, H, N)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     kl = 0
     if key_len is not None:
-        if key_len.dtype != torch.int32 or not key_len.is_cuda or key_len.numel() != B:
-            raise FAError(-1, "key_len must be a device int32 tensor of B elements")
+        if key_len.dtype != torch.int32 or not key_len.is_cuda or key_len.numel() != B or \
+                not key_len.is_contiguous():
+            raise FAError(-1, "key_len must be a contiguous device int32 tensor of B elements")
         kl = key_len.data_ptr()
-    if out is None:
-        out = torch.empty_like(q)
-    if lse is None:
-        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    out = _output(out, q.shape, q.dtype, q.device, "out")
+    lse = _output(lse, (B, H, N), torch.float32, q.device, "lse")
     stream = torch.cuda.current_stream(q.device).cuda_stream
     check(fa_forward_bias(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
                           ptr, B, H, N, d, float(scale), int(bool(causal)), kl,

@@ -358,10 +358,18 @@ extern "C" size_t fa_backward_workspace_bytes(int B, int H, int N, int d, int dt
 
 namespace {
 
+// Keep threshold of a dropout rate p in [0, 1): a draw u is kept iff
+// u >= floor(p * 2^32).  p * 2^32 only moves the binary exponent, so the
+// product is exact in double and the floor is that of the real number.
+uint32_t keep_threshold(const double p) {
+  const double t = std::floor(p * 4294967296.0);
+  return static_cast<uint32_t>(std::min(t, 4294967295.0));
+}
+
 // Dropout of the forward whose gradients are taken (fa_forward_dropout's
 // arguments); nullptr for none.
 struct DropArgs {
-  float p;
+  double p;
   uint64_t seed;
   uint32_t offset;
 };
@@ -391,7 +399,7 @@ int backward_dense(const void* q, const void* k, const void* v, const void* o, c
                    void* workspace, size_t workspace_bytes, void* stream, const DropArgs* drop,
                    const BiasArgs* mask = nullptr) {
   if (dtype != FA_DTYPE_BF16) return FA_ERR_DTYPE;
-  if (drop && !(drop->p >= 0.f && drop->p < 1.f)) return FA_ERR_SCALE;
+  if (drop && !(drop->p >= 0.0 && drop->p < 1.0)) return FA_ERR_SCALE;
   if (d != 64 && d != 128) return FA_ERR_HEAD_DIM;
   Shape s;
   bool empty = false;
@@ -457,12 +465,11 @@ int backward_dense(const void* q, const void* k, const void* v, const void* o, c
   if (drop) {
     // the forward's stream and threshold (fa_forward_dropout)
     p.drop = 1;
-    const double t = std::floor(static_cast<double>(drop->p) * 4294967296.0);
-    p.drop_threshold = static_cast<uint32_t>(std::min(t, 4294967295.0));
+    p.drop_threshold = keep_threshold(drop->p);
     p.seed_lo = static_cast<uint32_t>(drop->seed & 0xFFFFFFFFu);
     p.seed_hi = static_cast<uint32_t>(drop->seed >> 32);
     p.drop_offset = drop->offset;
-    p.keep_scale = static_cast<float>(1.0 / (1.0 - static_cast<double>(drop->p)));
+    p.keep_scale = static_cast<float>(1.0 / (1.0 - drop->p));
   }
   if (mask) {
     p.bias = mask->bias;
@@ -489,7 +496,7 @@ extern "C" int fa_backward(const void* q, const void* k, const void* v, const vo
 extern "C" int fa_backward_dropout(const void* q, const void* k, const void* v, const void* o,
                                    const float* lse, const void* dout, void* dq, void* dk,
                                    void* dv, int B, int H, int N, int d, float scale, int causal,
-                                   const int32_t* key_len_mask, int dtype, float p_drop,
+                                   const int32_t* key_len_mask, int dtype, double p_drop,
                                    uint64_t seed, uint32_t offset, void* workspace,
                                    size_t workspace_bytes, void* stream) {
   const DropArgs drop{p_drop, seed, offset};
@@ -789,10 +796,10 @@ extern "C" int fa_forward_varlen(const void* q, const void* k, const void* v, vo
 
 extern "C" int fa_forward_dropout(const void* q, const void* k, const void* v, void* o,
                                   float* lse, int B, int H, int N, int d, float scale, int causal,
-                                  const int32_t* key_len_mask, int dtype, float p_drop,
+                                  const int32_t* key_len_mask, int dtype, double p_drop,
                                   uint64_t seed, uint32_t offset, void* stream) {
   if (dtype != FA_DTYPE_BF16) return FA_ERR_DTYPE;
-  if (!(p_drop >= 0.f && p_drop < 1.f)) return FA_ERR_SCALE;
+  if (!(p_drop >= 0.0 && p_drop < 1.0)) return FA_ERR_SCALE;
   Shape s;
   bool empty = false;
   int st = check_scalars(B, H, N, d, scale, dtype, &s, &empty);
@@ -801,12 +808,11 @@ extern "C" int fa_forward_dropout(const void* q, const void* k, const void* v, v
   if (st != FA_OK) return st;
   fa::FwdParams p = make_params(q, k, v, o, lse, B, H, N, scale, key_len_mask, dtype);
   p.drop = 1;
-  const double t = std::floor(static_cast<double>(p_drop) * 4294967296.0);
-  p.drop_threshold = static_cast<uint32_t>(std::min(t, 4294967295.0));
+  p.drop_threshold = keep_threshold(p_drop);
   p.seed_lo = static_cast<uint32_t>(seed & 0xFFFFFFFFu);
   p.seed_hi = static_cast<uint32_t>(seed >> 32);
   p.drop_offset = offset;
-  p.keep_scale = static_cast<float>(1.0 / (1.0 - static_cast<double>(p_drop)));
+  p.keep_scale = static_cast<float>(1.0 / (1.0 - p_drop));
   if (fa::launch_fwd_bf16(p, d, causal != 0, static_cast<hipStream_t>(stream)) != hipSuccess)
     return FA_ERR_HIP;
   return FA_OK;

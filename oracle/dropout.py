@@ -15,7 +15,8 @@ fixing its random numbers.  The reading taken here:
     the 128-bit counter (j // 4, i, b * H + h, offset); output word j % 4 is
     the draw u_ij of query row i and key j of head h in batch entry b;
   * Z_ij = 1 iff u_ij >= floor(p * 2^32), so the keep probability is
-    1 - floor(p * 2^32) / 2^32.
+    1 - floor(p * 2^32) / 2^32; p is the binary64 rate the caller gives,
+    and the floor is that of the real product p * 2^32 (keep_threshold).
 
 The gradient (dropout_attention_backward) treats the mask Z as a constant of
 the step (the same seed and offset regenerate it): with P the undropped
@@ -39,7 +40,8 @@ import numpy as np
 
 from .attention import NEG_INF, _clamped_length, visible_mask
 
-__all__ = ["philox4x32_10", "dropout_keep", "dropout_attention", "dropout_attention_backward"]
+__all__ = ["philox4x32_10", "keep_threshold", "dropout_keep", "dropout_attention",
+           "dropout_attention_backward"]
 
 _M0, _M1 = 0xD2511F53, 0xCD9E8D57  # round multipliers
 _W0, _W1 = 0x9E3779B9, 0xBB67AE85  # key schedule (Weyl) increments
@@ -69,6 +71,13 @@ def philox4x32_10(counter, key):
     return tuple(x.astype(np.uint32) for x in (c0, c1, c2, c3))
 
 
+def keep_threshold(p):
+    """floor(p * 2^32) for a rate p in [0, 1): a draw u is kept iff u is at
+    least this.  p is taken as the binary64 number it is; multiplying by 2^32
+    moves only its exponent, so the product and its floor are exact."""
+    return min(int(float(p) * 2.0 ** 32), _MASK)
+
+
 def dropout_keep(b, h, H, N, Nk, p, seed, offset):
     """Boolean [N, Nk]: Z_ij of query row i and key j of head h in batch b."""
     i = np.arange(N, dtype=np.uint64)[:, None]
@@ -77,8 +86,7 @@ def dropout_keep(b, h, H, N, Nk, p, seed, offset):
                           (seed & _MASK, (seed >> 32) & _MASK))
     jj = np.broadcast_to(j & np.uint64(3), (N, Nk))
     u = np.choose(jj.astype(np.int64), [np.broadcast_to(w, (N, Nk)) for w in words])
-    threshold = np.uint32(min(int(p * 2.0 ** 32), _MASK))
-    return u >= threshold
+    return u >= np.uint32(keep_threshold(p))
 
 
 def dropout_attention(q, k, v, scale, p, seed, offset=0, causal=False, key_len=None,

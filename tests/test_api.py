@@ -45,7 +45,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     for name in declared_functions():
         assert hasattr(lib, name), name
     assert set(_lib.exported_symbols()) == set(declared_functions())
-    assert fa.fa_abi_version() == (1 << 16) | 8
+    assert fa.fa_abi_version() == (1 << 16) | 9
 
 
 def test_status_strings():
@@ -463,3 +463,20 @@ def test_bias_bad_arguments():
     assert bc(o=BI) == ALIAS
     assert bc(lse=BI + 2 * 64 * 64 * 4) == ALIAS
     assert bc(B=0, q=0, k=0, v=0, o=0, lse=0, bias=0) == OK
+
+
+def test_output_validation_helper():
+    """Caller-supplied outputs are checked for shape, dtype, device and
+    contiguity before any launch (the C ABI cannot see buffer sizes)."""
+    import torch
+    from io_aware_exact_forward_amd import _output, _workspace
+    dev = torch.device("cuda:0")
+    good_shape = (1, 2, 4, 64)
+    with pytest.raises(fa.FAError):     # wrong shape
+        _output(torch.zeros(1, 2, 3, 64, dtype=torch.bfloat16), good_shape, torch.bfloat16, dev, "out")
+    with pytest.raises(fa.FAError):     # wrong dtype
+        _output(torch.zeros(good_shape, dtype=torch.float32), good_shape, torch.bfloat16, dev, "out")
+    with pytest.raises(fa.FAError):     # host memory
+        _output(torch.zeros(good_shape, dtype=torch.bfloat16), good_shape, torch.bfloat16, dev, "out")
+    with pytest.raises(fa.FAError):     # host workspace
+        _workspace(torch.zeros(16, dtype=torch.uint8), 16, dev)

@@ -130,3 +130,42 @@ def test_dropout_backward_full_size_heads():
             assert err.max() <= TOL_MAX * np.abs(r).max(), (b, h, name, err.max())
             assert err.mean() <= TOL_MEAN * np.abs(r).mean(), (b, h, name, err.mean())
         say({"head": (b, h), "ok": True})
+
+
+GAP = __import__("json").load(open(__import__("os").path.join(
+    __import__("os").path.dirname(__file__), "golden", "dropout_gap_draws.json")))
+
+
+@pytest.mark.parametrize("case", GAP["cases"], ids=lambda c: f"p{c['p']}")
+def test_dropout_backward_rate_is_the_binary64_value(case):
+    """The backward regenerates the forward's mask from the binary64 rate:
+    with q = 0 (weights 1/n), V and dO rows one-hot (dO_i = e_i),
+    dV[j, i] = Z_ij / (n (1 - p)), so the stored gap draw
+    (tests/golden/make_dropout_gap_draws.py) decides one element of dV by at
+    least 0.15.  Every element of dQ, dK, dV against the oracle at this
+    file's tolerance, and that element to 1e-3."""
+    import torch
+    import io_aware_exact_forward_amd as fa
+    p, n, seed, off = case["p"], case["n"], case["seed"], case["offset"]
+    d = 64
+    q = np.zeros((1, 1, n, d), np.float32)
+    k = np.random.default_rng(7).standard_normal((1, 1, n, d), dtype=np.float32)
+    v = np.zeros((1, 1, n, d), np.float32)
+    v[0, 0, np.arange(n), np.arange(n)] = 1.0
+    qb, kb, vb, dob = (W.bf16_encode(x) for x in (q, k, v, v))
+    say(f"gap draw backward p={p} n={n} offset={off} row={case['row']} key={case['key']}")
+    tq, tk, tv, tdo = dev(qb), dev(kb), dev(vb), dev(dob)
+    o, lse = fa.forward_dropout(tq, tk, tv, p_drop=p, seed=seed, offset=off, scale=0.125)
+    dq, dk, dv = fa.backward_dropout(tq, tk, tv, o, lse, tdo, p_drop=p, seed=seed, offset=off,
+                                     scale=0.125)
+    torch.cuda.synchronize()
+    got = host(dq), host(dk), host(dv)
+    ex = lambda b: W.bf16_decode(b, np.float64)
+    ref = oracle.dropout_attention_backward(ex(qb), ex(kb), ex(vb), ex(dob), 0.125, p, seed,
+                                            off)[:3]
+    for g, r, name in zip(got, ref, ("dq", "dk", "dv")):
+        err = np.abs(g - r)
+        scale_max = max(np.abs(r).max(), 1e-30)
+        assert err.max() <= TOL_MAX * scale_max + 1e-6, (name, err.max())
+    want = 1.0 / (n * (1.0 - p)) if case["kept"] else 0.0
+    assert abs(got[2][0, 0, case["key"], case["row"]] - want) <= 1e-3

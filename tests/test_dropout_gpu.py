@@ -103,3 +103,44 @@ def test_dropout_mid_size():
         say("head", h, float(err.max()), float(err.mean()))
         amp = 1.0 / (1.0 - 0.1)
         assert err.max() <= TOL["bf16"]["o_max"] * amp and err.mean() <= TOL["bf16"]["o_mean"] * amp
+
+
+GAP = __import__("json").load(open(__import__("os").path.join(
+    __import__("os").path.dirname(__file__), "golden", "dropout_gap_draws.json")))
+
+
+def gap_problem(case, d=64):
+    """One head, n queries and keys, q = 0 (every weight 1/n), V rows one-hot
+    (V[j] = e_j): O[i, j] = Z_ij / (n (1 - p)), so the stored draw's pair
+    decides one output element by at least 0.15."""
+    n = case["n"]
+    q = np.zeros((1, 1, n, d), np.float32)
+    k = np.random.default_rng(7).standard_normal((1, 1, n, d), dtype=np.float32)
+    v = np.zeros((1, 1, n, d), np.float32)
+    v[0, 0, np.arange(n), np.arange(n)] = 1.0
+    return W.bf16_encode(q), W.bf16_encode(k), W.bf16_encode(v)
+
+
+@pytest.mark.parametrize("case", GAP["cases"], ids=lambda c: f"p{c['p']}")
+def test_dropout_rate_is_the_binary64_value(case):
+    """The stored draw lies between floor(p * 2^32) and floor(f32(p) * 2^32)
+    (tests/golden/make_dropout_gap_draws.py): the library must keep or drop
+    that pair as the binary64 rate says.  Every element against the oracle;
+    the values are multiples of 1 / (n (1 - p)) up to the bf16 rounding of O
+    (relative 2^-9 of at most 0.18), so the tolerance is 1e-3."""
+    import torch
+    import io_aware_exact_forward_amd as fa
+    p, n, seed, off = case["p"], case["n"], case["seed"], case["offset"]
+    qb, kb, vb = gap_problem(case)
+    dev = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to("cuda:0")
+    say(f"gap draw p={p} n={n} offset={off} row={case['row']} key={case['key']}")
+    o, lse = fa.forward_dropout(dev(qb), dev(kb), dev(vb), p_drop=p, seed=seed, offset=off,
+                                scale=0.125)
+    torch.cuda.synchronize()
+    o = W.bf16_decode(o.view(torch.int16).cpu().numpy().view(np.uint16), np.float64)
+    ex = lambda b: W.bf16_decode(b, np.float64)
+    o_ref, l_ref = oracle.dropout_attention(ex(qb), ex(kb), ex(vb), 0.125, p, seed, off)
+    assert np.abs(o - o_ref).max() <= 1e-3
+    assert np.abs(lse.cpu().numpy() - l_ref).max() <= 1e-3
+    want = 1.0 / (n * (1.0 - p)) if case["kept"] else 0.0
+    assert abs(o[0, 0, case["row"], case["key"]] - want) <= 1e-3

@@ -12,6 +12,7 @@ fail a pin.
 import json
 import math
 import os
+from fractions import Fraction
 
 import numpy as np
 import pytest
@@ -203,3 +204,47 @@ def test_dropout_gradient_head_selection_matches_full_problem():
                                                  causal=True, head_ids=[h], H_all=H, batch_ids=[b])
         for a, c in zip(part, full):
             assert np.allclose(a[0, 0], c[b, h], atol=1e-14)
+
+
+# ---- the keep threshold: one definition, pinned by exact rational arithmetic ----
+
+GAP = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "dropout_gap_draws.json")))
+
+
+@pytest.mark.parametrize("p", [0.0, 0.1, 0.2, 0.3, 0.5, 0.9, 0.123456789, 1.0 - 2.0 ** -53])
+def test_keep_threshold_is_floor_of_exact_product(p):
+    """floor(p * 2^32) of the binary64 rate, computed here with Fractions
+    (exact rationals), equals the oracle's threshold."""
+    assert D.keep_threshold(p) == math.floor(Fraction(p) * 2 ** 32)
+
+
+def test_keep_threshold_values():
+    """Hand-derived values: 0.3 is 0.29999999999999998889776975... in
+    binary64, times 2^32 is 1288490188.79..., so the threshold is
+    1288490188; rounded to binary32 first the rate would be
+    0.300000011920928955078125, giving exactly 1288490240 (a planted
+    misreading that the pin rejects)."""
+    assert D.keep_threshold(0.0) == 0
+    assert D.keep_threshold(0.5) == 2 ** 31
+    assert D.keep_threshold(0.1) == 429496729
+    assert D.keep_threshold(0.3) == 1288490188
+    assert D.keep_threshold(0.9) == 3865470566
+    assert D.keep_threshold(float(np.float32(0.3))) == 1288490240 != D.keep_threshold(0.3)
+    assert D.keep_threshold(float(np.float32(0.9))) == 3865470464 != D.keep_threshold(0.9)
+
+
+@pytest.mark.parametrize("case", GAP["cases"], ids=lambda c: f"p{c['p']}")
+def test_gap_draws(case):
+    """The stored draws (tests/golden/make_dropout_gap_draws.py) lie between
+    the two readings' thresholds, and dropout_keep decides them by the
+    binary64 rate: the GPU test on them fails if the library rounds the rate
+    to binary32."""
+    p, n, seed = case["p"], case["n"], case["seed"]
+    i, j, off = case["row"], case["key"], case["offset"]
+    words = D.philox4x32_10((j // 4, i, 0, off), (seed & 0xFFFFFFFF, seed >> 32))
+    u = int(words[j % 4])
+    assert u == case["draw"]
+    t64, t32 = D.keep_threshold(p), D.keep_threshold(float(np.float32(p)))
+    assert min(t64, t32) <= u < max(t64, t32)
+    keep = D.dropout_keep(0, 0, 1, n, n, p, seed, off)
+    assert bool(keep[i, j]) == (u >= t64) == case["kept"]

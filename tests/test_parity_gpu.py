@@ -1,8 +1,9 @@
 """GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
 
-Small cases compare every output element; the full-size workloads compare
-seeded samples of query rows the oracle computes one by one, plus properties
-that hold for every row (padding rows exactly 0 / -inf, finiteness).
+Small cases and the workloads up to 8 x 16 x 4096 compare every output
+element; the 8-head N = 32768 workload compares 512 seeded query rows per
+head, which the oracle computes one by one, plus properties that hold for
+every row (finiteness).
 """
 import math
 
@@ -52,30 +53,31 @@ def test_h32_n2048_causal_full():
     say(st)
 
 
-def test_h32_n8192_d128_causal_sampled():
+def test_h32_n8192_d128_causal_full():
+    """Every row of every head (262,144 rows): O max and mean error and LSE
+    error over all of them (the oracle takes ~15 s on 16 host threads)."""
     wl = W.workload("h32_n8192_d128_causal_bf16")
     inp = W.make_inputs(wl)
     say("case", wl.name)
     o, lse = run_hip(inp, wl.causal, wl.scale)
     assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
-    rows = sample_rows(wl.N, wl.H, 96, 7, extra=(0, 1, 63, 64, 127, 128, 4095, 8064, 8191))
-    st = compare(inp, o, lse, wl.causal, wl.scale, rows=rows, label=wl.name)
+    st = compare(inp, o, lse, wl.causal, wl.scale, label=wl.name)
     say(st)
+    assert st["rows_checked"] == wl.B * wl.H * wl.N
 
 
-def test_b8_keylen_sampled():
+def test_b8_keylen_full():
+    """Every row of every (batch, head): valid rows against the oracle (max,
+    mean and LSE error over all of them), padding rows exactly 0 / -inf."""
     wl = W.workload("b8_h16_n4096_d64_keylen_bf16")
     inp = W.make_inputs(wl)
     say("case", wl.name, "key_len", inp.key_len.tolist())
     o, lse = run_hip(inp, wl.causal, wl.scale)
     check_all_padding(inp, o, lse)
-    # rows around every sequence's length boundary plus random rows
-    extra = [0, 1, 127, 128, 4095]
-    for L in inp.key_len:
-        extra += [int(L) - 2, int(L) - 1, int(L), int(L) + 1]
-    rows = sample_rows(wl.N, wl.H, 48, 8, extra=extra)
-    st = compare(inp, o, lse, wl.causal, wl.scale, rows=rows, label=wl.name)
+    st = compare(inp, o, lse, wl.causal, wl.scale, label=wl.name)
     say(st)
+    lens = np.clip(inp.key_len.astype(np.int64), 0, wl.N)
+    assert st["rows_checked"] == wl.H * int(lens.sum())
 
 
 def test_h8_n32768_causal_sampled():
