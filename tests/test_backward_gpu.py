@@ -5,8 +5,8 @@ backward, and compares dQ, dK and dV element by element with
 oracle.attention_backward on the same exact bf16 inputs.
 
 Tolerance, per gradient tensor G (relative to the tensor's own scale, since
-gradient magnitudes differ between dQ, dK and dV): max |G - G_ref| <= 2e-2 *
-max |G_ref| and mean |G - G_ref| <= 1.5e-2 * mean |G_ref|.  The kernel's
+gradient magnitudes differ between dQ, dK and dV): max |G - G_ref| <= 1.2e-2 *
+max |G_ref| and mean |G - G_ref| <= 1.2e-2 * mean |G_ref|.  The kernel's
 roundings: the results are stored in bf16 (up to 2^-8 relative per element,
 about 2e-3 of the mean magnitude on average, which dominates the measured
 mean errors of 2-4e-3 once rows have tens of keys); P and dS enter their
@@ -16,8 +16,12 @@ are relative to the terms of a row, not to its sum: each row of dS sums to
 zero, so when a row has very few keys dQ and dK are differences of nearly
 equal terms, and with two keys the dS rounding (~2^-9 of each term, ~4e-3 of
 the difference) and the D error (~4e-3) add to the output rounding: ~1e-2 of
-the mean magnitude, which the bound covers with 50 % margin.  Padding rows
-and keys past a sequence's length must have exactly zero gradients.
+the mean magnitude.  Measured over every backward parity case (dense,
+grouped, packed, dropout, mask): worst max ratio 8.1e-3 and worst mean
+ratio 9.6e-3, both on the two-key rows of N = 2; the bounds leave 1.5x and
+1.25x above those (the inputs are seeded and the kernels deterministic).
+Padding rows and keys past a sequence's length must have exactly zero
+gradients.
 """
 import numpy as np
 import pytest
@@ -27,7 +31,7 @@ from io_aware_exact_forward_amd import workloads as W
 
 pytestmark = pytest.mark.gpu
 
-TOL_MAX, TOL_MEAN = 2e-2, 1.5e-2
+TOL_MAX, TOL_MEAN = 1.2e-2, 1.2e-2
 
 
 def say(*a):

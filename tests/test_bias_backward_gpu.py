@@ -3,8 +3,8 @@ against oracle.attention_backward(..., bias=M), every element of dQ, dK, dV.
 
 Each case runs the HIP forward with the mask (fa_forward_bias) for O and LSE,
 then the HIP backward with the same mask.  The tolerance is the backward's
-(tests/test_backward_gpu.py: per gradient tensor, max error <= 2e-2 *
-max |ref|, mean error <= 1.5e-2 * mean |ref|).  Cases: a full [B, H, N, ld]
+(tests/test_backward_gpu.py: per gradient tensor, max error <= 1.2e-2 *
+max |ref|, mean error <= 1.2e-2 * mean |ref|).  Cases: a full [B, H, N, ld]
 mask with padded rows (N not a multiple of 4) and -inf entries, masks
 broadcast over batch and over heads, d = 64 and 128, causal and not, with
 per-sequence lengths, and rows hidden entirely by the mask (their gradients
@@ -18,7 +18,7 @@ from io_aware_exact_forward_amd import workloads as W
 
 pytestmark = pytest.mark.gpu
 
-TOL_MAX, TOL_MEAN = 2e-2, 1.5e-2
+TOL_MAX, TOL_MEAN = 1.2e-2, 1.2e-2
 
 
 def say(*a):
@@ -114,4 +114,4 @@ def test_bias_backward_zero_mask_is_plain_backward():
         torch.cuda.synchronize()
         for x, y in zip(a, b):
             err = (x.float() - y.float()).abs().max().item()
-            assert err <= 2e-2 * x.float().abs().max().item(), err
+            assert err <= TOL_MAX * x.float().abs().max().item(), err
