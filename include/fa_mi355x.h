@@ -377,13 +377,35 @@ int fa_forward_bias(const void* q, const void* k, const void* v, void* o, float*
                     const int32_t* key_len_mask, int dtype, int64_t bias_stride_b,
                     int64_t bias_stride_h, int64_t bias_ld, void* stream);
 
+/*
+ * fa_forward_split for callers that cannot allocate device memory: code under
+ * HIP graph capture, serving loops and harnesses that forbid hipMalloc.  The
+ * same computation and kernels as fa_forward_split, with the key ranges' fp32
+ * partial results in a scratch area the library holds in device memory
+ * (FA_NOALLOC_SCRATCH_BYTES on every device it runs on, until the process
+ * ends) instead of a caller workspace.  Allocates nothing.
+ *   q, k, v, o, lse, B, H, Hkv, Nq, Nk, d, scale, causal, key_len_mask,
+ *   dtype, num_splits, stream: as fa_forward_split.
+ * Returns FA_ERR_WORKSPACE, before any HIP call, when the partial results,
+ * fa_split_workspace_bytes(B, H, Nq, Nk, d, num_splits) bytes, exceed
+ * FA_NOALLOC_SCRATCH_BYTES (num_splits = 1 needs none); other validation and
+ * errors as fa_forward_split.  Every call on one device shares that device's
+ * scratch: calls that overlap in time on one device (other streams, other
+ * host threads) race and must be ordered by the caller.  No scratch content
+ * carries over: each call writes every partial row it later reads.
+ */
+#define FA_NOALLOC_SCRATCH_BYTES (32u << 20)
+int fa_forward_split_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                             int B, int H, int Hkv, int Nq, int Nk, int d, float scale, int causal,
+                             const int32_t* key_len_mask, int dtype, int num_splits, void* stream);
+
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* fa_status_string(int status);
 
 /* ABI version of this header: (major << 16) | minor. */
 int fa_abi_version(void);
 
-#define FA_ABI_VERSION ((1 << 16) | 9)
+#define FA_ABI_VERSION ((1 << 16) | 10)
 
 #ifdef __cplusplus
 }

@@ -24,6 +24,7 @@ from ._lib import (  # noqa: F401
     fa_backward_workspace_bytes,
     fa_forward,
     fa_forward_split,
+    fa_forward_split_noalloc,
     fa_forward_varlen,
     fa_forward_dropout,
     fa_forward_bias,
@@ -37,6 +38,7 @@ from ._lib import (  # noqa: F401
 
 __all__ = [
     "forward", "forward_split", "backward", "naive_forward", "fa_forward", "fa_forward_split",
+    "fa_forward_split_noalloc",
     "fa_backward", "fa_backward_workspace_bytes", "fa_naive_backward", "naive_backward",
     "fa_forward_varlen", "forward_varlen", "fa_forward_dropout", "forward_dropout",
     "fa_forward_bias", "forward_bias", "fa_backward_gqa", "backward_gqa", "fa_backward_varlen",

@@ -90,6 +90,11 @@ _SIGNATURES = {
         ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float,
         ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
         ctypes.c_int64, ctypes.c_void_p]),
+    "fa_forward_split_noalloc": (ctypes.c_int, [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+        ctypes.c_float, ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+        ctypes.c_void_p]),
     "fa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "fa_abi_version": (ctypes.c_int, []),
 }
@@ -249,6 +254,14 @@ def fa_forward_bias(q, k, v, o, lse, bias, B, H, N, d, scale, causal, key_len_ma
 
 def fa_status_string(status) -> str:
     return status_string(status)
+
+
+def fa_forward_split_noalloc(q, k, v, o, lse, B, H, Hkv, Nq, Nk, d, scale, causal, key_len_mask,
+                             dtype, num_splits, stream) -> int:
+    return load().fa_forward_split_noalloc(q or None, k or None, v or None, o or None,
+                                           lse or None, B, H, Hkv, Nq, Nk, d, scale, int(causal),
+                                           key_len_mask or None, dtype, num_splits,
+                                           stream or None)
 
 
 def fa_abi_version() -> int:

@@ -289,14 +289,43 @@ extern "C" size_t fa_split_workspace_bytes(int B, int H, int Nq, int Nk, int d, 
   return split_workspace(sp, d);
 }
 
-extern "C" int fa_forward_split(const void* q, const void* k, const void* v, void* o, float* lse,
-                                int B, int H, int Hkv, int Nq, int Nk, int d, float scale,
-                                int causal, const int32_t* key_len_mask, int dtype, int num_splits,
-                                void* workspace, size_t workspace_bytes, void* stream) {
+// Scratch of fa_forward_split_noalloc: the key ranges' fp32 partial results.
+// Every device the library runs on holds its own copy until the process
+// ends.  In host code the name is only a stand-in for the device array:
+// host code uses the device address scratch_address() returns.
+static __device__ __align__(256) uint8_t scratch[FA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+std::mutex g_scratch_mu;
+void* g_scratch[64] = {};  // device address of scratch, per device
+
+// The current device's address of scratch, looked up once per device (with
+// that device current) and kept.
+int scratch_address(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return FA_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return FA_ERR_HIP;
+    g_scratch[dev] = ptr;
+  }
+  *out = g_scratch[dev];
+  return FA_OK;
+}
+
+// fa_forward_split with the partial results in the caller's workspace, or
+// (use_scratch) in the library's scratch, whose size bounds the problem.
+int forward_split(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                  int Hkv, int Nq, int Nk, int d, float scale, int causal,
+                  const int32_t* key_len_mask, int dtype, int num_splits, void* workspace,
+                  size_t workspace_bytes, bool use_scratch, void* stream) {
   SplitShape sp;
   bool empty = false;
   int st = check_split_scalars(B, H, Hkv, Nq, Nk, d, scale, dtype, num_splits, &sp, &empty);
   if (st != FA_OK || empty) return st;
+  if (use_scratch && split_workspace(sp, d) > FA_NOALLOC_SCRATCH_BYTES) return FA_ERR_WORKSPACE;
   // an empty cache (Nk = 0) is never read: k and v may then be NULL
   if (!q || !o || !lse || (Nk > 0 && (!k || !v))) return FA_ERR_NULL;
   if (!is_aligned(q, 16) || !is_aligned(k, 16) || !is_aligned(v, 16) || !is_aligned(o, 16))
@@ -310,6 +339,11 @@ extern "C" int fa_forward_split(const void* q, const void* k, const void* v, voi
       overlaps(lse, nl, key_len_mask, nkl))
     return FA_ERR_ALIAS;
   const size_t need = split_workspace(sp, d);
+  if (need > 0 && use_scratch) {
+    st = scratch_address(&workspace);
+    if (st != FA_OK) return st;
+    workspace_bytes = FA_NOALLOC_SCRATCH_BYTES;
+  }
   if (need > 0) {
     if (!workspace || workspace_bytes < need || !is_aligned(workspace, 256)) return FA_ERR_WORKSPACE;
     const int64_t nw = static_cast<int64_t>(need);
@@ -346,6 +380,24 @@ extern "C" int fa_forward_split(const void* q, const void* k, const void* v, voi
     if (fa::launch_merge(mp, d, true, hs) != hipSuccess) return FA_ERR_HIP;
   }
   return FA_OK;
+}
+
+}  // namespace
+
+extern "C" int fa_forward_split(const void* q, const void* k, const void* v, void* o, float* lse,
+                                int B, int H, int Hkv, int Nq, int Nk, int d, float scale,
+                                int causal, const int32_t* key_len_mask, int dtype, int num_splits,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  return forward_split(q, k, v, o, lse, B, H, Hkv, Nq, Nk, d, scale, causal, key_len_mask, dtype,
+                       num_splits, workspace, workspace_bytes, false, stream);
+}
+
+extern "C" int fa_forward_split_noalloc(const void* q, const void* k, const void* v, void* o,
+                                        float* lse, int B, int H, int Hkv, int Nq, int Nk, int d,
+                                        float scale, int causal, const int32_t* key_len_mask,
+                                        int dtype, int num_splits, void* stream) {
+  return forward_split(q, k, v, o, lse, B, H, Hkv, Nq, Nk, d, scale, causal, key_len_mask, dtype,
+                       num_splits, nullptr, 0, true, stream);
 }
 
 extern "C" size_t fa_backward_workspace_bytes(int B, int H, int N, int d, int dtype) {

@@ -36,7 +36,7 @@ def test_header_declares_expected_entry_points():
          "fa_forward_split", "fa_forward_varlen", "fa_forward_dropout", "fa_forward_bias",
          "fa_backward_workspace_bytes", "fa_backward", "fa_backward_gqa", "fa_backward_varlen",
          "fa_backward_dropout", "fa_backward_bias",
-         "fa_naive_backward",
+         "fa_naive_backward", "fa_forward_split_noalloc",
          "fa_status_string", "fa_abi_version"])
 
 
@@ -45,7 +45,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     for name in declared_functions():
         assert hasattr(lib, name), name
     assert set(_lib.exported_symbols()) == set(declared_functions())
-    assert fa.fa_abi_version() == (1 << 16) | 9
+    assert fa.fa_abi_version() == (1 << 16) | 10
 
 
 def test_status_strings():
@@ -480,3 +480,23 @@ def test_output_validation_helper():
         _output(torch.zeros(good_shape, dtype=torch.bfloat16), good_shape, torch.bfloat16, dev, "out")
     with pytest.raises(fa.FAError):     # host workspace
         _workspace(torch.zeros(16, dtype=torch.uint8), 16, dev)
+
+
+def test_split_noalloc_validates_before_any_hip_call():
+    """The allocation-free split entry point refuses bad arguments, and
+    problems whose partial results exceed its scratch, before touching the
+    device (these calls run without a GPU)."""
+    call = lambda **kw: fa.fa_forward_split_noalloc(*_noalloc_args(**kw))
+    assert call(q=0) == NULL
+    assert call(d=96) == HEAD_DIM
+    assert call(dtype=F32) == DTYPE
+    assert call(o=Q) == ALIAS
+    assert call(q=Q + 2) == ALIGN
+    # 8 heads x 1024 rows x 64 ranges of fp32 partials: 269 MB > 32 MiB
+    assert call(H=8, Nq=1024, Nk=8192, d=128, num_splits=64) == WORKSPACE
+    assert call(B=0) == OK
+
+
+def _noalloc_args(q=Q, k=K, v=V, o=O, lse=L, B=1, H=2, Hkv=2, Nq=64, Nk=1024, d=64, scale=0.125,
+                  causal=0, kl=0, dtype=BF16, num_splits=4, stream=0):
+    return (q, k, v, o, lse, B, H, Hkv, Nq, Nk, d, scale, causal, kl, dtype, num_splits, stream)
