@@ -115,8 +115,8 @@ def timed_steps(step, args, stream):
     import torch
     ev = []
     t0 = time.perf_counter()
-    n, prev = 0, None
-    while True:
+    n, prev, mean = 0, None, None
+    while args.settle_max_s > 0:
         blk = [torch.cuda.Event(enable_timing=True) for _ in range(11)]
         blk[0].record(stream)
         for i in range(10):
@@ -128,7 +128,7 @@ def timed_steps(step, args, stream):
         n += 10
         mean = sum(d) / 10
         if (n >= 60 and prev is not None and abs(mean - prev) <= 0.01 * prev) or \
-                time.perf_counter() - t0 > 2.0 or n >= 2000:
+                time.perf_counter() - t0 > args.settle_max_s or n >= 2000:
             break
         prev = mean
     settle = {"launches": n, "seconds": time.perf_counter() - t0,
@@ -602,6 +602,82 @@ def bench_varlen(args) -> int:
     return 0
 
 
+SWEEP_N = [256, 512, 1024, 2048, 4096, 8192, 16384, 32768]
+
+
+def bench_sweep(args) -> int:
+    """Sequence-length sweep of the forward, fused against the materialised
+    three-pass baseline: for B = 1, H = 32, d = 128, causal, bf16 Q, K, V
+    i.i.d. N(0, 1) (drawn on the device from a seeded generator), scale
+    1/sqrt(128), and N from 256 to 32768: milliseconds per call (events on
+    the launch stream, after the settle and warm-up of timed_steps), useful
+    TFLOP/s, and the allocation peak of one call above the resident inputs
+    (O and LSE for both; S and P for the naive path).  Prints one JSON line."""
+    import torch
+
+    import io_aware_exact_forward_amd as fa
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    H, d = 32, 128
+    scale = 1.0 / math.sqrt(d)
+    rows = []
+    for N in SWEEP_N:
+        g = torch.Generator(device=dev).manual_seed(5000 + N)
+        q, k, v = (torch.randn(1, H, N, d, device=dev, dtype=torch.bfloat16, generator=g)
+                   for _ in range(3))
+        out = torch.empty_like(q)
+        lse = torch.empty((1, H, N), dtype=torch.float32, device=dev)
+        flops = 4.0 * d * H * N * (N + 1) / 2
+        ms, _, _ = timed_steps(lambda: fa.forward(q, k, v, scale=scale, causal=True, out=out,
+                                                  lse=lse), args, stream)
+
+        def peak_of(fn):
+            torch.cuda.synchronize()
+            torch.cuda.empty_cache()
+            torch.cuda.reset_peak_memory_stats(dev)
+            base = torch.cuda.memory_allocated(dev)
+            r = fn()
+            torch.cuda.synchronize()
+            peak = torch.cuda.max_memory_allocated(dev) - base
+            del r
+            torch.cuda.empty_cache()
+            return peak
+        row = {"N": N, "fused_ms": ms, "fused_tflops": flops / (ms * 1e-3) / 1e12,
+               "fused_extra_peak_bytes": peak_of(lambda: fa.forward(q, k, v, scale=scale,
+                                                                    causal=True)),
+               "compulsory_bytes": 4 * H * N * d * 2 + H * N * 4,
+               "naive_matrix_bytes": 2 * H * N * N * 2}
+        need = fa.fa_naive_workspace_bytes(1, H, N, fa.FA_DTYPE_BF16)
+        if not args.no_naive and need < 0.8 * torch.cuda.mem_get_info(dev)[0]:
+            ws = torch.empty(need, dtype=torch.uint8, device=dev)
+            nrun = lambda: fa.naive_forward(q, k, v, scale=scale, causal=True, workspace=ws)
+            nrun()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(3):
+                nrun()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            del ws
+            torch.cuda.empty_cache()
+            nms = e0.elapsed_time(e1) / 3
+            row.update(naive_ms=nms, naive_tflops=flops / (nms * 1e-3) / 1e12,
+                       naive_extra_peak_bytes=peak_of(lambda: fa.naive_forward(
+                           q, k, v, scale=scale, causal=True)),
+                       speedup_of_fused=nms / ms)
+        rows.append(row)
+        print(json.dumps(row), file=sys.stderr, flush=True)
+        del q, k, v, out, lse
+        torch.cuda.empty_cache()
+    print(json.dumps({"metric": "attention fwd sequence-length sweep (bf16, 1 GPU)",
+                      "config": {"workload": "sweep_h32_d128_causal_bf16", "B": 1, "H": H,
+                                 "d": d, "causal": True, "N": SWEEP_N},
+                      "steps": args.steps, "warmup": args.warmup, "sweep": rows}), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -625,6 +701,12 @@ def main() -> int:
     ap.add_argument("--dropout", type=float, default=0.0,
                     help="square workloads: time fa_forward_dropout at this rate instead; the "
                          "backward workload: fa_backward_dropout of such a forward")
+    ap.add_argument("--settle-max-s", type=float, default=2.0,
+                    help="upper bound on the settle before the warm-up (0: none, e.g. for "
+                         "profiled runs that look at single launches)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="sequence-length sweep (N = 256 .. 32768, 32 heads, d = 128, causal) "
+                         "of the fused forward and the naive baseline: time and memory peak")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-naive", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -663,6 +745,8 @@ def main() -> int:
         print(json.dumps({"copy_probe_bytes": n, "copies": 3}), flush=True)
         return 0
 
+    if args.sweep:
+        return bench_sweep(args)
     if args.workload in W.DECODE_WORKLOADS:
         return bench_decode(args)
     if args.workload in W.BWD_WORKLOADS:

@@ -61,10 +61,11 @@ struct StageTag {
   static constexpr int value = S;
 };
 
-template <int D, int WAVES, int NSTAGE>
+// BKX, if not 0, sets the keys per streamed tile.
+template <int D, int WAVES, int NSTAGE, int BKX = 0>
 struct Bf16Cfg {
   static constexpr int BQ = 32 * WAVES;          // query rows per workgroup
-  static constexpr int BK = D == 128 ? 64 : 128; // keys per streamed tile
+  static constexpr int BK = BKX ? BKX : (D == 128 ? 64 : 128);  // keys per streamed tile
   static constexpr int ROW_BYTES = D * 2;
   static constexpr int CPR = D / 8;              // 16-byte chunks per row
   static constexpr int TILE_BYTES = BK * ROW_BYTES;  // one K or V tile (16 KiB)
@@ -81,15 +82,17 @@ struct Bf16Cfg {
 
 
 template <int D, bool CAUSAL, int WAVES, int NSTAGE, bool PINGPONG, bool DROP = false,
-          bool BIAS = false, bool PERSIST = false>
+          bool BIAS = false, bool PERSIST = false, int BKX = 0>
 // Two lockstep workgroups per CU (256 registers per lane), except with an
-// additive mask at d = 64, whose extra registers do not fit: one workgroup.
+// additive mask at d = 64, whose extra registers do not fit: one workgroup;
+// and three with 64-key tiles at d = 64 (168 registers).
 __global__ __launch_bounds__(64 * WAVES,
-                             (WAVES == 4 && NSTAGE == 2 && !(BIAS && D == 64)) ? 2 : 1)
+                             (WAVES == 4 && D == 64 && BKX == 64 && !BIAS && !DROP) ? 3
+                             : (WAVES == 4 && NSTAGE == 2 && !(BIAS && D == 64)) ? 2 : 1)
 void fa_fwd_bf16_kernel(FwdParams p) {
   static_assert(!(DROP || BIAS) || !PINGPONG, "dropout and bias run in the lockstep schedule");
   static_assert(!PERSIST || PINGPONG, "the persistent form is the ping-pong schedule's");
-  using C = Bf16Cfg<D, WAVES, NSTAGE>;
+  using C = Bf16Cfg<D, WAVES, NSTAGE, BKX>;
   __shared__ __attribute__((aligned(1024))) uint8_t lds[C::LDS_BYTES];
 
   const int tid = threadIdx.x;
@@ -1016,14 +1019,14 @@ void fa_fwd_bf16_kernel(FwdParams p) {
 }
 
 template <int D, bool CAUSAL, int WAVES, int NSTAGE, bool PINGPONG, bool DROP = false,
-          bool BIAS = false, bool PERSIST = false>
+          bool BIAS = false, bool PERSIST = false, int BKX = 0>
 hipError_t launch_cfg(FwdParams p, hipStream_t stream) {
-  using C = Bf16Cfg<D, WAVES, NSTAGE>;
+  using C = Bf16Cfg<D, WAVES, NSTAGE, BKX>;
   p.n_qtiles = (p.N + C::BQ - 1) / C::BQ;
   const int64_t items = (int64_t)p.n_qtiles * p.B * p.H * p.splits;
   // persistent: items / 2 units, p.persist per workgroup
   const dim3 grid((unsigned)(PERSIST ? items / 2 / p.persist : items));
-  hipLaunchKernelGGL((fa_fwd_bf16_kernel<D, CAUSAL, WAVES, NSTAGE, PINGPONG, DROP, BIAS, PERSIST>),
+  hipLaunchKernelGGL((fa_fwd_bf16_kernel<D, CAUSAL, WAVES, NSTAGE, PINGPONG, DROP, BIAS, PERSIST, BKX>),
                      grid, dim3(64 * WAVES), 0, stream, p);
   return hipGetLastError();
 }
@@ -1083,6 +1086,11 @@ hipError_t launch_d(const FwdParams& p, hipStream_t stream) {
     }
     return launch_cfg<D, CAUSAL, 8, kPingPongStages, true>(p, stream);
   }
+  // d = 64 with per-sequence lengths: 64-key tiles, three workgroups per CU
+  // (more waves to hide the softmax's dependency stalls: 8 x 16 x 4096 with
+  // ragged lengths 349 -> 330 us; without lengths, on the 32-head N = 2048
+  // causal workload, 128-key tiles at two per CU stay faster, 34.5 vs 37 us)
+  if (ragged64) return launch_cfg<D, CAUSAL, 4, 2, false, false, false, false, 64>(p, stream);
   return launch_cfg<D, CAUSAL, 4, 2, false>(p, stream);
 }
 
