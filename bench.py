@@ -259,9 +259,11 @@ def bench_decode(args) -> int:
     dev = torch.device("cuda:0")
     q, k, v, kl = to_device(inp, dev)
     B, H, Nk, d = wl.B, wl.H, wl.Nk, wl.d
+    Hkv = wl.kv_heads
     lens = [int(x) for x in np.clip(inp.key_len, 0, Nk)]
     flops = 4.0 * d * H * sum(lens)
-    algo_bytes = sum(H * (2 * L * d * 2 + 2 * d * 2 + 4) for L in lens)
+    # each valid K and V row of every key/value head read once; q, o, LSE
+    algo_bytes = sum(Hkv * 2 * L * d * 2 + H * (2 * d * 2 + 4) for L in lens)
     ws_bytes = fa.fa_split_workspace_bytes(B, H, 1, Nk, d, 0)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     out = torch.empty_like(q)
@@ -309,9 +311,10 @@ def bench_decode(args) -> int:
         pairs, done, t0 = 0, 0, time.perf_counter()
         for b in range(B):
             for h in range(H):
-                oracle.attention(qx[b:b + 1, h:h + 1], kx[b:b + 1, h:h + 1], vx[b:b + 1, h:h + 1],
-                                 wl.scale, causal=True, key_len=inp.key_len[b:b + 1],
-                                 end_aligned=True)
+                hk = h // (H // Hkv)  # the key/value head query head h reads
+                oracle.attention(qx[b:b + 1, h:h + 1], kx[b:b + 1, hk:hk + 1],
+                                 vx[b:b + 1, hk:hk + 1], wl.scale, causal=True,
+                                 key_len=inp.key_len[b:b + 1], end_aligned=True)
                 pairs += lens[b]
                 done += 1
                 if time.perf_counter() - t0 > args.cpu_seconds:

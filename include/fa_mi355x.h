@@ -154,10 +154,14 @@ int fa_naive_forward(const void* q, const void* k, const void* v, void* o, float
  *                O = 0 and LSE = -inf.
  *   dtype        FA_DTYPE_BF16 only (FA_ERR_DTYPE otherwise).
  *   num_splits   key ranges per query tile, >= 1, or 0 to let the library
- *                choose enough ranges to fill the device.  Ranges are whole
- *                128-key blocks, so fewer ranges than asked may be used.
+ *                choose enough ranges to fill the device (with Nq = 1 and
+ *                H / Hkv = 2, 4 or 8, one workgroup serves the query heads of a
+ *                key/value head, and the choice counts those workgroups).
+ *                Ranges are whole 128-key blocks, so fewer ranges than asked
+ *                may be used.
  *   workspace    device memory, 256-byte aligned, of at least
- *                fa_split_workspace_bytes(B, H, Nq, Nk, d, num_splits) bytes,
+ *                fa_split_workspace_bytes(B, H, Nq, Nk, d, num_splits) bytes
+ *                (enough for every Hkv dividing H),
  *                overlapping no other argument: fp32 partial outputs
  *                [ranges, B, H, Nq, d] and their log-sum-exp [ranges, B, H, Nq].
  *                When a single range is used it is not touched (NULL and 0 are

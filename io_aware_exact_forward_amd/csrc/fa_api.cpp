@@ -125,7 +125,7 @@ struct SplitShape {
 
 // Ranges are whole 128-key blocks.  With num_splits = 0: enough ranges that
 // 128-row query tiles times ranges reach 512 workgroups (two per CU).
-void plan_split(int B, int H, int Nq, int Nk, int num_splits, SplitShape* sp) {
+void plan_split(int B, int H, int Hkv, int Nq, int Nk, int num_splits, SplitShape* sp) {
   const int64_t kblocks = (int64_t(Nk) + kSplitBlock - 1) / kSplitBlock;
   if (kblocks == 0) {
     sp->splits = 1;
@@ -134,7 +134,12 @@ void plan_split(int B, int H, int Nq, int Nk, int num_splits, SplitShape* sp) {
   }
   int64_t want = num_splits;
   if (want == 0) {
-    const int64_t tiles = int64_t(B) * H * ((int64_t(Nq) + fa::kQueryTile - 1) / fa::kQueryTile);
+    // workgroups per range: one per query tile and head; a decode step with
+    // grouped heads runs one query tile per key/value head (grouped_decode)
+    const bool grouped = Nq == 1 && Hkv > 0 && Hkv < H;
+    const int64_t tiles = grouped ? int64_t(B) * Hkv
+                                  : int64_t(B) * H *
+                                        ((int64_t(Nq) + fa::kQueryTile - 1) / fa::kQueryTile);
     want = tiles > 0 ? (512 + tiles - 1) / tiles : 1;
   }
   want = std::max<int64_t>(1, std::min<int64_t>(want, kblocks));
@@ -160,7 +165,7 @@ int check_split_scalars(int B, int H, int Hkv, int Nq, int Nk, int d, float scal
   if (bh * Nq > kMaxElems / d || bh * Nk > kMaxElems / d) return FA_ERR_SHAPE;
   // byte offsets within one (batch, head) slice are 32-bit in the kernels
   if (int64_t(Nq) * d * 2 > INT_MAX || int64_t(Nk) * d * 2 > INT_MAX) return FA_ERR_SHAPE;
-  plan_split(B, H, Nq, Nk, num_splits, sp);
+  plan_split(B, H, Hkv, Nq, Nk, num_splits, sp);
   const int64_t qtiles = (int64_t(Nq) + fa::kQueryTile - 1) / fa::kQueryTile;
   if (qtiles * bh * sp->splits > INT_MAX) return FA_ERR_SHAPE;
   sp->bh = bh;
@@ -281,12 +286,21 @@ extern "C" int fa_naive_forward(const void* q, const void* k, const void* v, voi
 }
 
 extern "C" size_t fa_split_workspace_bytes(int B, int H, int Nq, int Nk, int d, int num_splits) {
-  SplitShape sp;
-  bool empty = false;
-  if (check_split_scalars(B, H, 1, Nq, Nk, d, 1.f, FA_DTYPE_BF16, num_splits, &sp, &empty) != FA_OK ||
-      empty)
-    return 0;
-  return split_workspace(sp, d);
+  // The automatic range count of a decode step depends on the number of
+  // key/value heads: the largest over every Hkv that divides H.
+  size_t most = 0;
+  for (int hkv = 1; hkv <= std::max(H, 1); ++hkv) {
+    if (H > 0 && H % hkv) continue;
+    if (Nq != 1 && hkv > 1) break;  // only decode depends on it
+    SplitShape sp;
+    bool empty = false;
+    if (check_split_scalars(B, H, hkv, Nq, Nk, d, 1.f, FA_DTYPE_BF16, num_splits, &sp,
+                            &empty) != FA_OK ||
+        empty)
+      return 0;
+    most = std::max(most, split_workspace(sp, d));
+  }
+  return most;
 }
 
 // Scratch of fa_forward_split_noalloc: the key ranges' fp32 partial results.
@@ -353,12 +367,22 @@ int forward_split(const void* q, const void* k, const void* v, void* o, float* l
       return FA_ERR_ALIAS;
   }
 
-  fa::FwdParams p = make_params(q, k, v, o, lse, B, H, Nq, scale, key_len_mask, dtype);
+  // A decode step with grouped heads: the G = H / Hkv query heads of a
+  // key/value head hold one row each, at stride d in q and o (and 1 in the
+  // LSE), which is the layout of G query rows of one head.  Every decode row
+  // sees the keys below its sequence's length, causal or not.  So the step
+  // runs as Hkv heads of G rows each, not causal, on the main kernel, whose
+  // products then go to the matrix cores and whose key/value tiles serve all
+  // G rows: each K and V row is read once per key range.
+  const bool grouped_decode = Nq == 1 && Hkv < H;
+  const int vH = grouped_decode ? Hkv : H, vN = grouped_decode ? H / Hkv : Nq;
+  fa::FwdParams p = make_params(q, k, v, o, lse, B, vH, vN, scale, key_len_mask, dtype);
   p.Nk = Nk;
   p.Hkv = Hkv;
   p.end_aligned = 1;
   p.splits = sp.splits;
   p.split_keys = sp.split_keys;
+  if (grouped_decode) causal = 0;
   hipStream_t hs = static_cast<hipStream_t>(stream);
   if (sp.splits > 1) {
     p.o_part = static_cast<float*>(workspace);
@@ -366,8 +390,8 @@ int forward_split(const void* q, const void* k, const void* v, void* o, float* l
   }
   // one query row: the row sees every key below its sequence's length
   // whether or not the mask is causal
-  const hipError_t e = Nq == 1 ? fa::launch_decode_bf16(p, d, hs)
-                               : fa::launch_fwd_bf16(p, d, causal != 0, hs);
+  const hipError_t e = Nq == 1 && !grouped_decode ? fa::launch_decode_bf16(p, d, hs)
+                                                  : fa::launch_fwd_bf16(p, d, causal != 0, hs);
   if (e != hipSuccess) return FA_ERR_HIP;
   if (sp.splits > 1) {
     fa::MergeParams mp{};

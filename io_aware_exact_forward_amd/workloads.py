@@ -212,43 +212,54 @@ def cache_inputs(B, H, Nq, Nk, d, seed, *, q_mult=1.0, key_len=None, Hkv=None):
 @dataclasses.dataclass(frozen=True)
 class DecodeWorkload:
     """One query row per (sequence, head) against a key cache of Nk rows
-    whose per-sequence lengths are uniform on [1, Nk]; causal, bf16."""
+    whose per-sequence lengths are uniform on [1, Nk]; causal, bf16.  Hkv
+    key/value heads (0: as many as query heads); query head h reads head
+    h // (H // Hkv)."""
     name: str
     B: int
     H: int
     Nk: int
     d: int
     seed: int
+    Hkv: int = 0
+
+    @property
+    def kv_heads(self) -> int:
+        return self.Hkv or self.H
 
     @property
     def scale(self) -> float:
         return 1.0 / math.sqrt(self.d)
 
     def describe(self) -> dict:
-        return {"workload": self.name, "B": self.B, "H": self.H, "Nq": 1, "Nk": self.Nk,
-                "d": self.d, "dtype": "bf16", "causal": True, "scale": self.scale,
-                "key_len": "per sequence, uniform on [1, Nk]"}
+        return {"workload": self.name, "B": self.B, "H": self.H, "Hkv": self.kv_heads, "Nq": 1,
+                "Nk": self.Nk, "d": self.d, "dtype": "bf16", "causal": True,
+                "scale": self.scale, "key_len": "per sequence, uniform on [1, Nk]"}
 
 
 DECODE_WORKLOADS = {
     # decode step of 8 sequences x 32 heads, d = 128, caches of up to 16384 keys
     "decode_b8_h32_k16384_d128_bf16": DecodeWorkload(
         "decode_b8_h32_k16384_d128_bf16", 8, 32, 16384, 128, 1006),
+    # the same with 32 query heads on 8 key/value heads (four per group)
+    "decode_b8_h32_hkv8_k16384_d128_bf16": DecodeWorkload(
+        "decode_b8_h32_hkv8_k16384_d128_bf16", 8, 32, 16384, 128, 1007, Hkv=8),
 }
 
 
 def decode_inputs(wl: DecodeWorkload, *, B=None, H=None, Nk=None, seed=None) -> "Inputs":
-    """q [B, H, 1, d], then k, v [B, H, Nk, d], then key lengths (same recipe);
-    keyword overrides give smaller variants."""
+    """q [B, H, 1, d], then k, v [B, Hkv, Nk, d], then key lengths (same
+    recipe); keyword overrides give smaller variants."""
     B = wl.B if B is None else B
     H = wl.H if H is None else H
     Nk = wl.Nk if Nk is None else Nk
     seed = wl.seed if seed is None else seed
     d = wl.d
+    Hkv = H if not wl.Hkv else wl.Hkv * H // wl.H
     rng = np.random.default_rng(seed)
     q = bf16_encode(rng.standard_normal((B, H, 1, d), dtype=np.float32))
-    k = bf16_encode(rng.standard_normal((B, H, Nk, d), dtype=np.float32))
-    v = bf16_encode(rng.standard_normal((B, H, Nk, d), dtype=np.float32))
+    k = bf16_encode(rng.standard_normal((B, Hkv, Nk, d), dtype=np.float32))
+    v = bf16_encode(rng.standard_normal((B, Hkv, Nk, d), dtype=np.float32))
     kl = rng.integers(1, Nk, size=B, endpoint=True, dtype=np.int64).astype(np.int32)
     sq = Workload(wl.name, B, H, Nk, d, "bf16", True, wl.scale, seed, ragged=True)
     return Inputs(sq, q, k, v, kl, None)

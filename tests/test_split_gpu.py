@@ -137,6 +137,28 @@ def test_split_reuses_a_caller_workspace():
         check(inp, True, 1 / np.sqrt(128), og, lse.cpu().numpy().astype(np.float64), "reuse")
 
 
+def test_grouped_decode_full_size():
+    """The grouped decode workload at full size (8 sequences, 32 query heads on
+    8 key/value heads, one query row against caches of up to 16384 keys), in
+    the automatic range count the benchmark uses; every row of every head
+    against the oracle."""
+    wl = W.DECODE_WORKLOADS["decode_b8_h32_hkv8_k16384_d128_bf16"]
+    inp = W.decode_inputs(wl)
+    say("decode", wl.name, "lengths", inp.key_len.tolist())
+    o, lse = run_split(inp, True, wl.scale, 0)
+    check(inp, True, wl.scale, o, lse, "grouped decode, all heads")
+
+
+@pytest.mark.parametrize("G", [2, 4, 8])
+def test_grouped_decode_negative_scale(G):
+    """Grouped decode with a negative scale (the sign folded into each
+    head's q) and several ranges."""
+    B, H, Nk, d = 2, 2 * G, 900, 128
+    inp = W.cache_inputs(B, H, 1, Nk, d, 9140 + G, key_len=[900, 301], Hkv=2)
+    o, lse = run_split(inp, True, -0.1, 3)
+    check(inp, True, -0.1, o, lse, f"grouped decode G={G}, negative scale")
+
+
 def test_decode_full_size_sampled_heads():
     """The decode workload at full size (8 sequences, 32 heads, one query row
     against caches of up to 16384 keys with per-sequence lengths), in the
@@ -155,9 +177,17 @@ def test_decode_full_size_sampled_heads():
 
 GQA_CASES = [
     # (B, H, Hkv, Nq, Nk, d, key_len, seed)
-    (2, 8, 2, 1, 2000, 128, [2000, 333], 9801),     # grouped decode
+    (2, 8, 2, 1, 2000, 128, [2000, 333], 9801),     # grouped decode (4 heads per group)
     (1, 6, 1, 130, 700, 64, None, 9802),            # multi-query, chunked prefill
     (2, 4, 2, 300, 300, 128, None, 9803),           # square
+    # decode: one workgroup serves the 2, 4 or 8 query heads of a key/value
+    # head; 3 and 16 heads per group take one workgroup per query head
+    (3, 4, 2, 1, 1500, 64, [1500, 0, 1], 9804),
+    (2, 16, 2, 1, 3001, 128, [3001, 2049], 9805),
+    (2, 16, 2, 1, 999, 64, [17, 999], 9806),
+    (1, 8, 1, 1, 1200, 128, [1200], 9807),
+    (2, 6, 2, 1, 777, 128, [777, 128], 9808),
+    (1, 16, 1, 1, 640, 64, [640], 9809),
 ]
 
 
