@@ -299,7 +299,9 @@ def bench_decode(args) -> int:
             "unit": "GB/s",
             "frac": gbs / PEAK_HBM_GBS,
             "traffic": stored_traffic(wl.name, "split"),
-            "kernel": "fa_decode_kernel + merge_kernel (one call; both inside the events)",
+            "kernel": ("fa_decode_balanced_kernel + merge_kernel" if Hkv == H else
+                       "fa_fwd_bf16_kernel (a key/value head's query heads as rows) + merge_kernel")
+                      + " (one call; both inside the events)",
             "kernel_hash": kernel_hash("split"),
         },
         "wall_s_timed_region": t_wall,

@@ -154,18 +154,25 @@ int fa_naive_forward(const void* q, const void* k, const void* v, void* o, float
  *                O = 0 and LSE = -inf.
  *   dtype        FA_DTYPE_BF16 only (FA_ERR_DTYPE otherwise).
  *   num_splits   key ranges per query tile, >= 1, or 0 to let the library
- *                choose enough ranges to fill the device (with Nq = 1 and
- *                H / Hkv = 2, 4 or 8, one workgroup serves the query heads of a
- *                key/value head, and the choice counts those workgroups).
- *                Ranges are whole 128-key blocks, so fewer ranges than asked
- *                may be used.
+ *                choose.  With 0, a decode step (Nq = 1) with Hkv = H that
+ *                would need more than one range per row to fill the device
+ *                is cut instead into P <= 512 equal shares of all rows'
+ *                visible keys (64-key units, rows laid end to end), one per
+ *                workgroup, whatever the per-sequence lengths (which are
+ *                read on the device); every other shape gets enough ranges
+ *                to fill the device (with Nq = 1 and Hkv < H one workgroup
+ *                serves the H / Hkv query heads of a key/value head, and the
+ *                choice counts those workgroups).  Ranges are whole 128-key
+ *                blocks, so fewer ranges than asked may be used.
  *   workspace    device memory, 256-byte aligned, of at least
  *                fa_split_workspace_bytes(B, H, Nq, Nk, d, num_splits) bytes
  *                (enough for every Hkv dividing H),
  *                overlapping no other argument: fp32 partial outputs
- *                [ranges, B, H, Nq, d] and their log-sum-exp [ranges, B, H, Nq].
- *                When a single range is used it is not touched (NULL and 0 are
- *                then accepted).
+ *                [ranges, B, H, Nq, d] and their log-sum-exp [ranges, B, H, Nq]
+ *                for key ranges; for balanced shares 4 (P + B H) partial rows
+ *                of d floats, their log-sum-exp, then B + 1 int64 unit
+ *                offsets.  When a single range is used it is not touched
+ *                (NULL and 0 are then accepted).
  *   Sizes        B, H, Nq, Nk >= 0 (nothing to do if B, H or Nq is 0; Nk = 0
  *                gives O = 0, LSE = -inf, and k, v may then be NULL); one
  *                (batch, head) slice of q and of

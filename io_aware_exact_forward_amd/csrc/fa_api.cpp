@@ -121,7 +121,17 @@ struct SplitShape {
   int64_t kv_elems = 0;  // B*H*Nk*d
   int splits = 1;        // ranges actually used
   int split_keys = kSplitBlock;
+  // decode step split into balanced shares of the visible keys
+  bool balanced = false;
+  int workgroups = 0;    // shares
+  int B = 0;
 };
+
+// Shares of a balanced decode step, one per 4-wave workgroup: two per CU
+// (the decode kernel's register use allows two at d = 128), all resident at
+// once.
+constexpr int kDecodeShares = 512;
+constexpr int kDecodeWaves = 4;  // partials per share and row
 
 // Ranges are whole 128-key blocks.  With num_splits = 0: enough ranges that
 // 128-row query tiles times ranges reach 512 workgroups (two per CU).
@@ -166,21 +176,44 @@ int check_split_scalars(int B, int H, int Hkv, int Nq, int Nk, int d, float scal
   // byte offsets within one (batch, head) slice are 32-bit in the kernels
   if (int64_t(Nq) * d * 2 > INT_MAX || int64_t(Nk) * d * 2 > INT_MAX) return FA_ERR_SHAPE;
   plan_split(B, H, Hkv, Nq, Nk, num_splits, sp);
+  // A decode step (one query row, a key/value head per query head) that the
+  // automatic plan would split: the visible keys of all rows are instead cut
+  // into equal shares on the device, whatever the per-sequence lengths, so no
+  // workgroup is left with a long sequence's range while the rest idle.
+  if (num_splits == 0 && Nq == 1 && Hkv == H && sp->splits > 1) {
+    const int64_t units = bh * ((int64_t(Nk) + 63) / 64);
+    sp->balanced = true;
+    sp->workgroups = static_cast<int>(std::min<int64_t>(kDecodeShares, units));
+    sp->splits = 1;
+  }
   const int64_t qtiles = (int64_t(Nq) + fa::kQueryTile - 1) / fa::kQueryTile;
   if (qtiles * bh * sp->splits > INT_MAX) return FA_ERR_SHAPE;
   sp->bh = bh;
+  sp->B = B;
   sp->rows = bh * Nq;
   sp->kv_elems = int64_t(B) * Hkv * Nk * d;
   return FA_OK;
 }
 
-size_t split_part_bytes(const SplitShape& sp, int d) {
-  return round256(size_t(sp.splits) * size_t(sp.rows) * size_t(d) * sizeof(float));
+// Partial results: [splits, rows] for key ranges, 4 (P + B*H) slots for
+// balanced decode shares (one per wave of each share and row).
+size_t split_slots(const SplitShape& sp) {
+  return sp.balanced ? kDecodeWaves * (size_t(sp.workgroups) + size_t(sp.rows))
+                     : size_t(sp.splits) * size_t(sp.rows);
 }
 
+size_t split_part_bytes(const SplitShape& sp, int d) {
+  return round256(split_slots(sp) * size_t(d) * sizeof(float));
+}
+
+size_t split_lse_bytes(const SplitShape& sp) { return round256(split_slots(sp) * sizeof(float)); }
+
 size_t split_workspace(const SplitShape& sp, int d) {
+  if (sp.balanced)  // partials, their LSE, then cum [B + 1] (int64)
+    return split_part_bytes(sp, d) + split_lse_bytes(sp) +
+           round256((size_t(sp.B) + 1) * sizeof(int64_t));
   if (sp.splits <= 1) return 0;
-  return split_part_bytes(sp, d) + round256(size_t(sp.splits) * size_t(sp.rows) * sizeof(float));
+  return split_part_bytes(sp, d) + split_lse_bytes(sp);
 }
 
 // One rocBLAS handle per device for the materialised path's two products.
@@ -384,25 +417,39 @@ int forward_split(const void* q, const void* k, const void* v, void* o, float* l
   p.split_keys = sp.split_keys;
   if (grouped_decode) causal = 0;
   hipStream_t hs = static_cast<hipStream_t>(stream);
-  if (sp.splits > 1) {
-    p.o_part = static_cast<float*>(workspace);
-    p.lse_part = reinterpret_cast<float*>(static_cast<char*>(workspace) + split_part_bytes(sp, d));
+  char* const ws = static_cast<char*>(workspace);
+  if (sp.splits > 1 || sp.balanced) {
+    p.o_part = reinterpret_cast<float*>(ws);
+    p.lse_part = reinterpret_cast<float*>(ws + split_part_bytes(sp, d));
+  }
+  fa::MergeParams mp{};
+  mp.o_part = p.o_part;
+  mp.lse_part = p.lse_part;
+  mp.o = o;
+  mp.lse = lse;
+  mp.rows = sp.rows;
+  mp.splits = sp.splits;
+  if (sp.balanced) {
+    // the decode kernel leaves partials of every row; the merge completes
+    // them
+    int64_t* cum =
+        reinterpret_cast<int64_t*>(ws + split_part_bytes(sp, d) + split_lse_bytes(sp));
+    if (fa::launch_decode_balanced_bf16(p, d, sp.workgroups, cum, hs) != hipSuccess)
+      return FA_ERR_HIP;
+    mp.cum = cum;
+    mp.key_len = key_len_mask;
+    mp.B = B;
+    mp.H = H;
+    mp.Nk = Nk;
+    mp.workgroups = sp.workgroups;
+    return fa::launch_merge(mp, d, true, hs) == hipSuccess ? FA_OK : FA_ERR_HIP;
   }
   // one query row: the row sees every key below its sequence's length
   // whether or not the mask is causal
   const hipError_t e = Nq == 1 && !grouped_decode ? fa::launch_decode_bf16(p, d, hs)
                                                   : fa::launch_fwd_bf16(p, d, causal != 0, hs);
   if (e != hipSuccess) return FA_ERR_HIP;
-  if (sp.splits > 1) {
-    fa::MergeParams mp{};
-    mp.o_part = p.o_part;
-    mp.lse_part = p.lse_part;
-    mp.o = o;
-    mp.lse = lse;
-    mp.rows = sp.rows;
-    mp.splits = sp.splits;
-    if (fa::launch_merge(mp, d, true, hs) != hipSuccess) return FA_ERR_HIP;
-  }
+  if (sp.splits > 1 && fa::launch_merge(mp, d, true, hs) != hipSuccess) return FA_ERR_HIP;
   return FA_OK;
 }
 

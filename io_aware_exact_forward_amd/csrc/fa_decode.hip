@@ -1,8 +1,16 @@
 // Attention for one query row per (batch, head) against a key cache: the
 // decode step of "IO-aware exact attention" (section "Common errors" names
-// decode as a shape that needs its own schedule).  One workgroup computes one
-// key range of one (batch, head); ranges are merged by their log-sum-exp
-// ("FlashAttention" glossary, section "Why a tile can be discarded").
+// decode as a shape that needs its own schedule).  A workgroup computes key
+// ranges of (batch, head) rows; a row split over several workgroups is merged
+// by the ranges' log-sum-exp ("FlashAttention" glossary, section "Why a tile
+// can be discarded").  Two ways to hand out the work:
+//  * fixed ranges: workgroup = (range of split_keys keys, (batch, head));
+//  * balanced: the visible keys of all rows, in 64-key units, are cut into
+//    equal shares, one per workgroup, whatever the per-sequence lengths.
+//    Rows are laid end to end (sequence by sequence, head by head, key
+//    order within a row) and workgroup w takes units [w T / P, (w + 1) T /
+//    P) of the T units (P workgroups).  The per-sequence lengths are read on
+//    the device, so the host needs none of them.
 //
 // With a single query row there is no matrix product to speak of: the work
 // is streaming K and V once from HBM.  Each wave takes 64 keys at a time:
@@ -17,8 +25,8 @@
 //    a numerator slice of 8 dimensions, rescaled when the maximum rises
 //    ("FlashAttention: Exact Attention as an IO-Aware Streaming Computation",
 //    section "Mathematical structure"); the weights never leave the lane.
-// At the end the wave's slices are summed across its lane groups and the
-// four waves' states are merged through LDS.  (One key row per lane would
+// At the end the wave's slices are summed across its lane groups; with fixed
+// ranges the four waves' states are then merged through LDS.  (One key row per lane would
 // need no sum across lanes, but its loads touch 64 rows per instruction and
 // ran 1.7x slower.)
 #include "fa_device.hpp"
@@ -30,32 +38,37 @@ namespace {
 constexpr int kDecodeWaves = 4;
 
 template <int D>
-__global__ __launch_bounds__(64 * kDecodeWaves) void fa_decode_kernel(FwdParams p) {
+struct DecodeLds {
+  float m[kDecodeWaves], l[kDecodeWaves];
+  __attribute__((aligned(16))) float o[kDecodeWaves][D];
+};
+
+__device__ __forceinline__ int seq_len(const FwdParams& p, int b) {
+  if (!p.key_len) return p.Nk;
+  const int kl = p.key_len[b];
+  return kl < 0 ? 0 : (kl > p.Nk ? p.Nk : kl);
+}
+
+// Keys [k0, k1) of row bh (sequence b, key/value head hk, L keys visible):
+// the four waves take 64 keys at a time in turn, then merge their states
+// through LDS.  Threads tid < D return element tid of the range's normalised
+// output in y and the range's log-sum-exp (natural log) in lse; the range
+// holds at least one key.  Ends with a barrier, so s may be reused at once.
+// One wave's pass over keys [k0, k1) of row bh (sequence b, key/value head
+// hk, L keys visible), 64 keys at a time with a stride of `step` keys (the
+// waves that share a range take its 64-key chunks in turn).  On return the
+// lanes of group 0 (lane < D/8) hold the wave's numerator for dimensions
+// 8 lane .. 8 lane + 7 in o, every lane the wave's running maximum m (log2
+// units, -inf if the wave saw no key) and denominator l.
+template <int D>
+__device__ __forceinline__ void decode_wave(const FwdParams& p, const int bh, const int b,
+                                            const int hk, const int L, const int k0, const int k1,
+                                            const int step, float (&o)[8], float& m, float& l) {
   constexpr int LPR = D / 8;   // lanes per K or V row (16 bytes each)
   constexpr int G = 64 / LPR;  // key groups per wave
   constexpr int IT = 64 / G;   // keys per group and chunk
   static_assert(LPR == 8 || LPR == 16, "d = 64 or 128");
-  __shared__ float m_lds[kDecodeWaves], l_lds[kDecodeWaves];
-  __shared__ __attribute__((aligned(16))) float o_lds[kDecodeWaves][D];
-
-  const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int lane = tid & 63;
-  const int x = blockIdx.x;
-  const int split = x % p.splits;
-  const int bh = x / p.splits;
-  const int b = bh / p.H, hq = bh - b * p.H;
-  const int hk = hq / (p.H / p.Hkv);
-  int L = p.Nk;
-  if (p.key_len) {
-    const int kl = p.key_len[b];
-    L = kl < 0 ? 0 : (kl > p.Nk ? p.Nk : kl);
-  }
-  L = __builtin_amdgcn_readfirstlane(L);
-  // this workgroup's keys: [k0, k1) (the row sits at position L - 1, so
-  // under the causal mask it sees every key below L as well)
-  const int k0 = split * p.split_keys;
-  const int k1 = min(L, k0 + p.split_keys);
+  const int lane = threadIdx.x & 63;
 
   const uint32_t row_bytes = D * 2;
   const void* kbase = (const uint16_t*)p.k + ((int64_t)b * p.Hkv + hk) * p.Nk * D;
@@ -65,18 +78,20 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void fa_decode_kernel(FwdParams 
 
   float m_run = kNegInf;  // running maximum of c * s (log2 units), wave-uniform
   float l_g = 0.f;        // denominator over group g's keys (the same in its LPR lanes)
-  float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};  // dims 8t .. 8t+7 over group g's keys
-  // this lane's part of q: dimensions 8t .. 8t+7 as bf16 pairs, the sign
-  // folded in for a negative scale
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o[e] = 0.f;  // dims 8t .. 8t+7 over group g's keys
+  // this lane's part of q: dimensions 8t .. 8t+7 as bf16 pairs.  Its first
+  // use is in the first chunk, after that chunk's K and V loads are issued,
+  // so the q load costs no round trip of its own; a negative scale therefore
+  // enters through the sign of c (exactly: negating q negates every fp32
+  // product and sum) rather than through q.
   const u32x4 qv = *(const u32x4*)((const uint16_t*)p.q + (int64_t)bh * D + 8 * t);
   uint32_t qt4[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const uint32_t w = qv[j];
-    qt4[j] = w ^ p.q_sign;
-  }
+  for (int j = 0; j < 4; ++j) qt4[j] = qv[j];
+  const float c = p.q_sign ? -p.c : p.c;
 
-  for (int c0 = k0 + 64 * wave; c0 < k1; c0 += 64 * kDecodeWaves) {
+  for (int c0 = k0; c0 < k1; c0 += step) {
     // ---- loads: rows c0 + g IT + i of K and V, 16 bytes (column t) each
     u32x4 kr[IT], vr[IT];
 #pragma unroll
@@ -104,7 +119,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void fa_decode_kernel(FwdParams 
       a += dpp_f32<0x4E>(a);   // quad_perm [2, 3, 0, 1]
       a += dpp_f32<0x141>(a);  // row_half_mirror: the 8-lane sum
       if constexpr (LPR == 16) a += dpp_f32<0x140>(a);  // row_mirror: the 16-lane sum
-      sc[i] = c0 + g * IT + i < k1 ? a * p.c : kNegInf;
+      sc[i] = c0 + g * IT + i < k1 ? a * c : kNegInf;
       mx = fmaxf(mx, sc[i]);
     }
     // ---- running maximum (over the wave's 64 keys) and weights
@@ -139,41 +154,205 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void fa_decode_kernel(FwdParams 
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[e] += __shfl_xor(o[e], off);
   }
+  m = m_run;
+  l = l_w;
+}
+
+// Keys [k0, k1) of row bh by the four waves of the workgroup, their states
+// merged through LDS.  Threads tid < D return element tid of the range's
+// normalised output in y and the range's log-sum-exp (natural log) in lse;
+// the range holds at least one key.
+template <int D>
+__device__ __forceinline__ void decode_range(const FwdParams& p, DecodeLds<D>& s, const int bh,
+                                             const int b, const int hk, const int L, const int k0,
+                                             const int k1, float& y, float& lse) {
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  float o[8], m_w, l_w;
+  decode_wave<D>(p, bh, b, hk, L, k0 + 64 * wave, k1, 64 * kDecodeWaves, o, m_w, l_w);
   if (lane == 0) {
-    m_lds[wave] = m_run;
-    l_lds[wave] = l_w;
+    s.m[wave] = m_w;
+    s.l[wave] = l_w;
   }
-  if (g == 0) {
-    *(f32x4*)&o_lds[wave][8 * t] = f32x4{o[0], o[1], o[2], o[3]};
-    *(f32x4*)&o_lds[wave][8 * t + 4] = f32x4{o[4], o[5], o[6], o[7]};
+  if (lane < D / 8) {
+    *(f32x4*)&s.o[wave][8 * lane] = f32x4{o[0], o[1], o[2], o[3]};
+    *(f32x4*)&s.o[wave][8 * lane + 4] = f32x4{o[4], o[5], o[6], o[7]};
   }
   __syncthreads();
 
-  // ---- merge of the four waves (each a common-reference summary) and output
+  // ---- merge of the four waves (each a common-reference summary)
   if (tid < D) {
     float m = kNegInf;
 #pragma unroll
-    for (int w = 0; w < kDecodeWaves; ++w) m = fmaxf(m, m_lds[w]);
+    for (int w = 0; w < kDecodeWaves; ++w) m = fmaxf(m, s.m[w]);
     float l = 0.f, a = 0.f;
     if (m != kNegInf) {
 #pragma unroll
       for (int w = 0; w < kDecodeWaves; ++w) {
-        if (m_lds[w] == kNegInf) continue;  // the wave saw no key
-        const float sc = fast_exp2(m_lds[w] - m);
-        l += sc * l_lds[w];
-        a += sc * o_lds[w][tid];
+        if (s.m[w] == kNegInf) continue;  // the wave saw no key
+        const float sc = fast_exp2(s.m[w] - m);
+        l += sc * s.l[w];
+        a += sc * s.o[w][tid];
       }
     }
     const bool any = l > 0.f;
-    const float y = any ? a / l : 0.f;
-    const float lse = any ? (m + __log2f(l)) * kLn2 : kNegInf;
-    if (p.o_part) {
-      const int64_t prow = (int64_t)split * p.B * p.H + bh;  // [split, B, H, 1]
-      p.o_part[prow * D + tid] = y;
-      if (tid == 0) p.lse_part[prow] = lse;
-    } else {
-      ((uint16_t*)p.o)[(int64_t)bh * D + tid] = (uint16_t)(pack_bf16x2(y, 0.f) & 0xFFFFu);
-      if (tid == 0) p.lse[bh] = lse;
+    y = any ? a / l : 0.f;
+    lse = any ? (m + __log2f(l)) * kLn2 : kNegInf;
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void store_row(const FwdParams& p, int64_t bh, float y, float lse) {
+  const int tid = threadIdx.x;
+  ((uint16_t*)p.o)[bh * D + tid] = (uint16_t)(pack_bf16x2(y, 0.f) & 0xFFFFu);
+  if (tid == 0) p.lse[bh] = lse;
+}
+
+template <int D>
+__device__ __forceinline__ void store_part(const FwdParams& p, int64_t slot, float y, float lse) {
+  const int tid = threadIdx.x;
+  p.o_part[slot * D + tid] = y;
+  if (tid == 0) p.lse_part[slot] = lse;
+}
+
+// Fixed ranges.  Key range major: the (batch, head) pairs of one range take
+// consecutive ids, so the heads of every sequence are dealt evenly over the
+// 8 XCDs (round-robin by id) whichever ranges its length leaves empty.
+template <int D>
+__global__ __launch_bounds__(64 * kDecodeWaves) void fa_decode_kernel(FwdParams p) {
+  __shared__ DecodeLds<D> s;
+  const int BH = p.B * p.H;
+  const int split = (int)blockIdx.x / BH;
+  const int bh = (int)blockIdx.x - split * BH;
+  const int b = bh / p.H, hq = bh - b * p.H;
+  const int hk = hq / (p.H / p.Hkv);
+  const int L = __builtin_amdgcn_readfirstlane(seq_len(p, b));
+  // this workgroup's keys: [k0, k1) (the row sits at position L - 1, so
+  // under the causal mask it sees every key below L as well)
+  const int k0 = split * p.split_keys;
+  const int k1 = min(L, k0 + p.split_keys);
+  float y = 0.f, lse = kNegInf;
+  if (k0 < k1) decode_range<D>(p, s, bh, b, hk, L, k0, k1, y, lse);
+  if (threadIdx.x < D) {
+    if (p.o_part) store_part<D>(p, (int64_t)split * BH + bh, y, lse);  // [split, B, H, 1]
+    else store_row<D>(p, bh, y, lse);
+  }
+}
+
+// Units (of 64 keys) of one row of sequence b.
+__device__ __forceinline__ int64_t row_units(const FwdParams& p, int b) {
+  return (seq_len(p, b) + 63) >> 6;
+}
+
+// A wave-uniform 64-bit value held in vector registers, moved to scalar ones.
+__device__ __forceinline__ int64_t uniform64(const int64_t x) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)x >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+__device__ __forceinline__ int64_t wave_incl_scan(int64_t x, const int lane) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int64_t y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  return x;
+}
+
+// Balanced shares, one per workgroup: share w = blockIdx.x of P = gridDim.x.
+// Every wave scans the per-sequence unit counts itself (a few wave-wide
+// steps per 64 sequences); wave 0 of workgroup 0 also stores the exclusive
+// prefix cum[b] (units before sequence b) and the total T = cum[B] for the
+// merge.  Unit u of the share goes to wave (u - begin) mod 4, so the four
+// waves read adjacent 16 KB (d = 128) chunks of K and V, as with fixed
+// ranges.  Each wave walks every row the share touches, one after the other
+// with no barrier, and leaves for each a partial result at slot
+// 4 (w + bh) + wave of o_part / lse_part (LSE -inf when it had no unit of
+// the row).  (Shares are consecutive and rows are consecutive, so w1 < w2
+// implies bh1 <= bh2 for any rows bh1 of w1 and bh2 of w2: w + bh never
+// repeats across shares, and 4 (P + B*H) slots hold every partial.)  Every
+// row is completed by the merge.
+template <int D>
+__global__ __launch_bounds__(64 * kDecodeWaves) void fa_decode_balanced_kernel(FwdParams p,
+                                                                               int64_t* cum) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const bool store_cum = blockIdx.x == 0 && wave == 0;
+  const int B = p.B, H = p.H;
+  int64_t T = 0;
+  for (int b0 = 0; b0 < B; b0 += 64) {
+    const int b = b0 + lane;
+    const int64_t n = b < B ? row_units(p, b) * H : 0;
+    const int64_t incl = wave_incl_scan(n, lane);
+    if (store_cum && b < B) cum[b] = T + incl - n;
+    T += __shfl(incl, 63);
+  }
+  if (store_cum && lane == 0) cum[B] = T;
+  T = uniform64(T);
+  const int64_t P = gridDim.x, w = blockIdx.x;
+  const int64_t begin = w * T / P, end = (w + 1) * T / P;
+  if (begin >= end) return;
+
+  // the sequence holding unit `begin`, and its first unit
+  int b = 0;
+  int64_t seq_base = 0;
+  {
+    int64_t run = 0;
+    for (int b0 = 0; b0 < B; b0 += 64) {
+      const int bl = b0 + lane;
+      const int64_t n = bl < B ? row_units(p, bl) * H : 0;
+      const int64_t incl = wave_incl_scan(n, lane);
+      const bool hit = n > 0 && begin >= run + incl - n && begin < run + incl;
+      const uint64_t mask = __ballot(hit);
+      if (mask) {
+        const int l = __builtin_ctzll(mask);
+        b = b0 + l;
+        seq_base = __shfl(run + incl - n, l);
+        break;
+      }
+      run += __shfl(incl, 63);
+    }
+  }
+  b = __builtin_amdgcn_readfirstlane(b);
+  seq_base = uniform64(seq_base);
+  int L = __builtin_amdgcn_readfirstlane(seq_len(p, b));
+  int64_t nb = (L + 63) >> 6;  // > 0: the sequence holds unit `begin`
+  const int group = H / p.Hkv;
+  for (int64_t u = begin; u < end;) {
+    const int h = (int)((u - seq_base) / nb);
+    const int64_t row_start = seq_base + h * nb, row_end = row_start + nb;
+    const int64_t seg_end = end < row_end ? end : row_end;
+    // this wave's first unit of the segment: the next u' >= u with
+    // (u' - begin) mod 4 == wave
+    const int64_t first = u + ((wave - (u - begin)) & (kDecodeWaves - 1));
+    const int k0 = (int)(first - row_start) * 64;
+    const int k1 = min(L, (int)(seg_end - row_start) * 64);
+    const int64_t bh = (int64_t)b * H + h;
+    float o[8], m, l;
+    decode_wave<D>(p, (int)bh, b, h / group, L, k0, k1, 64 * kDecodeWaves, o, m, l);
+    const int64_t slot = kDecodeWaves * (w + bh) + wave;
+    if (l > 0.f) {
+      const float inv = 1.f / l;
+      if (lane < D / 8) {
+        float* dst = p.o_part + slot * D + 8 * lane;
+        *(f32x4*)dst = f32x4{o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv};
+        *(f32x4*)(dst + 4) = f32x4{o[4] * inv, o[5] * inv, o[6] * inv, o[7] * inv};
+      }
+      if (lane == 0) p.lse_part[slot] = (m + __log2f(l)) * kLn2;
+    } else if (lane == 0) {
+      p.lse_part[slot] = kNegInf;  // no unit of this row
+    }
+    u = seg_end;
+    if (u == seq_base + H * nb && u < end) {
+      // the next sequence with a visible key (one exists: units remain)
+      seq_base = u;
+      do {
+        ++b;
+        L = __builtin_amdgcn_readfirstlane(seq_len(p, b));
+      } while (L == 0);
+      nb = (L + 63) >> 6;
     }
   }
 }
@@ -185,6 +364,15 @@ hipError_t launch_decode_bf16(const FwdParams& p, int d, hipStream_t stream) {
   const dim3 block(64 * kDecodeWaves);
   if (d == 128) hipLaunchKernelGGL((fa_decode_kernel<128>), grid, block, 0, stream, p);
   else hipLaunchKernelGGL((fa_decode_kernel<64>), grid, block, 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_balanced_bf16(const FwdParams& p, int d, int shares, int64_t* cum,
+                                       hipStream_t stream) {
+  const dim3 grid((unsigned)shares);
+  const dim3 block(64 * kDecodeWaves);
+  if (d == 128) hipLaunchKernelGGL((fa_decode_balanced_kernel<128>), grid, block, 0, stream, p, cum);
+  else hipLaunchKernelGGL((fa_decode_balanced_kernel<64>), grid, block, 0, stream, p, cum);
   return hipGetLastError();
 }
 

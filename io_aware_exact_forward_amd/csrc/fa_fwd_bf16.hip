@@ -105,11 +105,13 @@ void fa_fwd_bf16_kernel(FwdParams p) {
 
   // ---- tile assignment ----------------------------------------------------
   // Workgroup = (key range, (batch, head), query tile); consecutive ids
-  // take consecutive key ranges, then cycle over a chunk of at most 32
-  // (batch, head) pairs, then over the query tiles, then over the chunks.
-  // Within a chunk all the query tiles of a head run close together, so its
-  // K/V rows are reused from L2; with 32 pairs per chunk every head's tiles
-  // land on one XCD (workgroups are dealt round-robin to the 8 XCDs).
+  // cycle over a chunk of at most 32 (batch, head) pairs, then over the
+  // query tiles, then over the chunks, then over the key ranges.  Within a
+  // chunk all the query tiles of a head run close together, so its K/V rows
+  // are reused from L2; with 32 pairs per chunk every head's tiles, of every
+  // range, land on one XCD (workgroups are dealt round-robin to the 8 XCDs),
+  // and the heads of a sequence are spread evenly over the XCDs, so ranges
+  // left empty by a short sequence do not idle some XCDs.
   const int BH = p.B * p.H;
   // Persistent form (dense layout, one key range): workgroup w takes the
   // units w, w + G, w + 2G, ... (G workgroups, p.persist units each); unit
@@ -128,9 +130,9 @@ void fa_fwd_bf16_kernel(FwdParams p) {
   if constexpr (PERSIST) {
     item_of(0, bh, qt);
   } else {
-    int x = blockIdx.x;
-    split = x % p.splits;
-    x /= p.splits;
+    const int per_split = BH * p.n_qtiles;
+    split = (int)blockIdx.x / per_split;
+    const int x = (int)blockIdx.x - split * per_split;
     constexpr int kChunk = 32;
     const int chunk_wgs = kChunk * p.n_qtiles;
     const int chunk = x / chunk_wgs;

@@ -45,6 +45,13 @@ struct MergeParams {
   float* lse;              // [rows]
   int64_t rows;            // B * H * N
   int splits;
+  // balanced decode shares (cum non-null): row bh's partials sit at slots
+  // 4 (w + bh) + wave ([4 (P + B*H), d] and [4 (P + B*H)]) for the shares w
+  // that touch it
+  const int64_t* cum;      // [B + 1] units (64 keys of one row) before sequence b; cum[B] = total
+  const int32_t* key_len;  // device [B] or nullptr
+  int B, H, Nk;
+  int workgroups;          // P: shares (workgroups) of the decode kernel
 };
 
 // Parameters of the materialised (three-pass) path's softmax pass.
@@ -108,6 +115,11 @@ hipError_t launch_fwd_bf16(const FwdParams& p, int d, bool causal, hipStream_t s
 hipError_t launch_fwd_f32(const FwdParams& p, int d, bool causal, hipStream_t stream);
 // One query row per (batch, head) (Nq = 1, rows at the end of the keys), bf16.
 hipError_t launch_decode_bf16(const FwdParams& p, int d, hipStream_t stream);
+// The same with the visible keys of all rows cut into `shares` equal shares,
+// one per workgroup; writes cum[0..B] (see MergeParams) and partials for
+// every row, which the merge completes.
+hipError_t launch_decode_balanced_bf16(const FwdParams& p, int d, int shares, int64_t* cum,
+                                       hipStream_t stream);
 hipError_t launch_naive_softmax(const NaiveSoftmaxParams& p, bool bf16, hipStream_t stream);
 hipError_t launch_merge(const MergeParams& p, int d, bool bf16, hipStream_t stream);
 hipError_t launch_bwd_bf16(const BwdParams& p, int d, bool causal, hipStream_t stream);

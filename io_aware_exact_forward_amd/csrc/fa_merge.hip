@@ -14,9 +14,14 @@
 // average block outputs?").  A row with every L_s = -inf saw no key at all:
 // o = 0, L = -inf.
 //
-// One thread per four consecutive output elements of a row: the partial
-// outputs of a row are read once, as 16-byte loads, and the row's L_s by
-// every thread of the row (they are few and cached).
+// One wave per row.  The lanes read the row's L_s side by side (64 at a
+// time) and reduce the maximum and the weight sum across the wave; then the
+// wave streams the partial outputs, each lane D/64 dimensions of each, in a
+// loop without branches (a partial whose weight is 0 is read and discarded),
+// so that the loads of several partials are in flight together.  The
+// partials come in two layouts: fixed key ranges (slot s * rows + row for
+// range s) and the balanced shares of a decode step (slots 4 (w + row) +
+// wave for share w).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -26,46 +31,134 @@
 namespace fa {
 namespace {
 
-template <int D, bool BF16>
-__global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
-  constexpr int TPR = D / 4;  // threads per row
-  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t row = gid / TPR;
-  const int c4 = (int)(gid % TPR);
+constexpr int kMergeWaves = 4;  // rows per workgroup
+
+// The partials of one row: count K, slot of the k-th, and whether it exists
+// (a balanced share left empty by the division of the units wrote nothing).
+struct RowParts {
+  int64_t first, count;
+  int64_t stride;          // fixed ranges: slot = first + k * stride
+  int64_t w1, T, P;        // balanced: slot = first + k, share w1 + k / 4
+  bool balanced;
+  __device__ __forceinline__ int64_t slot(int64_t k) const {
+    return balanced ? first + k : first + k * stride;
+  }
+  __device__ __forceinline__ bool exists(int64_t k) const {
+    if (!balanced) return true;
+    const int64_t w = w1 + (k >> 2);
+    return w * T / P < (w + 1) * T / P;
+  }
+};
+
+template <int D, bool BF16, bool BALANCED>
+__global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(MergeParams p) {
+  constexpr int DPL = D / 64;  // dimensions per lane
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * kMergeWaves + (threadIdx.x >> 6);
   if (row >= p.rows) return;
 
-  float m = kNegInf;
-  for (int s = 0; s < p.splits; ++s) m = fmaxf(m, p.lse_part[(int64_t)s * p.rows + row]);
+  RowParts rp{};
+  bool none = false;  // the row saw no key at all
+  if constexpr (BALANCED) {
+    // Row bh (sequence b, head h; one query row) holds units [start, start
+    // + nb) of the T units laid end to end, start = cum[b] + h nb, nb =
+    // ceil(L_b / 64).  Share w of P covers units [w T / P, (w + 1) T / P), so
+    // unit u lies in share ((u + 1) P - 1) / T, the last w whose first unit
+    // is at most u.  Every non-empty share from the first unit's to the last
+    // unit's left four partials (one per wave) at slots 4 (w + bh) + 0..3,
+    // LSE -inf for a wave with no unit of the row.  A sequence with no
+    // visible key has no units.
+    const int b = (int)(row / p.H), h = (int)(row - (int64_t)b * p.H);
+    int L = p.Nk;
+    if (p.key_len) {
+      const int kl = p.key_len[b];
+      L = kl < 0 ? 0 : (kl > p.Nk ? p.Nk : kl);
+    }
+    const int64_t nb = (L + 63) >> 6;
+    none = nb == 0;
+    if (!none) {
+      const int64_t T = p.cum[p.B], P = p.workgroups;
+      const int64_t start = p.cum[b] + h * nb, last = start + nb - 1;
+      const int64_t w1 = ((start + 1) * P - 1) / T, w2 = ((last + 1) * P - 1) / T;
+      rp = RowParts{4 * (w1 + row), 4 * (w2 - w1 + 1), 1, w1, T, P, true};
+    }
+  } else {
+    rp = RowParts{row, p.splits, p.rows, 0, 1, 1, false};
+  }
 
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  // ---- maximum and weight sum over the partials' LSE, lane-parallel
+  float m = kNegInf;
+  if (!none) {
+    for (int64_t k0 = 0; k0 < rp.count; k0 += 64) {
+      const int64_t k = k0 + lane;
+      const float ls = k < rp.count && rp.exists(k) ? p.lse_part[rp.slot(k)] : kNegInf;
+      m = fmaxf(m, ls);
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  }
+  float acc[DPL];
+#pragma unroll
+  for (int e = 0; e < DPL; ++e) acc[e] = 0.f;
   float wsum = 0.f;
   if (m != kNegInf) {
-    for (int s = 0; s < p.splits; ++s) {
-      const float ls = p.lse_part[(int64_t)s * p.rows + row];
-      if (ls == kNegInf) continue;  // the range saw no key of this row
-      const float w = __expf(ls - m);
-      const f32x4 os = *(const f32x4*)(p.o_part + ((int64_t)s * p.rows + row) * D + 4 * c4);
-      wsum += w;
-      acc += w * os;
+    for (int64_t k0 = 0; k0 < rp.count; k0 += 64) {
+      const int64_t k = k0 + lane;
+      const float ls = k < rp.count && rp.exists(k) ? p.lse_part[rp.slot(k)] : kNegInf;
+      const float wk = ls == kNegInf ? 0.f : __expf(ls - m);  // this lane's partial's weight
+      float part = wk;
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) part += __shfl_xor(part, off);
+      wsum += part;
+      // ---- the outputs of these (up to) 64 partials, weighted
+      const int n = (int)min<int64_t>(64, rp.count - k0);
+      int j = 0;
+      for (; j + 4 <= n; j += 4) {
+        float wj[4];
+        float os[4][DPL];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          wj[i] = __shfl(wk, j + i);
+          const float* src = p.o_part + rp.slot(k0 + j + i) * D + DPL * lane;
+          if constexpr (DPL == 2) {
+            const f32x2 t = *(const f32x2*)src;
+            os[i][0] = t[0];
+            os[i][1] = t[1];
+          } else {
+            os[i][0] = *src;
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int e = 0; e < DPL; ++e) acc[e] += wj[i] > 0.f ? wj[i] * os[i][e] : 0.f;
+      }
+      for (; j < n; ++j) {
+        const float wv = __shfl(wk, j);
+        const float* src = p.o_part + rp.slot(k0 + j) * D + DPL * lane;
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) acc[e] += wv > 0.f ? wv * src[e] : 0.f;
+      }
     }
   }
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-  const f32x4 y = acc * inv;
   if constexpr (BF16) {
-    u32x2 w = {pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
-    *(u32x2*)((uint16_t*)p.o + row * D + 4 * c4) = w;
+    uint16_t* orow = (uint16_t*)p.o + row * D + DPL * lane;
+    if constexpr (DPL == 2) *(uint32_t*)orow = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+    else *orow = (uint16_t)(pack_bf16x2(acc[0] * inv, 0.f) & 0xFFFFu);
   } else {
-    *(f32x4*)((float*)p.o + row * D + 4 * c4) = y;
+    float* orow = (float*)p.o + row * D + DPL * lane;
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) orow[e] = acc[e] * inv;
   }
-  if (c4 == 0) p.lse[row] = wsum > 0.f ? m + __logf(wsum) : kNegInf;
+  if (lane == 0) p.lse[row] = wsum > 0.f ? m + __logf(wsum) : kNegInf;
 }
 
-template <int D, bool BF16>
+template <int D, bool BF16, bool BALANCED>
 hipError_t launch(const MergeParams& p, hipStream_t stream) {
-  constexpr int TPR = D / 4;
-  const int64_t threads = p.rows * TPR;
-  const int64_t blocks = (threads + 255) / 256;
-  hipLaunchKernelGGL((merge_kernel<D, BF16>), dim3((unsigned)blocks), dim3(256), 0, stream, p);
+  const int64_t blocks = (p.rows + kMergeWaves - 1) / kMergeWaves;
+  hipLaunchKernelGGL((merge_kernel<D, BF16, BALANCED>), dim3((unsigned)blocks),
+                     dim3(64 * kMergeWaves), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -73,8 +166,11 @@ hipError_t launch(const MergeParams& p, hipStream_t stream) {
 
 hipError_t launch_merge(const MergeParams& p, int d, bool bf16, hipStream_t stream) {
   if (p.rows == 0) return hipSuccess;
-  if (d == 128) return bf16 ? launch<128, true>(p, stream) : launch<128, false>(p, stream);
-  return bf16 ? launch<64, true>(p, stream) : launch<64, false>(p, stream);
+  if (p.cum) {  // balanced decode shares (bf16)
+    return d == 128 ? launch<128, true, true>(p, stream) : launch<64, true, true>(p, stream);
+  }
+  if (d == 128) return bf16 ? launch<128, true, false>(p, stream) : launch<128, false, false>(p, stream);
+  return bf16 ? launch<64, true, false>(p, stream) : launch<64, false, false>(p, stream);
 }
 
 }  // namespace fa

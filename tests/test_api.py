@@ -158,6 +158,19 @@ def test_split_workspace_size():
     assert fa.fa_split_workspace_bytes(1, 2, 64, 1024, 64, 100) == 8 * 128 * 64 * 4 + 8 * 128 * 4
     # 8 blocks in 3 ranges of 3, 3, 2 blocks; d = 128; one decode row per head
     assert fa.fa_split_workspace_bytes(2, 3, 1, 1000, 128, 3) == 3 * 6 * 128 * 4 + 256
+    # a decode step (one query row, as many key/value heads as query heads)
+    # with the automatic count: P = min(512, B*H*ceil(Nk/64)) balanced shares,
+    # partials in 4 (P + B*H) slots (one per wave of a share and row), then
+    # the unit prefix cum [B + 1] (int64)
+    r256 = lambda x: (x + 255) // 256 * 256
+    for B, H, Nk, d in ((2, 3, 1000, 128), (8, 32, 16384, 128), (130, 2, 700, 64)):
+        P = min(512, B * H * -(-Nk // 64))
+        slots = 4 * (P + B * H)
+        bal = r256(slots * d * 4) + r256(slots * 4) + r256((B + 1) * 8)
+        # (the size covers every Hkv dividing H, so grouped heads may need more)
+        assert fa.fa_split_workspace_bytes(B, H, 1, Nk, d, 0) >= bal, (B, H, Nk, d)
+        if (B, H) == (2, 3):  # Hkv = 1 needs 8 ranges x 6 rows here: less
+            assert fa.fa_split_workspace_bytes(B, H, 1, Nk, d, 0) == bal
     # many query tiles: the automatic choice stays at one range
     assert fa.fa_split_workspace_bytes(1, 32, 8192, 8192, 128, 0) == 0
     # no keys, empty problems and invalid arguments: 0

@@ -180,8 +180,8 @@ GQA_CASES = [
     (2, 8, 2, 1, 2000, 128, [2000, 333], 9801),     # grouped decode (4 heads per group)
     (1, 6, 1, 130, 700, 64, None, 9802),            # multi-query, chunked prefill
     (2, 4, 2, 300, 300, 128, None, 9803),           # square
-    # decode: one workgroup serves the 2, 4 or 8 query heads of a key/value
-    # head; 3 and 16 heads per group take one workgroup per query head
+    # decode: the G query heads of a key/value head run as G rows of one
+    # query tile (G = 2, 3, 4, 8 and 16 here)
     (3, 4, 2, 1, 1500, 64, [1500, 0, 1], 9804),
     (2, 16, 2, 1, 3001, 128, [3001, 2049], 9805),
     (2, 16, 2, 1, 999, 64, [17, 999], 9806),
