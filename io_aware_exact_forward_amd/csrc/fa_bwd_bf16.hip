@@ -153,8 +153,16 @@ __device__ __forceinline__ BwdLayout bwd_layout(const BwdParams& p, int b, int h
 // ---------------------------------------------------------------------------
 // dQ (and D): one workgroup per 128 query rows of one (batch, head)
 // ---------------------------------------------------------------------------
-// Workgroups per CU: two at d = 64; at d = 128 the accumulators of one
-// workgroup take the registers of two.
+// Two workgroups per CU (two waves per SIMD, so one wave's softmax work
+// runs under the other's products).  At d = 128 the kernel takes 32-key
+// tiles: a wave's dQ accumulators, Q and dO fragments, scores and staging
+// registers then fit the 256 registers a lane has at two waves per SIMD.
+// (With 64-key tiles it needed 364 and ran one workgroup per CU: the packed
+// 16-sequence backward took 15.95 ms instead of 13.95.)  The products are the
+// same 16-key steps in the same order either way.
+constexpr int kDqOccupancy = 2;
+// Workgroups per CU of the dK/dV kernel: two at d = 64; at d = 128 the
+// accumulators of one workgroup take the registers of two.
 template <int D>
 constexpr int kBwdOccupancy = D == 64 ? 2 : 1;
 
@@ -199,10 +207,10 @@ __device__ __forceinline__ uint32_t keep_nibble(const BwdParams& p, uint32_t key
 }
 
 template <int D, bool CAUSAL, int VAR>
-__global__ __launch_bounds__(256, kBwdOccupancy<D>) void fa_bwd_dq_kernel(BwdParams p) {
+__global__ __launch_bounds__(256, kDqOccupancy) void fa_bwd_dq_kernel(BwdParams p) {
   constexpr bool DROP = VAR == 1, BIAS = VAR == 2;
   using C = BwdCfg<D>;
-  constexpr int BQ = 128, BK = 64, NB = BK / 32;
+  constexpr int BQ = 128, BK = D == 128 ? 32 : 64, NB = BK / 32;
   constexpr int TILE = BK * C::ROW_BYTES;
   constexpr int LPT = BK * C::CPR / 256;  // 16-byte chunks per thread per tensor
   __shared__ __attribute__((aligned(16))) uint8_t lds[2][2 * TILE];
@@ -473,10 +481,11 @@ __global__ __launch_bounds__(256, (kDkdvOccupancy<D, VAR>)) void fa_bwd_dkdv_ker
   // Rows whose position is below the key length (the others are padding
   // or see no key), and the query tiles that see any key of this
   // workgroup: rows at positions >= k0 if causal.  Tile t of the loop is
-  // query tile qend - 1 - t % nt of query head hk*G + t / nt: every key tile
-  // of a sequence shares its last query tile, so the workgroups of one
-  // (batch, head) pair that run together start on the same rows and stream
-  // them in step (from L2) until each reaches its own first tile.
+  // query tile qend - 1 - t / G of query head hk*G + t % G (the G heads of a
+  // tile, then the next tile down): every key tile of a sequence shares its
+  // last query tile, so the workgroups of one (batch, key/value head) pair
+  // that run together start on the same rows and stream them in step (from
+  // L2), through every head, until each reaches its own first tile.
   const int qlim = max(0, min(lay.Nq, kv_lim - off));
   const int qfirst = CAUSAL ? max(0, k0 - off) / BQ : 0;
   const int qend = k0 < kv_lim ? (qlim + BQ - 1) / BQ : 0;
@@ -620,9 +629,9 @@ __global__ __launch_bounds__(256, (kDkdvOccupancy<D, VAR>)) void fa_bwd_dkdv_ker
     for (int t = 0; t < total; ++t) {
       const bool more = t + 1 < total;
       const int q0 = qi * BQ;
-      if (--qi < qfirst) {
-        qi = qend - 1;
-        ++g;
+      if (++g == G) {
+        g = 0;
+        --qi;
       }
       if (more) load_regs(g, qi * BQ);
       compute(t & 1, q0);
