@@ -8,9 +8,9 @@
 //  * balanced: the visible keys of all rows, in 64-key units, are cut into
 //    equal shares, one per workgroup, whatever the per-sequence lengths.
 //    Rows are laid end to end (sequence by sequence, head by head, key
-//    order within a row) and workgroup w takes units [w T / P, (w + 1) T /
-//    P) of the T units (P workgroups).  The per-sequence lengths are read on
-//    the device, so the host needs none of them.
+//    order within a row) and workgroup w takes units [w S, (w + 1) S) of
+//    the T units, S = ceil(T / P) for P workgroups.  The per-sequence
+//    lengths are read on the device, so the host needs none of them.
 //
 // With a single query row there is no matrix product to speak of: the work
 // is streaming K and V once from HBM.  Each wave takes 64 keys at a time:
@@ -261,11 +261,11 @@ __device__ __forceinline__ int64_t wave_incl_scan(int64_t x, const int lane) {
   return x;
 }
 
-// Balanced shares, one per workgroup: share w = blockIdx.x of P = gridDim.x.
-// Every wave scans the per-sequence unit counts itself (a few wave-wide
-// steps per 64 sequences); wave 0 of workgroup 0 also stores the exclusive
-// prefix cum[b] (units before sequence b) and the total T = cum[B] for the
-// merge.  Unit u of the share goes to wave (u - begin) mod 4, so the four
+// Balanced shares, one per workgroup: share w = blockIdx.x of P = gridDim.x
+// takes units [w S, min(T, (w + 1) S)), S = ceil(T / P).  Every wave scans
+// the per-sequence unit counts itself (a few wave-wide steps per 64
+// sequences); wave 0 of workgroup 0 also stores the exclusive prefix cum[b]
+// (units before sequence b) and the total T = cum[B] for the merge.  Unit u of the share goes to wave (u - begin) mod 4, so the four
 // waves read adjacent 16 KB (d = 128) chunks of K and V, as with fixed
 // ranges.  Each wave walks every row the share touches, one after the other
 // with no barrier, and leaves for each a partial result at slot
@@ -291,8 +291,10 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void fa_decode_balanced_kernel(F
   }
   if (store_cum && lane == 0) cum[B] = T;
   T = uniform64(T);
+  // S = ceil(T / P) units per share: only the last shares can be empty
   const int64_t P = gridDim.x, w = blockIdx.x;
-  const int64_t begin = w * T / P, end = (w + 1) * T / P;
+  const int64_t S = (T + P - 1) / P;
+  const int64_t begin = w * S, end = min(T, begin + S);
   if (begin >= end) return;
 
   // the sequence holding unit `begin`, and its first unit

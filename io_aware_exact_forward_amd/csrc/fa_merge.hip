@@ -25,6 +25,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "fa_device.hpp"
 #include "fa_internal.hpp"
 
@@ -33,21 +35,11 @@ namespace {
 
 constexpr int kMergeWaves = 4;  // rows per workgroup
 
-// The partials of one row: count K, slot of the k-th, and whether it exists
-// (a balanced share left empty by the division of the units wrote nothing).
+// The partials of one row: count K and the slot of the k-th (fixed ranges:
+// first + k * stride; balanced shares: first + k).
 struct RowParts {
-  int64_t first, count;
-  int64_t stride;          // fixed ranges: slot = first + k * stride
-  int64_t w1, T, P;        // balanced: slot = first + k, share w1 + k / 4
-  bool balanced;
-  __device__ __forceinline__ int64_t slot(int64_t k) const {
-    return balanced ? first + k : first + k * stride;
-  }
-  __device__ __forceinline__ bool exists(int64_t k) const {
-    if (!balanced) return true;
-    const int64_t w = w1 + (k >> 2);
-    return w * T / P < (w + 1) * T / P;
-  }
+  int64_t first, count, stride;
+  __device__ __forceinline__ int64_t slot(int64_t k) const { return first + k * stride; }
 };
 
 template <int D, bool BF16, bool BALANCED>
@@ -62,49 +54,84 @@ __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(MergeParams p) 
   if constexpr (BALANCED) {
     // Row bh (sequence b, head h; one query row) holds units [start, start
     // + nb) of the T units laid end to end, start = cum[b] + h nb, nb =
-    // ceil(L_b / 64).  Share w of P covers units [w T / P, (w + 1) T / P), so
-    // unit u lies in share ((u + 1) P - 1) / T, the last w whose first unit
-    // is at most u.  Every non-empty share from the first unit's to the last
-    // unit's left four partials (one per wave) at slots 4 (w + bh) + 0..3,
-    // LSE -inf for a wave with no unit of the row.  A sequence with no
-    // visible key has no units.
+    // ceil(L_b / 64).  Share w covers units [w S, (w + 1) S), S = ceil(T /
+    // P), so unit u lies in share u / S, and every share from the first
+    // unit's to the last unit's left four partials (one per wave) at slots
+    // 4 (w + bh) + 0..3, LSE -inf for a wave with no unit of the row.  A
+    // sequence with no visible key has no units.  (The three loads are
+    // independent: they are issued together.)
     const int b = (int)(row / p.H), h = (int)(row - (int64_t)b * p.H);
-    int L = p.Nk;
-    if (p.key_len) {
-      const int kl = p.key_len[b];
-      L = kl < 0 ? 0 : (kl > p.Nk ? p.Nk : kl);
-    }
+    const int kl = p.key_len ? p.key_len[b] : p.Nk;
+    const int64_t cb = p.cum[b], T = p.cum[p.B];
+    const int L = kl < 0 ? 0 : (kl > p.Nk ? p.Nk : kl);
     const int64_t nb = (L + 63) >> 6;
     none = nb == 0;
     if (!none) {
-      const int64_t T = p.cum[p.B], P = p.workgroups;
-      const int64_t start = p.cum[b] + h * nb, last = start + nb - 1;
-      const int64_t w1 = ((start + 1) * P - 1) / T, w2 = ((last + 1) * P - 1) / T;
-      rp = RowParts{4 * (w1 + row), 4 * (w2 - w1 + 1), 1, w1, T, P, true};
+      const int64_t S = (T + p.workgroups - 1) / p.workgroups;
+      const int64_t start = cb + h * nb, last = start + nb - 1;
+      const int64_t w1 = start / S, w2 = last / S;
+      rp = RowParts{4 * (w1 + row), 4 * (w2 - w1 + 1), 1};
     }
   } else {
-    rp = RowParts{row, p.splits, p.rows, 0, 1, 1, false};
+    rp = RowParts{row, p.splits, p.rows};
   }
 
-  // ---- maximum and weight sum over the partials' LSE, lane-parallel
-  float m = kNegInf;
-  if (!none) {
-    for (int64_t k0 = 0; k0 < rp.count; k0 += 64) {
-      const int64_t k = k0 + lane;
-      const float ls = k < rp.count && rp.exists(k) ? p.lse_part[rp.slot(k)] : kNegInf;
-      m = fmaxf(m, ls);
-    }
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-  }
   float acc[DPL];
 #pragma unroll
   for (int e = 0; e < DPL; ++e) acc[e] = 0.f;
   float wsum = 0.f;
-  if (m != kNegInf) {
+  float m = kNegInf;
+  // ---- few partials: their outputs are loaded together with their LSE
+  // (the addresses need no LSE), so the row costs one round trip less
+  auto few = [&](auto f_tag) __attribute__((always_inline)) {
+    constexpr int F = decltype(f_tag)::value;
+    float os[F][DPL];
+#pragma unroll
+    for (int k = 0; k < F; ++k) {
+      // past the count: partial 0 again (in bounds), weighted 0 below
+      const float* src = p.o_part + rp.slot(k < rp.count ? k : 0) * D + DPL * lane;
+      if constexpr (DPL == 2) {
+        const f32x2 t = *(const f32x2*)src;
+        os[k][0] = t[0];
+        os[k][1] = t[1];
+      } else {
+        os[k][0] = *src;
+      }
+    }
+    const float ls = lane < rp.count ? p.lse_part[rp.slot(lane)] : kNegInf;
+    m = ls;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+    if (m == kNegInf) return;
+    const float wk = ls == kNegInf ? 0.f : __expf(ls - m);
+    wsum = wk;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) wsum += __shfl_xor(wsum, off);
+#pragma unroll
+    for (int k = 0; k < F; ++k) {
+      const float wv =
+          __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wk), k));
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) acc[e] += wv > 0.f ? wv * os[k][e] : 0.f;
+    }
+  };
+  if (none) {
+  } else if (rp.count <= 8) {
+    few(std::integral_constant<int, 8>{});
+  } else if (rp.count <= 32) {
+    few(std::integral_constant<int, 32>{});
+  } else if (!none) {
+    // ---- maximum and weight sum over the partials' LSE, lane-parallel
     for (int64_t k0 = 0; k0 < rp.count; k0 += 64) {
       const int64_t k = k0 + lane;
-      const float ls = k < rp.count && rp.exists(k) ? p.lse_part[rp.slot(k)] : kNegInf;
+      const float ls = k < rp.count ? p.lse_part[rp.slot(k)] : kNegInf;
+      m = fmaxf(m, ls);
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+    for (int64_t k0 = 0; m != kNegInf && k0 < rp.count; k0 += 64) {
+      const int64_t k = k0 + lane;
+      const float ls = k < rp.count ? p.lse_part[rp.slot(k)] : kNegInf;
       const float wk = ls == kNegInf ? 0.f : __expf(ls - m);  // this lane's partial's weight
       float part = wk;
 #pragma unroll
@@ -118,7 +145,7 @@ __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(MergeParams p) 
         float os[4][DPL];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          wj[i] = __shfl(wk, j + i);
+          wj[i] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wk), j + i));
           const float* src = p.o_part + rp.slot(k0 + j + i) * D + DPL * lane;
           if constexpr (DPL == 2) {
             const f32x2 t = *(const f32x2*)src;
@@ -134,7 +161,7 @@ __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(MergeParams p) 
           for (int e = 0; e < DPL; ++e) acc[e] += wj[i] > 0.f ? wj[i] * os[i][e] : 0.f;
       }
       for (; j < n; ++j) {
-        const float wv = __shfl(wk, j);
+        const float wv = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wk), j));
         const float* src = p.o_part + rp.slot(k0 + j) * D + DPL * lane;
 #pragma unroll
         for (int e = 0; e < DPL; ++e) acc[e] += wv > 0.f ? wv * src[e] : 0.f;

@@ -76,6 +76,7 @@ CASES = [
     (2, 2, 200, 1500, 128, [1500, 333], 1.0, 9105),   # chunked prefill
     (2, 2, 300, 256, 64, [100, 256], 1.0, 9106),      # more rows than cached keys
     (2, 2, 130, 2000, 128, None, 4.0, 9107),          # peaky rows
+    (1, 2, 5, 9000, 64, None, 1.0, 9110),             # 64 asked: 36 ranges (more than 32 to merge)
 ]
 
 
