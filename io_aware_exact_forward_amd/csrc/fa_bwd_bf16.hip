@@ -416,19 +416,40 @@ __global__ __launch_bounds__(256, kDqOccupancy) void fa_bwd_dq_kernel(BwdParams 
 // well: one workgroup per CU (twice the registers) at d = 64 too.
 template <int D, int VAR>
 constexpr int kDkdvOccupancy = VAR != 0 ? 1 : kBwdOccupancy<D>;
+// Waves per dK/dV workgroup.  Eight (two per SIMD, a wave pair splitting the
+// rows) wherever the four-wave form runs one wave per SIMD: at d = 128 (the
+// packed 16-sequence backward 14.0 -> 10.45 ms, a dense causal one 20-25 %
+// faster; with dropout or a mask 3-48 % faster although a few registers
+// spill) and at d = 64 with dropout or a mask (18-31 % faster).  Plain d = 64
+// keeps four waves at two workgroups per CU (8-10 % faster than eight).
+template <int D, int VAR>
+constexpr int kDkdvWaves = (D == 128 || VAR != 0) ? 8 : 4;
 
-template <int D, bool CAUSAL, int VAR>
-__global__ __launch_bounds__(256, (kDkdvOccupancy<D, VAR>)) void fa_bwd_dkdv_kernel(BwdParams p) {
+// WAVES = 4: wave w owns keys 32w .. 32w+31 and every row of a query tile.
+// WAVES = 8: waves w and w + 4 own the same 32 keys and split each query
+// tile's rows between them (two waves per SIMD, each with half the score
+// registers); their dK and dV partial sums are added through LDS at the end.
+template <int D, bool CAUSAL, int VAR, int WAVES>
+__global__ __launch_bounds__(64 * WAVES, (WAVES == 8 ? 1 : kDkdvOccupancy<D, VAR>))
+void fa_bwd_dkdv_kernel(BwdParams p) {
   constexpr bool DROP = VAR == 1, BIAS = VAR == 2;
   using C = BwdCfg<D>;
-  // 64-row query tiles (at d = 128 the workgroup then holds 490 of the 512
-  // registers a lane has at one workgroup per CU)
+  // 64-row query tiles (at d = 128 with four waves the workgroup then holds
+  // 490 of the 512 registers a lane has at one workgroup per CU)
   constexpr int BKW = 128, BQ = 64, NQB = BQ / 32;
+  constexpr int NT = 64 * WAVES;     // threads
+  constexpr int RS = WAVES / 4;      // waves sharing a key group (row split)
+  constexpr int WQB = NQB / RS;      // 32-row blocks of a query tile per wave
+  static_assert(WAVES == 4 || WAVES == 8, "4 or 8 waves");
   constexpr int TILE = BQ * C::ROW_BYTES;
-  constexpr int LPT = BQ * C::CPR / 256;
+  constexpr int LPT = BQ * C::CPR / NT;
   // [stage][Q tile | dO tile | LSE2 (BQ floats) | D (BQ floats)]
   constexpr int STAGE = 2 * TILE + 2 * BQ * 4;
   __shared__ __attribute__((aligned(16))) uint8_t lds[2][STAGE];
+  // Eight waves: the workgroup's K and V rows stay in LDS ([K | V], chunks
+  // permuted as a plainly read tile) instead of in each wave's registers.
+  constexpr int KVT = BKW * C::ROW_BYTES;
+  __shared__ __attribute__((aligned(16))) uint8_t kv_lds[RS == 2 ? 2 * KVT : 16];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -444,7 +465,9 @@ __global__ __launch_bounds__(256, (kDkdvOccupancy<D, VAR>)) void fa_bwd_dkdv_ker
   const BwdLayout lay = bwd_layout<D>(p, b, hk * G, hk);
   const int kv_lim = lay.kv_lim, off = lay.off;
   const int k0 = kt_idx * BKW;
-  const int kw0 = k0 + 32 * wave;
+  // key group; row half (eight waves; 0 with four)
+  const int kgrp = RS == 2 ? (wave & 3) : wave, rh = RS == 2 ? (wave >> 2) : 0;
+  const int kw0 = k0 + 32 * kgrp;
   const int key = kw0 + l32;
   const bool key_ok = key < kv_lim;
   // additive mask column of this lane's key (clamped into the slice; values
@@ -458,18 +481,43 @@ __global__ __launch_bounds__(256, (kDkdvOccupancy<D, VAR>)) void fa_bwd_dkdv_ker
   const uint16_t* vg = (const uint16_t*)p.v + lay.kvbase;
   const int q_ld = lay.q_ld, kv_ld = lay.kv_ld;
 
-  bf16x8 kf[C::KD], vf[C::KD];
+  bf16x8 kf[RS == 2 ? 1 : C::KD], vf[RS == 2 ? 1 : C::KD];
+  if constexpr (RS == 2) {
+    // chunk c of the 128-key tile: row c / CPR, logical chunk c % CPR; keys
+    // at or past the length read as zeros (buffer range); the first barrier
+    // of the loop orders these stores before the reads
+    const uint32_t nb = (uint32_t)max(0, kv_lim - k0) * kv_ld * 2;
+    const int64_t at = lay.kvbase + (int64_t)k0 * kv_ld;
 #pragma unroll
-  for (int kk = 0; kk < C::KD; ++kk) {
-    u32x4 a = {0u, 0u, 0u, 0u}, v = {0u, 0u, 0u, 0u};
-    if (key_ok) {
-      const uint32_t ko = (uint32_t)key * kv_ld + 16 * kk + 8 * h;
-      a = *(const u32x4*)(kg + ko);
-      v = *(const u32x4*)(vg + ko);
+    for (int i = 0; i < BKW * C::CPR / NT; ++i) {
+      const int c = tid + NT * i, r = c / C::CPR, lc = c % C::CPR;
+      const uint32_t off = ((uint32_t)r * kv_ld + 8 * lc) * 2;
+      *(u32x4*)(&kv_lds[toff_p<D>(r, lc)]) = load_ranged_16((const uint16_t*)p.k + at, nb, off);
+      *(u32x4*)(&kv_lds[KVT + toff_p<D>(r, lc)]) = load_ranged_16((const uint16_t*)p.v + at, nb, off);
     }
-    kf[kk] = __builtin_bit_cast(bf16x8, a);
-    vf[kk] = __builtin_bit_cast(bf16x8, v);
+  } else {
+#pragma unroll
+    for (int kk = 0; kk < C::KD; ++kk) {
+      u32x4 a = {0u, 0u, 0u, 0u}, v = {0u, 0u, 0u, 0u};
+      if (key_ok) {
+        const uint32_t ko = (uint32_t)key * kv_ld + 16 * kk + 8 * h;
+        a = *(const u32x4*)(kg + ko);
+        v = *(const u32x4*)(vg + ko);
+      }
+      kf[kk] = __builtin_bit_cast(bf16x8, a);
+      vf[kk] = __builtin_bit_cast(bf16x8, v);
+    }
   }
+  // K and V fragments of this lane's key (row 32 kgrp + l32 of the tile),
+  // 16-wide head-dim chunk kk
+  auto k_frag = [&](int kk) __attribute__((always_inline)) {
+    if constexpr (RS == 2) return lds_b128(kv_lds, toff_p<D>(32 * kgrp + l32, 2 * kk + h));
+    else return kf[kk];
+  };
+  auto v_frag = [&](int kk) __attribute__((always_inline)) {
+    if constexpr (RS == 2) return lds_b128(kv_lds + KVT, toff_p<D>(32 * kgrp + l32, 2 * kk + h));
+    else return vf[kk];
+  };
 
   f32x16 dk[C::ND], dv[C::ND];
 #pragma unroll
@@ -497,7 +545,7 @@ __global__ __launch_bounds__(256, (kDkdvOccupancy<D, VAR>)) void fa_bwd_dkdv_ker
   u32x4 qst[LPT], dst[LPT];
   float aux = 0.f;  // LSE2 (threads 0..BQ-1) or D (threads BQ..2BQ-1) of one row
   const uint32_t q_off0 = ((uint32_t)(tid / C::CPR) * q_ld + 8 * (tid % C::CPR)) * 2;
-  const uint32_t q_step = (256 / C::CPR) * (uint32_t)q_ld * 2;
+  const uint32_t q_step = (NT / C::CPR) * (uint32_t)q_ld * 2;
   auto load_regs = [&](int g, int q0) __attribute__((always_inline)) {
     const int64_t hb = lay.base + g * lay.q_hs + (int64_t)q0 * q_ld;
     const uint32_t nb = (uint32_t)max(0, qlim - q0) * q_ld * 2;
@@ -525,7 +573,7 @@ __global__ __launch_bounds__(256, (kDkdvOccupancy<D, VAR>)) void fa_bwd_dkdv_ker
   auto store_lds = [&](int st) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < LPT; ++i) {
-      const int c = tid + 256 * i, r = c / C::CPR, lc = c % C::CPR;
+      const int c = tid + NT * i, r = c / C::CPR, lc = c % C::CPR;
       *(u32x4*)(&lds[st][toff_t<D>(r, lc)]) = qst[i];
       *(u32x4*)(&lds[st][TILE + toff_t<D>(r, lc)]) = dst[i];
     }
@@ -533,21 +581,24 @@ __global__ __launch_bounds__(256, (kDkdvOccupancy<D, VAR>)) void fa_bwd_dkdv_ker
   };
 
   auto compute = [&](int st, int q0) __attribute__((always_inline)) {
-    // rows all before the wave's first key, or the wave's keys all padding
-    if ((CAUSAL && q0 + BQ - 1 + off < kw0) || kw0 >= kv_lim) return;
+    // the wave's rows (blocks WQB*rh .. +WQB-1) all before its first key, or
+    // its keys all padding
+    const int wq0 = q0 + 32 * WQB * rh;
+    if ((CAUSAL && wq0 + 32 * WQB - 1 + off < kw0) || kw0 >= kv_lim) return;
     const uint8_t* qt = lds[st];
     const uint8_t* dt = lds[st] + TILE;
     const float* lse2 = (const float*)(lds[st] + 2 * TILE);
     const float* dd = lse2 + BQ;
-    bf16x8 pb[NQB][2], dsb[NQB][2];
+    bf16x8 pb[WQB][2], dsb[WQB][2];
 #pragma unroll
-    for (int qb = 0; qb < NQB; ++qb) {
+    for (int j = 0; j < WQB; ++j) {
+      const int qb = WQB * rh + j;
       f32x16 s = f32x16{}, dp = f32x16{};
       const int qr = 32 * qb + l32;
 #pragma unroll
       for (int kk = 0; kk < C::KD; ++kk) {
-        s = mfma_32x32x16_bf16(lds_b128(qt, toff_t<D>(qr, 2 * kk + h)), kf[kk], s);
-        dp = mfma_32x32x16_bf16(lds_b128(dt, toff_t<D>(qr, 2 * kk + h)), vf[kk], dp);
+        s = mfma_32x32x16_bf16(lds_b128(qt, toff_t<D>(qr, 2 * kk + h)), k_frag(kk), s);
+        dp = mfma_32x32x16_bf16(lds_b128(dt, toff_t<D>(qr, 2 * kk + h)), v_frag(kk), dp);
       }
       // lane = key, register r = row 32qb + acc_row(r, h)
       float pr[16], ds[16];
@@ -604,20 +655,21 @@ __global__ __launch_bounds__(256, (kDkdvOccupancy<D, VAR>)) void fa_bwd_dkdv_ker
       if ((!CAUSAL || kw0 + 31 <= qb0 + off) && qb0 + 31 < qlim && kw0 + 31 < kv_lim)
         probs(std::false_type{});
       else probs(std::true_type{});
-      pb[qb][0] = pack8(pr);
-      pb[qb][1] = pack8(pr + 8);
-      dsb[qb][0] = pack8(ds);
-      dsb[qb][1] = pack8(ds + 8);
+      pb[j][0] = pack8(pr);
+      pb[j][1] = pack8(pr + 8);
+      dsb[j][0] = pack8(ds);
+      dsb[j][1] = pack8(ds + 8);
     }
     // dV^T += dO^T P, dK^T += Q^T dS
 #pragma unroll
     for (int db = 0; db < C::ND; ++db)
 #pragma unroll
-      for (int qb = 0; qb < NQB; ++qb)
+      for (int j = 0; j < WQB; ++j)
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
-          dv[db] = mfma_32x32x16_bf16(tr_operand<D>(dt, 32 * qb + 16 * m, db, lane), pb[qb][m], dv[db]);
-          dk[db] = mfma_32x32x16_bf16(tr_operand<D>(qt, 32 * qb + 16 * m, db, lane), dsb[qb][m], dk[db]);
+          const int r0 = 32 * (WQB * rh + j) + 16 * m;
+          dv[db] = mfma_32x32x16_bf16(tr_operand<D>(dt, r0, db, lane), pb[j][m], dv[db]);
+          dk[db] = mfma_32x32x16_bf16(tr_operand<D>(qt, r0, db, lane), dsb[j][m], dk[db]);
         }
   };
 
@@ -640,8 +692,34 @@ __global__ __launch_bounds__(256, (kDkdvOccupancy<D, VAR>)) void fa_bwd_dkdv_ker
     }
   }
 
+  if constexpr (RS == 2) {
+    // Waves 4..7 hand their partial sums to waves 0..3 through LDS, dK then
+    // dV, laid out [key group][slice][register][lane] in fp32 (64 KiB per
+    // tensor at d = 128; every wave has passed the loop's last barrier).
+    static_assert(4 * C::ND * 16 * 64 * 4 <= (int)sizeof(lds), "reduction buffer");
+    float* red = reinterpret_cast<float*>(&lds[0][0]);
+    auto hand_over = [&](f32x16 (&acc)[C::ND]) __attribute__((always_inline)) {
+      if (rh == 1) {
+#pragma unroll
+        for (int db = 0; db < C::ND; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) red[((kgrp * C::ND + db) * 16 + r) * 64 + lane] = acc[db][r];
+      }
+      __syncthreads();
+      if (rh == 0) {
+#pragma unroll
+        for (int db = 0; db < C::ND; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[db][r] += red[((kgrp * C::ND + db) * 16 + r) * 64 + lane];
+      }
+      __syncthreads();
+    };
+    hand_over(dk);
+    hand_over(dv);
+  }
+
   // dK = scale * (dK^T)^T, dV = (dV^T)^T: lane = key, register r of slice db = dim
-  if (key < lay.Nk) {
+  if (key < lay.Nk && rh == 0) {
     uint16_t* dkg = (uint16_t*)p.dk + lay.kvbase + (uint32_t)key * kv_ld;
     uint16_t* dvg2 = (uint16_t*)p.dv + lay.kvbase + (uint32_t)key * kv_ld;
 #pragma unroll
@@ -671,8 +749,9 @@ hipError_t launch_bwd(const BwdParams& p, hipStream_t stream) {
     if (e != hipSuccess) return e;
   }
   if (dkdv_wgs > 0) {
-    hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, CAUSAL, VAR>), dim3((unsigned)dkdv_wgs), dim3(256), 0,
-                       stream, p);
+    constexpr int W = kDkdvWaves<D, VAR>;
+    hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, CAUSAL, VAR, W>), dim3((unsigned)dkdv_wgs),
+                       dim3(64 * W), 0, stream, p);
     return hipGetLastError();
   }
   return hipSuccess;

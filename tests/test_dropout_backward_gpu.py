@@ -97,18 +97,29 @@ def test_dropout_backward_against_oracle(case, causal):
     check(inp, do, causal, 1 / np.sqrt(d), p, seed, offset, got, f"{case} causal={causal}")
 
 
-def test_dropout_backward_rate_zero_is_plain_backward():
+@pytest.mark.parametrize("d", [64, 128])
+def test_dropout_backward_rate_zero_is_plain_backward(d):
+    """At rate 0 every weight is kept and scaled by 1: at d = 128 the dropout
+    kernels are the plain kernels' arithmetic, bit for bit; at d = 64 the
+    plain dK/dV kernel runs four waves per workgroup and the dropout one
+    eight (a wave pair splitting the rows, their sums added at the end), so
+    dK and dV agree to rounding and dQ bit for bit."""
     import torch
     import io_aware_exact_forward_amd as fa
-    inp, do_bits = W.grad_inputs(1, 2, 333, 128, 9810)
+    inp, do_bits = W.grad_inputs(1, 2, 333, d, 9810)
     q, k, v, do = dev(inp.q), dev(inp.k), dev(inp.v), dev(do_bits)
     for causal in (False, True):
         o, lse = fa.forward(q, k, v, causal=causal)
         a = fa.backward(q, k, v, o, lse, do, causal=causal)
         b = fa.backward_dropout(q, k, v, o, lse, do, p_drop=0.0, seed=3, causal=causal)
         torch.cuda.synchronize()
-        for x, y in zip(a, b):
-            assert torch.equal(x, y)
+        assert torch.equal(a[0], b[0])
+        for x, y in zip(a[1:], b[1:]):
+            if d == 128:
+                assert torch.equal(x, y)
+            else:
+                xf, yf = x.float(), y.float()
+                assert (xf - yf).abs().max() <= 1e-2 * xf.abs().max()
 
 
 def test_dropout_backward_full_size_heads():
