@@ -101,8 +101,11 @@ __device__ __forceinline__ u32x4 philox4x32_10(u32x4 c, uint32_t k0, uint32_t k1
     }
     const uint64_t p0 = (uint64_t)0xD2511F53u * c[0];
     const uint64_t p1 = (uint64_t)0xCD9E8D57u * c[2];
-    c = u32x4{(uint32_t)(p1 >> 32) ^ c[1] ^ k0, (uint32_t)p1, (uint32_t)(p0 >> 32) ^ c[3] ^ k1,
-              (uint32_t)p0};
+    // three-input exclusive or in one instruction (v_bitop3_b32, truth table
+    // 0x96 = a ^ b ^ c)
+    const uint32_t w0 = (uint32_t)__builtin_amdgcn_bitop3_b32((uint32_t)(p1 >> 32), c[1], k0, 0x96);
+    const uint32_t w2 = (uint32_t)__builtin_amdgcn_bitop3_b32((uint32_t)(p0 >> 32), c[3], k1, 0x96);
+    c = u32x4{w0, (uint32_t)p1, w2, (uint32_t)p0};
   }
   return c;
 }
