@@ -26,9 +26,9 @@
 //    ("FlashAttention: Exact Attention as an IO-Aware Streaming Computation",
 //    section "Mathematical structure"); the weights never leave the lane.
 // At the end the wave's slices are summed across its lane groups; with fixed
-// ranges the four waves' states are then merged through LDS.  (One key row per lane would
-// need no sum across lanes, but its loads touch 64 rows per instruction and
-// ran 1.7x slower.)
+// ranges the four waves' states are then merged through LDS.  (One key row
+// per lane would need no sum across lanes, but its loads touch 64 rows per
+// instruction and ran 1.7x slower.)
 #include "fa_device.hpp"
 #include "fa_internal.hpp"
 
@@ -49,11 +49,6 @@ __device__ __forceinline__ int seq_len(const FwdParams& p, int b) {
   return kl < 0 ? 0 : (kl > p.Nk ? p.Nk : kl);
 }
 
-// Keys [k0, k1) of row bh (sequence b, key/value head hk, L keys visible):
-// the four waves take 64 keys at a time in turn, then merge their states
-// through LDS.  Threads tid < D return element tid of the range's normalised
-// output in y and the range's log-sum-exp (natural log) in lse; the range
-// holds at least one key.  Ends with a barrier, so s may be reused at once.
 // One wave's pass over keys [k0, k1) of row bh (sequence b, key/value head
 // hk, L keys visible), 64 keys at a time with a stride of `step` keys (the
 // waves that share a range take its 64-key chunks in turn).  On return the
