@@ -73,6 +73,71 @@ def stored_traffic(workload: str, kind: str = "forward"):
     return ent.get("hbm_bytes_per_launch")
 
 
+def ceiling_record(dev, stream) -> dict:
+    """What the device's matrix cores deliver under a sustained dense load, measured
+    right after the timed steps: a pure-MFMA loop (lib/libfa_probe.so, bf16
+    v_mfma_f32_32x32x16 back to back on every SIMD) and torch.matmul on
+    8192 x 8192 x 8192 bf16 (the vendor GEMM).  Under such a load the engine
+    clock settles near 1.75-1.8 GHz, so these rates, not the 2.4 GHz dense
+    peak, are what an MFMA-bound kernel can approach on this machine.  Both
+    follow the power controller: they vary by about 10 % from machine to
+    machine and right after other heavy work."""
+    import ctypes
+
+    import torch
+
+    from io_aware_exact_forward_amd import build as _b
+
+    def timed(fn, reps):
+        for _ in range(5):
+            fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        e1.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / reps
+
+    rec = {}
+    path = _b.probe_lib_path()
+    if os.path.exists(path):
+        lib = ctypes.CDLL(path)
+        lib.fa_probe_mfma_bf16.restype = ctypes.c_int
+        lib.fa_probe_mfma_bf16.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                           ctypes.c_void_p]
+        lib.fa_probe_mfma_flops.restype = ctypes.c_double
+        lib.fa_probe_mfma_flops.argtypes = [ctypes.c_int, ctypes.c_int]
+        blocks = 2 * torch.cuda.get_device_properties(dev).multi_processor_count
+        iters = 1000
+        buf = torch.empty(blocks * 512, dtype=torch.float32, device=dev)
+
+        def probe():
+            if lib.fa_probe_mfma_bf16(blocks, iters, ctypes.c_void_p(buf.data_ptr()),
+                                      ctypes.c_void_p(stream.cuda_stream)) != 0:
+                raise RuntimeError("MFMA probe launch failed")
+        sec = timed(probe, 30)
+        rec["mfma_loop_tflops"] = lib.fa_probe_mfma_flops(blocks, iters) / sec / 1e12
+        del buf
+    g = torch.Generator(device=dev).manual_seed(11)
+    a = torch.randn(8192, 8192, device=dev, dtype=torch.bfloat16, generator=g)
+    b = torch.randn(8192, 8192, device=dev, dtype=torch.bfloat16, generator=g)
+    c = torch.empty(8192, 8192, device=dev, dtype=torch.bfloat16)
+    with torch.cuda.stream(stream):
+        sec = timed(lambda: torch.matmul(a, b, out=c), 20)
+    rec["gemm_bf16_8192_tflops"] = 2.0 * 8192 ** 3 / sec / 1e12
+    del a, b, c
+    torch.cuda.empty_cache()
+    return rec
+
+
+def ceiling_with_fracs(dev, stream, tflops) -> dict:
+    ceil = ceiling_record(dev, stream)
+    return dict(ceil, **{"frac_of_" + k[:-len("_tflops")]: tflops / v for k, v in ceil.items()})
+
+
 def stored_clock_cycles(workload: str, kind: str = "forward"):
     """GRBM_GUI_ACTIVE cycles per XCD per launch from the committed counter
     summary, if taken on the current kernel source; else None.  The count is
@@ -394,6 +459,7 @@ def bench_backward(args) -> int:
     stream = torch.cuda.current_stream(dev)
     ms, t_wall, settle = timed_steps(step, args, stream)
     tflops = flops / (ms * 1e-3) / 1e12
+    ceil = ceiling_with_fracs(dev, stream, tflops)
     result = {
         "metric": "attention bwd TFLOP/s (bf16, 1 GPU; useful 10*d flops per visible pair)"
                   + (f"; dropout p={drop}" if drop > 0 else "")
@@ -501,6 +567,7 @@ def bench_backward(args) -> int:
                       f"materialised; {dt:.1f} s",
             "seconds": dt,
         }
+    result["ceiling"] = ceil
     print(json.dumps(result), flush=True)
     return 0
 
@@ -553,6 +620,7 @@ def bench_varlen(args) -> int:
     stream = torch.cuda.current_stream(dev)
     ms, t_wall, settle = timed_steps(step, args, stream)
     tflops = flops / (ms * 1e-3) / 1e12
+    ceil = ceiling_with_fracs(dev, stream, tflops)
     kind = "backward" if args.backward else "forward"
     result = {
         "metric": ("attention bwd TFLOP/s (bf16, 1 GPU; useful 10*d flops per visible pair); "
@@ -603,6 +671,7 @@ def bench_varlen(args) -> int:
             "sample": f"{done} of {wl.B} sequences (shortest first), all heads, fp64; {dt:.1f} s",
             "seconds": dt,
         }
+    result["ceiling"] = ceil
     print(json.dumps(result), flush=True)
     return 0
 
@@ -826,6 +895,9 @@ def main() -> int:
         result["roofline"]["peak_at_measured_clock"] = clk["peak_at_clock"]
         result["roofline"]["frac_at_measured_clock"] = tflops / clk["peak_at_clock"]
         result["clock"] = clk
+
+    if wl.dtype == "bf16":
+        result["ceiling"] = ceiling_with_fracs(dev, stream, tflops)
 
     if args.dropout == 0 and not args.bias:
         model = kv_byte_model(wl, lens, esz)

@@ -4,7 +4,9 @@
 
 compiles every translation unit under csrc/ with hipcc for gfx950 and links
 them (plus rocBLAS, used by the materialised baseline's two products) into
-io_aware_exact_forward_amd/lib/libfa_mi355x.so.  It always recompiles.
+io_aware_exact_forward_amd/lib/libfa_mi355x.so, and builds the measurement
+helper csrc/probe/fa_mfma_probe.hip (the sustained matrix-core rate bench.py
+reports beside the roofline) into lib/libfa_probe.so.  It always recompiles.
 """
 from __future__ import annotations
 
@@ -20,6 +22,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIBDIR = os.path.join(PKG, "lib")
 LIBNAME = "libfa_mi355x.so"
+PROBE_LIBNAME = "libfa_probe.so"
+PROBE_SOURCE = os.path.join(CSRC, "probe", "fa_mfma_probe.hip")
 ARCH = "gfx950"
 
 SOURCES = ["fa_api.cpp", "fa_fwd_bf16.hip", "fa_fwd_f32.hip", "fa_merge.hip", "fa_decode.hip",
@@ -41,12 +45,22 @@ def lib_path() -> str:
     return os.path.join(LIBDIR, LIBNAME)
 
 
+def probe_lib_path() -> str:
+    return os.path.join(LIBDIR, PROBE_LIBNAME)
+
+
 def build(verbose: bool = False) -> str:
     cc = hipcc()
     os.makedirs(LIBDIR, exist_ok=True)
     with tempfile.TemporaryDirectory(prefix="fa_build_") as tmp:
         procs = []
         objs = []
+        probe_tmp = os.path.join(tmp, PROBE_LIBNAME)
+        probe_cmd = [cc, f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+                     *DEVICE_FLAGS, PROBE_SOURCE, "-o", probe_tmp]
+        if verbose:
+            print(" ".join(probe_cmd), flush=True)
+        probe_proc = subprocess.Popen(probe_cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)
         for src in SOURCES:
             obj = os.path.join(tmp, src.replace(".", "_") + ".o")
             cmd = [cc, f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-c",
@@ -67,6 +81,11 @@ def build(verbose: bool = False) -> str:
                 errors.append(f"{src}:\n{text}")
             elif verbose and text.strip():
                 print(text, flush=True)
+        out, _ = probe_proc.communicate()
+        if probe_proc.returncode != 0:
+            text = "\n".join(ln for ln in out.decode(errors="replace").splitlines()
+                             if "not a recognized feature" not in ln)
+            errors.append(f"probe/fa_mfma_probe.hip:\n{text}")
         if errors:
             raise RuntimeError("HIP build failed:\n" + "\n".join(errors))
         tmp_lib = os.path.join(tmp, LIBNAME)
@@ -78,9 +97,9 @@ def build(verbose: bool = False) -> str:
         if r.returncode != 0:
             raise RuntimeError("HIP link failed:\n" + r.stdout.decode(errors="replace"))
         # replace atomically so a loaded copy is never half-written
-        dst = lib_path()
-        shutil.copyfile(tmp_lib, dst + ".tmp")
-        os.replace(dst + ".tmp", dst)
+        for src, dst in ((tmp_lib, lib_path()), (probe_tmp, probe_lib_path())):
+            shutil.copyfile(src, dst + ".tmp")
+            os.replace(dst + ".tmp", dst)
     return lib_path()
 
 

@@ -513,3 +513,26 @@ def test_split_noalloc_validates_before_any_hip_call():
 def _noalloc_args(q=Q, k=K, v=V, o=O, lse=L, B=1, H=2, Hkv=2, Nq=64, Nk=1024, d=64, scale=0.125,
                   causal=0, kl=0, dtype=BF16, num_splits=4, stream=0):
     return (q, k, v, o, lse, B, H, Hkv, Nq, Nk, d, scale, causal, kl, dtype, num_splits, stream)
+
+
+def test_probe_library_exports_and_rejects_bad_arguments():
+    """The matrix-core rate probe bench.py reports beside the roofline is a
+    separate library (not part of the attention ABI); bad arguments return -1
+    before any HIP call."""
+    import ctypes
+
+    from io_aware_exact_forward_amd import build as _b
+
+    path = _b.probe_lib_path()
+    if not os.path.exists(path):
+        pytest.skip("probe library not built")
+    lib = ctypes.CDLL(path)
+    lib.fa_probe_mfma_bf16.restype = ctypes.c_int
+    lib.fa_probe_mfma_bf16.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.fa_probe_mfma_flops.restype = ctypes.c_double
+    lib.fa_probe_mfma_flops.argtypes = [ctypes.c_int, ctypes.c_int]
+    assert lib.fa_probe_mfma_bf16(0, 10, ctypes.c_void_p(A), None) == -1
+    assert lib.fa_probe_mfma_bf16(4, 0, ctypes.c_void_p(A), None) == -1
+    assert lib.fa_probe_mfma_bf16(4, 10, None, None) == -1
+    # 8 waves x 16 MFMAs per iteration x 32768 flops each
+    assert lib.fa_probe_mfma_flops(2, 3) == 2 * 3 * 8 * 16 * 2 * 32 * 32 * 16
