@@ -38,7 +38,9 @@
 //
 // Causal tiles run heaviest first; consecutive workgroups cycle over
 // (batch, head) so all tiles of a head land on one XCD when B*H is a
-// multiple of 8 (workgroups are dealt round-robin to the 8 XCDs).
+// multiple of 8 (workgroups are dealt round-robin to the 8 XCDs).  A
+// non-causal batch with per-sequence key lengths runs its sequences longest
+// first.
 #include "fa_bf16_tiles.hpp"
 #include "fa_device.hpp"
 #include "fa_internal.hpp"
@@ -55,6 +57,11 @@ constexpr float kWeightBound = 65536.0f;
 // measured slower.
 constexpr int kPingPongStages = 4;
 
+
+// Largest batch for which a launch over sequences of different lengths
+// orders its tiles longest sequence first (the order is worked out in every
+// workgroup, in O(B^2) scalar steps).
+constexpr int kLptBatches = 8;
 
 template <int S>
 struct StageTag {
@@ -129,6 +136,37 @@ void fa_fwd_bf16_kernel(FwdParams p) {
   int split = 0, bh, qt;
   if constexpr (PERSIST) {
     item_of(0, bh, qt);
+  } else if (!CAUSAL && p.key_len && !p.cu_q && p.splits == 1 && !p.end_aligned &&
+             p.B <= kLptBatches) {
+    // Dense batch with per-sequence key lengths, not causal: a query tile of
+    // sequence b costs ceil(L_b / BK) key tiles (a tile of rows past L_b
+    // only writes zeros), so the work differs between sequences only.  The
+    // grid takes the sequences in order of decreasing length (ties by
+    // index), each one's tiles query-tile major with the heads fastest (so
+    // a head's tiles keep one XCD when H is a multiple of 8): the longest
+    // work starts first, and each sequence's padding tiles, which finish at
+    // once, sit between it and the next.
+    const int per_seq = p.H * p.n_qtiles;
+    const int rank = (int)blockIdx.x / per_seq;
+    const int local = (int)blockIdx.x - rank * per_seq;
+    int len[kLptBatches];
+#pragma unroll
+    for (int i = 0; i < kLptBatches; ++i) {
+      const int L = i < p.B ? p.key_len[i] : -1;
+      len[i] = L < 0 ? (i < p.B ? 0 : -1) : (L > p.Nk ? p.Nk : L);
+    }
+    int sb = 0;
+#pragma unroll
+    for (int i = 0; i < kLptBatches; ++i) {
+      int ahead = 0;  // sequences before i in the order
+#pragma unroll
+      for (int j = 0; j < kLptBatches; ++j)
+        ahead += (j < p.B && (len[j] > len[i] || (len[j] == len[i] && j < i))) ? 1 : 0;
+      if (i < p.B && ahead == rank) sb = i;
+    }
+    sb = __builtin_amdgcn_readfirstlane(sb);
+    qt = local / p.H;
+    bh = sb * p.H + (local - qt * p.H);
   } else {
     const int per_split = BH * p.n_qtiles;
     split = (int)blockIdx.x / per_split;
