@@ -68,14 +68,17 @@ struct StageTag {
   static constexpr int value = S;
 };
 
-// BKX, if not 0, sets the keys per streamed tile.
-template <int D, int WAVES, int NSTAGE, int BKX = 0>
+// BKX, if not 0, sets the keys per streamed tile.  KS = 2 splits the waves
+// into two groups over the same query rows, each taking every other key tile
+// (an LDS stage then holds the two groups' tiles side by side).
+template <int D, int WAVES, int NSTAGE, int BKX = 0, int KS = 1>
 struct Bf16Cfg {
-  static constexpr int BQ = 32 * WAVES;          // query rows per workgroup
+  static constexpr int BQ = 32 * WAVES / KS;     // query rows per workgroup
   static constexpr int BK = BKX ? BKX : (D == 128 ? 64 : 128);  // keys per streamed tile
+  static constexpr int SK = KS * BK;             // keys per LDS stage
   static constexpr int ROW_BYTES = D * 2;
   static constexpr int CPR = D / 8;              // 16-byte chunks per row
-  static constexpr int TILE_BYTES = BK * ROW_BYTES;  // one K or V tile (16 KiB)
+  static constexpr int TILE_BYTES = SK * ROW_BYTES;  // the K (or V) rows of one stage
   static constexpr int STAGE_BYTES = 2 * TILE_BYTES; // K tile + V tile
   static constexpr int LDS_BYTES = NSTAGE * STAGE_BYTES;
   static constexpr int LOADS = TILE_BYTES / 1024 / WAVES;  // 1 KiB loads per wave per tensor
@@ -89,7 +92,7 @@ struct Bf16Cfg {
 
 
 template <int D, bool CAUSAL, int WAVES, int NSTAGE, bool PINGPONG, bool DROP = false,
-          bool BIAS = false, bool PERSIST = false, int BKX = 0>
+          bool BIAS = false, bool PERSIST = false, int BKX = 0, int KS = 1>
 // Two lockstep workgroups per CU (256 registers per lane), except with an
 // additive mask at d = 64, whose extra registers do not fit: one workgroup;
 // and three with 64-key tiles at d = 64 (168 registers).
@@ -99,7 +102,9 @@ __global__ __launch_bounds__(64 * WAVES,
 void fa_fwd_bf16_kernel(FwdParams p) {
   static_assert(!(DROP || BIAS) || !PINGPONG, "dropout and bias run in the lockstep schedule");
   static_assert(!PERSIST || PINGPONG, "the persistent form is the ping-pong schedule's");
-  using C = Bf16Cfg<D, WAVES, NSTAGE, BKX>;
+  static_assert(KS == 1 || (KS == 2 && WAVES == 8 && !PINGPONG && !DROP && !BIAS),
+                "the key split is a plain lockstep form of eight waves");
+  using C = Bf16Cfg<D, WAVES, NSTAGE, BKX, KS>;
   __shared__ __attribute__((aligned(1024))) uint8_t lds[C::LDS_BYTES];
 
   const int tid = threadIdx.x;
@@ -234,7 +239,10 @@ void fa_fwd_bf16_kernel(FwdParams p) {
 
   const uint16_t* __restrict__ qg = (const uint16_t*)p.q + base;
 
-  int qw0 = q0 + 32 * wave;  // first query row of this wave
+  // with the key split, waves w and w + WAVES/2 own the same rows; kgrp is
+  // the key group (even or odd key tiles)
+  const int kgrp = KS == 2 ? wave / (WAVES / 2) : 0;
+  int qw0 = q0 + 32 * (KS == 2 ? wave % (WAVES / 2) : wave);  // first query row of this wave
   int qrow = qw0 + l32;      // the query row this lane owns
   int qwpos = qw0 + off;     // key position of the wave's first row
   int qpos = qrow + off;     // key position of this lane's row
@@ -704,27 +712,30 @@ void fa_fwd_bf16_kernel(FwdParams p) {
   if constexpr (!PINGPONG) {
     // ---- lockstep schedule: every wave runs S, softmax and PV of a tile
     // between two barriers -------------------------------------------------
+    // steps: one LDS stage each (KS key tiles, one per key group)
+    const int nsteps = (ntiles + KS - 1) / KS;
 #pragma unroll
     for (int st = 0; st < NSTAGE - 1; ++st)
-      if (st < ntiles) load_tile(kv_first + st * C::BK, st);
+      if (st < nsteps) load_tile(kv_first + st * C::SK, st);
 
     // One streamed tile, read from LDS stage S (a compile-time constant:
     // the loop below cycles through the NSTAGE instantiations).
     auto step = [&](const int t, auto stage_tag) __attribute__((always_inline)) {
       constexpr int S = decltype(stage_tag)::value;
-      const int kv0 = kv_first + t * C::BK;
+      const int kvs = kv_first + t * C::SK;   // first key of the stage
+      const int kv0 = kvs + kgrp * C::BK;     // first key of this group's tile
       // Tile t has landed once at most the loads of the tiles issued after
       // it are still in flight; after the barrier every wave's part has
       // landed and every wave is done with tile t - 1, whose stage is
       // refilled.
-      const int later = min(NSTAGE - 2, ntiles - 1 - t);  // 0 .. NSTAGE - 2 (uniform)
+      const int later = min(NSTAGE - 2, nsteps - 1 - t);  // 0 .. NSTAGE - 2 (uniform)
       if (NSTAGE > 3 && later >= 2) vmem_wait<(NSTAGE > 3 ? 2 : 0) * C::LOADS_PER_TILE>();
       else if (later >= 1) vmem_wait<C::LOADS_PER_TILE>();
       else vmem_wait<0>();
       barrier_no_fence();
-      if (t + NSTAGE - 1 < ntiles) load_tile(kv0 + (NSTAGE - 1) * C::BK, (S + NSTAGE - 1) % NSTAGE);
-      if (skip_tile(kv0)) return;
-      uint32_t kbase = lds0 + S * C::STAGE_BYTES;
+      if (t + NSTAGE - 1 < nsteps) load_tile(kvs + (NSTAGE - 1) * C::SK, (S + NSTAGE - 1) % NSTAGE);
+      if (skip_tile(kv0) || (KS == 2 && kv0 >= kv_last)) return;
+      uint32_t kbase = lds0 + S * C::STAGE_BYTES + kgrp * C::BK * C::ROW_BYTES;
       asm volatile("" : "+s"(kbase));  // see the ping-pong schedule
       k_issue(G0, kbase, kr[0]);
       if constexpr (BIAS) bias_issue(kv0);
@@ -734,15 +745,50 @@ void fa_fwd_bf16_kernel(FwdParams p) {
       v_issue(G0, kbase + C::TILE_BYTES, vr[0]);
       pv(kbase + C::TILE_BYTES, pf, std::false_type{}, 0u);
     };
-    for (int t = 0; t < ntiles; t += NSTAGE) {
+    for (int t = 0; t < nsteps; t += NSTAGE) {
       step(t, StageTag<0>{});
-      if (t + 1 < ntiles) step(t + 1, StageTag<1>{});
+      if (t + 1 < nsteps) step(t + 1, StageTag<1>{});
       if constexpr (NSTAGE > 2) {
-        if (t + 2 < ntiles) step(t + 2, StageTag<2>{});
+        if (t + 2 < nsteps) step(t + 2, StageTag<2>{});
       }
       if constexpr (NSTAGE > 3) {
-        if (t + 3 < ntiles) step(t + 3, StageTag<3>{});
+        if (t + 3 < nsteps) step(t + 3, StageTag<3>{});
       }
+    }
+    if constexpr (KS == 2) {
+      // Key group 1 hands its running state (numerator, reference maximum,
+      // denominators; same lanes, same rows) to group 0 through LDS, and
+      // group 0 combines the two partial sums over disjoint key sets against
+      // their larger reference, as the block summaries of "FlashAttention"
+      // (section "Why a tile can be discarded") combine, then writes the rows.
+      constexpr int NV = C::ND * 16 + 3;
+      static_assert((WAVES / 2) * NV * 64 * 4 <= C::LDS_BYTES, "exchange fits the ring");
+      float* xs = (float*)lds + (wave % (WAVES / 2)) * NV * 64 + lane;
+      barrier_no_fence();  // every wave is done reading the ring (all loads have landed)
+      if (kgrp == 1) {
+#pragma unroll
+        for (int i = 0; i < C::ND; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) xs[(i * 16 + r) * 64] = o_acc[i][r];
+        xs[(C::ND * 16) * 64] = m_ref;
+        xs[(C::ND * 16 + 1) * 64] = l_run;
+        xs[(C::ND * 16 + 2) * 64] = lp_run + lp_run2;
+      }
+      __syncthreads();
+      if (kgrp == 1) return;
+      const float m1 = xs[(C::ND * 16) * 64];
+      const float m = fmaxf(m_ref, m1);
+      // -inf - (-inf) is never formed: a reference of -inf weighs 0
+      const float a0 = m_ref == kNegInf ? 0.f : fast_exp2(m_ref - m);
+      const float a1 = m1 == kNegInf ? 0.f : fast_exp2(m1 - m);
+      m_ref = m;
+      l_run = l_run * a0 + xs[(C::ND * 16 + 1) * 64] * a1;
+      lp_run = (lp_run + lp_run2) * a0 + xs[(C::ND * 16 + 2) * 64] * a1;
+      lp_run2 = 0.f;
+#pragma unroll
+      for (int i = 0; i < C::ND; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o_acc[i][r] = o_acc[i][r] * a0 + xs[(i * 16 + r) * 64] * a1;
     }
   } else {
     // ---- ping-pong schedule ----------------------------------------------
@@ -1066,14 +1112,14 @@ void fa_fwd_bf16_kernel(FwdParams p) {
 }
 
 template <int D, bool CAUSAL, int WAVES, int NSTAGE, bool PINGPONG, bool DROP = false,
-          bool BIAS = false, bool PERSIST = false, int BKX = 0>
+          bool BIAS = false, bool PERSIST = false, int BKX = 0, int KS = 1>
 hipError_t launch_cfg(FwdParams p, hipStream_t stream) {
-  using C = Bf16Cfg<D, WAVES, NSTAGE, BKX>;
+  using C = Bf16Cfg<D, WAVES, NSTAGE, BKX, KS>;
   p.n_qtiles = (p.N + C::BQ - 1) / C::BQ;
   const int64_t items = (int64_t)p.n_qtiles * p.B * p.H * p.splits;
   // persistent: items / 2 units, p.persist per workgroup
   const dim3 grid((unsigned)(PERSIST ? items / 2 / p.persist : items));
-  hipLaunchKernelGGL((fa_fwd_bf16_kernel<D, CAUSAL, WAVES, NSTAGE, PINGPONG, DROP, BIAS, PERSIST, BKX>),
+  hipLaunchKernelGGL((fa_fwd_bf16_kernel<D, CAUSAL, WAVES, NSTAGE, PINGPONG, DROP, BIAS, PERSIST, BKX, KS>),
                      grid, dim3(64 * WAVES), 0, stream, p);
   return hipGetLastError();
 }
@@ -1138,6 +1184,16 @@ hipError_t launch_d(const FwdParams& p, hipStream_t stream) {
   // ragged lengths 349 -> 330 us; without lengths, on the 32-head N = 2048
   // causal workload, 128-key tiles at two per CU stay faster, 34.5 vs 37 us)
   if (ragged64) return launch_cfg<D, CAUSAL, 4, 2, false, false, false, false, 64>(p, stream);
+  // A causal grid of 128-row tiles that the device holds at once (two per
+  // CU) is as slow as its heaviest tile, which sees the most keys: there each
+  // workgroup gets eight waves in two groups over alternate key tiles, so
+  // the heaviest tiles take half as long and the light ones fill in behind.
+  if constexpr (CAUSAL) {
+    const int cus = device_cus();
+    if (!p.key_len && !p.cu_q && p.splits == 1 && cus > 0 &&
+        (int64_t)p.B * p.H * ((p.N + 127) / 128) <= 2 * (int64_t)cus)
+      return launch_cfg<D, CAUSAL, 8, 2, false, false, false, false, 0, 2>(p, stream);
+  }
   return launch_cfg<D, CAUSAL, 4, 2, false>(p, stream);
 }
 
