@@ -91,6 +91,38 @@ def test_h8_n32768_causal_sampled():
 
 
 # ---------------------------------------------------------------------------
+# Launch forms chosen by grid size
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_causal_grid_beyond_one_pass(d):
+    """A causal batch whose 128-row grid does not fit the device at once
+    (24 heads x 24 tiles = 576 workgroups > two per CU) but is too small for
+    the 256-row form: the four-wave lockstep launch.  (Smaller causal grids,
+    such as every case of the edge sweep below, take the two-key-group form.)
+    Ragged N; every element compared."""
+    N = 3000
+    inp = W.random_inputs(3, 8, N, d, "bf16", seed=2100 + d)
+    scale = 1.0 / math.sqrt(d)
+    say("case lockstep causal", d)
+    o, lse = run_hip(inp, True, scale)
+    compare(inp, o, lse, True, scale, label=f"lockstep causal d={d}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_causal_two_key_groups_odd_tiles(d):
+    """The two-key-group form with an odd number of key tiles per query tile
+    (group 1 idles on the last step), a ragged last query tile and several
+    query tiles per head; every element compared."""
+    N = 1000 if d == 64 else 900
+    inp = W.random_inputs(2, 3, N, d, "bf16", seed=2200 + d)
+    scale = 1.0 / math.sqrt(d)
+    say("case two key groups", d)
+    o, lse = run_hip(inp, True, scale)
+    compare(inp, o, lse, True, scale, label=f"two key groups d={d}")
+
+
+# ---------------------------------------------------------------------------
 # Edge sweep at small sizes: every element compared
 # ---------------------------------------------------------------------------
 
