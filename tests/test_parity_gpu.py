@@ -155,6 +155,32 @@ def test_key_length_mix(dtype, d, causal):
     compare(inp, o, lse, causal, scale, label=f"keylen {dtype} d={d} causal={causal}")
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_key_lengths_longest_first_order(d):
+    """A non-causal batch of at most 8 sequences with key lengths runs its
+    sequences longest first, each followed by its padding tiles: lengths
+    with ties, an empty, a negative and an over-long one, so that the
+    ranking has to be a permutation for every tile to be written once."""
+    import torch
+    import io_aware_exact_forward_amd as fa
+    from parity_util import from_device, to_device
+
+    N = 300
+    key_len = [300, 0, 129, 300, -3, 64, 1000, 129]
+    inp = W.random_inputs(len(key_len), 2, N, d, "bf16", seed=88, key_len=key_len)
+    scale = 1.0 / math.sqrt(d)
+    say("case longest first", d)
+    q, k, v, kl = to_device(inp)
+    # outputs start as NaN, so a tile that no workgroup writes shows up
+    out = torch.full_like(q, float("nan"))
+    lse_t = torch.full(q.shape[:3], float("nan"), dtype=torch.float32, device=q.device)
+    fa.forward(q, k, v, scale=scale, causal=False, key_len=kl, out=out, lse=lse_t)
+    torch.cuda.synchronize()
+    o, lse = from_device(out), lse_t.cpu().numpy().astype(np.float64)
+    check_all_padding(inp, o, lse)
+    compare(inp, o, lse, False, scale, label=f"longest first d={d}")
+
+
 @pytest.mark.parametrize("q_mult", [3.0, 10.0])
 @pytest.mark.parametrize("d", [64, 128])
 def test_peaky_rows(q_mult, d):
