@@ -38,9 +38,10 @@
 //
 // Causal tiles run heaviest first; consecutive workgroups cycle over
 // (batch, head) so all tiles of a head land on one XCD when B*H is a
-// multiple of 8 (workgroups are dealt round-robin to the 8 XCDs).  A
-// non-causal batch with per-sequence key lengths runs its sequences longest
-// first.
+// multiple of 8 (workgroups are dealt round-robin to the 8 XCDs).  With
+// per-sequence key lengths a non-causal batch runs its sequences longest
+// first, and a causal one its query tiles by index, last first, across all
+// sequences.
 #include "fa_bf16_tiles.hpp"
 #include "fa_device.hpp"
 #include "fa_internal.hpp"
@@ -172,6 +173,17 @@ void fa_fwd_bf16_kernel(FwdParams p) {
     sb = __builtin_amdgcn_readfirstlane(sb);
     qt = local / p.H;
     bh = sb * p.H + (local - qt * p.H);
+  } else if (CAUSAL && p.key_len && !p.cu_q && p.splits == 1 && !p.end_aligned) {
+    // Causal batch with per-sequence key lengths: a query tile's work grows
+    // with its index up to its sequence's length, so the grid runs the query
+    // tiles of every (batch, head) from the last to the first, one round
+    // per tile index ((batch, head) fastest; a head keeps one XCD when B*H is
+    // a multiple of 8), which puts the heaviest tiles of every sequence
+    // first instead of those of the first sequences.
+    const int x = (int)blockIdx.x;
+    const int r = x / BH;
+    bh = x - r * BH;
+    qt = p.n_qtiles - 1 - r;
   } else {
     const int per_split = BH * p.n_qtiles;
     split = (int)blockIdx.x / per_split;
