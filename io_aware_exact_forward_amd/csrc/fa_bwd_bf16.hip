@@ -181,7 +181,8 @@ constexpr int kBwdOccupancy = D == 64 ? 2 : 1;
 // a chunk is then the heads of one sequence (equal work), each XCD runs one
 // pair at a time on all its CUs, and up to 32 workgroups share every Q/dO
 // row through the L2 instead of 8 (on the packed 16-sequence backward its
-// fetch fell from 7.4x to 1.6x the compulsory bytes, time unchanged).
+// fetch fell from 7.4x to 1.7x the compulsory bytes; the kernel is bound by
+// its products, and its time moved by 1-2.5 %).
 struct GridPos {
   int pair, tile;
 };
