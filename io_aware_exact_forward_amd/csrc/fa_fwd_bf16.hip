@@ -38,7 +38,10 @@
 //
 // Causal tiles run heaviest first; consecutive workgroups cycle over
 // (batch, head) so all tiles of a head land on one XCD when B*H is a
-// multiple of 8 (workgroups are dealt round-robin to the 8 XCDs).  With
+// multiple of 8 (workgroups are dealt round-robin to the 8 XCDs).  A causal
+// grid of 128-row tiles that fits the device at most twice over splits each
+// tile's keys between two wave groups, and when its pairs of tiles (j,
+// n - 1 - j) fill the device a workgroup takes a whole pair.  With
 // per-sequence key lengths a non-causal batch runs its sequences longest
 // first, and a causal one its query tiles by index, last first, across all
 // sequences.
@@ -93,7 +96,7 @@ struct Bf16Cfg {
 
 
 template <int D, bool CAUSAL, int WAVES, int NSTAGE, bool PINGPONG, bool DROP = false,
-          bool BIAS = false, bool PERSIST = false, int BKX = 0, int KS = 1>
+          bool BIAS = false, bool PERSIST = false, int BKX = 0, int KS = 1, bool PAIR = false>
 // Two lockstep workgroups per CU (256 registers per lane), except with an
 // additive mask at d = 64, whose extra registers do not fit: one workgroup;
 // and three with 64-key tiles at d = 64 (168 registers).
@@ -105,6 +108,7 @@ void fa_fwd_bf16_kernel(FwdParams p) {
   static_assert(!PERSIST || PINGPONG, "the persistent form is the ping-pong schedule's");
   static_assert(KS == 1 || (KS == 2 && WAVES == 8 && !PINGPONG && !DROP && !BIAS),
                 "the key split is a plain lockstep form of eight waves");
+  static_assert(!PAIR || (KS == 2 && CAUSAL), "the paired form is a causal key split");
   using C = Bf16Cfg<D, WAVES, NSTAGE, BKX, KS>;
   __shared__ __attribute__((aligned(1024))) uint8_t lds[C::LDS_BYTES];
 
@@ -140,8 +144,20 @@ void fa_fwd_bf16_kernel(FwdParams p) {
     iqt = (i & 1) ? j : p.n_qtiles - 1 - j;
   };
   int split = 0, bh, qt;
+  int pair_j = 0;  // paired form: the light query tile of this workgroup's pair
   if constexpr (PERSIST) {
     item_of(0, bh, qt);
+  } else if (PAIR) {
+    // Paired form (causal, dense, as many keys as queries): workgroup x
+    // takes query tiles n_qtiles - 1 - j and j of (batch, head) x % BH,
+    // j = x / BH, which together see n_qtiles + 1 tiles' worth of keys
+    // (one tile when the two coincide: the middle tile of an odd count), so
+    // every workgroup has the same work; (batch, head) fastest, so a head
+    // keeps one XCD when BH is a multiple of 8.
+    const int x = (int)blockIdx.x;
+    pair_j = x / BH;
+    bh = x - pair_j * BH;
+    qt = p.n_qtiles - 1 - pair_j;
   } else if (!CAUSAL && p.key_len && !p.cu_q && p.splits == 1 && !p.end_aligned &&
              p.B <= kLptBatches) {
     // Dense batch with per-sequence key lengths, not causal: a query tile of
@@ -248,6 +264,15 @@ void fa_fwd_bf16_kernel(FwdParams p) {
   const int kv_first = split * p.split_keys;
   const int kv_last = min(n_kv, kv_first + p.split_keys);
   int ntiles = kv_last > kv_first ? (kv_last - kv_first + C::BK - 1) / C::BK : 0;
+  // Paired form: the heavy query tile qt has ntiles key tiles, the light
+  // one n_l (none when it is qt itself).  Group 0 takes the heavy tile's
+  // key tiles 0 .. g0 - 1; group 1 the light tile's n_l key tiles, then the
+  // heavy tile's from the last one down to g0: g0 = ceil((ntiles + n_l) / 2)
+  // steps, group 1 idle in the last one when the total is odd.  In the
+  // first n_l steps both groups work on the same keys, so group 1 reads
+  // group 0's half of the stage and its own half is not fetched.
+  const int n_l = PAIR && pair_j != qt ? (min(kv_lim, pair_j * C::BQ + C::BQ) + C::BK - 1) / C::BK : 0;
+  const int g0 = PAIR ? (ntiles + n_l + 1) / 2 : 0;
 
   const uint16_t* __restrict__ qg = (const uint16_t*)p.q + base;
 
@@ -259,18 +284,32 @@ void fa_fwd_bf16_kernel(FwdParams p) {
   int qwpos = qw0 + off;     // key position of the wave's first row
   int qpos = qrow + off;     // key position of this lane's row
 
+  // Paired form: group 1 starts on the light tile's rows (the heavy tile's
+  // are taken over after its last light key tile).
+  const int qw0_heavy = qw0;
+  bool light_pending = PAIR && kgrp == 1 && n_l > 0;
+  if (light_pending) {
+    qw0 = pair_j * C::BQ + 32 * (wave % (WAVES / 2));
+    qrow = qw0 + l32;
+    qwpos = qw0 + off;
+    qpos = qrow + off;
+  }
+
   // ---- Q fragments (B operand of S^T = K Q^T) -----------------------------
   // (the persistent form loads them at the start of each query tile)
   bf16x8 qf[D / 16];
-  if constexpr (!PERSIST) {
+  auto load_q = [&](const int row, bf16x8 (&dst)[D / 16]) __attribute__((always_inline)) {
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
       u32x4 w = {0u, 0u, 0u, 0u};
-      if (qrow < N) w = *(const u32x4*)(qg + (int64_t)qrow * q_ld + 16 * kk + 8 * h);
+      if (row < N) w = *(const u32x4*)(qg + (int64_t)row * q_ld + 16 * kk + 8 * h);
       w ^= p.q_sign;
-      qf[kk] = __builtin_bit_cast(bf16x8, w);
+      dst[kk] = __builtin_bit_cast(bf16x8, w);
     }
-  }
+  };
+  if constexpr (!PERSIST) load_q(qrow, qf);
+  // paired form, group 1: the heavy tile's rows (loaded during the first step)
+  bf16x8 qf_heavy[PAIR ? D / 16 : 1];
 
   // ---- K/V tile loads: HBM -> LDS, range-checked ---------------------------
   // Buffer range = the valid keys of this (batch, head): loads beyond it
@@ -725,17 +764,90 @@ void fa_fwd_bf16_kernel(FwdParams p) {
     // ---- lockstep schedule: every wave runs S, softmax and PV of a tile
     // between two barriers -------------------------------------------------
     // steps: one LDS stage each (KS key tiles, one per key group)
-    const int nsteps = (ntiles + KS - 1) / KS;
+    const int nsteps = PAIR ? g0 : (ntiles + KS - 1) / KS;
+    // Paired form: the first key of group g's tile in step t, and whether
+    // the group has one (its stage half is zero-filled otherwise).
+    auto pair_kv = [&](const int g, const int t) __attribute__((always_inline)) {
+      return (g == 0 || t < n_l ? t : ntiles - 1 - (t - n_l)) * C::BK;
+    };
+    auto pair_has = [&](const int g, const int t) __attribute__((always_inline)) {
+      return t < (g == 0 ? g0 : ntiles + n_l - g0);
+    };
+    // The loads of step t into a stage: KS consecutive tiles, or in the
+    // paired form the two groups' tiles (the first half of each wave's
+    // loads fills group 0's half of the stage).
+    auto load_step = [&](const int t, const int stage) __attribute__((always_inline)) {
+      if constexpr (PAIR) {
+        static_assert(C::LOADS % 2 == 0, "a wave's loads split evenly between the halves");
+        uint8_t* ks = lds + stage * C::STAGE_BYTES;
+        uint8_t* vs = ks + C::TILE_BYTES;
+#pragma unroll
+        for (int i = 0; i < C::LOADS; ++i) {
+          const int g = i < C::LOADS / 2 ? 0 : 1;
+          const int blk = (WAVES * i + wave) * 1024;
+          const bool fetch = g == 0 ? t < g0 : t >= n_l && pair_has(1, t);
+          const uint32_t nb = __builtin_amdgcn_readfirstlane(fetch ? valid_bytes : 0u);
+          // koff/voff hold the row within the stage, which for group 1's
+          // half is BK rows on: the tile start is taken back by BK rows
+          // (modulo 2^32; the per-lane sum is the true offset)
+          const uint32_t toff = __builtin_amdgcn_readfirstlane(
+              (uint32_t)(pair_kv(g, t) - g * C::BK) * row_stride);
+          load_lds_16(kbase, nb, ks + blk, koff[i] + toff);
+          load_lds_16(vbase, nb, vs + blk, voff[i] + toff);
+        }
+      } else {
+        load_tile(kv_first + t * C::SK, stage);
+      }
+    };
+    // Paired form, group 1 after its last light key tile: the light rows
+    // are written out (as in the epilogue below) and the wave takes over
+    // the heavy tile's rows with a fresh state.
+    auto finish_light = [&]() __attribute__((always_inline)) {
+      light_pending = false;
+      const float l_tot = halves_sum(l_run);
+      const float lp_tot = halves_sum(lp_run + lp_run2);
+      const bool valid = qpos < kv_lim && lp_tot > 0.f;
+      const float inv = valid ? 1.f / lp_tot : 0.f;
+      const float lse_row = valid ? (m_ref + __log2f(l_tot)) * kLn2 : kNegInf;
+      if (qrow < N) {
+        uint16_t* og = (uint16_t*)p.o + base + (int64_t)qrow * q_ld;
+#pragma unroll
+        for (int db = 0; db < C::ND; ++db) {
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int d0 = 32 * db + 8 * g + 4 * h;
+            float y[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) y[e] = valid ? o_acc[db][4 * g + e] * inv : 0.f;
+            u32x2 w = {pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
+            *(u32x2*)(og + d0) = w;
+          }
+        }
+        if (h == 0) p.lse[lse_base + (int64_t)qrow * lse_ld] = lse_row;
+      }
+#pragma unroll
+      for (int i = 0; i < C::ND; ++i) o_acc[i] = f32x16{};
+      m_ref = kNegInf;
+      l_run = 0.f;
+      lp_run = 0.f;
+      lp_run2 = 0.f;
+      qw0 = qw0_heavy;
+      qrow = qw0 + l32;
+      qwpos = qw0 + off;
+      qpos = qrow + off;
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk) qf[kk] = qf_heavy[PAIR ? kk : 0];
+    };
 #pragma unroll
     for (int st = 0; st < NSTAGE - 1; ++st)
-      if (st < nsteps) load_tile(kv_first + st * C::SK, st);
+      if (st < nsteps) load_step(st, st);
 
     // One streamed tile, read from LDS stage S (a compile-time constant:
     // the loop below cycles through the NSTAGE instantiations).
     auto step = [&](const int t, auto stage_tag) __attribute__((always_inline)) {
       constexpr int S = decltype(stage_tag)::value;
-      const int kvs = kv_first + t * C::SK;   // first key of the stage
-      const int kv0 = kvs + kgrp * C::BK;     // first key of this group's tile
+      // first key of this group's tile
+      const int kv0 = PAIR ? pair_kv(kgrp, t) : kv_first + t * C::SK + kgrp * C::BK;
       // Tile t has landed once at most the loads of the tiles issued after
       // it are still in flight; after the barrier every wave's part has
       // landed and every wave is done with tile t - 1, whose stage is
@@ -745,9 +857,19 @@ void fa_fwd_bf16_kernel(FwdParams p) {
       else if (later >= 1) vmem_wait<C::LOADS_PER_TILE>();
       else vmem_wait<0>();
       barrier_no_fence();
-      if (t + NSTAGE - 1 < nsteps) load_tile(kvs + (NSTAGE - 1) * C::SK, (S + NSTAGE - 1) % NSTAGE);
-      if (skip_tile(kv0) || (KS == 2 && kv0 >= kv_last)) return;
-      uint32_t kbase = lds0 + S * C::STAGE_BYTES + kgrp * C::BK * C::ROW_BYTES;
+      if (t + NSTAGE - 1 < nsteps) load_step(t + NSTAGE - 1, (S + NSTAGE - 1) % NSTAGE);
+      // group 1's half of the stage (group 0's during the light steps of
+      // the paired form)
+      int half = kgrp;
+      if constexpr (PAIR) {
+        if (t == 0 && light_pending) load_q(qw0_heavy + l32, qf_heavy);
+        if (light_pending && t >= n_l) finish_light();
+        if (!pair_has(kgrp, t) || skip_tile(kv0)) return;
+        if (t < n_l) half = 0;
+      } else {
+        if (skip_tile(kv0) || (KS == 2 && kv0 >= kv_last)) return;
+      }
+      uint32_t kbase = lds0 + S * C::STAGE_BYTES + half * C::BK * C::ROW_BYTES;
       asm volatile("" : "+s"(kbase));  // see the ping-pong schedule
       k_issue(G0, kbase, kr[0]);
       if constexpr (BIAS) bias_issue(kv0);
@@ -766,6 +888,9 @@ void fa_fwd_bf16_kernel(FwdParams p) {
       if constexpr (NSTAGE > 3) {
         if (t + 3 < nsteps) step(t + 3, StageTag<3>{});
       }
+    }
+    if constexpr (PAIR) {
+      if (light_pending) finish_light();  // group 1 had no heavy key tile
     }
     if constexpr (KS == 2) {
       // Key group 1 hands its running state (numerator, reference maximum,
@@ -1124,14 +1249,16 @@ void fa_fwd_bf16_kernel(FwdParams p) {
 }
 
 template <int D, bool CAUSAL, int WAVES, int NSTAGE, bool PINGPONG, bool DROP = false,
-          bool BIAS = false, bool PERSIST = false, int BKX = 0, int KS = 1>
+          bool BIAS = false, bool PERSIST = false, int BKX = 0, int KS = 1, bool PAIR = false>
 hipError_t launch_cfg(FwdParams p, hipStream_t stream) {
   using C = Bf16Cfg<D, WAVES, NSTAGE, BKX, KS>;
   p.n_qtiles = (p.N + C::BQ - 1) / C::BQ;
-  const int64_t items = (int64_t)p.n_qtiles * p.B * p.H * p.splits;
+  // paired form: one workgroup per pair of query tiles
+  const int64_t items = PAIR ? (int64_t)((p.n_qtiles + 1) / 2) * p.B * p.H
+                             : (int64_t)p.n_qtiles * p.B * p.H * p.splits;
   // persistent: items / 2 units, p.persist per workgroup
   const dim3 grid((unsigned)(PERSIST ? items / 2 / p.persist : items));
-  hipLaunchKernelGGL((fa_fwd_bf16_kernel<D, CAUSAL, WAVES, NSTAGE, PINGPONG, DROP, BIAS, PERSIST, BKX, KS>),
+  hipLaunchKernelGGL((fa_fwd_bf16_kernel<D, CAUSAL, WAVES, NSTAGE, PINGPONG, DROP, BIAS, PERSIST, BKX, KS, PAIR>),
                      grid, dim3(64 * WAVES), 0, stream, p);
   return hipGetLastError();
 }
@@ -1203,8 +1330,18 @@ hipError_t launch_d(const FwdParams& p, hipStream_t stream) {
   if constexpr (CAUSAL) {
     const int cus = device_cus();
     if (!p.key_len && !p.cu_q && p.splits == 1 && cus > 0 &&
-        (int64_t)p.B * p.H * ((p.N + 127) / 128) <= 2 * (int64_t)cus)
+        (int64_t)p.B * p.H * ((p.N + 127) / 128) <= 2 * (int64_t)cus) {
+      // When the pairs of query tiles (j, n - 1 - j) fill the device, one
+      // workgroup per pair: each CU then runs one workgroup of equal work
+      // instead of a heavy and a light one in turn, and pays one start and
+      // one drain (about 2 us each) instead of two (32 x 2048 at d = 64:
+      // 32.0 -> 29.8 us; 64 x 1024: 20.9 -> 18.5).  With fewer pairs the
+      // unpaired tiles spread wider (32 x 1024, 128 pairs: 14.5 vs 18.0 us).
+      if (p.Nk == p.N && !p.end_aligned && !p.o_part &&
+          (int64_t)p.B * p.H * (((p.N + 127) / 128 + 1) / 2) >= (int64_t)cus)
+        return launch_cfg<D, CAUSAL, 8, 2, false, false, false, false, 0, 2, true>(p, stream);
       return launch_cfg<D, CAUSAL, 8, 2, false, false, false, false, 0, 2>(p, stream);
+    }
   }
   return launch_cfg<D, CAUSAL, 4, 2, false>(p, stream);
 }

@@ -99,7 +99,8 @@ def test_causal_grid_beyond_one_pass(d):
     """A causal batch whose 128-row grid does not fit the device at once
     (24 heads x 24 tiles = 576 workgroups > two per CU) but is too small for
     the 256-row form: the four-wave lockstep launch.  (Smaller causal grids,
-    such as every case of the edge sweep below, take the two-key-group form.)
+    such as every case of the edge sweep below, take the two-key-group form,
+    paired when the pairs fill the device.)
     Ragged N; every element compared."""
     N = 3000
     inp = W.random_inputs(3, 8, N, d, "bf16", seed=2100 + d)
@@ -120,6 +121,21 @@ def test_causal_two_key_groups_odd_tiles(d):
     say("case two key groups", d)
     o, lse = run_hip(inp, True, scale)
     compare(inp, o, lse, True, scale, label=f"two key groups d={d}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("B,H,N", [(2, 32, 1000), (5, 32, 300), (4, 64, 100)])
+def test_causal_paired_tiles(d, B, H, N):
+    """The paired form: a causal grid of 128-row tiles whose pairs (query tiles
+    j and n - 1 - j of one head) fill the device's 256 compute units.  Even
+    tile count with a middle pair whose second group sees only the light
+    tile (N = 1000), odd count with the middle tile alone and a ragged last
+    tile (N = 300), one tile per head (N = 100); every element compared."""
+    inp = W.random_inputs(B, H, N, d, "bf16", seed=2300 + d + N)
+    scale = 1.0 / math.sqrt(d)
+    say("case paired", B, H, N, d)
+    o, lse = run_hip(inp, True, scale)
+    compare(inp, o, lse, True, scale, label=f"paired {B}x{H}x{N} d={d}")
 
 
 # ---------------------------------------------------------------------------
